@@ -1,0 +1,194 @@
+"""fp64 CPU oracle for the Mesa layer (test infrastructure, not product code).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  It shares no code with the HIP path.
+
+What it computes (MesaNet: "Sequence Modeling by Locally Optimal Test-Time
+Training", technical summary, "Mesa layer" section):
+
+* The layer's map at time t minimises the forget-weighted, Lambda-regularised
+  squared error over the prefix (the section's objective, argmin over Phi of
+  1/2 sum_{t'<=t} zeta_{tt'} ||v_t' - Phi k_t'||^2 + 1/2 Tr(Phi Lambda Phi^T)),
+  and the output is Phi_t q_t.
+* With zeta_{tt'} = beta_t' * prod_{i=t'+1..t} gamma_i (our reading of the
+  "cumulative forget factor"; beta is the per-token write strength), the first
+  order condition gives Phi_t = G_t (H_t + Lambda)^{-1} with
+  H_t = gamma_t H_{t-1} + beta_t k_t k_t^T and G_t = gamma_t G_{t-1} + beta_t v_t k_t^T.
+* The method does not invert: it solves (H_t + Lambda) x_t = q_t by conjugate
+  gradient (same section: the optimal query response is found by CG), with a
+  fixed number of steps or a stopping criterion whose step count varies per
+  token ("dynamic compute" paragraph), and emits o_t = G_t x_t.
+
+This file runs that recurrence token by token with explicit H_t and G_t, and
+solves every system twice: by the CG schedule (the result the GPU path must
+match) and exactly (``numpy.linalg.solve``, the definition).
+
+CG variant (the pages say only "CG"): Hestenes-Stiefel conjugate gradient from
+x_0 = 0 with the recursive residual, as in Saad, "Iterative Methods for Sparse
+Linear Systems", 2nd ed., Algorithm 6.18.  A token stops before an iteration
+when sqrt(rho) <= tol (tol > 0), when rho == 0, or when p.(A p) <= 0; a
+stopped token never restarts.  ``steps`` counts executed alpha updates.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full"]
+
+
+def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
+    """Lambda per head as a full [H, d, d] matrix (accepts a [H, d] diagonal)."""
+    lam = np.asarray(lam, dtype=np.float64)
+    if lam.shape == (H, d):
+        out = np.zeros((H, d, d))
+        idx = np.arange(d)
+        out[:, idx, idx] = lam
+        return out
+    if lam.shape == (H, d, d):
+        return lam.copy()
+    raise ValueError(f"lambda must be [H, d] or [H, d, d], got {lam.shape}")
+
+
+def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
+             forced_steps: np.ndarray | None = None):
+    """Batched conjugate gradient on A[s] x = q[s], fp64.
+
+    A: [S, d, d] symmetric positive definite; q: [S, d].
+    forced_steps: optional [S] ints -- run exactly that many iterations per
+    system (the breakdown guard still applies) instead of the tolerance test.
+    Returns (x [S, d], steps [S] int64).
+    """
+    A = np.asarray(A, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    S = q.shape[0]
+    x = np.zeros_like(q)
+    r = q.copy()
+    p = r.copy()
+    rho = np.einsum("sd,sd->s", r, r)
+    steps = np.zeros(S, dtype=np.int64)
+    stopped = np.zeros(S, dtype=bool)
+    if forced_steps is not None:
+        forced_steps = np.asarray(forced_steps).reshape(S)
+    for it in range(int(max_steps)):
+        if forced_steps is not None:
+            go = it < forced_steps
+        elif tol > 0:
+            go = np.sqrt(rho) > tol
+        else:
+            go = np.ones(S, dtype=bool)
+        go &= ~stopped
+        go &= rho > 0
+        stopped |= ~go
+        if not go.any():
+            break
+        w = np.matmul(A, p[:, :, None])[:, :, 0]
+        pw = np.einsum("sd,sd->s", p, w)
+        ok = pw > 0
+        stopped |= go & ~ok
+        go &= ok
+        alpha = np.where(go, rho / np.where(go, pw, 1.0), 0.0)
+        x += alpha[:, None] * p
+        r -= alpha[:, None] * w
+        rho_new = np.einsum("sd,sd->s", r, r)
+        beta = np.where(go, rho_new / np.where(go, rho, 1.0), 0.0)
+        p = np.where(go[:, None], r + beta[:, None] * p, p)
+        rho = np.where(go, rho_new, rho)
+        steps += go
+    return x, steps
+
+
+def _flat(a, S, *tail):
+    return np.asarray(a, dtype=np.float64).reshape(S, *tail)
+
+
+def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
+                 h0=None, g0=None, forced_steps=None, exact: bool = True,
+                 record_every: int | None = None):
+    """Token-by-token Mesa layer over [B, H, T, d] inputs, fp64.
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv]; gamma, beta: [B, H, T];
+    lam: [H, dk] diagonal or [H, dk, dk] SPD; h0: [B, H, dk, dk]; g0: [B, H, dv, dk].
+    forced_steps: optional [B, H, T] CG step counts (see :func:`cg_solve`).
+    record_every: if given, H and G after every ``record_every``-th token
+    (and after the last token) are returned in ``states``.
+
+    Returns a dict with o_cg, x_cg, steps, H_final, G_final (and o_exact,
+    x_exact when ``exact``), shaped like the inputs.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hh, T, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    S = B * Hh
+    qf = _flat(q, S, T, dk)
+    kf = _flat(k, S, T, dk)
+    vf = _flat(v, S, T, dv)
+    gf = _flat(gamma, S, T)
+    bf = _flat(beta, S, T)
+    Lam = diag_or_full(lam, Hh, dk)
+    Lam = np.broadcast_to(Lam[None], (B, Hh, dk, dk)).reshape(S, dk, dk)
+    Hs = np.zeros((S, dk, dk)) if h0 is None else _flat(h0, S, dk, dk).copy()
+    Gs = np.zeros((S, dv, dk)) if g0 is None else _flat(g0, S, dv, dk).copy()
+    fs = None if forced_steps is None else np.asarray(forced_steps).reshape(S, T)
+
+    o_cg = np.zeros((S, T, dv))
+    x_cg = np.zeros((S, T, dk))
+    steps = np.zeros((S, T), dtype=np.int64)
+    o_ex = np.zeros((S, T, dv)) if exact else None
+    x_ex = np.zeros((S, T, dk)) if exact else None
+    states = []
+    for t in range(T):
+        kt = kf[:, t]
+        g_t = gf[:, t][:, None, None]
+        b_t = bf[:, t][:, None, None]
+        # state update; k_i*k_j is formed first so H stays exactly symmetric
+        Hs = g_t * Hs + b_t * (kt[:, :, None] * kt[:, None, :])
+        Gs = g_t * Gs + b_t * (vf[:, t][:, :, None] * kt[:, None, :])
+        A = Hs + Lam
+        xs, ns = cg_solve(A, qf[:, t], max_steps, tol,
+                          None if fs is None else fs[:, t])
+        x_cg[:, t] = xs
+        steps[:, t] = ns
+        o_cg[:, t] = np.matmul(Gs, xs[:, :, None])[:, :, 0]
+        if exact:
+            xe = np.linalg.solve(A, qf[:, t][:, :, None])[:, :, 0]
+            x_ex[:, t] = xe
+            o_ex[:, t] = np.matmul(Gs, xe[:, :, None])[:, :, 0]
+        if record_every and ((t + 1) % record_every == 0 or t == T - 1):
+            states.append((t + 1, Hs.reshape(B, Hh, dk, dk).copy(),
+                           Gs.reshape(B, Hh, dv, dk).copy()))
+    out = dict(
+        o_cg=o_cg.reshape(B, Hh, T, dv),
+        x_cg=x_cg.reshape(B, Hh, T, dk),
+        steps=steps.reshape(B, Hh, T),
+        H_final=Hs.reshape(B, Hh, dk, dk),
+        G_final=Gs.reshape(B, Hh, dv, dk),
+        states=states,
+    )
+    if exact:
+        out["o_exact"] = o_ex.reshape(B, Hh, T, dv)
+        out["x_exact"] = x_ex.reshape(B, Hh, T, dk)
+    return out
+
+
+def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: float,
+                     forced_steps=None, exact: bool = False):
+    """One recurrent step for N sequences x H heads, fp64.
+
+    q, k: [N, H, dk]; v: [N, H, dv]; gamma, beta: [N, H]; lam: [H, dk] or
+    [H, dk, dk]; h: [N, H, dk, dk]; g: [N, H, dv, dk] (not modified).
+    Returns dict(o, x, steps, h, g[, o_exact]) for the new token.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    N, Hh, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    res = mesa_forward(q[:, :, None], np.asarray(k)[:, :, None], np.asarray(v)[:, :, None],
+                       np.asarray(gamma)[:, :, None], np.asarray(beta)[:, :, None], lam,
+                       max_steps=max_steps, tol=tol, h0=h, g0=g,
+                       forced_steps=None if forced_steps is None
+                       else np.asarray(forced_steps).reshape(N, Hh, 1),
+                       exact=exact)
+    out = dict(o=res["o_cg"][:, :, 0], x=res["x_cg"][:, :, 0], steps=res["steps"][:, :, 0],
+               h=res["H_final"], g=res["G_final"])
+    if exact:
+        out["o_exact"] = res["o_exact"][:, :, 0]
+    return out

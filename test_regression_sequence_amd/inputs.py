@@ -1,0 +1,264 @@
+"""Seeded synthetic inputs for the Mesa layer forward and decode step.
+
+This module only draws random numbers and shapes them.  It performs none of
+the layer's own arithmetic on the values it hands out (no state update, no
+solve, no output), so both the HIP path and the fp64 oracle can consume the
+same draws without sharing any of the method's code.  The one exception is
+documented at :func:`make_decode_inputs`: a pre-filled decode state is a
+weighted Gram matrix of random tokens, which is how such a state is
+distributed; it is an input to the decode step, never a result compared by a
+test.
+
+Workloads (method: MesaNet, "Sequence Modeling by Locally Optimal Test-Time
+Training", technical summary, Mesa layer section):
+
+* q, k ~ N(0, 1), then each token vector L2-normalised (the architecture
+  section normalises queries and keys before the layer);
+* v ~ N(0, 1);
+* gamma_t = sigmoid(u), u ~ U(lo, hi) -- the forget factor of each token;
+* beta_t  ~ U(0, 1) or Beta(a, b) -- the write strength of each token;
+* Lambda  = diag(lambda), either a constant or drawn per (head, dim).
+
+bf16 inputs are produced as: draw in fp64 -> normalise -> cast to fp32 ->
+round to nearest even bf16.  Arrays returned here always hold float32 values;
+for bf16 configurations those values are exactly representable in bf16, and
+``*_bits`` holds the raw uint16 encodings.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
+    "make_decode_inputs", "round_to_bf16", "bf16_bits", "bits_to_f32",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class FwdConfig:
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    chunk: int
+    dtype: str                  # "f32" or "bf16": dtype of q, k, v
+    gamma_logit: tuple          # (lo, hi) of u, gamma = sigmoid(u)
+    beta_dist: tuple            # ("uniform", lo, hi) or ("beta", a, b)
+    lam_dist: tuple             # ("const", c) or ("uniform", lo, hi) per (head, dim)
+    max_steps: int
+    tol: float                  # <= 0: fixed max_steps
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.T
+
+    def replace(self, **kw) -> "FwdConfig":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    N: int                      # sequences
+    H: int
+    d: int
+    prefill: int                # tokens folded into the starting state
+    dtype: str
+    gamma_logit: tuple
+    beta_dist: tuple
+    lam_dist: tuple
+    max_steps: int
+    tol: float
+    seed: int
+
+    def replace(self, **kw) -> "DecodeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+_LM_GATES = dict(gamma_logit=(2.0, 6.0), beta_dist=("uniform", 0.0, 1.0))
+
+CONFIGS = {
+    1: FwdConfig("tiny-f32", B=1, H=1, T=256, d=16, chunk=64, dtype="f32",
+                 lam_dist=("const", 1.0), max_steps=16, tol=1e-6, seed=0, **_LM_GATES),
+    2: FwdConfig("mid-d64-bf16", B=4, H=8, T=2048, d=64, chunk=64, dtype="bf16",
+                 lam_dist=("uniform", 0.25, 1.0), max_steps=15, tol=0.0, seed=1, **_LM_GATES),
+    3: FwdConfig("lm1b-d128-bf16", B=8, H=16, T=4096, d=128, chunk=64, dtype="bf16",
+                 lam_dist=("uniform", 0.25, 1.0), max_steps=30, tol=0.0, seed=2, **_LM_GATES),
+    4: FwdConfig("long-dynamic-d128-bf16", B=1, H=16, T=32768, d=128, chunk=64, dtype="bf16",
+                 gamma_logit=(4.0, 9.0), beta_dist=("beta", 5.0, 1.0),
+                 lam_dist=("const", 0.25), max_steps=64, tol=1e-4, seed=3),
+    5: DecodeConfig("decode-d128", N=256, H=16, d=128, prefill=1024, dtype="bf16",
+                    lam_dist=("uniform", 0.25, 1.0), max_steps=32, tol=1e-4, seed=4,
+                    **_LM_GATES),
+}
+
+
+# ----------------------------------------------------------------------------
+# bf16 helpers (round to nearest, ties to even, on the fp32 bit pattern)
+# ----------------------------------------------------------------------------
+
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """uint16 bf16 encodings of fp32 values, rounded to nearest even."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = u + np.uint32(0x7FFF) + lsb
+    bits = (r >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        bits[nan] = np.uint16(0x7FC0)
+    return bits
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to_bf16(x32: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16, returned as fp32."""
+    return bits_to_f32(bf16_bits(x32))
+
+
+# ----------------------------------------------------------------------------
+# draws
+# ----------------------------------------------------------------------------
+
+def _unit_gauss(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return x
+
+
+def _beta(rng, dist, shape):
+    if dist[0] == "uniform":
+        return rng.uniform(dist[1], dist[2], shape)
+    if dist[0] == "beta":
+        return rng.beta(dist[1], dist[2], shape)
+    raise ValueError(dist)
+
+
+def _lam(rng, dist, H, d):
+    if dist[0] == "const":
+        return np.full((H, d), float(dist[1]))
+    if dist[0] == "uniform":
+        return rng.uniform(dist[1], dist[2], (H, d))
+    raise ValueError(dist)
+
+
+def _finish(x64: np.ndarray, dtype: str):
+    x32 = x64.astype(np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits(x32)
+        return bits_to_f32(bits), bits
+    return x32, None
+
+
+def make_fwd_inputs(cfg: FwdConfig) -> dict:
+    """Inputs of one chunked-forward workload.
+
+    Draw order (one ``numpy.random.default_rng(seed)`` stream): q, k, v, u,
+    beta, lambda.  Shapes: q, k, v ``[B, H, T, d]``; gamma, beta ``[B, H, T]``;
+    lam ``[H, d]`` (the diagonal of Lambda per head).
+    """
+    rng = np.random.default_rng(cfg.seed)
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    q, qb = _finish(_unit_gauss(rng, shp), cfg.dtype)
+    k, kb = _finish(_unit_gauss(rng, shp), cfg.dtype)
+    v, vb = _finish(rng.standard_normal(shp), cfg.dtype)
+    u = rng.uniform(cfg.gamma_logit[0], cfg.gamma_logit[1], shp[:3])
+    gamma = (1.0 / (1.0 + np.exp(-u))).astype(np.float32)
+    beta = _beta(rng, cfg.beta_dist, shp[:3]).astype(np.float32)
+    lam = _lam(rng, cfg.lam_dist, cfg.H, cfg.d).astype(np.float32)
+    out = dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam, cfg=cfg)
+    if cfg.dtype == "bf16":
+        out.update(q_bits=qb, k_bits=kb, v_bits=vb)
+    return out
+
+
+def _prefill_block(seed: int, block: int, P: int, prefill: int, d: int,
+                   gamma_logit, beta_dist, dtype: str):
+    """Random prefix tokens for P (sequence, head) pairs and their state.
+
+    The state is the weighted Gram matrix of the prefix: H = sum_j w_j k_j k_j^T,
+    G = sum_j w_j v_j k_j^T with w_j = beta_j * prod_{i>j} gamma_i, i.e. what a
+    zero state becomes after absorbing the prefix.  It is drawn here as an
+    *input* of the decode step (a structured random SPD matrix), in fp64, then
+    symmetrised and cast to fp32.
+    """
+    rng = np.random.default_rng([seed, 1, block])
+    k, _ = _finish(_unit_gauss(rng, (P, prefill, d)), dtype)
+    v, _ = _finish(rng.standard_normal((P, prefill, d)), dtype)
+    u = rng.uniform(gamma_logit[0], gamma_logit[1], (P, prefill))
+    gamma = (1.0 / (1.0 + np.exp(-u))).astype(np.float32).astype(np.float64)
+    beta = _beta(rng, beta_dist, (P, prefill)).astype(np.float32).astype(np.float64)
+    # survival of token j to the end of the prefix: prod_{i=j+1}^{L-1} gamma_i
+    logg = np.log(gamma)
+    surv = np.exp(np.cumsum(logg[:, ::-1], axis=1)[:, ::-1] - logg)
+    w = beta * surv
+    k64 = k.astype(np.float64)
+    v64 = v.astype(np.float64)
+    kw = k64 * w[:, :, None]
+    Hs = np.matmul(kw.transpose(0, 2, 1), k64)
+    Gs = np.matmul(v64.transpose(0, 2, 1), kw)
+    Hs = 0.5 * (Hs + Hs.transpose(0, 2, 1))
+    return Hs.astype(np.float32), Gs.astype(np.float32)
+
+
+def make_decode_inputs(cfg: DecodeConfig, block: int = 64) -> dict:
+    """Inputs of one recurrent decode step.
+
+    The new token's q, k, v, u, beta and lambda come from
+    ``default_rng(seed)`` in that order; the starting states of the pairs come
+    from independent streams ``default_rng([seed, 1, b])`` per block ``b`` of
+    ``block`` consecutive (sequence, head) pairs, so memory stays bounded.
+    Shapes: q, k, v ``[N, H, d]``; gamma, beta ``[N, H]``; lam ``[H, d]``;
+    h, g ``[N, H, d, d]`` fp32 (row-major, ``g[n][k]`` = value dim n, key dim k).
+    """
+    rng = np.random.default_rng(cfg.seed)
+    shp = (cfg.N, cfg.H, cfg.d)
+    q, qb = _finish(_unit_gauss(rng, shp), cfg.dtype)
+    k, kb = _finish(_unit_gauss(rng, shp), cfg.dtype)
+    v, vb = _finish(rng.standard_normal(shp), cfg.dtype)
+    u = rng.uniform(cfg.gamma_logit[0], cfg.gamma_logit[1], shp[:2])
+    gamma = (1.0 / (1.0 + np.exp(-u))).astype(np.float32)
+    beta = _beta(rng, cfg.beta_dist, shp[:2]).astype(np.float32)
+    lam = _lam(rng, cfg.lam_dist, cfg.H, cfg.d).astype(np.float32)
+    pairs = cfg.N * cfg.H
+    h = np.empty((pairs, cfg.d, cfg.d), np.float32)
+    g = np.empty((pairs, cfg.d, cfg.d), np.float32)
+    if cfg.prefill > 0:
+        for b0 in range(0, pairs, block):
+            P = min(block, pairs - b0)
+            hb, gb = _prefill_block(cfg.seed, b0 // block, P, cfg.prefill, cfg.d,
+                                    cfg.gamma_logit, cfg.beta_dist, cfg.dtype)
+            h[b0:b0 + P] = hb
+            g[b0:b0 + P] = gb
+    else:
+        h[:] = 0
+        g[:] = 0
+    out = dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam,
+               h=h.reshape(cfg.N, cfg.H, cfg.d, cfg.d),
+               g=g.reshape(cfg.N, cfg.H, cfg.d, cfg.d), cfg=cfg)
+    if cfg.dtype == "bf16":
+        out.update(q_bits=qb, k_bits=kb, v_bits=vb)
+    return out
+
+
+def small_fwd(B=1, H=2, T=200, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0,
+              seed=123, lam=("uniform", 0.25, 1.0), gamma_logit=(2.0, 6.0),
+              beta=("uniform", 0.0, 1.0)) -> FwdConfig:
+    """A small workload with the language-model distributions (parity sizes)."""
+    return FwdConfig(f"small-B{B}H{H}T{T}d{d}c{chunk}-{dtype}", B=B, H=H, T=T, d=d,
+                     chunk=chunk, dtype=dtype, gamma_logit=gamma_logit, beta_dist=beta,
+                     lam_dist=lam, max_steps=max_steps, tol=tol, seed=seed)
+
+
+def select_slices(B: int, H: int, count: int, seed: int = 99) -> np.ndarray:
+    """A fixed random subset of (b, h) slice indices (flattened b*H + h)."""
+    rng = np.random.default_rng([seed, B, H])
+    n = min(count, B * H)
+    return np.sort(rng.choice(B * H, size=n, replace=False))

@@ -1,0 +1,123 @@
+"""Plant plausible slips in a private copy of the oracle and check the pins catch them.
+
+Each mutation edits the oracle's source text, loads it as a throwaway module
+(on the CPU; the real oracle is untouched) and runs the independent checks of
+``test_oracle_pins`` against it.  Every mutation must make at least one check
+fail, which shows the pins constrain each part of the oracle's arithmetic.
+"""
+import importlib.util
+import os
+import types
+
+import numpy as np
+import pytest
+
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "mesa_oracle.py")
+
+MUTATIONS = {
+    "no_decay_on_G": ("Gs = g_t * Gs + b_t", "Gs = Gs + b_t"),
+    "no_decay_on_H": ("Hs = g_t * Hs + b_t", "Hs = Hs + b_t"),
+    "no_write_strength_on_H": ("Hs = g_t * Hs + b_t * (", "Hs = g_t * Hs + ("),
+    "G_transposed": ("(vf[:, t][:, :, None] * kt[:, None, :])", "(kt[:, :, None] * vf[:, t][:, None, :])"),
+    "lambda_decayed": ("A = Hs + Lam", "A = Hs + g_t * Lam"),
+    "lambda_dropped": ("A = Hs + Lam", "A = Hs + 1e-3 * Lam"),
+    "solve_before_update": [("kt = kf[:, t]\n", "kt = kf[:, t]\n        Hprev = Hs\n"),
+                            ("A = Hs + Lam", "A = Hprev + Lam")],
+    "residual_sign": ("r -= alpha[:, None] * w", "r += alpha[:, None] * w"),
+    "cg_beta_inverted": ("beta = np.where(go, rho_new / np.where(go, rho, 1.0), 0.0)",
+                         "beta = np.where(go, rho / np.where(go, rho_new, 1.0), 0.0)"),
+    "step_length_wrong": ("alpha = np.where(go, rho / np.where(go, pw, 1.0), 0.0)",
+                          "alpha = np.where(go, 1.0 / np.where(go, pw, 1.0), 0.0)"),
+    "output_reads_query": ("o_cg[:, t] = np.matmul(Gs, xs[:, :, None])[:, :, 0]",
+                           "o_cg[:, t] = np.matmul(Gs, qf[:, t][:, :, None])[:, :, 0]"),
+    "forget_factor_shifted": ("g_t = gf[:, t][:, None, None]",
+                              "g_t = gf[:, max(t - 1, 0)][:, None, None]"),
+    "tolerance_ignored": ("go = np.sqrt(rho) > tol", "go = np.ones(S, dtype=bool)"),
+    "direction_not_updated": ("p = np.where(go[:, None], r + beta[:, None] * p, p)",
+                              "p = np.where(go[:, None], r, p)"),
+}
+
+
+def load_mutant(name):
+    edits = MUTATIONS[name]
+    if isinstance(edits, tuple):
+        edits = [edits]
+    src = open(SRC).read()
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
+        src = src.replace(old, new, 1)
+    mod = types.ModuleType(f"mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def run_pins(m):
+    """Independent checks; return the list of those that fail for module m."""
+    failed = []
+    rng = np.random.default_rng(0)
+    # P1: brute-force objective, diagonal and full Lambda, dk != dv
+    for seed, T, dk, dv, full in [(2, 12, 4, 3, False), (3, 9, 3, 4, True)]:
+        rng = np.random.default_rng(seed)
+        q, k, v, gamma, beta = pins.rand_slice(rng, T, dk, dv)
+        if full:
+            M = rng.standard_normal((dk, dk)); lam = (M @ M.T + 0.5 * np.eye(dk))[None]; Lam = lam[0]
+        else:
+            lam = rng.uniform(0.2, 1.5, (1, dk)); Lam = np.diag(lam[0])
+        ref = pins.brute_force_objective(q[0, 0], k[0, 0], v[0, 0], gamma[0, 0], beta[0, 0], Lam)
+        try:
+            res = m.mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0)
+            if pins.rel(res["o_exact"][0, 0], ref) > 1e-10 or pins.rel(res["o_cg"][0, 0], ref) > 1e-8:
+                failed.append("P1")
+        except Exception:
+            failed.append("P1-crash")
+    # P4: Krylov projections
+    d = 4
+    rng = np.random.default_rng(1)
+    Mi = rng.integers(-3, 4, (d, d))
+    A = (Mi @ Mi.T + np.diag(rng.integers(1, 4, d))).astype(np.int64)
+    qv = np.array([1, -2, 3, 1])
+    from fractions import Fraction
+    Aq = [[Fraction(int(a)) for a in row] for row in A]
+    qq = [Fraction(int(x)) for x in qv]
+    for n in range(1, d + 1):
+        ref = np.array([float(z) for z in pins._krylov_iterate(Aq, qq, n)])
+        x, steps = m.cg_solve(A[None].astype(float), qv[None].astype(float), n, 0.0)
+        if pins.rel(x[0], ref) > 1e-9:
+            failed.append("P4")
+            break
+    # P5: one step == scaled GLA
+    rng = np.random.default_rng(7)
+    T, dk, dv = 10, 5, 4
+    q, k, v, gamma, beta = pins.rand_slice(rng, T, dk, dv)
+    lam = rng.uniform(0.3, 1.0, (1, dk))
+    try:
+        res = m.mesa_forward(q, k, v, gamma, beta, lam, max_steps=1, tol=0.0, exact=False)
+        g, b = gamma[0, 0], beta[0, 0]
+        for t in range(T):
+            qt = q[0, 0, t]
+            sc = [pins.zeta(g, b, t, j) * float(k[0, 0, j] @ qt) for j in range(t + 1)]
+            quad = float(qt @ (lam[0] * qt)) + sum(s * float(k[0, 0, j] @ qt) for j, s in enumerate(sc))
+            ref = float(qt @ qt) / quad * sum(s * v[0, 0, j] for j, s in enumerate(sc))
+            if pins.rel(res["o_cg"][0, 0, t], ref) > 1e-12:
+                failed.append("P5")
+                break
+    except Exception:
+        failed.append("P5-crash")
+    # P7: tolerance stops before an iteration
+    x, n = m.cg_solve(np.eye(3)[None] * 2.0, np.array([[1e-7, 0.0, 0.0]]), 10, 1e-6)
+    if n[0] != 0:
+        failed.append("P7")
+    return failed
+
+
+def test_unmutated_oracle_passes_all():
+    import oracle.mesa_oracle as real
+    assert run_pins(real) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    assert run_pins(load_mutant(name)), f"mutation {name} slipped past every pin"

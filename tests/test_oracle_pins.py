@@ -1,0 +1,349 @@
+"""Pins of the fp64 oracle against facts that do not depend on its own code.
+
+Every check here derives its expected value from the mathematics of the Mesa
+layer's objective (MesaNet page, technical summary, "Mesa layer" section) by a
+route that shares nothing with ``oracle/mesa_oracle.py``: a brute-force
+least-squares fit of the objective, a library ridge regression, exact rational
+Krylov projections, closed forms of one CG step and of the first token, and
+exact invariances.  A plausible slip in the oracle (a dropped decay, a wrong
+sign, a transposed state, a mis-indexed forget factor) fails at least one of
+them; ``test_oracle_mutations.py`` plants such slips and checks that.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import cg_solve, mesa_forward, mesa_decode_step
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------------------
+# independent references
+# ---------------------------------------------------------------------------
+
+def zeta(gamma, beta, t, tp):
+    """Forget weight of token tp seen at time t: beta_tp * prod_{i=tp+1..t} gamma_i."""
+    w = float(beta[tp])
+    for i in range(tp + 1, t + 1):
+        w *= float(gamma[i])
+    return w
+
+
+def brute_force_objective(q, k, v, gamma, beta, Lam):
+    """Minimise the layer's objective directly, one output row at a time.
+
+    For each t and output row i: min_phi sum_{t'<=t} zeta_{tt'} (v_{t'i} - phi.k_{t'})^2
+    + phi^T Lambda phi, solved as an ordinary least-squares problem on the
+    stacked system [sqrt(zeta) K ; L^T] phi = [sqrt(zeta) v_i ; 0] with
+    Lambda = L L^T.  Single (b, h) slice: q, k [T, dk]; v [T, dv].
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    Lt = np.linalg.cholesky(Lam).T
+    out = np.zeros((T, dv))
+    for t in range(T):
+        z = np.array([zeta(gamma, beta, t, tp) for tp in range(t + 1)])
+        sz = np.sqrt(z)[:, None]
+        Asys = np.vstack([sz * k[: t + 1], Lt])
+        Phi = np.zeros((dv, dk))
+        for i in range(dv):
+            rhs = np.concatenate([sz[:, 0] * v[: t + 1, i], np.zeros(dk)])
+            Phi[i] = np.linalg.lstsq(Asys, rhs, rcond=None)[0]
+        out[t] = Phi @ q[t]
+    return out
+
+
+def rand_slice(rng, T, dk, dv, gamma_lo=0.5):
+    q = rng.standard_normal((1, 1, T, dk))
+    k = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    gamma = rng.uniform(gamma_lo, 1.0, (1, 1, T))
+    beta = rng.uniform(0.05, 1.0, (1, 1, T))
+    return q, k, v, gamma, beta
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (den if den > 0 else 1.0)
+
+
+# ---------------------------------------------------------------------------
+# P1: the exact solution is the minimiser of the objective
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,T,dk,dv,full_lam", [
+    (0, 8, 2, 2, False), (1, 10, 3, 2, False), (2, 12, 4, 3, False),
+    (3, 9, 3, 4, True), (4, 12, 4, 4, True),
+])
+def test_p1_exact_solution_minimises_objective(seed, T, dk, dv, full_lam):
+    rng = np.random.default_rng(seed)
+    q, k, v, gamma, beta = rand_slice(rng, T, dk, dv)
+    if full_lam:
+        M = rng.standard_normal((dk, dk))
+        lam = (M @ M.T + 0.5 * np.eye(dk))[None]
+        Lam = lam[0]
+    else:
+        lam = rng.uniform(0.2, 1.5, (1, dk))
+        Lam = np.diag(lam[0])
+    ref = brute_force_objective(q[0, 0], k[0, 0], v[0, 0], gamma[0, 0], beta[0, 0], Lam)
+    res = mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0)
+    assert rel(res["o_exact"][0, 0], ref) < 1e-10
+    # dk CG steps reach the exact solve (finite termination, P3) on these tiny systems
+    assert rel(res["o_cg"][0, 0], ref) < 1e-8
+
+
+@pytest.mark.parametrize("alpha", [0.3, 2.0])
+def test_p1_no_forgetting_is_prefix_ridge_regression(alpha):
+    """gamma = beta = 1, Lambda = alpha I: every prefix is a plain ridge fit."""
+    from sklearn.linear_model import Ridge
+    rng = np.random.default_rng(11)
+    T, dk, dv = 10, 4, 3
+    q = rng.standard_normal((1, 1, T, dk))
+    k = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    ones = np.ones((1, 1, T))
+    res = mesa_forward(q, k, v, ones, ones, np.full((1, dk), alpha), max_steps=dk, tol=0.0)
+    for t in range(T):
+        model = Ridge(alpha=alpha, fit_intercept=False, solver="svd")
+        model.fit(k[0, 0, : t + 1], v[0, 0, : t + 1])
+        ref = model.coef_ @ q[0, 0, t]
+        assert rel(res["o_exact"][0, 0, t], ref) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# P2: H_t is symmetric, H_t + Lambda is SPD with the stated spectrum bounds
+# ---------------------------------------------------------------------------
+
+def test_p2_state_symmetric_spd_with_bounds():
+    rng = np.random.default_rng(5)
+    T, d = 40, 6
+    q, k, v, gamma, beta = rand_slice(rng, T, d, d, gamma_lo=0.7)
+    lam = rng.uniform(0.25, 1.0, (1, d))
+    res = mesa_forward(q, k, v, gamma, beta, lam, max_steps=3, tol=0.0, record_every=1)
+    for (t1, Hs, _Gs) in res["states"]:
+        Ht = Hs[0, 0]
+        assert np.array_equal(Ht, Ht.T)
+        t = t1 - 1
+        ev = np.linalg.eigvalsh(Ht + np.diag(lam[0]))
+        upper = lam.max() + sum(zeta(gamma[0, 0], beta[0, 0], t, j) * float(k[0, 0, j] @ k[0, 0, j])
+                                for j in range(t + 1))
+        assert ev.min() >= lam.min() * (1 - 1e-12)
+        assert ev.max() <= upper * (1 + 1e-12)
+        # H_t = sum_j zeta_tj k_j k_j^T, assembled without the recurrence
+        direct = sum(zeta(gamma[0, 0], beta[0, 0], t, j) * np.outer(k[0, 0, j], k[0, 0, j])
+                     for j in range(t + 1))
+        assert rel(Ht, direct) < 1e-12
+
+
+def test_p2_cross_state_orientation():
+    """G_t = sum_j zeta_tj v_j k_j^T with rows indexed by the value dimension."""
+    rng = np.random.default_rng(6)
+    T, dk, dv = 7, 3, 5
+    q, k, v, gamma, beta = rand_slice(rng, T, dk, dv)
+    res = mesa_forward(q, k, v, gamma, beta, np.ones((1, dk)), max_steps=1, tol=0.0)
+    direct = sum(zeta(gamma[0, 0], beta[0, 0], T - 1, j) * np.outer(v[0, 0, j], k[0, 0, j])
+                 for j in range(T))
+    assert res["G_final"].shape == (1, 1, dv, dk)
+    assert rel(res["G_final"][0, 0], direct) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P3: finite termination on the configurations' own distributions
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [16, 32])
+def test_p3_d_steps_equal_exact_solve(d):
+    from test_regression_sequence_amd.inputs import small_fwd, make_fwd_inputs
+    cfg = small_fwd(B=1, H=2, T=48, d=d, chunk=16, dtype="f32", max_steps=d)
+    x = make_fwd_inputs(cfg)
+    res = mesa_forward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"],
+                       max_steps=d, tol=0.0)
+    assert rel(res["o_cg"], res["o_exact"]) < 1e-10
+    assert rel(res["x_cg"], res["x_exact"]) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# P4: n-step CG is the A-norm projection onto the Krylov space (exact rationals)
+# ---------------------------------------------------------------------------
+
+def _frac_solve(M, b):
+    n = len(M)
+    A = [[Fraction(x) for x in row] + [Fraction(bb)] for row, bb in zip(M, b)]
+    for c in range(n):
+        piv = next(r for r in range(c, n) if A[r][c] != 0)
+        A[c], A[piv] = A[piv], A[c]
+        for r in range(n):
+            if r != c and A[r][c] != 0:
+                f = A[r][c] / A[c][c]
+                A[r] = [a - f * bcol for a, bcol in zip(A[r], A[c])]
+    return [A[i][n] / A[i][i] for i in range(n)]
+
+
+def _krylov_iterate(A, q, n):
+    """x_n = V (V^T A V)^{-1} V^T q, V = [q, Aq, ..., A^{n-1} q], exactly."""
+    d = len(q)
+    matvec = lambda x: [sum(A[i][j] * x[j] for j in range(d)) for i in range(d)]
+    V = [list(q)]
+    for _ in range(n - 1):
+        V.append(matvec(V[-1]))
+    AV = [matvec(vv) for vv in V]
+    M = [[sum(V[a][i] * AV[b][i] for i in range(d)) for b in range(n)] for a in range(n)]
+    rhs = [sum(V[a][i] * q[i] for i in range(d)) for a in range(n)]
+    c = _frac_solve(M, rhs)
+    return [sum(c[a] * V[a][i] for a in range(n)) for i in range(d)]
+
+
+@pytest.mark.parametrize("seed,d", [(0, 3), (1, 4), (2, 5), (3, 6)])
+def test_p4_cg_iterates_are_krylov_projections(seed, d):
+    rng = np.random.default_rng(seed)
+    Mi = rng.integers(-3, 4, (d, d))
+    A = (Mi @ Mi.T + np.diag(rng.integers(1, 4, d))).astype(np.int64)
+    q = rng.integers(-4, 5, d).astype(np.int64)
+    q[0] = q[0] if q[0] != 0 else 1
+    Aq = [[Fraction(int(a)) for a in row] for row in A]
+    qq = [Fraction(int(x)) for x in q]
+    for n in range(1, d + 1):
+        ref = np.array([float(z) for z in _krylov_iterate(Aq, qq, n)])
+        x, steps = cg_solve(A[None].astype(float), q[None].astype(float), n, 0.0)
+        assert steps[0] == n
+        assert rel(x[0], ref) < 1e-9, (n, x[0], ref)
+
+
+# ---------------------------------------------------------------------------
+# P5: one CG step is a normalised gated-linear-attention read-out
+# ---------------------------------------------------------------------------
+
+def test_p5_one_step_is_scaled_gla():
+    rng = np.random.default_rng(7)
+    T, dk, dv = 20, 5, 4
+    q, k, v, gamma, beta = rand_slice(rng, T, dk, dv)
+    lam = rng.uniform(0.3, 1.0, (1, dk))
+    res = mesa_forward(q, k, v, gamma, beta, lam, max_steps=1, tol=0.0, exact=False)
+    g, b = gamma[0, 0], beta[0, 0]
+    for t in range(T):
+        qt = q[0, 0, t]
+        scores = [zeta(g, b, t, j) * float(k[0, 0, j] @ qt) for j in range(t + 1)]
+        quad = float(qt @ (lam[0] * qt)) + sum(zeta(g, b, t, j) * float(k[0, 0, j] @ qt) ** 2
+                                              for j in range(t + 1))
+        alpha = float(qt @ qt) / quad
+        ref = alpha * sum(s * v[0, 0, j] for j, s in enumerate(scores))
+        assert rel(res["o_cg"][0, 0, t], ref) < 1e-12
+        assert res["steps"][0, 0, t] == 1
+
+
+# ---------------------------------------------------------------------------
+# P6: first token, closed form (Sherman-Morrison)
+# ---------------------------------------------------------------------------
+
+def test_p6_first_token_sherman_morrison():
+    rng = np.random.default_rng(8)
+    dk, dv = 6, 5
+    q, k, v, gamma, beta = rand_slice(rng, 1, dk, dv)
+    lam = rng.uniform(0.3, 1.2, (1, dk))
+    res = mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0)
+    kk, qq, vv, bb = k[0, 0, 0], q[0, 0, 0], v[0, 0, 0], beta[0, 0, 0]
+    li = 1.0 / lam[0]
+    ref = bb * vv * float(kk @ (li * qq)) / (1.0 + bb * float(kk @ (li * kk)))
+    assert rel(res["o_exact"][0, 0, 0], ref) < 1e-12
+    assert rel(res["o_cg"][0, 0, 0], ref) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# P7: special cases
+# ---------------------------------------------------------------------------
+
+def test_p7_zero_steps_gives_zero_output():
+    rng = np.random.default_rng(9)
+    q, k, v, gamma, beta = rand_slice(rng, 6, 4, 4)
+    res = mesa_forward(q, k, v, gamma, beta, np.ones((1, 4)), max_steps=0, tol=0.0)
+    assert np.all(res["o_cg"] == 0) and np.all(res["steps"] == 0)
+
+
+def test_p7_no_writes_gives_zero_output_and_one_step_solve():
+    rng = np.random.default_rng(10)
+    q, k, v, gamma, _ = rand_slice(rng, 6, 4, 3)
+    beta = np.zeros_like(gamma)
+    for tol in (0.0, 1e-6):
+        res = mesa_forward(q, k, v, gamma, beta, np.full((1, 4), 0.5), max_steps=5, tol=tol)
+        assert np.all(res["o_cg"] == 0)
+        # H = 0, Lambda = 0.5 I: one step lands on q / 0.5, then rho == 0 stops CG
+        assert np.allclose(res["x_cg"], q / 0.5, rtol=1e-15, atol=0)
+        assert np.all(res["steps"] == 1)
+
+
+def test_p7_tolerance_stops_before_iteration():
+    """A residual already at or under tol runs zero iterations."""
+    A = np.eye(3)[None] * 2.0
+    qv = np.array([[1e-7, 0.0, 0.0]])
+    x, n = cg_solve(A, qv, 10, 1e-6)
+    assert n[0] == 0 and np.all(x == 0)
+    x, n = cg_solve(A, qv * 100, 10, 1e-6)
+    assert n[0] == 1 and np.allclose(x, qv * 50)
+
+
+# ---------------------------------------------------------------------------
+# P8: invariances
+# ---------------------------------------------------------------------------
+
+def test_p8_joint_scaling_of_beta_lambda_states():
+    rng = np.random.default_rng(12)
+    T, d = 16, 5
+    q, k, v, gamma, beta = rand_slice(rng, T, d, d)
+    lam = rng.uniform(0.25, 1.0, (1, d))
+    h0 = rng.standard_normal((1, 1, d, d)); h0 = h0 @ h0.transpose(0, 1, 3, 2)
+    g0 = rng.standard_normal((1, 1, d, d))
+    c = 4.0
+    for tol in (0.0, 1e-3):
+        a = mesa_forward(q, k, v, gamma, beta, lam, h0=h0, g0=g0, max_steps=4, tol=tol, exact=False)
+        b = mesa_forward(q, k, v, gamma, c * beta, c * lam, h0=c * h0, g0=c * g0,
+                         max_steps=4, tol=tol, exact=False)
+        assert np.array_equal(a["steps"], b["steps"])
+        assert rel(b["o_cg"], a["o_cg"]) < 1e-14
+        assert rel(c * b["x_cg"], a["x_cg"]) < 1e-14
+
+
+def test_p8_linear_in_values():
+    rng = np.random.default_rng(13)
+    q, k, v, gamma, beta = rand_slice(rng, 12, 4, 4)
+    lam = np.full((1, 4), 0.7)
+    a = mesa_forward(q, k, v, gamma, beta, lam, max_steps=3, tol=0.0, exact=False)
+    b = mesa_forward(q, k, -2.0 * v, gamma, beta, lam, max_steps=3, tol=0.0, exact=False)
+    assert rel(b["o_cg"], -2.0 * a["o_cg"]) < 1e-14
+
+
+def test_p8_energy_error_monotone():
+    rng = np.random.default_rng(14)
+    d = 12
+    M = rng.standard_normal((d, d))
+    A = M @ M.T / d + 0.5 * np.eye(d)
+    qv = rng.standard_normal(d)
+    xs = np.linalg.solve(A, qv)
+    errs = []
+    for n in range(d + 1):
+        x, _ = cg_solve(A[None], qv[None], n, 0.0)
+        e = x[0] - xs
+        errs.append(float(e @ A @ e))
+    assert all(errs[i + 1] <= errs[i] * (1 + 1e-9) + 1e-28 for i in range(d))
+    assert errs[-1] < 1e-20 * errs[0]
+
+
+# ---------------------------------------------------------------------------
+# decode step == one more token of the forward recurrence
+# ---------------------------------------------------------------------------
+
+def test_decode_step_continues_forward():
+    rng = np.random.default_rng(15)
+    T, d = 9, 4
+    q, k, v, gamma, beta = rand_slice(rng, T + 1, d, d)
+    lam = rng.uniform(0.25, 1.0, (1, d))
+    full = mesa_forward(q, k, v, gamma, beta, lam, max_steps=3, tol=0.0)
+    pre = mesa_forward(q[:, :, :T], k[:, :, :T], v[:, :, :T], gamma[:, :, :T], beta[:, :, :T],
+                       lam, max_steps=3, tol=0.0)
+    dec = mesa_decode_step(q[:, :, T], k[:, :, T], v[:, :, T], gamma[:, :, T], beta[:, :, T], lam,
+                           pre["H_final"], pre["G_final"], max_steps=3, tol=0.0)
+    assert rel(dec["o"], full["o_cg"][:, :, T]) < 1e-13
+    assert rel(dec["h"], full["H_final"]) < 1e-14
