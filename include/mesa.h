@@ -1,0 +1,146 @@
+/*
+ * libmesa -- forward pass of the Mesa layer on one AMD MI355X (gfx950).
+ *
+ * Method: MesaNet, "Sequence Modeling by Locally Optimal Test-Time Training"
+ * (technical summary, "Mesa layer" section).  For every token t the layer
+ * keeps two decayed states,
+ *
+ *     H_t = gamma_t H_{t-1} + beta_t k_t k_t^T        (dk x dk, symmetric)
+ *     G_t = gamma_t G_{t-1} + beta_t v_t k_t^T        (dv x dk)
+ *
+ * solves (H_t + Lambda) x_t = q_t by conjugate gradient and emits
+ * o_t = G_t x_t.  This is the closed-form optimum of the section's
+ * forget-weighted, Lambda-regularised least-squares objective with cumulative
+ * forget factor zeta_{tt'} = beta_t' prod_{i=t'+1..t} gamma_i, reached
+ * approximately by CG as the section prescribes; the number of CG steps is
+ * either fixed or set per token by a residual test (the section's "dynamic
+ * compute" paragraph).  Chunkwise-parallel evaluation over the sequence
+ * (same section, "parallelisation") gives mesa_fwd_chunked; the O(1)
+ * recurrent form gives mesa_decode_step.
+ *
+ * CG: Hestenes-Stiefel from x_0 = 0 with the recursive residual r.  Before
+ * each iteration a token stops if max_steps iterations are done, if
+ * tol > 0 and ||r||_2 <= tol, or if r.r == 0; it also stops (without
+ * updating) if p.(A p) <= 0.  A stopped token never restarts.  steps[t] is
+ * the number of executed updates.  tol <= 0 selects the fixed-step mode.
+ *
+ * Conventions common to every call
+ *   - All tensor pointers are device pointers owned by the caller.  The
+ *     library never allocates or frees device memory; scratch memory comes in
+ *     through `workspace`.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and holds
+ *     no global mutable state, so calls on different streams may overlap as
+ *     long as they do not write the same buffers.
+ *   - All arguments are validated before anything is launched.  On any error
+ *     the call returns a non-zero status, launches nothing and writes nothing.
+ *     Launch failures reported by the runtime return MESA_ERR_HIP.
+ *   - Numeric preconditions are documented, not checked: 0 < gamma <= 1,
+ *     beta >= 0, lambda > 0, finite inputs, symmetric h0 / h_state.
+ *   - Tensors are dense and row-major with the last index fastest.  States are
+ *     [.., dk, dk] for H and [.., dv, dk] for G (row = value dimension).
+ *   - Supported sizes: dk == dv; dk in {16, 32, 64, 128} for MESA_F32 inputs
+ *     and dk in {32, 64, 128} for MESA_BF16 inputs; chunk in {16, 32, 64};
+ *     any T >= 0 (a last, shorter chunk is handled); B, H >= 1.
+ *   - Pointers must be 16-byte aligned.
+ */
+#ifndef MESA_H_
+#define MESA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MESA_ABI_VERSION 1
+
+typedef enum {
+  MESA_OK = 0,
+  MESA_ERR_INVALID_ARG = 1,  /* null required pointer, negative size, ...        */
+  MESA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (d, chunk, dk != dv)  */
+  MESA_ERR_ALIGNMENT = 3,    /* a pointer is not 16-byte aligned                 */
+  MESA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required       */
+  MESA_ERR_HIP = 5           /* the HIP runtime reported an error                */
+} mesa_status;
+
+typedef enum {
+  MESA_F32 = 0,   /* q, k, v are float32; states and arithmetic are fp32          */
+  MESA_BF16 = 1   /* q, k, v are bfloat16; MFMA in bf16 with fp32 accumulation,
+                     CG vectors, scalars and carried states in fp32             */
+} mesa_dtype;
+
+typedef struct {
+  int32_t B, H, T;      /* batch, heads, tokens per sequence                       */
+  int32_t dk, dv;       /* key / value head dims (dk == dv)                        */
+  int32_t chunk;        /* tokens per chunk of the parallel form                   */
+  int32_t max_steps;    /* CG iteration cap, >= 0                                  */
+  float tol;            /* residual tolerance; <= 0 runs exactly max_steps         */
+  mesa_dtype in_dtype;  /* dtype of q, k, v                                        */
+} mesa_fwd_desc;
+
+/* Bytes of scratch memory mesa_fwd_chunked needs for `d` (the decayed
+ * chunk-boundary states).  Returns 0 for an invalid or unsupported
+ * descriptor, and for T == 0. */
+size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d);
+
+/* Chunkwise-parallel Mesa forward over whole sequences
+ * (MesaNet page, technical summary, "Mesa layer": objective, CG query
+ * response, chunk-parallel states, dynamic CG step count).
+ *
+ *   q, k   [B, H, T, dk]  in_dtype        queries / keys
+ *   v      [B, H, T, dv]  in_dtype        values
+ *   gamma  [B, H, T]      fp32            forget factor of each token
+ *   beta   [B, H, T]      fp32            write strength of each token
+ *   lambda [H, dk]        fp32            diagonal of Lambda per head (> 0)
+ *   h0     [B, H, dk, dk] fp32 or NULL    state before token 0 (NULL = 0)
+ *   g0     [B, H, dv, dk] fp32 or NULL
+ *   o      [B, H, T, dv]  fp32            out: o_t = G_t x_t
+ *   h_final, g_final      fp32 or NULL    out: states after token T-1
+ *   steps  [B, H, T]      int32 or NULL   out: CG iterations per token
+ *   x_out  [B, H, T, dk]  fp32 or NULL    out: the CG solution x_t
+ *   workspace             device memory of at least
+ *                         mesa_fwd_workspace_bytes(d) bytes (may be NULL
+ *                         when that is 0)
+ *
+ * h_final / g_final of one call are valid h0 / g0 of the next call on the
+ * continuation of the sequence, and valid decode states. */
+mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
+                             const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0,
+                             float* o, float* h_final, float* g_final,
+                             int32_t* steps, float* x_out,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* One recurrent step for N sequences x H heads, states updated in place
+ * (MesaNet page, technical summary, "Mesa layer": O(1) inference form).
+ *
+ *   q, k    [N, H, dk]  in_dtype; v [N, H, dv] in_dtype
+ *   gamma, beta [N, H]  fp32
+ *   lambda  [H, dk]     fp32
+ *   h_state [N, H, dk, dk] fp32, in/out: H_{t-1} -> H_t
+ *   g_state [N, H, dv, dk] fp32, in/out: G_{t-1} -> G_t
+ *   o       [N, H, dv]  fp32 out
+ *   steps   [N, H]      int32 out or NULL
+ *   x_out   [N, H, dk]  fp32 out or NULL
+ * Supported: dk == dv == 128 or 64, either in_dtype. */
+mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                             const void* q, const void* k, const void* v, mesa_dtype in_dtype,
+                             const float* gamma, const float* beta, const float* lambda,
+                             float* h_state, float* g_state,
+                             float* o, int32_t* steps, float* x_out,
+                             int32_t max_steps, float tol, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* mesa_status_string(mesa_status s);
+
+/* MESA_ABI_VERSION of the built library. */
+int32_t mesa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MESA_H_ */

@@ -50,13 +50,15 @@ def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
 
 
 def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
-             forced_steps: np.ndarray | None = None):
+             forced_steps: np.ndarray | None = None, residuals: bool = False):
     """Batched conjugate gradient on A[s] x = q[s], fp64.
 
     A: [S, d, d] symmetric positive definite; q: [S, d].
     forced_steps: optional [S] ints -- run exactly that many iterations per
     system (the breakdown guard still applies) instead of the tolerance test.
-    Returns (x [S, d], steps [S] int64).
+    Returns (x [S, d], steps [S] int64); with ``residuals=True`` also the
+    recursive residual norms ||r|| after the last executed iteration and
+    before it (equal to ||q|| for systems that ran no iteration).
     """
     A = np.asarray(A, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
@@ -65,6 +67,7 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
     r = q.copy()
     p = r.copy()
     rho = np.einsum("sd,sd->s", r, r)
+    rho_prev = rho.copy()
     steps = np.zeros(S, dtype=np.int64)
     stopped = np.zeros(S, dtype=bool)
     if forced_steps is not None:
@@ -92,8 +95,11 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
         rho_new = np.einsum("sd,sd->s", r, r)
         beta = np.where(go, rho_new / np.where(go, rho, 1.0), 0.0)
         p = np.where(go[:, None], r + beta[:, None] * p, p)
+        rho_prev = np.where(go, rho, rho_prev)
         rho = np.where(go, rho_new, rho)
         steps += go
+    if residuals:
+        return x, steps, np.sqrt(rho), np.sqrt(rho_prev)
     return x, steps
 
 
@@ -103,7 +109,7 @@ def _flat(a, S, *tail):
 
 def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                  h0=None, g0=None, forced_steps=None, exact: bool = True,
-                 record_every: int | None = None):
+                 record_every: int | None = None, solve_at=None):
     """Token-by-token Mesa layer over [B, H, T, d] inputs, fp64.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv]; gamma, beta: [B, H, T];
@@ -111,6 +117,9 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     forced_steps: optional [B, H, T] CG step counts (see :func:`cg_solve`).
     record_every: if given, H and G after every ``record_every``-th token
     (and after the last token) are returned in ``states``.
+    solve_at: optional [T] bool -- solve and emit outputs only at these token
+    positions (the state recurrence still runs over every token); outputs at
+    other positions are left at zero.  Used to sample long sequences.
 
     Returns a dict with o_cg, x_cg, steps, H_final, G_final (and o_exact,
     x_exact when ``exact``), shaped like the inputs.
@@ -133,6 +142,8 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     o_cg = np.zeros((S, T, dv))
     x_cg = np.zeros((S, T, dk))
     steps = np.zeros((S, T), dtype=np.int64)
+    res_norm = np.zeros((S, T))
+    res_prev = np.zeros((S, T))
     o_ex = np.zeros((S, T, dv)) if exact else None
     x_ex = np.zeros((S, T, dk)) if exact else None
     states = []
@@ -143,11 +154,18 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
         # state update; k_i*k_j is formed first so H stays exactly symmetric
         Hs = g_t * Hs + b_t * (kt[:, :, None] * kt[:, None, :])
         Gs = g_t * Gs + b_t * (vf[:, t][:, :, None] * kt[:, None, :])
+        if solve_at is not None and not solve_at[t]:
+            if record_every and ((t + 1) % record_every == 0 or t == T - 1):
+                states.append((t + 1, Hs.reshape(B, Hh, dk, dk).copy(),
+                               Gs.reshape(B, Hh, dv, dk).copy()))
+            continue
         A = Hs + Lam
-        xs, ns = cg_solve(A, qf[:, t], max_steps, tol,
-                          None if fs is None else fs[:, t])
+        xs, ns, rn, rp = cg_solve(A, qf[:, t], max_steps, tol,
+                                  None if fs is None else fs[:, t], residuals=True)
         x_cg[:, t] = xs
         steps[:, t] = ns
+        res_norm[:, t] = rn
+        res_prev[:, t] = rp
         o_cg[:, t] = np.matmul(Gs, xs[:, :, None])[:, :, 0]
         if exact:
             xe = np.linalg.solve(A, qf[:, t][:, :, None])[:, :, 0]
@@ -160,6 +178,8 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
         o_cg=o_cg.reshape(B, Hh, T, dv),
         x_cg=x_cg.reshape(B, Hh, T, dk),
         steps=steps.reshape(B, Hh, T),
+        res_norm=res_norm.reshape(B, Hh, T),
+        res_prev=res_prev.reshape(B, Hh, T),
         H_final=Hs.reshape(B, Hh, dk, dk),
         G_final=Gs.reshape(B, Hh, dv, dk),
         states=states,
@@ -188,6 +208,7 @@ def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: fl
                        else np.asarray(forced_steps).reshape(N, Hh, 1),
                        exact=exact)
     out = dict(o=res["o_cg"][:, :, 0], x=res["x_cg"][:, :, 0], steps=res["steps"][:, :, 0],
+               res_norm=res["res_norm"][:, :, 0], res_prev=res["res_prev"][:, :, 0],
                h=res["H_final"], g=res["G_final"])
     if exact:
         out["o_exact"] = res["o_exact"][:, :, 0]

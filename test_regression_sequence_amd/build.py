@@ -1,0 +1,71 @@
+"""Build libmesa.so (HIP for gfx950) in-tree with hipcc.
+
+    python -m test_regression_sequence_amd.build
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libmesa.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU ops are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every csrc/*.hip into libmesa.so (always recompiles)."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-shared"], "-c", *inc, src, "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        if len(procs) >= jobs:
+            _drain(procs, verbose)
+    _drain(procs, verbose)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if out.returncode != 0:
+        raise RuntimeError(f"link failed:\n{out.stdout}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _drain(procs, verbose):
+    while procs:
+        cmd, pr = procs.pop(0)
+        out, _ = pr.communicate()
+        text = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed: {' '.join(cmd)}\n{text}")
+        if verbose and text.strip():
+            print(text, file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

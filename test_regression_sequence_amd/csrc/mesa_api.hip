@@ -1,0 +1,124 @@
+// C ABI of libmesa: argument validation, workspace carving, kernel launches.
+// Every check runs before the first launch, so a failing call writes nothing.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/mesa.h"
+#include "mesa_kernels.h"
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool supported_dim(mesa_dtype dt, int d) {
+  if (dt == MESA_F32) return d == 16 || d == 32 || d == 64 || d == 128;
+  return d == 32 || d == 64 || d == 128;
+}
+
+mesa_status check_desc(const mesa_fwd_desc* d) {
+  if (!d) return MESA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1 || d->chunk < 1 || d->max_steps < 0)
+    return MESA_ERR_INVALID_ARG;
+  if (d->in_dtype != MESA_F32 && d->in_dtype != MESA_BF16) return MESA_ERR_INVALID_ARG;
+  if (std::isnan(d->tol)) return MESA_ERR_INVALID_ARG;
+  if (d->dk != d->dv || !supported_dim(d->in_dtype, d->dk)) return MESA_ERR_UNSUPPORTED;
+  if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return MESA_ERR_UNSUPPORTED;
+  // grid and index ranges used by the kernels
+  const long long bh = (long long)d->B * d->H;
+  const long long nc = (d->T + d->chunk - 1) / d->chunk;
+  if (bh > (1LL << 24) || bh * nc > (1LL << 31) - 1 || bh * d->T * (long long)d->dk > (1LL << 40))
+    return MESA_ERR_UNSUPPORTED;
+  return MESA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mesa_abi_version(void) { return MESA_ABI_VERSION; }
+
+const char* mesa_status_string(mesa_status s) {
+  switch (s) {
+    case MESA_OK: return "ok";
+    case MESA_ERR_INVALID_ARG: return "invalid argument";
+    case MESA_ERR_UNSUPPORTED: return "unsupported size or configuration";
+    case MESA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case MESA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MESA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d) {
+  if (check_desc(d) != MESA_OK || d->T == 0) return 0;
+  const size_t nc = (size_t)(d->T + d->chunk - 1) / d->chunk;
+  const size_t bh = (size_t)d->B * d->H;
+  return 2 * bh * nc * mesa::snapshot_bytes(d->in_dtype == MESA_BF16, d->dk);
+}
+
+mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0, float* o, float* h_final,
+                             float* g_final, int32_t* steps, float* x_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const mesa_status st = check_desc(d);
+  if (st != MESA_OK) return st;
+  const bool any_tokens = d->T > 0;
+  if (any_tokens && (!q || !k || !v || !gamma || !beta || !lambda || !o)) return MESA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final, steps, x_out, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+  const size_t need = mesa_fwd_workspace_bytes(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MESA_ERR_WORKSPACE;
+  if (!any_tokens && !h_final && !g_final) return MESA_OK;
+
+  const bool bf16 = d->in_dtype == MESA_BF16;
+  const int D = d->dk, C = d->chunk;
+  const int BH = d->B * d->H;
+  const int NC = (d->T + C - 1) / C;
+  const size_t snap = (size_t)BH * NC * mesa::snapshot_bytes(bf16, D);
+
+  mesa::ScanParams sp{};
+  sp.k = k; sp.v = v; sp.gamma = gamma; sp.beta = beta; sp.h0 = h0; sp.g0 = g0;
+  sp.h_final = h_final; sp.g_final = g_final;
+  sp.hb = workspace;
+  sp.gb = workspace ? static_cast<char*>(workspace) + snap : nullptr;
+  sp.BH = BH; sp.T = d->T; sp.NC = NC;
+  if (mesa::launch_scan(bf16, D, C, sp, stream) != hipSuccess) return MESA_ERR_HIP;
+  if (!any_tokens) return MESA_OK;
+
+  mesa::CgParams cp{};
+  cp.q = q; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
+  cp.hb = sp.hb; cp.gb = sp.gb; cp.o = o; cp.steps = steps; cp.x_out = x_out;
+  cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
+  cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
+  if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
+  return MESA_OK;
+}
+
+mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+                             const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
+                             const float* beta, const float* lambda, float* h_state,
+                             float* g_state, float* o, int32_t* steps, float* x_out,
+                             int32_t max_steps, float tol, hipStream_t stream) {
+  if (N < 0 || H < 1 || dk < 1 || dv < 1 || max_steps < 0 || std::isnan(tol)) return MESA_ERR_INVALID_ARG;
+  if (in_dtype != MESA_F32 && in_dtype != MESA_BF16) return MESA_ERR_INVALID_ARG;
+  if (dk != dv || (dk != 64 && dk != 128)) return MESA_ERR_UNSUPPORTED;
+  if ((long long)N * H > (1LL << 31) - 1) return MESA_ERR_UNSUPPORTED;
+  if (N == 0) return MESA_OK;
+  if (!q || !k || !v || !gamma || !beta || !lambda || !h_state || !g_state || !o)
+    return MESA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, gamma, beta, lambda, h_state, g_state, o, steps, x_out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+
+  mesa::DecodeParams dp{};
+  dp.q = q; dp.k = k; dp.v = v; dp.gamma = gamma; dp.beta = beta; dp.lam = lambda;
+  dp.h = h_state; dp.g = g_state; dp.o = o; dp.steps = steps; dp.x_out = x_out;
+  dp.P = N * H; dp.H = H; dp.max_steps = max_steps;
+  dp.tol2 = tol > 0.f ? tol * tol : -1.f;
+  if (mesa::launch_decode(in_dtype == MESA_BF16, dk, dp, stream) != hipSuccess) return MESA_ERR_HIP;
+  return MESA_OK;
+}
+
+}  // extern "C"

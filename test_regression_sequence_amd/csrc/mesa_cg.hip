@@ -1,0 +1,349 @@
+// Chunked conjugate-gradient solve and read-out of the Mesa layer.
+//
+// MesaNet page, technical summary, "Mesa layer" section: the optimal query
+// response x_t = (H_t + Lambda)^{-1} q_t is found by conjugate gradient, the
+// output is o_t = G_t x_t, the step count per token follows a stopping
+// criterion ("dynamic compute"), and the work is parallel over chunks
+// (parallelisation paragraph).  Inside chunk c (tokens s..s+C-1, boundary
+// states Hb = H_{s-1}, Gb = G_{s-1}):
+//
+//   b_t = sum_{i=s..t} log gamma_i,  Gamma_t = e^{b_t},
+//   W_tj = e^{b_t - b_j} beta_j for j <= t (else 0),
+//   H_t p = Gamma_t Hb p + sum_{j<=t} W_tj (k_j . p) k_j,
+//   o_t   = Gamma_t Gb x_t + sum_{j<=t} W_tj (k_j . x_t) v_j.
+//
+// One workgroup per chunk, one wave per 16 tokens; the waves never
+// synchronise inside the CG loop (every token's iteration touches only its
+// own vectors and read-only chunk data), so each wave leaves the loop as soon
+// as its 16 tokens have stopped.  All matrix products run on MFMA in a
+// transposed orientation: the per-token vectors are the B operand, so lane l
+// of a wave holds token 16w + l%16 and dims 16a + 4(l/16) + {0..3} of every
+// CG vector, MFMA results land directly in that layout, and the CG scalars
+// need only a 4-lane reduction.  The bf16 path permutes the contraction
+// index of each 16x16x32 MFMA so that this register layout feeds it without
+// any data movement; A operands are the boundary state (registers) and the
+// chunk's keys in LDS.
+#include "mesa_common.h"
+#include "mesa_kernels.h"
+
+namespace mesa {
+
+namespace {
+
+template <bool BF16, int D, int C>
+struct CgLds;
+
+template <int D, int C>
+struct CgLds<true, D, C> {
+  static constexpr int CP = (C < 32) ? 32 : C;
+  static constexpr int KS = D + 8;     // row stride of Ks (elements)
+  static constexpr int TS = CP + 8;    // row stride of KT, VT
+  __bf16 Ks[C * KS];                   // K chunk, [token][dim]
+  __bf16 KT[D * TS];                   // K chunk, [dim][token]
+  __bf16 VT[D * TS];                   // V chunk, [dim][token]
+};
+
+template <int D, int C>
+struct CgLds<false, D, C> {
+  static constexpr int S = D + 1;
+  float M[D * S];                      // Hb during CG, Gb for the read-out, [row][col]
+  float Ks[C * S];                     // K chunk [token][dim]
+  float Vs[C * S];                     // V chunk [token][dim]
+};
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+template <bool BF16, int D, int C>
+__global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
+  constexpr int ND = D / 16;   // dim tiles
+  constexpr int NW = C / 16;   // waves = token tiles
+  constexpr int NM = ND / 2;   // bf16 k-blocks over dims (pairs of dim tiles)
+  using L = CgLds<BF16, D, C>;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+  const int h = bh % p.H;
+  const int T = p.T, s = c * C, Lc = min(C, T - s);
+  const size_t row0 = (size_t)bh * T + s;
+  const int tloc = 16 * w + tl;
+  const bool valid = tloc < Lc;
+
+  __shared__ float bcum[C];
+  __shared__ float betas[C];
+  __shared__ __attribute__((aligned(16))) L lds;
+
+  // ---- gate prefix b_t (wave 0, inclusive scan) ------------------------------
+  if (w == 0) {
+    float v = 0.f, bt = 0.f;
+    if (lane < C && lane < Lc) {
+      v = logf(p.gamma[row0 + lane]);
+      bt = p.beta[row0 + lane];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(v, o, 64);
+      if (lane >= o) v += t;
+    }
+    if (lane < C) {
+      bcum[lane] = v;
+      betas[lane] = bt;
+    }
+  }
+
+  // ---- stage the chunk's keys and values --------------------------------------
+  if constexpr (BF16) {
+    constexpr int CP = L::CP, KS = L::KS, TS = L::TS;
+    const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
+    const uint16_t* Vg = static_cast<const uint16_t*>(p.v);
+    for (int pc = tid; pc < (CP / 2) * (D / 8); pc += 64 * NW) {
+      const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+      const int j0 = 2 * jp, j1 = j0 + 1;
+      const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      u16x8 k0 = z, k1 = z, v0 = z, v1 = z;
+      if (j0 < Lc) {
+        k0 = *reinterpret_cast<const u16x8*>(Kg + (row0 + j0) * D + 8 * c8);
+        v0 = *reinterpret_cast<const u16x8*>(Vg + (row0 + j0) * D + 8 * c8);
+      }
+      if (j1 < Lc) {
+        k1 = *reinterpret_cast<const u16x8*>(Kg + (row0 + j1) * D + 8 * c8);
+        v1 = *reinterpret_cast<const u16x8*>(Vg + (row0 + j1) * D + 8 * c8);
+      }
+      if (j0 < C) *reinterpret_cast<u16x8*>(&lds.Ks[j0 * KS + 8 * c8]) = k0;
+      if (j1 < C) *reinterpret_cast<u16x8*>(&lds.Ks[j1 * KS + 8 * c8]) = k1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = 8 * c8 + e;
+        *reinterpret_cast<uint32_t*>(&lds.KT[n * TS + j0]) = (uint32_t)k0[e] | ((uint32_t)k1[e] << 16);
+        *reinterpret_cast<uint32_t*>(&lds.VT[n * TS + j0]) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+      }
+    }
+  } else {
+    constexpr int S = L::S;
+    const float* Kg = static_cast<const float*>(p.k);
+    const float* Vg = static_cast<const float*>(p.v);
+    const float* Hg = static_cast<const float*>(p.hb) + ((size_t)bh * p.NC + c) * D * D;
+    for (int pc = tid; pc < C * D; pc += 64 * NW) {
+      const int j = pc / D, d = pc % D;
+      lds.Ks[j * S + d] = (j < Lc) ? Kg[(row0 + j) * D + d] : 0.f;
+      lds.Vs[j * S + d] = (j < Lc) ? Vg[(row0 + j) * D + d] : 0.f;
+    }
+    for (int pc = tid; pc < D * D; pc += 64 * NW) lds.M[(pc / D) * S + pc % D] = Hg[pc];
+  }
+  __syncthreads();
+
+  // ---- per-token constants ----------------------------------------------------
+  const float bt = bcum[tloc];
+  const float Gam = __expf(bt);
+  float W[NW][4];
+#pragma unroll
+  for (int jt = 0; jt < NW; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * jt + 4 * g + i;
+      W[jt][i] = (jt <= w && j <= tloc && valid) ? __expf(bt - bcum[j]) * betas[j] : 0.f;
+    }
+  f32x4 lam[ND], r[ND], x[ND], pv[ND], acc[ND];
+#pragma unroll
+  for (int a = 0; a < ND; ++a) {
+    lam[a] = *reinterpret_cast<const f32x4*>(p.lam + (size_t)h * D + 16 * a + 4 * g);
+    r[a] = valid ? load4<BF16>(p.q, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+    x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pv[a] = r[a];
+  }
+
+  // boundary state as MFMA A operand (bf16 path: registers)
+  bf16x8 mfrag[BF16 ? ND : 1][BF16 ? NM : 1];
+  if constexpr (BF16) {
+    const bf16x8* Hf = static_cast<const bf16x8*>(p.hb) + ((size_t)bh * p.NC + c) * (D * D / 8);
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) mfrag[nt][m] = Hf[(nt * NM + m) * 64 + lane];
+  }
+
+  // y <- A y-operand: Gamma_t * Mb u + (sum_j W_tj (k_j.u) Y_j) for u = src
+  // (Mb = Hb or Gb, Y = K or V); returns through out[].
+  auto chunk_product = [&](const f32x4* src, f32x4* out, bool use_values) {
+    f32x4 sc[NW];
+    if constexpr (BF16) {
+      constexpr int KS = L::KS, TS = L::TS;
+      bf16x8 ub[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) ub[m] = pack8(src[2 * m], src[2 * m + 1]);
+#pragma unroll
+      for (int nt = 0; nt < ND; ++nt) {
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) t = mfma_bf16(mfrag[nt][m], ub[m], t);
+        out[nt] = t * Gam;
+      }
+#pragma unroll
+      for (int jt = 0; jt < NW; ++jt) {
+        if (jt > w) continue;
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const __bf16* row = &lds.Ks[(16 * jt + tl) * KS + 32 * m + 4 * g];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          t = mfma_bf16(a, ub[m], t);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] *= W[jt][i];
+        sc[jt] = t;
+      }
+      const __bf16* Y = use_values ? lds.VT : lds.KT;
+#pragma unroll
+      for (int mj = 0; mj < (NW + 1) / 2; ++mj) {
+        if (2 * mj > w) continue;
+        const f32x4 hi = (2 * mj + 1 <= w && 2 * mj + 1 < NW) ? sc[(2 * mj + 1) % NW] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x8 sb = pack8(sc[2 * mj], hi);
+#pragma unroll
+        for (int nt = 0; nt < ND; ++nt) {
+          const __bf16* row = &Y[(16 * nt + tl) * TS + 32 * mj + 4 * g];
+          const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(row);
+          const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(row + 16);
+          const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          out[nt] = mfma_bf16(a, sb, out[nt]);
+        }
+      }
+    } else {
+      constexpr int S = L::S;
+#pragma unroll
+      for (int nt = 0; nt < ND; ++nt) {
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a = 0; a < ND; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t = mfma_f32(lds.M[(16 * nt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
+        out[nt] = t * Gam;
+      }
+#pragma unroll
+      for (int jt = 0; jt < NW; ++jt) {
+        if (jt > w) continue;
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a = 0; a < ND; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t = mfma_f32(lds.Ks[(16 * jt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] *= W[jt][i];
+        sc[jt] = t;
+      }
+      const float* Y = use_values ? lds.Vs : lds.Ks;
+#pragma unroll
+      for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+        for (int jt = 0; jt < NW; ++jt) {
+          if (jt > w) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[nt] = mfma_f32(Y[(16 * jt + 4 * g + i) * S + 16 * nt + tl], sc[jt][i], out[nt]);
+        }
+    }
+  };
+
+  // ---- conjugate gradient -----------------------------------------------------
+  float rho = 0.f;
+#pragma unroll
+  for (int a = 0; a < ND; ++a) rho += dot4(r[a], r[a]);
+  rho = sum_lane_groups(rho);
+  int n = 0;
+  bool stopped = false;
+  for (int it = 0; it < p.max_steps; ++it) {
+    const bool active = !stopped && rho > 0.f && rho > p.tol2;
+    if (!__any(active)) break;
+    chunk_product(pv, acc, false);
+    float pw = 0.f;
+#pragma unroll
+    for (int a = 0; a < ND; ++a) {
+      acc[a] += lam[a] * pv[a];
+      pw += dot4(pv[a], acc[a]);
+    }
+    pw = sum_lane_groups(pw);
+    const bool ok = active && pw > 0.f;
+    stopped = !ok;
+    const float alpha = ok ? rho / pw : 0.f;
+    float rr = 0.f;
+#pragma unroll
+    for (int a = 0; a < ND; ++a) {
+      x[a] += alpha * pv[a];
+      r[a] -= alpha * acc[a];
+      rr += dot4(r[a], r[a]);
+    }
+    rr = sum_lane_groups(rr);
+    const float bet = ok ? rr / rho : 0.f;
+#pragma unroll
+    for (int a = 0; a < ND; ++a) pv[a] = ok ? r[a] + bet * pv[a] : pv[a];
+    rho = ok ? rr : rho;
+    n += ok ? 1 : 0;
+  }
+
+  // ---- read-out o_t = G_t x_t -------------------------------------------------
+  if constexpr (BF16) {
+    const bf16x8* Gf = static_cast<const bf16x8*>(p.gb) + ((size_t)bh * p.NC + c) * (D * D / 8);
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) mfrag[nt][m] = Gf[(nt * NM + m) * 64 + lane];
+  } else {
+    constexpr int S = L::S;
+    __syncthreads();  // every wave is done reading Hb
+    const float* Gg = static_cast<const float*>(p.gb) + ((size_t)bh * p.NC + c) * D * D;
+    for (int pc = tid; pc < D * D; pc += 64 * NW) lds.M[(pc / D) * S + pc % D] = Gg[pc];
+    __syncthreads();
+  }
+  chunk_product(x, acc, true);
+
+  if (valid) {
+    const size_t orow = (row0 + tloc) * D;
+#pragma unroll
+    for (int a = 0; a < ND; ++a) *reinterpret_cast<f32x4*>(p.o + orow + 16 * a + 4 * g) = acc[a];
+    if (p.x_out) {
+#pragma unroll
+      for (int a = 0; a < ND; ++a) *reinterpret_cast<f32x4*>(p.x_out + orow + 16 * a + 4 * g) = x[a];
+    }
+    if (p.steps && g == 0) p.steps[row0 + tloc] = n;
+  }
+}
+
+template <bool BF16, int D, int C>
+hipError_t launch_cg_t(const CgParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.BH * p.NC);
+  hipLaunchKernelGGL((cg_kernel<BF16, D, C>), grid, dim3(64 * (C / 16)), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_cg_d(int C, const CgParams& p, hipStream_t s) {
+  switch (C) {
+    case 16: return launch_cg_t<BF16, D, 16>(p, s);
+    case 32: return launch_cg_t<BF16, D, 32>(p, s);
+    case 64: return launch_cg_t<BF16, D, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s) {
+  if (bf16) {
+    switch (D) {
+      case 32: return launch_cg_d<true, 32>(C, p, s);
+      case 64: return launch_cg_d<true, 64>(C, p, s);
+      case 128: return launch_cg_d<true, 128>(C, p, s);
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_cg_d<false, 16>(C, p, s);
+      case 32: return launch_cg_d<false, 32>(C, p, s);
+      case 64: return launch_cg_d<false, 64>(C, p, s);
+      case 128: return launch_cg_d<false, 128>(C, p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mesa

@@ -1,0 +1,81 @@
+// Device-side helpers shared by the Mesa kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mesa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// D = 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16] and receives D[4(l/16)..+3][l%16].
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = 16x16x4 fp32 MFMA.  Lane l supplies A[l%16][l/16], B[l/16][l%16] and
+// receives D[4(l/16)..+3][l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+// Two bf16 values packed low-first into one dword.
+__device__ __forceinline__ uint32_t pack2(__bf16 lo, __bf16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
+// wave).  Every participating lane receives the bitwise-identical result.
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Load 4 consecutive input elements (fp32 or bf16 storage) as fp32.
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4(const void* base, size_t idx) {
+  if constexpr (BF16) {
+    const u16x4 u = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + idx);
+    return f32x4{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])};
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if constexpr (BF16) {
+    return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  } else {
+    return static_cast<const float*>(base)[idx];
+  }
+}
+
+}  // namespace mesa

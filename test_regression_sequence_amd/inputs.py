@@ -26,7 +26,9 @@ for bf16 configurations those values are exactly representable in bf16, and
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -231,12 +233,25 @@ def make_decode_inputs(cfg: DecodeConfig, block: int = 64) -> dict:
     h = np.empty((pairs, cfg.d, cfg.d), np.float32)
     g = np.empty((pairs, cfg.d, cfg.d), np.float32)
     if cfg.prefill > 0:
-        for b0 in range(0, pairs, block):
+        def work(b0):
             P = min(block, pairs - b0)
             hb, gb = _prefill_block(cfg.seed, b0 // block, P, cfg.prefill, cfg.d,
                                     cfg.gamma_logit, cfg.beta_dist, cfg.dtype)
             h[b0:b0 + P] = hb
             g[b0:b0 + P] = gb
+        # blocks draw from independent streams, so the thread count does not change the result
+        workers = max(1, min(16, os.cpu_count() or 1))
+        try:
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(1)
+        except ImportError:  # pragma: no cover
+            limit = None
+        try:
+            with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+                list(ex.map(work, range(0, pairs, block)))
+        finally:
+            if limit is not None:
+                limit.restore_original_limits()
     else:
         h[:] = 0
         g[:] = 0

@@ -1,0 +1,192 @@
+"""Python binding of libmesa (ctypes).  Argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module passes device
+pointers of torch tensors and the current HIP stream through the C ABI
+declared in ``include/mesa.h``, and allocates outputs with torch.  There is no
+fallback: if the library is missing, every call raises ``MesaError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MesaError", "lib", "library_path", "FwdDesc", "MESA_F32", "MESA_BF16",
+    "workspace_bytes", "fwd_chunked", "decode_step", "abi_version", "status_string",
+]
+
+MESA_F32 = 0
+MESA_BF16 = 1
+STATUS = {0: "MESA_OK", 1: "MESA_ERR_INVALID_ARG", 2: "MESA_ERR_UNSUPPORTED",
+          3: "MESA_ERR_ALIGNMENT", 4: "MESA_ERR_WORKSPACE", 5: "MESA_ERR_HIP"}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class MesaError(RuntimeError):
+    def __init__(self, msg, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("max_steps", ctypes.c_int32), ("tol", ctypes.c_float), ("in_dtype", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmesa.so")
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise MesaError(f"{path} is not built; run `python -m test_regression_sequence_amd.build`")
+        L = ctypes.CDLL(path)
+        P, S, I32, F = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+        L.mesa_abi_version.restype = I32
+        L.mesa_abi_version.argtypes = []
+        L.mesa_status_string.restype = ctypes.c_char_p
+        L.mesa_status_string.argtypes = [ctypes.c_int]
+        L.mesa_fwd_workspace_bytes.restype = S
+        L.mesa_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdDesc)]
+        L.mesa_fwd_chunked.restype = ctypes.c_int
+        L.mesa_fwd_chunked.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, S, P]
+        L.mesa_decode_step.restype = ctypes.c_int
+        L.mesa_decode_step.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, P, P,
+                                       P, P, I32, F, P]
+        _LIB = L
+    return _LIB
+
+
+def abi_version() -> int:
+    return int(lib().mesa_abi_version())
+
+
+def status_string(code: int) -> str:
+    return lib().mesa_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise MesaError(f"{what}: {STATUS.get(code, code)} ({status_string(code)})", code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MESA_F32
+    if t.dtype == torch.bfloat16:
+        return MESA_BF16
+    raise MesaError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None):
+    if not t.is_cuda:
+        raise MesaError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MesaError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise MesaError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise MesaError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_desc(B, H, T, d, chunk, max_steps, tol, dtype_code) -> FwdDesc:
+    return FwdDesc(B, H, T, d, d, chunk, max_steps, float(tol), dtype_code)
+
+
+def workspace_bytes(B, H, T, d, chunk, max_steps=0, tol=0.0, dtype=torch.bfloat16) -> int:
+    code = MESA_BF16 if dtype == torch.bfloat16 else MESA_F32
+    desc = make_desc(B, H, T, d, chunk, max_steps, tol, code)
+    return int(lib().mesa_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
+                tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
+                return_steps: bool = True, return_x: bool = False, out=None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Chunked Mesa forward; q, k, v [B, H, T, d] (fp32 or bf16) on the GPU.
+
+    gamma, beta [B, H, T] fp32; lam [H, d] fp32; h0, g0 optional [B, H, d, d]
+    fp32.  Returns a dict with ``o`` [B, H, T, d] fp32 and, on request,
+    ``steps`` [B, H, T] int32, ``x`` [B, H, T, d], ``h_final``, ``g_final``.
+    ``out`` may pass preallocated result tensors (same keys).
+    """
+    B, H, T, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (B, H, T, d), q.dtype)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(beta, "beta", (B, H, T), torch.float32)
+    _need(lam, "lam", (H, d), torch.float32)
+    for name, t in (("h0", h0), ("g0", g0)):
+        if t is not None:
+            _need(t, name, (B, H, d, d), torch.float32)
+    desc = make_desc(B, H, T, d, chunk, max_steps, tol, code)
+    L = lib()
+    need = int(L.mesa_fwd_workspace_bytes(ctypes.byref(desc)))
+    dev = q.device
+    out = dict(out or {})
+    res = {}
+    res["o"] = out.get("o") if out.get("o") is not None else torch.empty((B, H, T, d), device=dev, dtype=torch.float32)
+    if return_steps:
+        res["steps"] = out.get("steps") if out.get("steps") is not None else torch.empty((B, H, T), device=dev, dtype=torch.int32)
+    if return_x:
+        res["x"] = out.get("x") if out.get("x") is not None else torch.empty((B, H, T, d), device=dev, dtype=torch.float32)
+    if return_state:
+        res["h_final"] = out.get("h_final") if out.get("h_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+        res["g_final"] = out.get("g_final") if out.get("g_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code_ = L.mesa_fwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                               _ptr(lam), _ptr(h0), _ptr(g0), _ptr(res["o"]), _ptr(res.get("h_final")),
+                               _ptr(res.get("g_final")), _ptr(res.get("steps")), _ptr(res.get("x")),
+                               _ptr(workspace), ctypes.c_size_t(wbytes), _stream(stream))
+    _check(code_, "mesa_fwd_chunked")
+    return res
+
+
+def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int = 32,
+                tol: float = 1e-4, return_steps: bool = True, return_x: bool = False,
+                out=None, stream=None) -> dict:
+    """One recurrent step; q, k, v [N, H, d]; h_state, g_state [N, H, d, d] fp32, updated in place."""
+    N, H, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, H, d), q.dtype)
+    _need(gamma, "gamma", (N, H), torch.float32)
+    _need(beta, "beta", (N, H), torch.float32)
+    _need(lam, "lam", (H, d), torch.float32)
+    _need(h_state, "h_state", (N, H, d, d), torch.float32)
+    _need(g_state, "g_state", (N, H, d, d), torch.float32)
+    dev = q.device
+    out = dict(out or {})
+    res = {"o": out.get("o") if out.get("o") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)}
+    if return_steps:
+        res["steps"] = out.get("steps") if out.get("steps") is not None else torch.empty((N, H), device=dev, dtype=torch.int32)
+    if return_x:
+        res["x"] = out.get("x") if out.get("x") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)
+    code_ = lib().mesa_decode_step(N, H, d, d, _ptr(q), _ptr(k), _ptr(v), code, _ptr(gamma), _ptr(beta),
+                                   _ptr(lam), _ptr(h_state), _ptr(g_state), _ptr(res["o"]),
+                                   _ptr(res.get("steps")), _ptr(res.get("x")), int(max_steps),
+                                   float(tol), _stream(stream))
+    _check(code_, "mesa_decode_step")
+    return res

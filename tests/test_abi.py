@@ -1,0 +1,110 @@
+"""The C ABI library: load, exported symbols, host-side validation (CPU only).
+
+No call here launches a kernel: every call either queries host-side
+information or fails validation before the first launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_regression_sequence_amd import mesa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mesa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mesa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mesa.lib()
+    names = header_functions()
+    assert {"mesa_fwd_chunked", "mesa_decode_step", "mesa_fwd_workspace_bytes",
+            "mesa_status_string", "mesa_abi_version"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert mesa.abi_version() == 1
+    for code in range(6):
+        assert mesa.status_string(code)
+    assert mesa.status_string(99) == "unknown status"
+
+
+def desc(**kw):
+    base = dict(B=2, H=3, T=130, dk=64, dv=64, chunk=64, max_steps=5, tol=0.0, in_dtype=mesa.MESA_BF16)
+    base.update(kw)
+    return mesa.FwdDesc(*[base[f] for f, _ in mesa.FwdDesc._fields_])
+
+
+def ws(d):
+    return mesa.lib().mesa_fwd_workspace_bytes(ctypes.byref(d))
+
+
+def test_workspace_sizes():
+    # 2 states x B*H x ceil(T/C) chunks x d^2 x element size
+    assert ws(desc()) == 2 * 6 * 3 * 64 * 64 * 2
+    assert ws(desc(in_dtype=mesa.MESA_F32)) == 2 * 6 * 3 * 64 * 64 * 4
+    assert ws(desc(T=0)) == 0
+    assert ws(desc(dk=48, dv=48)) == 0
+    assert ws(desc(dk=64, dv=32)) == 0
+    assert ws(desc(chunk=48)) == 0
+    assert ws(desc(B=8, H=16, T=4096, dk=128, dv=128)) == 512 * 1024 * 1024
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def call_fwd(d, q=FAKE, k=FAKE, v=FAKE, gamma=FAKE, beta=FAKE, lam=FAKE, o=FAKE,
+             h0=None, workspace=FAKE, wbytes=1 << 40):
+    P = ctypes.c_void_p
+    return mesa.lib().mesa_fwd_chunked(ctypes.byref(d), P(q), P(k), P(v), P(gamma), P(beta), P(lam),
+                                       P(h0), None, P(o), None, None, None, None, P(workspace),
+                                       ctypes.c_size_t(wbytes), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=0), 1), (dict(H=-1), 1), (dict(T=-5), 1), (dict(max_steps=-1), 1),
+    (dict(tol=float("nan")), 1), (dict(in_dtype=7), 1),
+    (dict(dk=48, dv=48), 2), (dict(dk=64, dv=128), 2), (dict(chunk=128), 2),
+    (dict(dk=16, dv=16), 2),  # bf16 needs dk >= 32
+])
+def test_fwd_rejects_bad_descriptors(kw, expect):
+    assert call_fwd(desc(**kw)) == expect
+
+
+def test_fwd_rejects_missing_pointers_alignment_and_workspace():
+    d = desc()
+    assert call_fwd(d, q=0) == 1
+    assert call_fwd(d, o=0) == 1
+    assert call_fwd(d, lam=0) == 1
+    assert call_fwd(d, k=FAKE + 4) == 3
+    assert call_fwd(d, h0=FAKE + 8) == 3
+    assert call_fwd(d, workspace=0) == 4
+    assert call_fwd(d, wbytes=ws(d) - 1) == 4
+
+
+def call_dec(N=4, H=2, dk=128, dv=128, dtype=1, q=FAKE, h=FAKE, o=FAKE, max_steps=8, tol=1e-4):
+    P = ctypes.c_void_p
+    return mesa.lib().mesa_decode_step(N, H, dk, dv, P(q), P(FAKE), P(FAKE), dtype, P(FAKE), P(FAKE),
+                                       P(FAKE), P(h), P(FAKE), P(o), None, None, max_steps,
+                                       ctypes.c_float(tol), None)
+
+
+def test_decode_validation():
+    assert call_dec(N=-1) == 1
+    assert call_dec(H=0) == 1
+    assert call_dec(max_steps=-2) == 1
+    assert call_dec(tol=float("nan")) == 1
+    assert call_dec(dtype=3) == 1
+    assert call_dec(dk=96, dv=96) == 2
+    assert call_dec(dk=128, dv=64) == 2
+    assert call_dec(q=0) == 1
+    assert call_dec(h=0) == 1
+    assert call_dec(o=FAKE + 2) == 3
+    assert call_dec(N=0) == 0  # nothing to do, nothing launched

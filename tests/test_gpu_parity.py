@@ -1,0 +1,183 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Bars (relative L2 over the compared outputs, fp64):
+  * fp32 inputs: <= 1e-4 against the oracle's CG at the GPU's per-token step counts;
+  * bf16 inputs (bf16 MFMA, fp32 accumulation): <= 2e-2.
+Dynamic-CG step counts are compared to the oracle run with the GPU's counts
+(several counts are correct near the threshold); the stopping decision itself
+is checked for validity against the oracle's residuals.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import dev_inputs, oracle_on_slices, rel_l2
+from test_regression_sequence_amd import mesa
+from test_regression_sequence_amd.inputs import (
+    CONFIGS, make_decode_inputs, make_fwd_inputs, select_slices, small_fwd,
+)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mesa.lib()
+
+
+def run_fwd(x, cfg=None, **kw):
+    cfg = cfg or x["cfg"]
+    d = dev_inputs(x)
+    args = dict(chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol, return_steps=True)
+    args.update(kw)
+    res = mesa.fwd_chunked(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d["lam"], **args)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def check_against_oracle(x, gpu, idx, tol, check_states=False):
+    """Compare GPU outputs of slices idx with the oracle at the GPU's step counts."""
+    cfg = x["cfg"]
+    steps = gpu["steps"].reshape(cfg.B * cfg.H, cfg.T)[idx]
+    refs = oracle_on_slices(x, idx, steps_gpu=steps)
+    o_gpu = gpu["o"].reshape(cfg.B * cfg.H, cfg.T, cfg.d)[idx]
+    o_ref = np.stack([r["o_cg"][0, 0] for r in refs])
+    err = rel_l2(o_gpu, o_ref)
+    # forced mode reproduces the GPU's counts unless the oracle hit a breakdown earlier
+    s_ref = np.stack([r["steps"][0, 0] for r in refs])
+    assert np.array_equal(s_ref, steps), "oracle could not run the GPU's step counts"
+    assert err <= tol, f"rel L2 {err:.3e} > {tol}"
+    if check_states:
+        for i, r in zip(idx, refs):
+            pass
+    return err, refs
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+def test_config1_tiny_fp32_dynamic():
+    x = make_fwd_inputs(CONFIGS[1])
+    gpu = run_fwd(x, return_x=True)
+    err, refs = check_against_oracle(x, gpu, [0], TOL["f32"])
+    n = gpu["steps"][0, 0]
+    assert n.max() <= 16 and n.min() >= 1
+    # a stop before the cap means the residual reached the tolerance
+    r = refs[0]
+    stopped_early = n < CONFIGS[1].max_steps
+    assert np.all(r["res_norm"][0, 0][stopped_early] <= 1e-6 * 1.05)
+    assert np.all(r["res_prev"][0, 0][n > 0] > 1e-6 * 0.95)
+    # and the oracle's own schedule takes (nearly) the same number of steps
+    free = oracle_on_slices(x, [0])[0]["steps"][0, 0]
+    assert np.mean(np.abs(free - n)) < 0.5
+    print(f"config1 rel L2 {err:.3e}")
+
+
+def test_config2_mid_bf16_fixed15():
+    x = make_fwd_inputs(CONFIGS[2])
+    gpu = run_fwd(x)
+    assert np.all(gpu["steps"] == 15)
+    idx = select_slices(4, 8, 3)
+    err, _ = check_against_oracle(x, gpu, idx, TOL["bf16"])
+    print(f"config2 rel L2 {err:.3e}")
+
+
+def test_config3_lm1b_bf16_fixed30():
+    x = make_fwd_inputs(CONFIGS[3])
+    gpu = run_fwd(x)
+    assert np.all(gpu["steps"] == 30)
+    idx = select_slices(8, 16, 2)
+    err, _ = check_against_oracle(x, gpu, idx, TOL["bf16"])
+    assert np.all(np.isfinite(gpu["o"]))
+    print(f"config3 rel L2 {err:.3e}")
+
+
+def test_config4_long_dynamic_sampled_tokens():
+    cfg = CONFIGS[4]
+    x = make_fwd_inputs(cfg)
+    gpu = run_fwd(x)
+    n = gpu["steps"]
+    assert n.min() >= 1 and n.max() <= cfg.max_steps
+    idx = select_slices(1, 16, 1)
+    rng = np.random.default_rng(4)
+    at = np.zeros(cfg.T, bool)
+    at[rng.choice(cfg.T, 96, replace=False)] = True
+    at[-64:] = True
+    steps = n.reshape(16, cfg.T)[idx]
+    ref = oracle_on_slices(x, idx, steps_gpu=steps, solve_at=at)[0]
+    o_gpu = gpu["o"].reshape(16, cfg.T, cfg.d)[idx][0][at]
+    err = rel_l2(o_gpu, ref["o_cg"][0, 0][at])
+    assert err <= TOL["bf16"], err
+    # stopping decisions are valid up to the bf16 matvec's perturbation of the residual
+    ns = steps[0][at]
+    early = ns < cfg.max_steps
+    assert np.mean(ref["res_norm"][0, 0][at][early] <= 1e-4 * 1.5) > 0.95
+    print(f"config4 rel L2 {err:.3e}, steps mean {n.mean():.2f} max {n.max()}")
+
+
+def test_config5_decode_step():
+    cfg = CONFIGS[5]
+    x = make_decode_inputs(cfg)
+    d = dev_inputs(x)
+    h0 = x["h"].copy()
+    res = mesa.decode_step(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d["lam"], d["h"], d["g"],
+                           max_steps=cfg.max_steps, tol=cfg.tol, return_x=True)
+    torch.cuda.synchronize()
+    o = res["o"].cpu().numpy()
+    n = res["steps"].cpu().numpy()
+    h1 = d["h"].cpu().numpy()
+    g1 = d["g"].cpu().numpy()
+    assert n.min() >= 1 and n.max() <= cfg.max_steps
+    from oracle import mesa_decode_step
+    rng = np.random.default_rng(5)
+    pick = rng.choice(cfg.N * cfg.H, 64, replace=False)
+    sel = lambda a: a.reshape(cfg.N * cfg.H, *a.shape[2:])[pick]
+    heads = pick % cfg.H
+    ref_o, ref_h, ref_g = [], [], []
+    for i, p in enumerate(pick):
+        hh = heads[i]
+        r = mesa_decode_step(sel(x["q"])[i][None, None], sel(x["k"])[i][None, None],
+                             sel(x["v"])[i][None, None], sel(x["gamma"])[i][None, None],
+                             sel(x["beta"])[i][None, None], x["lam"][hh:hh + 1],
+                             sel(x["h"])[i][None, None], sel(x["g"])[i][None, None],
+                             max_steps=cfg.max_steps, tol=cfg.tol,
+                             forced_steps=sel(n)[i].reshape(1, 1))
+        ref_o.append(r["o"][0, 0]); ref_h.append(r["h"][0, 0]); ref_g.append(r["g"][0, 0])
+    err = rel_l2(sel(o), np.stack(ref_o))
+    assert err <= TOL["bf16"], err
+    assert rel_l2(sel(h1), np.stack(ref_h)) < 1e-6
+    assert rel_l2(sel(g1), np.stack(ref_g)) < 1e-6
+    hs = h1.reshape(-1, cfg.d, cfg.d)
+    assert np.array_equal(hs, hs.transpose(0, 2, 1)), "H lost exact symmetry"
+    print(f"config5 rel L2 {err:.3e}, steps mean {n.mean():.2f}")
+
+
+# ---------------------------------------------------------------------------
+# small cases across dtypes, head dims, chunk sizes and ragged sequence ends
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    ("f32", 16, 64, 200), ("f32", 32, 16, 77), ("f32", 64, 32, 150), ("f32", 128, 64, 130),
+    ("bf16", 32, 32, 100), ("bf16", 64, 64, 200), ("bf16", 64, 16, 70), ("bf16", 128, 64, 200),
+    ("bf16", 128, 32, 96), ("bf16", 128, 16, 33),
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,T", SMALL)
+def test_small_fixed_steps(dtype, d, chunk, T):
+    cfg = small_fwd(B=1, H=2, T=T, d=d, chunk=chunk, dtype=dtype, max_steps=8)
+    x = make_fwd_inputs(cfg)
+    gpu = run_fwd(x, return_state=True, return_x=True)
+    err, refs = check_against_oracle(x, gpu, [0, 1], TOL[dtype])
+    # carried states after the last token
+    Hr = np.stack([r["H_final"][0, 0] for r in refs])
+    Gr = np.stack([r["G_final"][0, 0] for r in refs])
+    st_tol = 1e-5 if dtype == "f32" else 1e-4
+    assert rel_l2(gpu["h_final"].reshape(2, d, d), Hr) < st_tol
+    assert rel_l2(gpu["g_final"].reshape(2, d, d), Gr) < st_tol
+    assert rel_l2(gpu["x"].reshape(2, T, d), np.stack([r["x_cg"][0, 0] for r in refs])) < TOL[dtype]
