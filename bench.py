@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked Mesa forward (and the decode step) on one MI355X.
+
+One *step* is one call of ``mesa_fwd_chunked`` -- the state scan plus the
+chunked CG solve and read-out -- over the 1B-LM-shaped layer workload
+(B=8, H=16, T=4096, d=128, chunk 64, bf16 q/k/v with fp32 accumulation,
+30 fixed CG steps), inputs resident in HBM.  The JSON line reports:
+
+* value: tokens/s = B*H*T / (time per step);
+* roofline: the CG kernel (the dominant kernel) -- counted flops per launch
+  over its average duration, measured with HIP events on the stream it runs
+  on, against the bf16 dense MFMA peak;
+* decode: the recurrent decode step (256 sequences x 16 heads, d=128, fp32
+  states, CG tolerance 1e-4 / at most 32 steps): HBM bytes moved per step
+  over its duration, against the HBM peak;
+* cpu_baseline: the fp64 oracle on a bounded sample of the same workload.
+
+Counted flops per token follow the chunkwise algorithm (causal half of the
+intra-chunk products, nbar = (C+1)/2 keys on average):
+  scan  F_s = 2 dk^2 + 2 dv dk
+  CG    F_c = 2 dk^2 + 4 dk nbar + 10 dk   per iteration
+  out   F_o = 2 dv dk + 2 dk nbar + 2 dv nbar
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def flops_per_token(d: int, C: int, n_steps: float) -> dict:
+    nbar = (C + 1) / 2.0
+    f_s = 2 * d * d + 2 * d * d
+    f_c = 2 * d * d + 4 * d * nbar + 10 * d
+    f_o = 2 * d * d + 2 * d * nbar + 2 * d * nbar
+    return {"scan": f_s, "cg_iter": f_c, "out": f_o, "cg_kernel": n_steps * f_c + f_o,
+            "total": f_s + n_steps * f_c + f_o}
+
+
+def decode_bytes_per_pair(d: int, in_bytes: int = 2) -> int:
+    # H and G read + written (fp32), q/k/v in, gamma/beta in, o out, steps out
+    return 2 * 2 * 4 * d * d + 3 * in_bytes * d + 2 * 4 + 4 * d + 4
+
+
+def time_events(fn, iters):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def bench_forward(cfg, steps, warmup):
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs
+
+    x = make_fwd_inputs(cfg)
+    dev = "cuda"
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(x["q"]).to(dev).to(dt)
+    k = torch.from_numpy(x["k"]).to(dev).to(dt)
+    v = torch.from_numpy(x["v"]).to(dev).to(dt)
+    gamma = torch.from_numpy(x["gamma"]).to(dev)
+    beta = torch.from_numpy(x["beta"]).to(dev)
+    lam = torch.from_numpy(x["lam"]).to(dev)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    need = mesa.workspace_bytes(B, H, T, d, cfg.chunk, dtype=dt)
+    ws = torch.empty(need, device=dev, dtype=torch.uint8)
+    o = torch.empty((B, H, T, d), device=dev, dtype=torch.float32)
+    st = torch.empty((B, H, T), device=dev, dtype=torch.int32)
+    out = {"o": o, "steps": st}
+    kw = dict(chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol, workspace=ws, out=out)
+
+    def step():
+        mesa.fwd_chunked(q, k, v, gamma, beta, lam, **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_events(step, steps)
+    wall = (time.perf_counter() - t0) / steps * 1e3
+
+    # per-kernel durations: events around each of the two launches, same stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    scan_ms, cg_ms = [], []
+    for _ in range(max(3, steps // 2)):
+        ev[0].record()
+        mesa.fwd_scan(k, v, gamma, beta, chunk=cfg.chunk, workspace=ws)
+        ev[1].record()
+        mesa.fwd_solve(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                       tol=cfg.tol, workspace=ws, o=o, steps=st)
+        ev[2].record()
+        torch.cuda.synchronize()
+        scan_ms.append(ev[0].elapsed_time(ev[1]))
+        cg_ms.append(ev[1].elapsed_time(ev[2]))
+    n = st.cpu().numpy()
+    return dict(ms=ms, wall_ms=wall, scan_ms=float(np.mean(scan_ms)), cg_ms=float(np.mean(cg_ms)),
+                steps_mean=float(n.mean()), steps_max=int(n.max()), x=x)
+
+
+def bench_decode(cfg, steps, warmup):
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_decode_inputs
+
+    x = make_decode_inputs(cfg)
+    dev = "cuda"
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(x["q"]).to(dev).to(dt)
+    k = torch.from_numpy(x["k"]).to(dev).to(dt)
+    v = torch.from_numpy(x["v"]).to(dev).to(dt)
+    gamma = torch.from_numpy(x["gamma"]).to(dev)
+    beta = torch.from_numpy(x["beta"]).to(dev)
+    lam = torch.from_numpy(x["lam"]).to(dev)
+    h = torch.from_numpy(x["h"]).to(dev)
+    g = torch.from_numpy(x["g"]).to(dev)
+    o = torch.empty((cfg.N, cfg.H, cfg.d), device=dev, dtype=torch.float32)
+    st = torch.empty((cfg.N, cfg.H), device=dev, dtype=torch.int32)
+    del x
+
+    def step():
+        mesa.decode_step(q, k, v, gamma, beta, lam, h, g, max_steps=cfg.max_steps, tol=cfg.tol,
+                         out={"o": o, "steps": st})
+
+    # the first call measures the step count on the generated state
+    step()
+    torch.cuda.synchronize()
+    n_first = st.cpu().numpy()
+    for _ in range(warmup):
+        step()
+    ms = time_events(step, steps)
+    n = st.cpu().numpy()
+    pairs = cfg.N * cfg.H
+    in_bytes = 2 if cfg.dtype == "bf16" else 4
+    nbytes = pairs * decode_bytes_per_pair(cfg.d, in_bytes) + cfg.H * cfg.d * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"decode step: {cfg.N} seqs x {cfg.H} heads, d={cfg.d}, fp32 states, "
+                    f"{cfg.dtype} q/k/v, CG tol {cfg.tol:g} max {cfg.max_steps}",
+        "us_per_step": round(ms * 1e3, 2),
+        "pairs_per_s": round(pairs / (ms * 1e-3), 1),
+        "seq_tokens_per_s": round(cfg.N / (ms * 1e-3), 1),
+        "bytes_per_step": int(nbytes),
+        "achieved_GBs": round(gbs, 1),
+        "peak_GBs": PEAK_HBM_GBS,
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "cg_steps_first_call_mean": round(float(n_first.mean()), 2),
+        "cg_steps_mean": round(float(n.mean()), 2),
+    }
+
+
+def cpu_baseline(x, slices: int, tokens: int):
+    from threadpoolctl import threadpool_limits
+    from oracle import mesa_forward
+    cfg = x["cfg"]
+    rng = np.random.default_rng(7)
+    flat = rng.choice(cfg.B * cfg.H, size=slices, replace=False)
+    b, h = flat // cfg.H, flat % cfg.H
+    T = min(tokens, cfg.T)
+    sl = lambda a: a[b, h][:, None, :T]
+    lam = x["lam"][h]
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for i in range(slices):
+            mesa_forward(sl(x["q"])[i:i + 1], sl(x["k"])[i:i + 1], sl(x["v"])[i:i + 1],
+                         sl(x["gamma"])[i:i + 1], sl(x["beta"])[i:i + 1], lam[i:i + 1],
+                         max_steps=cfg.max_steps, tol=cfg.tol, exact=False)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(slices * T / dt, 2),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{slices} (b,h) slices x first {T} tokens of the same workload, fp64 NumPy, "
+                  f"CG schedule only (no exact solve), one BLAS thread; {dt:.1f} s",
+        "host": platform.processor() or platform.machine(),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4],
+                    help="forward workload: 2 (d=64), 3 (d=128, default), 4 (T=32768, dynamic CG)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Mesa layer's (b, h) slices shard across GPUs "
+              "with no communication, and this build runs and reports a single MI355X. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mesa.lib()
+    cfg = CONFIGS[args.workload]
+    fw = bench_forward(cfg, args.steps, args.warmup)
+    tokens = cfg.B * cfg.H * cfg.T
+    n_avg = fw["steps_mean"]
+    f = flops_per_token(cfg.d, cfg.chunk, n_avg)
+    cg_flops = f["cg_kernel"] * tokens
+    cg_tflops = cg_flops / (fw["cg_ms"] * 1e-3) / 1e12
+    total_tflops = f["total"] * tokens / (fw["ms"] * 1e-3) / 1e12
+
+    line = {
+        "metric": "Mesa fwd tokens/s (B*H*T/s) at d=128",
+        "value": round(tokens / (fw["ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fw["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; q,k L2-normalised Gaussian, v Gaussian, gamma=sigmoid(U), beta~U(0,1))",
+        "config": {
+            "workload": f"{cfg.name}: chunked Mesa forward B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
+                        f"chunk={cfg.chunk}, {'fixed %d' % cfg.max_steps if cfg.tol <= 0 else 'tol %g max %d' % (cfg.tol, cfg.max_steps)} CG steps",
+            "B": cfg.B, "H": cfg.H, "T": cfg.T, "d": cfg.d, "chunk": cfg.chunk,
+            "cg_steps_mean": round(n_avg, 3),
+        },
+        "roofline": {
+            "kernel": "cg_kernel (chunked CG solve + read-out)",
+            "bound": "mfma",
+            "achieved": round(cg_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(cg_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": cg_flops,
+            "avg_launch_ms": round(fw["cg_ms"], 4),
+        },
+        "kernels_ms": {"scan": round(fw["scan_ms"], 4), "cg": round(fw["cg_ms"], 4)},
+        "fwd_counted_TFLOPs": round(total_tflops, 2),
+        "fwd_frac_of_mfma_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_ms_per_step": round(fw["wall_ms"], 4),
+    }
+    if not args.no_decode:
+        line["decode"] = bench_decode(CONFIGS[5], args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

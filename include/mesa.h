@@ -115,6 +115,29 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* The two phases of mesa_fwd_chunked, for callers that want them apart
+ * (e.g. building decode states from a prompt without solving, or timing).
+ *
+ * mesa_fwd_scan: the inter-chunk state scan only.  Reads k, v, gamma, beta,
+ * h0, g0; writes the chunk-boundary states into `workspace` and, when given,
+ * h_final / g_final.  q, lambda and o are not needed.
+ *
+ * mesa_fwd_solve: the chunked CG solve and read-out only.  Reads q, k, v,
+ * gamma, beta, lambda and the boundary states a preceding mesa_fwd_scan
+ * with the same descriptor and inputs left in `workspace` (stream order);
+ * writes o, steps, x_out.  Same arguments and rules as mesa_fwd_chunked. */
+mesa_status mesa_fwd_scan(const mesa_fwd_desc* d, const void* k, const void* v,
+                          const float* gamma, const float* beta,
+                          const float* h0, const float* g0,
+                          float* h_final, float* g_final,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+mesa_status mesa_fwd_solve(const mesa_fwd_desc* d,
+                           const void* q, const void* k, const void* v,
+                           const float* gamma, const float* beta, const float* lambda,
+                           float* o, int32_t* steps, float* x_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One recurrent step for N sequences x H heads, states updated in place
  * (MesaNet page, technical summary, "Mesa layer": O(1) inference form).
  *

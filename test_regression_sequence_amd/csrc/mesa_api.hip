@@ -56,44 +56,82 @@ size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d) {
   return 2 * bh * nc * mesa::snapshot_bytes(d->in_dtype == MESA_BF16, d->dk);
 }
 
-mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
-                             const float* gamma, const float* beta, const float* lambda,
-                             const float* h0, const float* g0, float* o, float* h_final,
-                             float* g_final, int32_t* steps, float* x_out, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+enum Phase { kScan = 1, kSolve = 2 };
+
+mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const void* k,
+                     const void* v, const float* gamma, const float* beta, const float* lambda,
+                     const float* h0, const float* g0, float* o, float* h_final, float* g_final,
+                     int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   const mesa_status st = check_desc(d);
   if (st != MESA_OK) return st;
   const bool any_tokens = d->T > 0;
-  if (any_tokens && (!q || !k || !v || !gamma || !beta || !lambda || !o)) return MESA_ERR_INVALID_ARG;
+  if (any_tokens && (!k || !v || !gamma || !beta)) return MESA_ERR_INVALID_ARG;
+  if (any_tokens && (phases & kSolve) && (!q || !lambda || !o)) return MESA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final, steps, x_out, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
   const size_t need = mesa_fwd_workspace_bytes(d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MESA_ERR_WORKSPACE;
-  if (!any_tokens && !h_final && !g_final) return MESA_OK;
 
   const bool bf16 = d->in_dtype == MESA_BF16;
   const int D = d->dk, C = d->chunk;
   const int BH = d->B * d->H;
   const int NC = (d->T + C - 1) / C;
   const size_t snap = (size_t)BH * NC * mesa::snapshot_bytes(bf16, D);
+  void* hb = workspace;
+  void* gb = workspace ? static_cast<char*>(workspace) + snap : nullptr;
 
-  mesa::ScanParams sp{};
-  sp.k = k; sp.v = v; sp.gamma = gamma; sp.beta = beta; sp.h0 = h0; sp.g0 = g0;
-  sp.h_final = h_final; sp.g_final = g_final;
-  sp.hb = workspace;
-  sp.gb = workspace ? static_cast<char*>(workspace) + snap : nullptr;
-  sp.BH = BH; sp.T = d->T; sp.NC = NC;
-  if (mesa::launch_scan(bf16, D, C, sp, stream) != hipSuccess) return MESA_ERR_HIP;
-  if (!any_tokens) return MESA_OK;
-
-  mesa::CgParams cp{};
-  cp.q = q; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
-  cp.hb = sp.hb; cp.gb = sp.gb; cp.o = o; cp.steps = steps; cp.x_out = x_out;
-  cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
-  cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
-  if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
+  if ((phases & kScan) && (any_tokens || h_final || g_final)) {
+    mesa::ScanParams sp{};
+    sp.k = k; sp.v = v; sp.gamma = gamma; sp.beta = beta; sp.h0 = h0; sp.g0 = g0;
+    sp.h_final = h_final; sp.g_final = g_final;
+    sp.hb = hb; sp.gb = gb;
+    sp.BH = BH; sp.T = d->T; sp.NC = NC;
+    if (mesa::launch_scan(bf16, D, C, sp, stream) != hipSuccess) return MESA_ERR_HIP;
+  }
+  if ((phases & kSolve) && any_tokens) {
+    mesa::CgParams cp{};
+    cp.q = q; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
+    cp.hb = hb; cp.gb = gb; cp.o = o; cp.steps = steps; cp.x_out = x_out;
+    cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
+    cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
+    if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
+  }
   return MESA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0, float* o, float* h_final,
+                             float* g_final, int32_t* steps, float* x_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
+                  steps, x_out, workspace, workspace_bytes, stream);
+}
+
+mesa_status mesa_fwd_scan(const mesa_fwd_desc* d, const void* k, const void* v, const float* gamma,
+                          const float* beta, const float* h0, const float* g0, float* h_final,
+                          float* g_final, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return fwd_impl(kScan, d, nullptr, k, v, gamma, beta, nullptr, h0, g0, nullptr, h_final, g_final,
+                  nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+mesa_status mesa_fwd_solve(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                           const float* gamma, const float* beta, const float* lambda, float* o,
+                           int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return fwd_impl(kSolve, d, q, k, v, gamma, beta, lambda, nullptr, nullptr, o, nullptr, nullptr,
+                  steps, x_out, workspace, workspace_bytes, stream);
 }
 
 mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,

@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "MesaError", "lib", "library_path", "FwdDesc", "MESA_F32", "MESA_BF16",
-    "workspace_bytes", "fwd_chunked", "decode_step", "abi_version", "status_string",
+    "workspace_bytes", "fwd_chunked", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
+    "status_string",
 ]
 
 MESA_F32 = 0
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.mesa_fwd_chunked.restype = ctypes.c_int
         L.mesa_fwd_chunked.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        P, S, P]
+        L.mesa_fwd_scan.restype = ctypes.c_int
+        L.mesa_fwd_scan.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, S, P]
+        L.mesa_fwd_solve.restype = ctypes.c_int
+        L.mesa_fwd_solve.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, S, P]
         L.mesa_decode_step.restype = ctypes.c_int
         L.mesa_decode_step.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, P, P,
                                        P, P, I32, F, P]
@@ -162,6 +167,30 @@ def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 
                                _ptr(workspace), ctypes.c_size_t(wbytes), _stream(stream))
     _check(code_, "mesa_fwd_chunked")
     return res
+
+
+def fwd_scan(k, v, gamma, beta, *, chunk: int, workspace: torch.Tensor, h0=None, g0=None,
+             h_final=None, g_final=None, stream=None):
+    """State scan only: boundary states into ``workspace``, optional final states."""
+    B, H, T, d = k.shape
+    desc = make_desc(B, H, T, d, chunk, 0, 0.0, _dtype_code(k))
+    wbytes = workspace.numel() * workspace.element_size()
+    code_ = lib().mesa_fwd_scan(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                                _ptr(h0), _ptr(g0), _ptr(h_final), _ptr(g_final), _ptr(workspace),
+                                ctypes.c_size_t(wbytes), _stream(stream))
+    _check(code_, "mesa_fwd_scan")
+
+
+def fwd_solve(q, k, v, gamma, beta, lam, *, chunk: int, max_steps: int, tol: float,
+              workspace: torch.Tensor, o: torch.Tensor, steps=None, x=None, stream=None):
+    """CG solve + read-out only, from the boundary states a preceding fwd_scan left in ``workspace``."""
+    B, H, T, d = q.shape
+    desc = make_desc(B, H, T, d, chunk, max_steps, tol, _dtype_code(q))
+    wbytes = workspace.numel() * workspace.element_size()
+    code_ = lib().mesa_fwd_solve(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                                 _ptr(lam), _ptr(o), _ptr(steps), _ptr(x), _ptr(workspace),
+                                 ctypes.c_size_t(wbytes), _stream(stream))
+    _check(code_, "mesa_fwd_solve")
 
 
 def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int = 32,
