@@ -329,19 +329,12 @@ hipError_t launch_cg_d(int C, const CgParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s) {
-  if (bf16) {
-    switch (D) {
-      case 32: return launch_cg_d<true, 32>(C, p, s);
-      case 64: return launch_cg_d<true, 64>(C, p, s);
-      case 128: return launch_cg_d<true, 128>(C, p, s);
-    }
-  } else {
-    switch (D) {
-      case 16: return launch_cg_d<false, 16>(C, p, s);
-      case 32: return launch_cg_d<false, 32>(C, p, s);
-      case 64: return launch_cg_d<false, 64>(C, p, s);
-      case 128: return launch_cg_d<false, 128>(C, p, s);
-    }
+  if (bf16) return launch_cg_bf16(D, C, p, s);
+  switch (D) {
+    case 16: return launch_cg_d<false, 16>(C, p, s);
+    case 32: return launch_cg_d<false, 32>(C, p, s);
+    case 64: return launch_cg_d<false, 64>(C, p, s);
+    case 128: return launch_cg_d<false, 128>(C, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -46,10 +46,16 @@ __device__ __forceinline__ uint32_t pack2(__bf16 lo, __bf16 hi) {
 
 // Sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
 // wave).  Every participating lane receives the bitwise-identical result.
+// Uses the gfx950 cross-row swaps: permlane16_swap(v, v) yields, in every
+// lane, {value of the even 16-lane row, value of the odd row} of its row
+// pair; permlane32_swap(v, v) yields {value of lanes 0-31, value of lanes
+// 32-63} for the same lane position.  Both sums are formed in the same order
+// in every lane.
 __device__ __forceinline__ float sum_lane_groups(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -58,6 +58,7 @@ struct DecodeParams {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
+hipError_t launch_cg_bf16(int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s);
 
 // Bytes of one (b, h, chunk) boundary snapshot of H (or of G).
