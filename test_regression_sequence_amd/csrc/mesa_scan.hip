@@ -13,15 +13,18 @@
 // registers, and writes the state *before* each chunk (the boundary state
 // the CG kernel starts from) into the workspace.
 //
-// Work split: one workgroup (4 waves) per (b, h, state in {H, G}, 16-row
-// stripe of the state), so a (b, h) uses 2*D/16 workgroups that the launch
-// maps onto one XCD (they share the chunk's keys through that XCD's L2).
-// The chunk delta K^T diag(w) X is an MFMA contraction over the chunk's
-// tokens: bf16 MFMA for bf16 inputs with the scaled operand split into
-// bf16 hi + lo parts (so the carried fp32 state does not pick up a bf16
-// rounding of beta*tail*x), fp32 MFMA for fp32 inputs.
+// Work split: a workgroup (4 waves) owns either a whole state (H or G) of
+// one (b, h) -- FULL -- or one 16-row stripe of it, so there are 2 or 2*D/16
+// workgroups per (b, h); the launch picks the split that fills the GPU and
+// maps the workgroups of one (b, h) onto one XCD (they share the chunk's keys
+// in that XCD's L2).  The next chunk's keys, values and gates are loaded into
+// registers while the current chunk is processed.  The chunk delta
+// K^T diag(w) X is an MFMA contraction over the chunk's tokens: bf16 MFMA for
+// bf16 inputs with the scaled operand split into bf16 hi + lo parts (so the
+// carried fp32 state does not pick up a bf16 rounding of beta*tail*x), fp32
+// MFMA for fp32 inputs.
 //
-// Snapshot layouts (consumed only by the CG kernel):
+// Snapshot layouts (consumed only by the CG kernels):
 //   fp32 path: row-major [D][D] fp32, H[r][c] and G[v][k].
 //   bf16 path: MFMA A-operand fragments.  Fragment f = nt*(D/32) + m holds,
 //     for lane l (tl = l%16, g = l/16), 8 bf16: row 16*nt + tl, columns
@@ -35,12 +38,38 @@ namespace {
 
 constexpr int kScanThreads = 256;
 
-template <bool BF16, int D, int C>
+template <bool BF16, int D, int C, bool FULL>
+struct ScanShape {
+  static constexpr int ND = D / 16;
+  static constexpr int CP = (C < 32) ? 32 : C;       // token dim padded to one bf16 k-block
+  static constexpr int U = FULL ? 2 : 2 * ND;          // workgroups per (b, h)
+  static constexpr int MROWS = FULL ? D : 16;          // state rows (A-operand rows) owned
+  static constexpr bool PAIR = FULL && BF16;           // a unit = both m-tiles of a fragment
+  static constexpr int TPU = PAIR ? 2 : 1;             // tiles per unit
+  static constexpr int NU = FULL ? (PAIR ? (ND / 2) * ND : ND * ND) : ND;
+  static constexpr int UPW = (NU + 3) / 4;             // units per wave
+  // register prefetch: pieces of the chunk each thread loads
+  static constexpr int NPX = BF16 ? (CP / 2) * (D / 8) : C * (D / 4);   // X pieces
+  static constexpr int PPX = (NPX + kScanThreads - 1) / kScanThreads;
+  static constexpr int NPK = BF16 ? (CP / 2) * (MROWS / 8) : C * (MROWS / 4);  // K pieces (A operand)
+  static constexpr int PPK = (NPK + kScanThreads - 1) / kScanThreads;
+  static constexpr int AS = CP + 8;                    // bf16 row stride of transposed LDS arrays
+  static constexpr size_t LDS_A = BF16 ? (size_t)MROWS * AS * 2 : (size_t)CP * MROWS * 4;
+  static constexpr size_t LDS_B = BF16 ? (size_t)2 * D * AS * 2 : (size_t)CP * D * 4;
+};
+
+template <bool BF16>
+struct Piece;
+template <>
+struct Piece<true> { u16x8 a, b; };   // two token rows (j0, j1), 8 columns each
+template <>
+struct Piece<false> { f32x4 a; };     // one token row, 4 columns
+
+template <bool BF16, int D, int C, bool FULL>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
-  constexpr int ND = D / 16;          // 16-wide tiles per state dimension
-  constexpr int TPW = (ND + 3) / 4;   // state tiles owned by each wave
-  constexpr int CP = (C < 32) ? 32 : C;  // token dim padded to one bf16 MFMA k-block
-  constexpr int U = 2 * ND;           // workgroups per (b, h)
+  using S = ScanShape<BF16, D, C, FULL>;
+  constexpr int ND = S::ND, CP = S::CP, U = S::U, MROWS = S::MROWS, TPU = S::TPU, UPW = S::UPW;
+  constexpr int AS = S::AS;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
@@ -50,207 +79,297 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
   const int local = blockIdx.x >> 3;
   const int bh = (local / U) * 8 + xcd;
   if (bh >= p.BH) return;
-  const int u = local % U;
-  const int which = u / ND;           // 0: H, 1: G
-  const int mt = u % ND;              // 16-row stripe of the (H or G^T) state
-
+  const int u0 = local % U;
+  const int which = FULL ? u0 : u0 / ND;   // 0: H, 1: G
+  const int mpart = FULL ? 0 : u0 % ND;    // stripe (non-FULL)
   const int T = p.T, NC = p.NC;
-  const void* X = which ? p.v : p.k;  // the second factor of the chunk delta
-  const size_t row0 = (size_t)bh * T;
+  const void* X = which ? p.v : p.k;      // the second factor of the chunk delta
+  const size_t rowbase = (size_t)bh * T;
 
-  __shared__ float logg[C];
-  __shared__ float wsc[C];            // beta_j * tail_j
-  __shared__ float gamma_c;
-  // A operand: K restricted to this stripe's 16 state rows; B operand: w .* X.
-  __shared__ __attribute__((aligned(16))) char lds_a[BF16 ? 16 * (CP + 8) * 2 : CP * 16 * 4];
-  __shared__ __attribute__((aligned(16))) char lds_b[BF16 ? 2 * D * (CP + 8) * 2 : CP * D * 4];
+  __shared__ __attribute__((aligned(16))) char lds_a[S::LDS_A];
+  __shared__ __attribute__((aligned(16))) char lds_b[S::LDS_B];
 
-  // Running state.  Tile ti of this wave is (mt, nt = wave + 4 ti); lane holds
-  // O[16 mt + 4 g + i][16 nt + tl], where O = H for H and O = G^T for G.
-  f32x4 st[TPW];
+  // ---- ownership: unit list of this wave ----------------------------------------
+  auto unit_mt = [&](int u, int h) -> int {
+    if constexpr (FULL) return S::PAIR ? 2 * (u / ND) + h : u / ND;
+    else return mpart;
+  };
+  auto unit_nt = [&](int u) -> int { return FULL ? u % ND : u; };
+
+  // Running state: lane holds O[16 mt + 4 g + i][16 nt + tl], O = H (H) or G^T (G).
+  f32x4 st[UPW][TPU];
   const float* init = which ? p.g0 : p.h0;
 #pragma unroll
-  for (int ti = 0; ti < TPW; ++ti) {
-    const int nt = wave + 4 * ti;
-    st[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nt < ND && init) {
-      const float* base = init + (size_t)bh * D * D;
-      if (which == 0) {
+  for (int ui = 0; ui < UPW; ++ui)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[ti][i] = base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl];
-      } else {
-        st[ti] = *reinterpret_cast<const f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g);
+    for (int h = 0; h < TPU; ++h) {
+      const int u = wave + 4 * ui;
+      st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < S::NU && init) {
+        const int mt = unit_mt(u, h), nt = unit_nt(u);
+        const float* base = init + (size_t)bh * D * D;
+        if (which == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[ui][h][i] = base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl];
+        } else {
+          st[ui][h] = *reinterpret_cast<const f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g);
+        }
       }
     }
-  }
+
+  // ---- register prefetch of one chunk -------------------------------------------
+  struct Raw {
+    Piece<BF16> x[S::PPX];
+    Piece<BF16> k[S::PPK];
+    float lg, bt;
+  };
+  auto fetch = [&](int c, Raw& r) {
+    const int s = c * C, Lc = min(C, T - s);
+    r.lg = 0.f;
+    r.bt = 0.f;
+    if (lane < Lc) {
+      r.lg = logf(p.gamma[rowbase + s + lane]);
+      r.bt = p.beta[rowbase + s + lane];
+    }
+    if constexpr (BF16) {
+      const uint16_t* Xg = static_cast<const uint16_t*>(X);
+      const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
+      const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = tid + q * kScanThreads;
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        r.x[q].a = z;
+        r.x[q].b = z;
+        if (pc < S::NPX) {
+          if (2 * jp < Lc) r.x[q].a = *reinterpret_cast<const u16x8*>(Xg + (rowbase + s + 2 * jp) * D + 8 * c8);
+          if (2 * jp + 1 < Lc) r.x[q].b = *reinterpret_cast<const u16x8*>(Xg + (rowbase + s + 2 * jp + 1) * D + 8 * c8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < S::PPK; ++q) {
+        const int pc = tid + q * kScanThreads;
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        const int col = (FULL ? 0 : 16 * mpart) + 8 * c8;
+        r.k[q].a = z;
+        r.k[q].b = z;
+        if (pc < S::NPK) {
+          if (2 * jp < Lc) r.k[q].a = *reinterpret_cast<const u16x8*>(Kg + (rowbase + s + 2 * jp) * D + col);
+          if (2 * jp + 1 < Lc) r.k[q].b = *reinterpret_cast<const u16x8*>(Kg + (rowbase + s + 2 * jp + 1) * D + col);
+        }
+      }
+    } else {
+      const float* Xg = static_cast<const float*>(X);
+      const float* Kg = static_cast<const float*>(p.k);
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = tid + q * kScanThreads;
+        const int j = pc / (D / 4), c4 = pc % (D / 4);
+        r.x[q].a = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pc < S::NPX && j < Lc) r.x[q].a = *reinterpret_cast<const f32x4*>(Xg + (rowbase + s + j) * D + 4 * c4);
+      }
+#pragma unroll
+      for (int q = 0; q < S::PPK; ++q) {
+        const int pc = tid + q * kScanThreads;
+        const int j = pc / (MROWS / 4), c4 = pc % (MROWS / 4);
+        const int col = (FULL ? 0 : 16 * mpart) + 4 * c4;
+        r.k[q].a = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pc < S::NPK && j < Lc) r.k[q].a = *reinterpret_cast<const f32x4*>(Kg + (rowbase + s + j) * D + col);
+      }
+    }
+  };
+
+  Raw cur, nxt;
+  if (NC > 0) fetch(0, cur);
 
   for (int c = 0; c < NC; ++c) {
-    const int s = c * C;
-    const int Lc = min(C, T - s);
+    if (c + 1 < NC) fetch(c + 1, nxt);
 
-    // ---- snapshot of the state before chunk c --------------------------------
+    // ---- snapshot of the state before chunk c ----------------------------------
     {
       const size_t snap = ((size_t)bh * NC + c) * D * D;
 #pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        const int nt = wave + 4 * ti;
-        if (nt >= ND) continue;
+      for (int ui = 0; ui < UPW; ++ui) {
+        const int u = wave + 4 * ui;
+        if (u >= S::NU) continue;
+        const int nt = unit_nt(u);
         if constexpr (BF16) {
           __bf16* dst = static_cast<__bf16*>(which ? p.gb : p.hb) + snap;
-          const int frag = nt * (ND / 2) + (mt >> 1);
-          bf16x4 h4;
+          if constexpr (S::PAIR) {
+            const int frag = nt * (ND / 2) + u / ND;
+            *reinterpret_cast<bf16x8*>(dst + ((size_t)frag * 64 + lane) * 8) = pack8(st[ui][0], st[ui][1]);
+          } else {
+            const int mt = unit_mt(u, 0);
+            const int frag = nt * (ND / 2) + (mt >> 1);
+            bf16x4 h4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) h4[i] = (__bf16)st[ti][i];
-          *reinterpret_cast<bf16x4*>(dst + ((size_t)frag * 64 + lane) * 8 + 4 * (mt & 1)) = h4;
+            for (int i = 0; i < 4; ++i) h4[i] = (__bf16)st[ui][0][i];
+            *reinterpret_cast<bf16x4*>(dst + ((size_t)frag * 64 + lane) * 8 + 4 * (mt & 1)) = h4;
+          }
         } else {
           float* dst = static_cast<float*>(which ? p.gb : p.hb) + snap;
-          if (which == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl] = st[ti][i];
-          } else {
-            *reinterpret_cast<f32x4*>(dst + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g) = st[ti];
+          for (int h = 0; h < TPU; ++h) {
+            const int mt = unit_mt(u, h);
+            if (which == 0) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dst[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl] = st[ui][h][i];
+            } else {
+              *reinterpret_cast<f32x4*>(dst + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g) = st[ui][h];
+            }
           }
         }
       }
     }
 
-    // ---- gates: w_j = beta_j * prod_{i=j+1..e} gamma_i, Gamma_c --------------
-    __syncthreads();  // previous chunk's readers of the LDS buffers are done
-    if (tid < C) logg[tid] = (tid < Lc) ? logf(p.gamma[row0 + s + tid]) : 0.f;
-    __syncthreads();
-    if (tid < C) {
-      float suf = 0.f;
-      for (int i = tid + 1; i < Lc; ++i) suf += logg[i];
-      wsc[tid] = (tid < Lc) ? p.beta[row0 + s + tid] * expf(suf) : 0.f;
-      if (tid == 0) gamma_c = (Lc > 0) ? expf(suf + logg[0]) : 1.f;
+    // ---- gates (every wave, in registers): w_j = beta_j prod_{i>j} gamma_i ------
+    float suf = cur.lg;  // inclusive suffix sum of log gamma
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_down(suf, o, 64);
+      if (lane + o < 64) suf += t;
     }
-    __syncthreads();
+    // sum over i > j; the shuffle runs with every lane active, then lane 63 drops it
+    const float next = __shfl_down(suf, 1, 64);
+    const float after = (lane < 63) ? next : 0.f;
+    const float wj = cur.bt * expf(after);                              // 0 past the chunk end
+    const float gamma_c = expf(__shfl(suf, 0, 64));
 
-    // ---- stage operands ------------------------------------------------------
+    // ---- stage operands (LDS is free once every wave finished chunk c-1) -------
+    __syncthreads();
     if constexpr (BF16) {
-      __bf16* KT = reinterpret_cast<__bf16*>(lds_a);              // [16][CP+8]
-      __bf16* XH = reinterpret_cast<__bf16*>(lds_b);              // [D][CP+8]
-      __bf16* XL = XH + D * (CP + 8);                             // [D][CP+8]
-      const uint16_t* Xg = static_cast<const uint16_t*>(X);
-      const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
-      // pieces: (token pair jp, 8-column group c8); one dword LDS write per column
-      constexpr int NP = (CP / 2) * (D / 8);
-      for (int pc = tid; pc < NP; pc += kScanThreads) {
+      __bf16* KT = reinterpret_cast<__bf16*>(lds_a);  // [MROWS][AS]: K^T rows of the owned stripe
+      __bf16* XH = reinterpret_cast<__bf16*>(lds_b);  // [D][AS]: (w .* X)^T, hi part
+      __bf16* XL = XH + D * AS;                       // lo part
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = tid + q * kScanThreads;
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
-        const int j0 = 2 * jp, j1 = j0 + 1;
-        u16x8 a = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, b = a;
-        if (j0 < Lc) a = *reinterpret_cast<const u16x8*>(Xg + (row0 + s + j0) * D + 8 * c8);
-        if (j1 < Lc) b = *reinterpret_cast<const u16x8*>(Xg + (row0 + s + j1) * D + 8 * c8);
-        const float w0 = (j0 < Lc) ? wsc[j0] : 0.f, w1 = (j1 < Lc) ? wsc[j1] : 0.f;
+        // shuffles before any lane leaves: every lane of the wave participates
+        const float w0 = __shfl(wj, (2 * jp) & 63, 64), w1 = __shfl(wj, (2 * jp + 1) & 63, 64);
+        if (pc >= S::NPX) continue;
+        const float ww0 = (2 * jp < C) ? w0 : 0.f, ww1 = (2 * jp + 1 < C) ? w1 : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x0 = w0 * bf16_to_f32(a[e]), x1 = w1 * bf16_to_f32(b[e]);
+          const float x0 = ww0 * bf16_to_f32(cur.x[q].a[e]), x1 = ww1 * bf16_to_f32(cur.x[q].b[e]);
           const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
           const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
           const int n = 8 * c8 + e;
-          *reinterpret_cast<uint32_t*>(XH + n * (CP + 8) + j0) = pack2(h0, h1);
-          *reinterpret_cast<uint32_t*>(XL + n * (CP + 8) + j0) = pack2(l0, l1);
+          *reinterpret_cast<uint32_t*>(XH + n * AS + 2 * jp) = pack2(h0, h1);
+          *reinterpret_cast<uint32_t*>(XL + n * AS + 2 * jp) = pack2(l0, l1);
         }
       }
-      // A operand: K^T rows 16 mt .. 16 mt + 15
-      for (int pc = tid; pc < (CP / 2) * 2; pc += kScanThreads) {
-        const int jp = pc % (CP / 2), half = pc / (CP / 2);
-        const int j0 = 2 * jp, j1 = j0 + 1;
-        u16x8 a = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, b = a;
-        if (j0 < Lc) a = *reinterpret_cast<const u16x8*>(Kg + (row0 + s + j0) * D + 16 * mt + 8 * half);
-        if (j1 < Lc) b = *reinterpret_cast<const u16x8*>(Kg + (row0 + s + j1) * D + 16 * mt + 8 * half);
+#pragma unroll
+      for (int q = 0; q < S::PPK; ++q) {
+        const int pc = tid + q * kScanThreads;
+        if (pc >= S::NPK) continue;
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int m = 8 * half + e;
-          *reinterpret_cast<uint32_t*>(KT + m * (CP + 8) + j0) =
-              (uint32_t)a[e] | ((uint32_t)b[e] << 16);
+          const int m = 8 * c8 + e;
+          *reinterpret_cast<uint32_t*>(KT + m * AS + 2 * jp) =
+              (uint32_t)cur.k[q].a[e] | ((uint32_t)cur.k[q].b[e] << 16);
         }
       }
     } else {
-      float* Ks = reinterpret_cast<float*>(lds_a);                // [CP][16]
-      float* Xs = reinterpret_cast<float*>(lds_b);                // [CP][D] = w_j * X[j][n]
-      const float* Xg = static_cast<const float*>(X);
-      const float* Kg = static_cast<const float*>(p.k);
-      for (int pc = tid; pc < C * (D / 4); pc += kScanThreads) {
+      float* Ks = reinterpret_cast<float*>(lds_a);    // [CP][MROWS]
+      float* Xs = reinterpret_cast<float*>(lds_b);    // [CP][D] = w_j * X[j][n]
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = tid + q * kScanThreads;
         const int j = pc / (D / 4), c4 = pc % (D / 4);
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (j < Lc) a = *reinterpret_cast<const f32x4*>(Xg + (row0 + s + j) * D + 4 * c4) * wsc[j];
-        *reinterpret_cast<f32x4*>(Xs + j * D + 4 * c4) = a;
+        const float w = __shfl(wj, j & 63, 64);
+        if (pc >= S::NPX) continue;
+        *reinterpret_cast<f32x4*>(Xs + j * D + 4 * c4) = cur.x[q].a * w;
       }
-      for (int pc = tid; pc < C * 4; pc += kScanThreads) {
-        const int j = pc / 4, c4 = pc % 4;
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (j < Lc) a = *reinterpret_cast<const f32x4*>(Kg + (row0 + s + j) * D + 16 * mt + 4 * c4);
-        *reinterpret_cast<f32x4*>(Ks + j * 16 + 4 * c4) = a;
+#pragma unroll
+      for (int q = 0; q < S::PPK; ++q) {
+        const int pc = tid + q * kScanThreads;
+        if (pc >= S::NPK) continue;
+        const int j = pc / (MROWS / 4), c4 = pc % (MROWS / 4);
+        *reinterpret_cast<f32x4*>(Ks + j * MROWS + 4 * c4) = cur.k[q].a;
       }
     }
     __syncthreads();
 
-    // ---- delta tiles and state update ----------------------------------------
-    const float gc = gamma_c;
+    // ---- delta tiles and state update --------------------------------------------
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-      const int nt = wave + 4 * ti;
-      if (nt >= ND) continue;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-        const __bf16* KT = reinterpret_cast<const __bf16*>(lds_a);
-        const __bf16* XH = reinterpret_cast<const __bf16*>(lds_b);
-        const __bf16* XL = XH + D * (CP + 8);
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + 4 * ui;
+      if (u >= S::NU) continue;
+      const int nt = unit_nt(u);
 #pragma unroll
-        for (int kb = 0; kb < CP / 32; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(KT + tl * (CP + 8) + 32 * kb + 8 * g);
-          const bf16x8 bh_ = *reinterpret_cast<const bf16x8*>(XH + (16 * nt + tl) * (CP + 8) + 32 * kb + 8 * g);
-          const bf16x8 bl_ = *reinterpret_cast<const bf16x8*>(XL + (16 * nt + tl) * (CP + 8) + 32 * kb + 8 * g);
-          acc = mfma_bf16(a, bh_, acc);
-          acc = mfma_bf16(a, bl_, acc);
-        }
-      } else {
-        const float* Ks = reinterpret_cast<const float*>(lds_a);
-        const float* Xs = reinterpret_cast<const float*>(lds_b);
+      for (int h = 0; h < TPU; ++h) {
+        const int mt = unit_mt(u, h);
+        const int mrow = FULL ? 16 * mt : 0;   // row offset inside the owned A rows
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF16) {
+          const __bf16* KT = reinterpret_cast<const __bf16*>(lds_a);
+          const __bf16* XH = reinterpret_cast<const __bf16*>(lds_b);
+          const __bf16* XL = XH + D * AS;
+#pragma unroll
+          for (int kb = 0; kb < CP / 32; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(KT + (mrow + tl) * AS + 32 * kb + 8 * g);
+            const bf16x8 bh_ = *reinterpret_cast<const bf16x8*>(XH + (16 * nt + tl) * AS + 32 * kb + 8 * g);
+            const bf16x8 bl_ = *reinterpret_cast<const bf16x8*>(XL + (16 * nt + tl) * AS + 32 * kb + 8 * g);
+            acc = mfma_bf16(a, bh_, acc);
+            acc = mfma_bf16(a, bl_, acc);
+          }
+        } else {
+          const float* Ks = reinterpret_cast<const float*>(lds_a);
+          const float* Xs = reinterpret_cast<const float*>(lds_b);
 #pragma unroll 4
-        for (int kb = 0; kb < C / 4; ++kb) {
-          acc = mfma_f32(Ks[(4 * kb + g) * 16 + tl], Xs[(4 * kb + g) * D + 16 * nt + tl], acc);
+          for (int kb = 0; kb < C / 4; ++kb)
+            acc = mfma_f32(Ks[(4 * kb + g) * MROWS + mrow + tl], Xs[(4 * kb + g) * D + 16 * nt + tl], acc);
         }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[ti][i] = gc * st[ti][i] + acc[i];
+        for (int i = 0; i < 4; ++i) st[ui][h][i] = gamma_c * st[ui][h][i] + acc[i];
+      }
     }
+    if (c + 1 < NC) cur = nxt;
   }
 
-  // ---- final state (fp32, row-major) ------------------------------------------
+  // ---- final state (fp32, row-major) ----------------------------------------------
   float* fin = which ? p.g_final : p.h_final;
   if (fin) {
     float* base = fin + (size_t)bh * D * D;
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-      const int nt = wave + 4 * ti;
-      if (nt >= ND) continue;
-      if (which == 0) {
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + 4 * ui;
+      if (u >= S::NU) continue;
+      const int nt = unit_nt(u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl] = st[ti][i];
-      } else {
-        *reinterpret_cast<f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g) = st[ti];
+      for (int h = 0; h < TPU; ++h) {
+        const int mt = unit_mt(u, h);
+        if (which == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl] = st[ui][h][i];
+        } else {
+          *reinterpret_cast<f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g) = st[ui][h];
+        }
       }
     }
   }
 }
 
-template <bool BF16, int D, int C>
+template <bool BF16, int D, int C, bool FULL>
 hipError_t launch_scan_t(const ScanParams& p, hipStream_t s) {
-  constexpr int U = 2 * (D / 16);
+  constexpr int U = ScanShape<BF16, D, C, FULL>::U;
   const int groups = (p.BH + 7) / 8;
   const dim3 grid(groups * 8 * U);
-  hipLaunchKernelGGL((scan_kernel<BF16, D, C>), grid, dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL>), grid, dim3(kScanThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <bool BF16, int D>
 hipError_t launch_scan_d(int C, const ScanParams& p, hipStream_t s) {
+  // A whole state per workgroup once there are enough (b, h) slices to give
+  // every CU work; otherwise one 16-row stripe per workgroup for parallelism.
+  const bool full = 2LL * p.BH >= 256;
   switch (C) {
-    case 16: return launch_scan_t<BF16, D, 16>(p, s);
-    case 32: return launch_scan_t<BF16, D, 32>(p, s);
-    case 64: return launch_scan_t<BF16, D, 64>(p, s);
+    case 16: return full ? launch_scan_t<BF16, D, 16, true>(p, s) : launch_scan_t<BF16, D, 16, false>(p, s);
+    case 32: return full ? launch_scan_t<BF16, D, 32, true>(p, s) : launch_scan_t<BF16, D, 32, false>(p, s);
+    case 64: return full ? launch_scan_t<BF16, D, 64, true>(p, s) : launch_scan_t<BF16, D, 64, false>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -78,29 +78,44 @@ def test_config1_tiny_fp32_dynamic():
     print(f"config1 rel L2 {err:.3e}")
 
 
+def check_final_states(x, gpu, idx, tol):
+    """h_final / g_final of slices idx against the oracle's recurrence (no solves)."""
+    cfg = x["cfg"]
+    refs = oracle_on_slices(x, idx, solve_at=np.zeros(cfg.T, bool))
+    d = cfg.d
+    Hg = gpu["h_final"].reshape(-1, d, d)[idx]
+    Gg = gpu["g_final"].reshape(-1, d, d)[idx]
+    eh = rel_l2(Hg, np.stack([r["H_final"][0, 0] for r in refs]))
+    eg = rel_l2(Gg, np.stack([r["G_final"][0, 0] for r in refs]))
+    assert eh < tol and eg < tol, (eh, eg)
+    return eh, eg
+
+
 def test_config2_mid_bf16_fixed15():
     x = make_fwd_inputs(CONFIGS[2])
-    gpu = run_fwd(x)
+    gpu = run_fwd(x, return_state=True)
     assert np.all(gpu["steps"] == 15)
     idx = select_slices(4, 8, 3)
     err, _ = check_against_oracle(x, gpu, idx, TOL["bf16"])
-    print(f"config2 rel L2 {err:.3e}")
+    eh, eg = check_final_states(x, gpu, idx, 1e-4)
+    print(f"config2 rel L2 {err:.3e}; final states {eh:.1e} {eg:.1e}")
 
 
 def test_config3_lm1b_bf16_fixed30():
     x = make_fwd_inputs(CONFIGS[3])
-    gpu = run_fwd(x)
+    gpu = run_fwd(x, return_state=True)
     assert np.all(gpu["steps"] == 30)
     idx = select_slices(8, 16, 2)
     err, _ = check_against_oracle(x, gpu, idx, TOL["bf16"])
     assert np.all(np.isfinite(gpu["o"]))
-    print(f"config3 rel L2 {err:.3e}")
+    eh, eg = check_final_states(x, gpu, idx, 1e-4)
+    print(f"config3 rel L2 {err:.3e}; final states {eh:.1e} {eg:.1e}")
 
 
 def test_config4_long_dynamic_sampled_tokens():
     cfg = CONFIGS[4]
     x = make_fwd_inputs(cfg)
-    gpu = run_fwd(x)
+    gpu = run_fwd(x, return_state=True)
     n = gpu["steps"]
     assert n.min() >= 1 and n.max() <= cfg.max_steps
     idx = select_slices(1, 16, 1)
@@ -117,7 +132,8 @@ def test_config4_long_dynamic_sampled_tokens():
     ns = steps[0][at]
     early = ns < cfg.max_steps
     assert np.mean(ref["res_norm"][0, 0][at][early] <= 1e-4 * 1.5) > 0.95
-    print(f"config4 rel L2 {err:.3e}, steps mean {n.mean():.2f} max {n.max()}")
+    eh, eg = check_final_states(x, gpu, idx, 1e-4)
+    print(f"config4 rel L2 {err:.3e}, steps mean {n.mean():.2f} max {n.max()}; final states {eh:.1e} {eg:.1e}")
 
 
 def test_config5_decode_step():
