@@ -4,11 +4,11 @@
 // technical summary, "Mesa layer": CG query response, chunk-parallel states,
 // dynamic CG step count); this file is the tuned bf16 path.
 //
-// One wave per workgroup: the wave owns token tile w (16 tokens) of chunk c.
-// The NW = C/16 tiles of a chunk are launched as consecutive workgroups of
-// the same XCD so they share the chunk's boundary states and keys in that
-// XCD's L2.  Waves never wait for one another, so tiles with fewer causal
-// keys (smaller w) or earlier CG convergence simply finish sooner.
+// One wave per chunk.  The wave loads the chunk's boundary state and keys
+// once, then runs the CG of its NW = C/16 token tiles one after another (each
+// tile leaves its loop as soon as its 16 tokens have stopped), parks every
+// tile's solution x in LDS, and finally loads Gb and the values once for the
+// read-out of all tiles.
 //
 // Register layout (lane l, tl = l%16, g = l/16): every CG vector of token
 // 16w + tl keeps dims 16a + 4g + {0..3} (a < D/16) as f32x4 v[a].  Matrix
@@ -25,10 +25,9 @@
 //   kc[nt][mj]  key columns: K[32mj+4g+{0..3}, 32mj+16+4g+{0..3}][16nt+tl]
 //               (value columns for the read-out).
 // The state and the row fragments are fetched from global memory in one
-// batch (a single memory round trip); the column fragments are then formed
-// from the row fragments by an exact MFMA transpose, so the CG loop touches
-// no memory at all.
-// MFMA accumulators stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
+// batch; the column fragments are then formed from the row fragments by an
+// exact MFMA transpose, so the CG loop touches no memory.  MFMA accumulators
+// stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -42,29 +41,23 @@ void cg_bf16_kernel(CgParams p) {
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
 
   const int lane = threadIdx.x, tl = lane & 15, g = lane >> 4;
-  const int xcd = blockIdx.x & 7;
-  const int local = blockIdx.x >> 3;
-  const int chunk = (local / NW) * 8 + xcd;
-  if (chunk >= p.BH * p.NC) return;
-  // heavier tiles (more causal keys) are dispatched first
-  const int w = __builtin_amdgcn_readfirstlane(NW - 1 - (local % NW));
+  const int chunk = blockIdx.x;
   const int bh = chunk / p.NC, c = chunk % p.NC;
   const int h = bh % p.H;
   const int T = p.T, s = c * C, Lc = min(C, T - s);
   const size_t row0 = (size_t)bh * T + s;
-  const int tloc = 16 * w + tl;
-  const bool valid = tloc < Lc;
-  const int nrows = min(16 * (w + 1), Lc);  // key rows this tile can see
 
+  __shared__ f32x4 xs[NW * ND * 64];   // solutions of the tiles, [tile][a][lane]
   __shared__ float lam_s[D];
   __shared__ float bcum[C];
   __shared__ float betas[C];
 
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v);
+  const uint16_t* Qg = static_cast<const uint16_t*>(p.q);
   const size_t snap = (size_t)chunk * (D * D / 8);
 
-  // ---- one batch of loads: state, key rows, key columns, query, gates --------
+  // ---- one batch of loads: state, key rows, gates, Lambda ----------------------
   bf16x8 mf[ND][NM];
   bf16x8 kr[NW][NM];
   bf16x8 kc[ND][NMJ];
@@ -75,8 +68,7 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) mf[nt][m] = F[(nt * NM + m) * 64 + lane];
   };
-  // row fragments of X (K or V): X[16jt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}],
-  // zero for j-tiles past w and rows past nrows
+  // row fragments X[16jt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}], zero past Lc
   auto load_rows = [&](const uint16_t* X, bf16x8 (&dst)[NW][NM]) {
 #pragma unroll
     for (int jt = 0; jt < NW; ++jt) {
@@ -84,7 +76,7 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         u16x4 lo = u16x4{0, 0, 0, 0}, hi = lo;
-        if (jt <= w && j < nrows) {
+        if (j < Lc) {
           const uint16_t* src = X + (row0 + j) * D + 32 * m + 4 * g;
           lo = *reinterpret_cast<const u16x4*>(src);
           hi = *reinterpret_cast<const u16x4*>(src + 16);
@@ -117,17 +109,24 @@ void cg_bf16_kernel(CgParams p) {
       }
     }
   };
+  // keep the loop-invariant MFMA A operands in accumulation registers
+  auto pin_operands = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) asm volatile("" : "+a"(mf[nt][m]));
+#pragma unroll
+    for (int jt = 0; jt < NW; ++jt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) asm volatile("" : "+a"(kr[jt][m]));
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+      for (int mj = 0; mj < NMJ; ++mj) asm volatile("" : "+a"(kc[nt][mj]));
+  };
+
   load_state(p.hb);
   load_rows(Kg, kr);
-
-  f32x4 r[ND], x[ND], pv[ND], acc[ND];
-  const uint16_t* Qg = static_cast<const uint16_t*>(p.q);
-#pragma unroll
-  for (int a = 0; a < ND; ++a) {
-    r[a] = valid ? load4<true>(Qg, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
-    x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pv[a] = r[a];
-  }
   {
     float lg = 0.f, bt = 0.f;
     if (lane < Lc) {
@@ -147,64 +146,44 @@ void cg_bf16_kernel(CgParams p) {
   }
   __syncthreads();
   columns_from_rows(kr);
-
-  // keep the loop-invariant MFMA A operands in accumulation registers
-  auto pin_operands = [&]() {
-#pragma unroll
-    for (int nt = 0; nt < ND; ++nt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) asm volatile("" : "+a"(mf[nt][m]));
-#pragma unroll
-    for (int jt = 0; jt < NW; ++jt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) asm volatile("" : "+a"(kr[jt][m]));
-#pragma unroll
-    for (int nt = 0; nt < ND; ++nt)
-#pragma unroll
-      for (int mj = 0; mj < NMJ; ++mj) asm volatile("" : "+a"(kc[nt][mj]));
-  };
   pin_operands();
 
-  // ---- per-token constants -------------------------------------------------------
-  const float btl = bcum[tloc];
-  const float Gam = expf(btl);
-  float W[NW][4];
-#pragma unroll
-  for (int jt = 0; jt < NW; ++jt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * jt + 4 * g + i;
-      W[jt][i] = (jt <= w && j <= tloc && valid) ? expf(btl - bcum[j]) * betas[j] : 0.f;
-    }
+  // ---- per-tile machinery ----------------------------------------------------------
+  float W[NW][4];   // causal decayed weights W_tj of the current tile's tokens
+  float Gam = 1.f;  // Gamma_t of the current tile's token
+  int w = 0;        // current tile (wave-uniform)
 
   // S^T <- W .* (K U^T): the causal, decayed key scores of the tile's tokens
   auto scores = [&](const bf16x8* ub, bf16x8* sb) {
     f32x4 sc[NW];
 #pragma unroll
     for (int jt = 0; jt < NW; ++jt) {
-      sc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (jt <= w) {
+        sc[jt] = mfma_bf16(kr[jt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int m = 0; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
+        for (int m = 1; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
+        asm volatile("" : "+v"(sc[jt]));
       }
-      asm volatile("" : "+v"(sc[jt]));
     }
 #pragma unroll
     for (int mj = 0; mj < NMJ; ++mj) {
-      const int jl = 2 * mj, jh = (2 * mj + 1) % NW;
-      const f32x4 lo = sc[jl] * f32x4{W[jl][0], W[jl][1], W[jl][2], W[jl][3]};
-      const f32x4 hi = (2 * mj + 1 < NW) ? sc[jh] * f32x4{W[jh][0], W[jh][1], W[jh][2], W[jh][3]}
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-      sb[mj] = pack8(lo, hi);
+      if (2 * mj <= w) {
+        const int jl = 2 * mj, jh = (2 * mj + 1) % NW;
+        const f32x4 lo = sc[jl] * f32x4{W[jl][0], W[jl][1], W[jl][2], W[jl][3]};
+        f32x4 hi = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (2 * mj + 1 <= w) hi = sc[jh] * f32x4{W[jh][0], W[jh][1], W[jh][2], W[jh][3]};
+        sb[mj] = pack8(lo, hi);
+      }
     }
   };
   // acc <- Gam * (Mb U^T) + lam .* U (when with_lambda) + Y^T S^T
+  f32x4 acc[ND];
   auto product = [&](const f32x4* u, const bf16x8* ub, const bf16x8* sb, const bool with_lambda) {
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 t = mfma_bf16(mf[nt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int m = 0; m < NM; ++m) t = mfma_bf16(mf[nt][m], ub[m], t);
+      for (int m = 1; m < NM; ++m) t = mfma_bf16(mf[nt][m], ub[m], t);
       asm volatile("" : "+v"(t));
       acc[nt] = t * Gam;
       if (with_lambda) acc[nt] += *reinterpret_cast<const f32x4*>(&lam_s[16 * nt + 4 * g]) * u[nt];
@@ -219,84 +198,122 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) asm volatile("" : "+v"(acc[nt]));
   };
+  auto tile_constants = [&]() {
+    const int tloc = 16 * w + tl;
+    const bool valid = tloc < Lc;
+    const float btl = bcum[tloc];
+    Gam = expf(btl);
+#pragma unroll
+    for (int jt = 0; jt < NW; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * jt + 4 * g + i;
+        W[jt][i] = (jt <= w && j <= tloc && valid) ? expf(btl - bcum[j]) * betas[j] : 0.f;
+      }
+  };
 
-  // ---- conjugate gradient ---------------------------------------------------------
-  float rho = 0.f;
-#pragma unroll
-  for (int a = 0; a < ND; ++a) rho += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
-  rho = sum_lane_groups(rho);
-  int n = 0;
-  bool stopped = false;
-  for (int it = 0; it < p.max_steps; ++it) {
-    const bool active = !stopped && rho > 0.f && rho > p.tol2;
-    if (!__any(active)) break;
-    pin_operands();
-    bf16x8 ub[NM], sb[NMJ];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) ub[m] = pack8(pv[2 * m], pv[2 * m + 1]);
-    scores(ub, sb);
-    product(pv, ub, sb, true);
-    float pw = 0.f;
-#pragma unroll
-    for (int a = 0; a < ND; ++a)
-      pw += pv[a][0] * acc[a][0] + pv[a][1] * acc[a][1] + pv[a][2] * acc[a][2] + pv[a][3] * acc[a][3];
-    pw = sum_lane_groups(pw);
-    const bool ok = active && pw > 0.f;
-    stopped = !ok;
-    const float alpha = ok ? rho * __builtin_amdgcn_rcpf(pw) : 0.f;
-    float rr = 0.f;
+  // ---- conjugate gradient, tile by tile -------------------------------------------
+  for (int wt = 0; wt < NW; ++wt) {
+    w = __builtin_amdgcn_readfirstlane(wt);
+    const int tloc = 16 * w + tl;
+    const bool valid = tloc < Lc;
+    tile_constants();
+    f32x4 r[ND], x[ND], pv[ND];
 #pragma unroll
     for (int a = 0; a < ND; ++a) {
-      x[a] += alpha * pv[a];
-      r[a] -= alpha * acc[a];
-      rr += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
+      r[a] = valid ? load4<true>(Qg, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pv[a] = r[a];
     }
-    rr = sum_lane_groups(rr);
-    // a stopped token keeps x and r (alpha = 0); its direction becomes r, which
-    // stays finite and is never used again
-    const float bet = ok ? rr * __builtin_amdgcn_rcpf(rho) : 0.f;
+    float rho = 0.f;
 #pragma unroll
-    for (int a = 0; a < ND; ++a) pv[a] = r[a] + bet * pv[a];
-    rho = ok ? rr : rho;
-    n += ok ? 1 : 0;
+    for (int a = 0; a < ND; ++a) rho += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
+    rho = sum_lane_groups(rho);
+    int n = 0;
+    bool stopped = false;
+    for (int it = 0; it < p.max_steps; ++it) {
+      const bool active = !stopped && rho > 0.f && rho > p.tol2;
+      if (!__any(active)) break;
+      pin_operands();
+      bf16x8 ub[NM], sb[NMJ];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) ub[m] = pack8(pv[2 * m], pv[2 * m + 1]);
+      scores(ub, sb);
+      product(pv, ub, sb, true);
+      float pw = 0.f;
+#pragma unroll
+      for (int a = 0; a < ND; ++a)
+        pw += pv[a][0] * acc[a][0] + pv[a][1] * acc[a][1] + pv[a][2] * acc[a][2] + pv[a][3] * acc[a][3];
+      pw = sum_lane_groups(pw);
+      const bool ok = active && pw > 0.f;
+      stopped = !ok;
+      const float alpha = ok ? rho * __builtin_amdgcn_rcpf(pw) : 0.f;
+      float rr = 0.f;
+#pragma unroll
+      for (int a = 0; a < ND; ++a) {
+        x[a] += alpha * pv[a];
+        r[a] -= alpha * acc[a];
+        rr += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
+      }
+      rr = sum_lane_groups(rr);
+      // a stopped token keeps x and r (alpha = 0); its direction becomes r,
+      // which stays finite and is never used again
+      const float bet = ok ? rr * __builtin_amdgcn_rcpf(rho) : 0.f;
+      // p <- r + bet p in place (three-operand FMA; the two-address form would
+      // tie the result to r, which stays live, and cost a copy per element)
+#pragma unroll
+      for (int a = 0; a < ND; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm("v_fma_f32 %0, %1, %0, %2" : "+v"(pv[a][i]) : "v"(bet), "v"(r[a][i]));
+      rho = ok ? rr : rho;
+      n += ok ? 1 : 0;
+    }
+#pragma unroll
+    for (int a = 0; a < ND; ++a) xs[(w * ND + a) * 64 + lane] = x[a];
+    if (valid) {
+      if (p.x_out) {
+#pragma unroll
+        for (int a = 0; a < ND; ++a)
+          *reinterpret_cast<f32x4*>(p.x_out + (row0 + tloc) * D + 16 * a + 4 * g) = x[a];
+      }
+      if (p.steps && g == 0) p.steps[row0 + tloc] = n;
+    }
   }
 
   // ---- read-out o_t = Gamma_t Gb x_t + sum_j W_tj (k_j . x_t) v_j ------------------
-  // Gb and the value columns replace Hb and the key columns; their loads are
-  // in flight while the scores of x against the keys are formed.
+  // Gb and the value columns replace Hb and the key columns (the key rows stay:
+  // the scores of x are against the keys).
   load_state(p.gb);
   {
     bf16x8 vr[NW][NM];
     load_rows(Vg, vr);
     columns_from_rows(vr);
   }
-  {
+  pin_operands();
+  for (int wt = 0; wt < NW; ++wt) {
+    w = __builtin_amdgcn_readfirstlane(wt);
+    const int tloc = 16 * w + tl;
+    tile_constants();
+    f32x4 x[ND];
+#pragma unroll
+    for (int a = 0; a < ND; ++a) x[a] = xs[(w * ND + a) * 64 + lane];
     bf16x8 xb[NM], sb[NMJ];
 #pragma unroll
     for (int m = 0; m < NM; ++m) xb[m] = pack8(x[2 * m], x[2 * m + 1]);
     scores(xb, sb);
     pin_operands();
     product(x, xb, sb, false);
-  }
-
-  if (valid) {
-    const size_t orow = (row0 + tloc) * D;
+    if (tloc < Lc) {
 #pragma unroll
-    for (int a = 0; a < ND; ++a) *reinterpret_cast<f32x4*>(p.o + orow + 16 * a + 4 * g) = acc[a];
-    if (p.x_out) {
-#pragma unroll
-      for (int a = 0; a < ND; ++a) *reinterpret_cast<f32x4*>(p.x_out + orow + 16 * a + 4 * g) = x[a];
+      for (int a = 0; a < ND; ++a)
+        *reinterpret_cast<f32x4*>(p.o + (row0 + tloc) * D + 16 * a + 4 * g) = acc[a];
     }
-    if (p.steps && g == 0) p.steps[row0 + tloc] = n;
   }
 }
 
 template <int D, int C>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
-  constexpr int NW = C / 16;
-  const long long chunks = (long long)p.BH * p.NC;
-  const long long groups = (chunks + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * NW));
+  const dim3 grid((unsigned)((long long)p.BH * p.NC));
   hipLaunchKernelGGL((cg_bf16_kernel<D, C>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
