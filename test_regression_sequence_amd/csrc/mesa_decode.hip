@@ -6,14 +6,22 @@
 // solve (H + Lambda) x = q by conjugate gradient (fixed steps or residual
 // test), emit o = G x.  The step is bound by streaming H and G through HBM
 // (2 * 4 * d^2 bytes read and written per (sequence, head) pair); the CG
-// iterations run on the register-resident H between the two streams.
+// iterations run on the register-resident H, and with few registers per wave
+// several pairs share each CU, so one pair's solve overlaps others' streams.
 //
-// One workgroup of 256 threads per pair.  Thread (rg, j) owns column j of H
-// for the rows of row group rg; a row of H is read and written by D
-// consecutive threads, so the H stream is fully coalesced.  H is symmetric,
-// so column j equals row j and the matrix-vector product needs only a
-// broadcast of p (LDS) and a sum over the row groups.  The update forms
-// k_r*k_j before scaling, so an exactly symmetric H stays exactly symmetric.
+// One workgroup of NW = 4 waves per pair; both states move as 16-byte row
+// segments, every wave instruction covering 1 KB of contiguous memory.
+//   H: thread t holds the 4 columns 4(t % Q) .. +3 (Q = D/4 column quads) of
+//      R consecutive rows (R = D*Q/(64 NW)).  H is symmetric, so y = H p is
+//      the column sums sum_r H[r][j] p_r: a thread forms its part for 4
+//      columns, the row groups of a wave combine by lane swaps, and the waves
+//      combine through LDS at the iteration's single barrier.
+//   CG vectors: every wave keeps all D entries (lane l holds entries l + 64e),
+//      so both dot products are wave-local and all waves take identical
+//      decisions.
+//   G: the same row segments; o = G x is reduced across the lanes of a row.
+// The update forms k_r*k_j before scaling, so an exactly symmetric H stays
+// exactly symmetric.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -21,118 +29,160 @@ namespace mesa {
 
 namespace {
 
-constexpr int kDecThreads = 256;
-
-template <int NWAVES>
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  v = wave_sum(v);
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NWAVES; ++i) s += red[i];
-  __syncthreads();
-  return s;
-}
+constexpr int kDecWaves = 4;
 
 template <bool BF16, int D>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
-  constexpr int RG = kDecThreads / D;  // row groups
-  constexpr int RPT = D / RG;          // rows of H per thread
-  constexpr int NWV = kDecThreads / 64;
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) {
+  constexpr int NW = kDecWaves;
+  constexpr int Q = D / 4;                   // 16-byte column quads per row
+  constexpr int TPR = 64 / Q;                // row groups per wave (lanes sharing a quad)
+  constexpr int RPT = D / (NW * TPR);        // rows per thread
+  constexpr int EPL = D / 64;                // CG vector entries per lane
+  static_assert(TPR == 2 || TPR == 4, "a wave holds 2 or 4 row groups");
+  static_assert(RPT % 4 == 0, "rows per thread in fours");
   const int pair = blockIdx.x;
   const int h = pair % p.H;
-  const int tid = threadIdx.x, j = tid % D, rg = tid / D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int cq = lane % Q;                       // column quad
+  const int row0 = (wave * TPR + lane / Q) * RPT;  // first row of this thread
 
-  __shared__ float ks[D], qs[D], vs[D], xs[D], pvec[D];
-  __shared__ float part[RG][D];
-  __shared__ float red[NWV];
+  __shared__ float ks[D], qs[D], vs[D], lam_s[D];
+  __shared__ __attribute__((aligned(16))) float pb[NW][D];      // per-wave copy of p, then x
+  __shared__ __attribute__((aligned(16))) float part[2][NW][D]; // per-wave column sums, double buffered
 
-  if (tid < D) {
-    ks[tid] = load1<BF16>(p.k, (size_t)pair * D + tid);
-    qs[tid] = load1<BF16>(p.q, (size_t)pair * D + tid);
-    vs[tid] = load1<BF16>(p.v, (size_t)pair * D + tid);
+  for (int i = tid; i < D; i += 64 * NW) {
+    ks[i] = load1<BF16>(p.k, (size_t)pair * D + i);
+    qs[i] = load1<BF16>(p.q, (size_t)pair * D + i);
+    vs[i] = load1<BF16>(p.v, (size_t)pair * D + i);
+    lam_s[i] = p.lam[(size_t)h * D + i];
   }
   const float gam = p.gamma[pair], bet = p.beta[pair];
+
+  // ---- H <- gamma H + beta (k k^T), kept in registers, written back --------------
+  // wave-uniform base plus a 32-bit per-lane byte offset (row0, cq) plus a
+  // constant per row: lets every row share one address register.  The states
+  // are touched once per step, so they stream with nontemporal hints (each
+  // wave then covers its 16 KB of a state contiguously at full HBM rate).
+  char* Hb = reinterpret_cast<char*>(p.h + (size_t)pair * D * D);
+  char* Gb = reinterpret_cast<char*>(p.g + (size_t)pair * D * D);
+  const uint64_t voff = (uint32_t)((row0 * D + 4 * cq) * 4);
+  auto at = [&](char* base, int i) { return reinterpret_cast<f32x4*>(base + voff + i * D * 4); };
+  f32x4 hreg[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) hreg[i] = __builtin_nontemporal_load(at(Hb, i));
   __syncthreads();
-
-  // ---- H <- gamma H + beta (k k^T), kept in registers --------------------------
-  float* Hp = p.h + (size_t)pair * D * D;
-  float hreg[RPT];
-  const float kj = ks[j];
+  const f32x4 kq = *reinterpret_cast<const f32x4*>(&ks[4 * cq]);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rg * RPT + i;
-    hreg[i] = Hp[(size_t)row * D + j];
-  }
+    const float kr = ks[row0 + i];
+    f32x4 hv;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = rg * RPT + i;
-    const float hv = gam * hreg[i] + bet * (ks[row] * kj);
+    for (int e = 0; e < 4; ++e) hv[e] = gam * hreg[i][e] + bet * (kr * kq[e]);
     hreg[i] = hv;
-    Hp[(size_t)row * D + j] = hv;
+    __builtin_nontemporal_store(hv, at(Hb, i));
   }
 
-  // ---- CG on (H + Lambda) x = q; vector index j lives in thread j (rg == 0) ----
-  const bool owner = rg == 0;
-  const float lamj = p.lam[(size_t)h * D + j];
-  float xj = 0.f, rj = owner ? qs[j] : 0.f, pj = rj;
-  float rho = block_sum<NWV>(rj * rj, red);
+  // ---- CG on (H + Lambda) x = q -------------------------------------------------------
+  float xv[EPL], rv[EPL], pv[EPL], lv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    xv[e] = 0.f;
+    rv[e] = qs[lane + 64 * e];
+    pv[e] = rv[e];
+    lv[e] = lam_s[lane + 64 * e];
+  }
+  // identical in every lane by construction; taken from lane 0 so that the
+  // loop's exit tests are wave-uniform beyond doubt (a barrier is inside)
+  auto vsum = [&](const float* a, const float* b) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s += a[e] * b[e];
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_sum(s))));
+  };
+  float* mypb = pb[wave];
+  float rho = vsum(rv, rv);
   int n = 0;
   for (int it = 0; it < p.max_steps; ++it) {
     if (!(rho > 0.f && rho > p.tol2)) break;
-    if (owner) pvec[j] = pj;
-    __syncthreads();
-    float acc = 0.f;
+    // publish p to this wave's own LDS copy (read back by the same wave only)
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) acc += hreg[i] * pvec[rg * RPT + i];
-    part[rg][j] = acc;
-    __syncthreads();
-    float wj = 0.f;
-    if (owner) {
+    for (int e = 0; e < EPL; ++e) mypb[lane + 64 * e] = pv[e];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the writes above have landed
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < RG; ++q) wj += part[q][j];
-      wj += lamj * pj;
+    for (int i4 = 0; i4 < RPT / 4; ++i4) {
+      const f32x4 pr = *reinterpret_cast<const f32x4*>(&mypb[row0 + 4 * i4]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += hreg[4 * i4 + u] * pr[u];
     }
-    const float pw = block_sum<NWV>(pj * wj, red);
+    // combine the row groups of this wave: lanes l, l^32 (and l^16 when 4 groups)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (TPR == 4) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
+        acc[e] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      }
+      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
+      acc[e] = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    }
+    float(*pt)[D] = part[it & 1];
+    if (lane < Q) *reinterpret_cast<f32x4*>(&pt[wave][4 * cq]) = acc;
+    __syncthreads();
+    float wv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int j = lane + 64 * e;
+      float y = pt[0][j];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) y += pt[q][j];
+      wv[e] = y + lv[e] * pv[e];
+    }
+    const float pw = vsum(pv, wv);
     if (!(pw > 0.f)) break;
     const float alpha = rho / pw;
-    xj += alpha * pj;
-    rj -= alpha * wj;
-    const float rr = block_sum<NWV>(rj * rj, red);
-    pj = rj + (rr / rho) * pj;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      xv[e] += alpha * pv[e];
+      rv[e] -= alpha * wv[e];
+    }
+    const float rr = vsum(rv, rv);
+    const float bcg = rr / rho;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) pv[e] = rv[e] + bcg * pv[e];
     rho = rr;
     ++n;
   }
-  if (owner) xs[j] = xj;
-  __syncthreads();
-
-  // ---- G <- gamma G + beta (v k^T); o = G x ------------------------------------
-  float* Gp = p.g + (size_t)pair * D * D;
-  if (tid < D) {
-    const int row = tid;
-    const float bv = bet * vs[row];
-    float o = 0.f;
-#pragma unroll 4
-    for (int c4 = 0; c4 < D / 4; ++c4) {
-      f32x4 gv = *reinterpret_cast<const f32x4*>(Gp + (size_t)row * D + 4 * c4);
+  // x to this wave's LDS copy for the G read-out
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gv[e] = gam * gv[e] + bv * ks[4 * c4 + e];
-        o += gv[e] * xs[4 * c4 + e];
-      }
-      *reinterpret_cast<f32x4*>(Gp + (size_t)row * D + 4 * c4) = gv;
-    }
-    p.o[(size_t)pair * D + row] = o;
-    if (p.x_out) p.x_out[(size_t)pair * D + row] = xs[row];
+  for (int e = 0; e < EPL; ++e) mypb[lane + 64 * e] = xv[e];
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+
+  // ---- G <- gamma G + beta (v k^T); o = G x ------------------------------------------
+  f32x4 greg[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) greg[i] = __builtin_nontemporal_load(at(Gb, i));
+  const f32x4 xq = *reinterpret_cast<const f32x4*>(&mypb[4 * cq]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = row0 + i;
+    const float bv = bet * vs[row];
+    f32x4 gv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[e] = gam * greg[i][e] + bv * kq[e];
+    __builtin_nontemporal_store(gv, at(Gb, i));
+    const float s = group_sum<Q>(gv[0] * xq[0] + gv[1] * xq[1] + gv[2] * xq[2] + gv[3] * xq[3]);
+    if (cq == 0) p.o[(size_t)pair * D + row] = s;
+  }
+  if (wave == 0 && p.x_out) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) p.x_out[(size_t)pair * D + lane + 64 * e] = xv[e];
   }
   if (tid == 0 && p.steps) p.steps[pair] = n;
 }
 
 template <bool BF16, int D>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<BF16, D>), dim3(p.P), dim3(kDecThreads), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<BF16, D>), dim3(p.P), dim3(64 * kDecWaves), 0, s, p);
   return hipGetLastError();
 }
 
