@@ -167,6 +167,51 @@ def bench_decode(cfg, steps, warmup):
     }
 
 
+def kernel_source_digest(names=("mesa_cg_bf16.hip", "mesa_common.h", "mesa_kernels.h")) -> str:
+    """sha256 over the sources of the CG kernel (ties a traffic record to one kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "test_regression_sequence_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(digest: str):
+    """HBM bytes per CG launch from the committed counter summary, or None.
+
+    The summary holds one line ``traffic_json: {...}`` with the FETCH_SIZE and
+    WRITE_SIZE readings per dispatch, each already scaled by the factor a plain
+    copy of known size gives for the same counter.  A record taken on another
+    version of the kernel's sources does not count.
+    """
+    path = os.path.join(ROOT, "profiles", "cg_bf16_lm1b_d128_hbm_traffic.md")
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source_sha256") == digest:
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
+def calibrate_copy(mib: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n, "launches": reps}), flush=True)
+
+
 def cpu_baseline(x, slices: int, tokens: int):
     from threadpoolctl import threadpool_limits
     from oracle import mesa_forward
@@ -207,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -222,6 +269,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
     mesa.lib()
     cfg = CONFIGS[args.workload]
     fw = bench_forward(cfg, args.steps, args.warmup)
@@ -231,6 +281,10 @@ def main():
     cg_flops = f["cg_kernel"] * tokens
     cg_tflops = cg_flops / (fw["cg_ms"] * 1e-3) / 1e12
     total_tflops = f["total"] * tokens / (fw["ms"] * 1e-3) / 1e12
+    traffic = None
+    rec = recorded_traffic(kernel_source_digest()) if cfg.name == "lm1b-d128-bf16" else None
+    if rec is not None:
+        traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
     line = {
         "metric": "Mesa fwd tokens/s (B*H*T/s) at d=128",
@@ -258,7 +312,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(cg_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "flops_per_launch": cg_flops,
             "avg_launch_ms": round(fw["cg_ms"], 4),
         },
