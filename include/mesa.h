@@ -80,9 +80,11 @@ typedef struct {
   mesa_dtype in_dtype;  /* dtype of q, k, v                                        */
 } mesa_fwd_desc;
 
-/* Bytes of scratch memory mesa_fwd_chunked needs for `d` (the decayed
- * chunk-boundary states).  Returns 0 for an invalid or unsupported
- * descriptor, and for T == 0. */
+/* Bytes of scratch memory mesa_fwd_chunked needs for `d`: the decayed
+ * chunk-boundary states and, for MESA_BF16 inputs, one int32 per chunk
+ * (rounded up to 256 bytes) recording which chunks the strong-decay kernel
+ * solves.  Returns 0 for an invalid or unsupported descriptor, and for
+ * T == 0. */
 size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d);
 
 /* Chunkwise-parallel Mesa forward over whole sequences

@@ -53,7 +53,8 @@ size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d) {
   if (check_desc(d) != MESA_OK || d->T == 0) return 0;
   const size_t nc = (size_t)(d->T + d->chunk - 1) / d->chunk;
   const size_t bh = (size_t)d->B * d->H;
-  return 2 * bh * nc * mesa::snapshot_bytes(d->in_dtype == MESA_BF16, d->dk);
+  const bool bf16 = d->in_dtype == MESA_BF16;
+  return 2 * bh * nc * mesa::snapshot_bytes(bf16, d->dk) + (bf16 ? mesa::flag_bytes(bh * nc) : 0);
 }
 
 }  // extern "C"
@@ -85,6 +86,8 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
   const size_t snap = (size_t)BH * NC * mesa::snapshot_bytes(bf16, D);
   void* hb = workspace;
   void* gb = workspace ? static_cast<char*>(workspace) + snap : nullptr;
+  int32_t* flags = (workspace && bf16) ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * snap)
+                                       : nullptr;
 
   if ((phases & kScan) && (any_tokens || h_final || g_final)) {
     mesa::ScanParams sp{};
@@ -97,7 +100,7 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
   if ((phases & kSolve) && any_tokens) {
     mesa::CgParams cp{};
     cp.q = q; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
-    cp.hb = hb; cp.gb = gb; cp.o = o; cp.steps = steps; cp.x_out = x_out;
+    cp.hb = hb; cp.gb = gb; cp.o = o; cp.steps = steps; cp.x_out = x_out; cp.unscaled = flags;
     cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
     cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
     if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;

@@ -4,11 +4,28 @@
 // technical summary, "Mesa layer": CG query response, chunk-parallel states,
 // dynamic CG step count); this file is the tuned bf16 path.
 //
+// Within a chunk of tokens s..e with b_t = sum_{i=s..t} log gamma_i and
+// Gamma_t = e^{b_t}, the system of token t is
+//     A_t = Gamma_t Hb + sum_{j<=t} e^{b_t - b_j} beta_j k_j k_j^T + Lambda.
+// Divided by Gamma_t it becomes
+//     A_t / Gamma_t = Hb + sum_{j<=t} w_j k_j k_j^T + Lambda / Gamma_t,
+//     w_j = beta_j e^{-b_j},
+// whose key weights no longer depend on t.  CG on (A_t / Gamma_t) xh = q from
+// xh = 0 has exactly the residuals, search directions and step counts of CG
+// on A_t x = q, with xh = Gamma_t x; and the output needs no rescaling:
+//     o_t = G_t x = Gb xh + sum_{j<=t} w_j (k_j . xh) v_j.
+// So the weights fold into the key (value) columns once per chunk, the
+// boundary-state product needs no per-token multiply, and the causal mask is
+// all that is left per iteration.  A chunk that decays so strongly that
+// e^{-b_j} could overflow (e^{-b_e} > e^40) is only flagged here; the kernel
+// in mesa_cg_bf16_unscaled.hip then solves it in the unscaled form.
+//
 // One wave per chunk.  The wave loads the chunk's boundary state and keys
 // once, then runs the CG of its NW = C/16 token tiles one after another (each
 // tile leaves its loop as soon as its 16 tokens have stopped), parks every
-// tile's solution x in LDS, and finally loads Gb and the values once for the
-// read-out of all tiles.
+// tile's solution in LDS, and finally loads Gb and the values once for the
+// read-out of all tiles.  Every tile has its own straight-line code (the
+// causal extent of a tile is a compile-time constant).
 //
 // Register layout (lane l, tl = l%16, g = l/16): every CG vector of token
 // 16w + tl keeps dims 16a + 4g + {0..3} (a < D/16) as f32x4 v[a].  Matrix
@@ -22,18 +39,24 @@
 //               written by the scan kernel: row 16nt+tl, cols 32m+4g+{0..3},
 //               32m+16+4g+{0..3};
 //   kr[jt][m]   key rows:    K[16jt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}];
-//   kc[nt][mj]  key columns: K[32mj+4g+{0..3}, 32mj+16+4g+{0..3}][16nt+tl]
-//               (value columns for the read-out).
+//   kc[nt][mj]  weighted key columns: w_j K[j][16nt+tl] for
+//               j = 32mj+4g+{0..3}, 32mj+16+4g+{0..3} (weighted value
+//               columns for the read-out).
 // The state and the row fragments are fetched from global memory in one
-// batch; the column fragments are then formed from the row fragments by an
-// exact MFMA transpose, so the CG loop touches no memory.  MFMA accumulators
-// stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
+// batch; the column fragments are then formed from the (weighted) row
+// fragments by an exact MFMA transpose, so the CG loop touches no global
+// memory.  MFMA accumulators stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
+#include <type_traits>
+
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
 
 namespace {
+
+template <int W>
+using tile_c = std::integral_constant<int, W>;
 
 template <int D, int C>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -47,7 +70,7 @@ void cg_bf16_kernel(CgParams p) {
   const int T = p.T, s = c * C, Lc = min(C, T - s);
   const size_t row0 = (size_t)bh * T + s;
 
-  __shared__ f32x4 xs[NW * ND * 64];   // solutions of the tiles, [tile][a][lane]
+  __shared__ f32x4 xs[NW * ND * 64];   // solutions xh of the tiles, [tile][a][lane]
   __shared__ float lam_s[D];
   __shared__ float bcum[C];
   __shared__ float betas[C];
@@ -109,6 +132,25 @@ void cg_bf16_kernel(CgParams p) {
       }
     }
   };
+  // rows times the per-row key weight w_{16jt+tl} (scaled form), rounded to bf16
+  auto weighted_rows = [&](const bf16x8 (&rows)[NW][NM], bf16x8 (&dst)[NW][NM]) {
+#pragma unroll
+    for (int jt = 0; jt < NW; ++jt) {
+      const int j = 16 * jt + tl;
+      const float wj = (j < Lc) ? betas[j] * expf(-bcum[j]) : 0.f;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const u16x8 u = __builtin_bit_cast(u16x8, rows[jt][m]);
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = wj * bf16_to_f32(u[e]);
+          hi[e] = wj * bf16_to_f32(u[4 + e]);
+        }
+        dst[jt][m] = pack8(lo, hi);
+      }
+    }
+  };
   // keep the loop-invariant MFMA A operands in accumulation registers
   auto pin_operands = [&]() {
 #pragma unroll
@@ -145,79 +187,72 @@ void cg_bf16_kernel(CgParams p) {
     for (int i = lane; i < D; i += 64) lam_s[i] = p.lam[(size_t)h * D + i];
   }
   __syncthreads();
-  columns_from_rows(kr);
+  // the chunk's total decay decides the form (wave-uniform); a chunk left to
+  // the unscaled kernel is flagged for it
+  const bool scaled = __builtin_amdgcn_readfirstlane(bcum[Lc - 1] >= -kMaxScaledDecay ? 1 : 0) != 0;
+  if (lane == 0) p.unscaled[chunk] = scaled ? 0 : 1;
+  if (!scaled) return;
+  {
+    bf16x8 wr[NW][NM];
+    weighted_rows(kr, wr);
+    columns_from_rows(wr);
+  }
   pin_operands();
 
   // ---- per-tile machinery ----------------------------------------------------------
-  float W[NW][4];   // causal decayed weights W_tj of the current tile's tokens
-  float Gam = 1.f;  // Gamma_t of the current tile's token
-  int w = 0;        // current tile (wave-uniform)
 
-  // S^T <- W .* (K U^T): the causal, decayed key scores of the tile's tokens
-  auto scores = [&](const bf16x8* ub, bf16x8* sb) {
-    f32x4 sc[NW];
-#pragma unroll
-    for (int jt = 0; jt < NW; ++jt) {
-      if (jt <= w) {
-        sc[jt] = mfma_bf16(kr[jt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int m = 1; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
-        asm volatile("" : "+v"(sc[jt]));
-      }
-    }
-#pragma unroll
-    for (int mj = 0; mj < NMJ; ++mj) {
-      if (2 * mj <= w) {
-        const int jl = 2 * mj, jh = (2 * mj + 1) % NW;
-        const f32x4 lo = sc[jl] * f32x4{W[jl][0], W[jl][1], W[jl][2], W[jl][3]};
-        f32x4 hi = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (2 * mj + 1 <= w) hi = sc[jh] * f32x4{W[jh][0], W[jh][1], W[jh][2], W[jh][3]};
-        sb[mj] = pack8(lo, hi);
-      }
-    }
-  };
-  // acc <- Gam * (Mb U^T) + lam .* U (when with_lambda) + Y^T S^T
+  // acc[nt] <- Mb U^T + Y^T S^T with S^T the causal key scores of the tile's
+  // tokens (the weights sit in the key columns; only the diagonal block needs
+  // the mask j <= t).  Issue order: score MFMAs, boundary-state MFMAs, then
+  // the mask and packing of the scores (long finished by then), then the
+  // intra-chunk MFMAs; the VALU work on acc comes after all of them, so no
+  // instruction waits on an MFMA issued just before it.
   f32x4 acc[ND];
-  auto product = [&](const f32x4* u, const bf16x8* ub, const bf16x8* sb, const bool with_lambda) {
+  auto matvec = [&](auto wc, const bf16x8* ub) {
+    constexpr int w = decltype(wc)::value;
+    f32x4 sc[w + 1];
+#pragma unroll
+    for (int jt = 0; jt <= w; ++jt) {
+      sc[jt] = mfma_bf16(kr[jt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int m = 1; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
+    }
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) {
-      f32x4 t = mfma_bf16(mf[nt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      acc[nt] = mfma_bf16(mf[nt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int m = 1; m < NM; ++m) t = mfma_bf16(mf[nt][m], ub[m], t);
-      asm volatile("" : "+v"(t));
-      acc[nt] = t * Gam;
-      if (with_lambda) acc[nt] += *reinterpret_cast<const f32x4*>(&lam_s[16 * nt + 4 * g]) * u[nt];
+      for (int m = 1; m < NM; ++m) acc[nt] = mfma_bf16(mf[nt][m], ub[m], acc[nt]);
     }
 #pragma unroll
-    for (int mj = 0; mj < NMJ; ++mj) {
-      if (2 * mj <= w) {
+    for (int jt = 0; jt <= w; ++jt) asm volatile("" : "+v"(sc[jt]));
+    bf16x8 sb[w / 2 + 1];
 #pragma unroll
-        for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(kc[nt][mj], sb[mj], acc[nt]);
-      }
+    for (int i = 0; i < 4; ++i) sc[w][i] = (4 * g + i <= tl) ? sc[w][i] : 0.f;
+#pragma unroll
+    for (int mj = 0; mj <= w / 2; ++mj) {
+      const f32x4 hi = (2 * mj + 1 <= w) ? sc[2 * mj + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[mj] = pack8(sc[2 * mj], hi);
     }
+#pragma unroll
+    for (int mj = 0; mj <= w / 2; ++mj)
+#pragma unroll
+      for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(kc[nt][mj], sb[mj], acc[nt]);
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) asm volatile("" : "+v"(acc[nt]));
   };
-  auto tile_constants = [&]() {
-    const int tloc = 16 * w + tl;
-    const bool valid = tloc < Lc;
-    const float btl = bcum[tloc];
-    Gam = expf(btl);
-#pragma unroll
-    for (int jt = 0; jt < NW; ++jt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * jt + 4 * g + i;
-        W[jt][i] = (jt <= w && j <= tloc && valid) ? expf(btl - bcum[j]) * betas[j] : 0.f;
-      }
-  };
 
-  // ---- conjugate gradient, tile by tile -------------------------------------------
-  for (int wt = 0; wt < NW; ++wt) {
-    w = __builtin_amdgcn_readfirstlane(wt);
+  // ---- conjugate gradient of one tile -------------------------------------------
+  auto solve_tile = [&](auto wc) {
+    constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
     const bool valid = tloc < Lc;
-    tile_constants();
+    // Lambda / Gamma_t of the lane's token, held for the whole loop
+    f32x4 lt[ND];
+    {
+      const float lscale = expf(-bcum[tloc]);
+#pragma unroll
+      for (int a = 0; a < ND; ++a) lt[a] = *reinterpret_cast<const f32x4*>(&lam_s[16 * a + 4 * g]) * lscale;
+    }
     f32x4 r[ND], x[ND], pv[ND];
 #pragma unroll
     for (int a = 0; a < ND; ++a) {
@@ -235,27 +270,35 @@ void cg_bf16_kernel(CgParams p) {
       const bool active = !stopped && rho > 0.f && rho > p.tol2;
       if (!__any(active)) break;
       pin_operands();
-      bf16x8 ub[NM], sb[NMJ];
+      bf16x8 ub[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) ub[m] = pack8(pv[2 * m], pv[2 * m + 1]);
-      scores(ub, sb);
-      product(pv, ub, sb, true);
-      float pw = 0.f;
+      matvec(wc, ub);
+      // w = acc + (Lambda / Gamma_t) .* p and p.w, two independent chains
+      float pw0 = 0.f, pw1 = 0.f;
 #pragma unroll
-      for (int a = 0; a < ND; ++a)
-        pw += pv[a][0] * acc[a][0] + pv[a][1] * acc[a][1] + pv[a][2] * acc[a][2] + pv[a][3] * acc[a][3];
-      pw = sum_lane_groups(pw);
+      for (int a = 0; a < ND; ++a) {
+        acc[a] += lt[a] * pv[a];
+        pw0 += pv[a][0] * acc[a][0];
+        pw1 += pv[a][1] * acc[a][1];
+        pw0 += pv[a][2] * acc[a][2];
+        pw1 += pv[a][3] * acc[a][3];
+      }
+      const float pw = sum_lane_groups(pw0 + pw1);
       const bool ok = active && pw > 0.f;
       stopped = !ok;
       const float alpha = ok ? rho * __builtin_amdgcn_rcpf(pw) : 0.f;
-      float rr = 0.f;
+      float rr0 = 0.f, rr1 = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
         x[a] += alpha * pv[a];
         r[a] -= alpha * acc[a];
-        rr += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
+        rr0 += r[a][0] * r[a][0];
+        rr1 += r[a][1] * r[a][1];
+        rr0 += r[a][2] * r[a][2];
+        rr1 += r[a][3] * r[a][3];
       }
-      rr = sum_lane_groups(rr);
+      const float rr = sum_lane_groups(rr0 + rr1);
       // a stopped token keeps x and r (alpha = 0); its direction becomes r,
       // which stays finite and is never used again
       const float bet = ok ? rr * __builtin_amdgcn_rcpf(rho) : 0.f;
@@ -272,50 +315,65 @@ void cg_bf16_kernel(CgParams p) {
     for (int a = 0; a < ND; ++a) xs[(w * ND + a) * 64 + lane] = x[a];
     if (valid) {
       if (p.x_out) {
+        // x = xh / Gamma_t
+        const float xscale = expf(-bcum[tloc]);
 #pragma unroll
         for (int a = 0; a < ND; ++a)
-          *reinterpret_cast<f32x4*>(p.x_out + (row0 + tloc) * D + 16 * a + 4 * g) = x[a];
+          *reinterpret_cast<f32x4*>(p.x_out + (row0 + tloc) * D + 16 * a + 4 * g) = x[a] * xscale;
       }
       if (p.steps && g == 0) p.steps[row0 + tloc] = n;
     }
-  }
+  };
 
-  // ---- read-out o_t = Gamma_t Gb x_t + sum_j W_tj (k_j . x_t) v_j ------------------
-  // Gb and the value columns replace Hb and the key columns (the key rows stay:
-  // the scores of x are against the keys).
-  load_state(p.gb);
-  {
-    bf16x8 vr[NW][NM];
-    load_rows(Vg, vr);
-    columns_from_rows(vr);
-  }
-  pin_operands();
-  for (int wt = 0; wt < NW; ++wt) {
-    w = __builtin_amdgcn_readfirstlane(wt);
+  // ---- read-out of one tile: o_t = Gb xh + sum_{j<=t} w_j (k_j . xh) v_j --------
+  auto readout_tile = [&](auto wc) {
+    constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
-    tile_constants();
     f32x4 x[ND];
 #pragma unroll
     for (int a = 0; a < ND; ++a) x[a] = xs[(w * ND + a) * 64 + lane];
-    bf16x8 xb[NM], sb[NMJ];
+    bf16x8 xb[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) xb[m] = pack8(x[2 * m], x[2 * m + 1]);
-    scores(xb, sb);
     pin_operands();
-    product(x, xb, sb, false);
+    matvec(wc, xb);
     if (tloc < Lc) {
 #pragma unroll
       for (int a = 0; a < ND; ++a)
         *reinterpret_cast<f32x4*>(p.o + (row0 + tloc) * D + 16 * a + 4 * g) = acc[a];
     }
+  };
+
+  auto for_tiles = [&](auto fn) {
+    fn(tile_c<0>{});
+    if constexpr (NW > 1) fn(tile_c<(NW > 1 ? 1 : 0)>{});
+    if constexpr (NW > 2) fn(tile_c<(NW > 2 ? 2 : 0)>{});
+    if constexpr (NW > 3) fn(tile_c<(NW > 3 ? 3 : 0)>{});
+  };
+
+  for_tiles(solve_tile);
+
+  // Gb and the (weighted) value columns replace Hb and the key columns (the
+  // key rows stay: the scores of x are against the keys).
+  load_state(p.gb);
+  {
+    bf16x8 vr[NW][NM];
+    load_rows(Vg, vr);
+    bf16x8 wr[NW][NM];
+    weighted_rows(vr, wr);
+    columns_from_rows(wr);
   }
+  pin_operands();
+  for_tiles(readout_tile);
 }
 
 template <int D, int C>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((long long)p.BH * p.NC));
   hipLaunchKernelGGL((cg_bf16_kernel<D, C>), grid, dim3(64), 0, s, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_cg_bf16_unscaled(D, C, p, s);
 }
 
 template <int D>

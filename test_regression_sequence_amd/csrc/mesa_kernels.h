@@ -35,9 +35,14 @@ struct CgParams {
   float* o;              // [BH, T, D]
   int32_t* steps;        // [BH, T] or null
   float* x_out;          // [BH, T, D] or null
+  int32_t* unscaled;     // [BH, NC] bf16 path: chunks left to the unscaled kernel
   int BH, H, T, NC, max_steps;
   float tol2;            // tol*tol, or -1 for the fixed-step mode
 };
+
+// Largest total decay -sum(log gamma) of a chunk that the scaled bf16 CG kernel
+// handles: e^40 keeps its decay-scaled weights far inside the fp32 range.
+constexpr float kMaxScaledDecay = 40.f;
 
 struct DecodeParams {
   const void* q;         // [P, D]  (P = N*H pairs)
@@ -59,9 +64,13 @@ struct DecodeParams {
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_cg_bf16(int D, int C, const CgParams& p, hipStream_t s);
+hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s);
 
 // Bytes of one (b, h, chunk) boundary snapshot of H (or of G).
 inline size_t snapshot_bytes(bool bf16, int D) { return (size_t)D * D * (bf16 ? 2 : 4); }
+
+// Bytes of the per-chunk form flags of the bf16 path (whole 256-byte blocks).
+inline size_t flag_bytes(size_t chunks) { return (chunks * 4 + 255) / 256 * 256; }
 
 }  // namespace mesa

@@ -48,13 +48,14 @@ def ws(d):
 
 def test_workspace_sizes():
     # 2 states x B*H x ceil(T/C) chunks x d^2 x element size
-    assert ws(desc()) == 2 * 6 * 3 * 64 * 64 * 2
+    # (+ one int32 flag per chunk in 256-byte blocks for bf16 inputs)
+    assert ws(desc()) == 2 * 6 * 3 * 64 * 64 * 2 + 256
     assert ws(desc(in_dtype=mesa.MESA_F32)) == 2 * 6 * 3 * 64 * 64 * 4
     assert ws(desc(T=0)) == 0
     assert ws(desc(dk=48, dv=48)) == 0
     assert ws(desc(dk=64, dv=32)) == 0
     assert ws(desc(chunk=48)) == 0
-    assert ws(desc(B=8, H=16, T=4096, dk=128, dv=128)) == 512 * 1024 * 1024
+    assert ws(desc(B=8, H=16, T=4096, dk=128, dv=128)) == 512 * 1024 * 1024 + 8192 * 4
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first

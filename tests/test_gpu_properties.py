@@ -203,3 +203,27 @@ def test_decode_other_dims_and_dtypes(dtype, d):
     assert rel_l2(res["o"].cpu().numpy(), r["o"]) <= 1e-4
     assert rel_l2(dv["h"].cpu().numpy(), r["h"]) < 1e-6
     assert rel_l2(dv["g"].cpu().numpy(), r["g"]) < 1e-6
+
+
+@pytest.mark.parametrize("d,chunk", [(128, 64), (64, 32)])
+def test_strong_decay_chunks(d, chunk):
+    """Chunks whose total decay exceeds e^-40 take the unscaled kernel; mixed with normal chunks."""
+    cfg = small_fwd(B=1, H=2, T=5 * chunk - 7, d=d, chunk=chunk, dtype="bf16", max_steps=8)
+    x = make_fwd_inputs(cfg)
+    g = x["gamma"].copy()
+    # chunks 1 and 3 forget fast (gamma = 0.3: about e^-77 over 64 tokens), the others as drawn
+    for c in (1, 3):
+        g[:, :, c * chunk:(c + 1) * chunk] = np.float32(0.3)
+    g[:, 1, 4 * chunk:] = np.float32(0.05)  # the ragged last chunk of head 1 as well
+    x = dict(x, gamma=g)
+    dv = dev_inputs(x)
+    r = fwd(dv, cfg, return_x=True, return_state=True)
+    refs = oracle_all(x, r["steps"])
+    o_ref = np.stack([rr["o_cg"][0, 0] for rr in refs])
+    x_ref = np.stack([rr["x_cg"][0, 0] for rr in refs])
+    assert rel_l2(r["o"].reshape(2, cfg.T, d), o_ref) <= TOL["bf16"]
+    assert rel_l2(r["x"].reshape(2, cfg.T, d), x_ref) <= TOL["bf16"]
+    for c in range(5):
+        sl = slice(c * chunk, min((c + 1) * chunk, cfg.T))
+        e = rel_l2(r["o"].reshape(2, cfg.T, d)[:, sl], o_ref[:, sl])
+        assert e <= TOL["bf16"], (c, e)
