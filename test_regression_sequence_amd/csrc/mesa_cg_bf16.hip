@@ -167,8 +167,20 @@ void cg_bf16_kernel(CgParams p) {
       for (int mj = 0; mj < NMJ; ++mj) asm volatile("" : "+a"(kc[nt][mj]));
   };
 
+  // queries of one tile as raw bf16 (zero past Lc); the next tile's are
+  // fetched while the current tile iterates
+  u16x4 qraw[ND];
+  auto fetch_q = [&](const int w) {
+    const int tloc = 16 * w + tl;
+#pragma unroll
+    for (int a = 0; a < ND; ++a)
+      qraw[a] = tloc < Lc ? *reinterpret_cast<const u16x4*>(Qg + (row0 + tloc) * D + 16 * a + 4 * g)
+                          : u16x4{0, 0, 0, 0};
+  };
+
   load_state(p.hb);
   load_rows(Kg, kr);
+  fetch_q(0);
   {
     float lg = 0.f, bt = 0.f;
     if (lane < Lc) {
@@ -256,10 +268,12 @@ void cg_bf16_kernel(CgParams p) {
     f32x4 r[ND], x[ND], pv[ND];
 #pragma unroll
     for (int a = 0; a < ND; ++a) {
-      r[a] = valid ? load4<true>(Qg, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+      r[a] = f32x4{bf16_to_f32(qraw[a][0]), bf16_to_f32(qraw[a][1]), bf16_to_f32(qraw[a][2]),
+                   bf16_to_f32(qraw[a][3])};
       x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
       pv[a] = r[a];
     }
+    if constexpr (w + 1 < NW) fetch_q(w + 1);
     float rho = 0.f;
 #pragma unroll
     for (int a = 0; a < ND; ++a) rho += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
