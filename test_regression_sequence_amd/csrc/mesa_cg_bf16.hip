@@ -91,19 +91,19 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) mf[nt][m] = F[(nt * NM + m) * 64 + lane];
   };
-  // row fragments X[16jt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}], zero past Lc
+  // row fragments X[16jt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}].  Rows past Lc
+  // (a ragged last chunk) repeat row Lc-1: their weight w_j is 0, so their
+  // weighted columns are zero and they contribute nothing.  Every load is
+  // unconditional, so the whole batch is in flight at once.
   auto load_rows = [&](const uint16_t* X, bf16x8 (&dst)[NW][NM]) {
 #pragma unroll
     for (int jt = 0; jt < NW; ++jt) {
-      const int j = 16 * jt + tl;
+      const int j = min(16 * jt + tl, Lc - 1);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        u16x4 lo = u16x4{0, 0, 0, 0}, hi = lo;
-        if (j < Lc) {
-          const uint16_t* src = X + (row0 + j) * D + 32 * m + 4 * g;
-          lo = *reinterpret_cast<const u16x4*>(src);
-          hi = *reinterpret_cast<const u16x4*>(src + 16);
-        }
+        const uint16_t* src = X + (row0 + j) * D + 32 * m + 4 * g;
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(src);
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 16);
         dst[jt][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -167,26 +167,31 @@ void cg_bf16_kernel(CgParams p) {
       for (int mj = 0; mj < NMJ; ++mj) asm volatile("" : "+a"(kc[nt][mj]));
   };
 
-  // queries of one tile as raw bf16 (zero past Lc); the next tile's are
-  // fetched while the current tile iterates
+  // queries of one tile as raw bf16 (tokens past Lc read row Lc-1 and are
+  // zeroed when converted); the next tile's are fetched while the current
+  // tile iterates
   u16x4 qraw[ND];
   auto fetch_q = [&](const int w) {
-    const int tloc = 16 * w + tl;
+    const int tq = min(16 * w + tl, Lc - 1);
 #pragma unroll
-    for (int a = 0; a < ND; ++a)
-      qraw[a] = tloc < Lc ? *reinterpret_cast<const u16x4*>(Qg + (row0 + tloc) * D + 16 * a + 4 * g)
-                          : u16x4{0, 0, 0, 0};
+    for (int a = 0; a < ND; ++a) qraw[a] = *reinterpret_cast<const u16x4*>(Qg + (row0 + tq) * D + 16 * a + 4 * g);
   };
 
-  load_state(p.hb);
-  load_rows(Kg, kr);
-  fetch_q(0);
+  // gates first: their prefix scan overlaps the state and key loads
   {
     float lg = 0.f, bt = 0.f;
+    float lam_v[(D + 63) / 64];
     if (lane < Lc) {
-      lg = logf(p.gamma[row0 + lane]);
+      lg = p.gamma[row0 + lane];
       bt = p.beta[row0 + lane];
     }
+#pragma unroll
+    for (int i = 0; i < (D + 63) / 64; ++i)
+      lam_v[i] = (lane + 64 * i < D) ? p.lam[(size_t)h * D + lane + 64 * i] : 0.f;
+    load_state(p.hb);
+    load_rows(Kg, kr);
+    fetch_q(0);
+    lg = lane < Lc ? logf(lg) : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float t = __shfl_up(lg, o, 64);
@@ -196,7 +201,9 @@ void cg_bf16_kernel(CgParams p) {
       bcum[lane] = lg;
       betas[lane] = bt;
     }
-    for (int i = lane; i < D; i += 64) lam_s[i] = p.lam[(size_t)h * D + i];
+#pragma unroll
+    for (int i = 0; i < (D + 63) / 64; ++i)
+      if (lane + 64 * i < D) lam_s[lane + 64 * i] = lam_v[i];
   }
   __syncthreads();
   // the chunk's total decay decides the form (wave-uniform); a chunk left to
@@ -268,8 +275,9 @@ void cg_bf16_kernel(CgParams p) {
     f32x4 r[ND], x[ND], pv[ND];
 #pragma unroll
     for (int a = 0; a < ND; ++a) {
-      r[a] = f32x4{bf16_to_f32(qraw[a][0]), bf16_to_f32(qraw[a][1]), bf16_to_f32(qraw[a][2]),
-                   bf16_to_f32(qraw[a][3])};
+      r[a] = valid ? f32x4{bf16_to_f32(qraw[a][0]), bf16_to_f32(qraw[a][1]), bf16_to_f32(qraw[a][2]),
+                           bf16_to_f32(qraw[a][3])}
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
       x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
       pv[a] = r[a];
     }
