@@ -13,12 +13,12 @@
 // registers, and writes the state *before* each chunk (the boundary state
 // the CG kernel starts from) into the workspace.
 //
-// Work split: a workgroup (4 waves) owns either a whole state (H or G) of
-// one (b, h) -- FULL -- or one 16-row stripe of it, so there are 2 or 2*D/16
+// Work split: a workgroup owns either a whole state (H or G) of one (b, h)
+// -- FULL, 8 waves -- or one 16-row stripe of it (4 waves), so there are 2 or 2*D/16
 // workgroups per (b, h); the launch picks the split that fills the GPU and
 // maps the workgroups of one (b, h) onto one XCD (they share the chunk's keys
-// in that XCD's L2).  The next chunk's keys, values and gates are loaded into
-// registers while the current chunk is processed.  The chunk delta
+// in that XCD's L2).  The keys, values and gates of the chunk after next are
+// loaded into registers while the current chunk is processed.  The chunk delta
 // K^T diag(w) X is an MFMA contraction over the chunk's tokens: bf16 MFMA for
 // bf16 inputs with the scaled operand split into bf16 hi + lo parts (so the
 // carried fp32 state does not pick up a bf16 rounding of beta*tail*x), fp32
@@ -36,7 +36,6 @@ namespace mesa {
 
 namespace {
 
-constexpr int kScanThreads = 256;
 
 template <bool BF16, int D, int C, bool FULL>
 struct ScanShape {
@@ -47,12 +46,16 @@ struct ScanShape {
   static constexpr bool PAIR = FULL && BF16;           // a unit = both m-tiles of a fragment
   static constexpr int TPU = PAIR ? 2 : 1;             // tiles per unit
   static constexpr int NU = FULL ? (PAIR ? (ND / 2) * ND : ND * ND) : ND;
-  static constexpr int UPW = (NU + 3) / 4;             // units per wave
+  // a whole state per workgroup takes 8 waves, a stripe 4 (state and
+  // prefetch registers per thread stay well under the VGPR file)
+  static constexpr int THREADS = FULL ? 512 : 256;
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int UPW = (NU + WAVES - 1) / WAVES; // units per wave
   // register prefetch: pieces of the chunk each thread loads
   static constexpr int NPX = BF16 ? (CP / 2) * (D / 8) : C * (D / 4);   // X pieces
-  static constexpr int PPX = (NPX + kScanThreads - 1) / kScanThreads;
+  static constexpr int PPX = (NPX + THREADS - 1) / THREADS;
   static constexpr int NPK = BF16 ? (CP / 2) * (MROWS / 8) : C * (MROWS / 4);  // K pieces (A operand)
-  static constexpr int PPK = (NPK + kScanThreads - 1) / kScanThreads;
+  static constexpr int PPK = (NPK + THREADS - 1) / THREADS;
   static constexpr int AS = CP + 8;                    // bf16 row stride of transposed LDS arrays
   static constexpr size_t LDS_A = BF16 ? (size_t)MROWS * AS * 2 : (size_t)CP * MROWS * 4;
   static constexpr size_t LDS_B = BF16 ? (size_t)2 * D * AS * 2 : (size_t)CP * D * 4;
@@ -66,7 +69,7 @@ template <>
 struct Piece<false> { f32x4 a; };     // one token row, 4 columns
 
 template <bool BF16, int D, int C, bool FULL>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
+__global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_kernel(ScanParams p) {
   using S = ScanShape<BF16, D, C, FULL>;
   constexpr int ND = S::ND, CP = S::CP, U = S::U, MROWS = S::MROWS, TPU = S::TPU, UPW = S::UPW;
   constexpr int AS = S::AS;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
   for (int ui = 0; ui < UPW; ++ui)
 #pragma unroll
     for (int h = 0; h < TPU; ++h) {
-      const int u = wave + 4 * ui;
+      const int u = wave + S::WAVES * ui;
       st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (u < S::NU && init) {
         const int mt = unit_mt(u, h), nt = unit_nt(u);
@@ -123,74 +126,76 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
     Piece<BF16> k[S::PPK];
     float lg, bt;
   };
+  // Every load is unconditional (indices clamped into the chunk and the piece
+  // list) so a fetch never waits on memory: the loads land while the previous
+  // chunk is processed.  Rows past the chunk end repeat its last row; their
+  // weight w_j is 0 (beta is taken as 0 there), so they add nothing.  The
+  // raw gamma is kept; its log is taken when the chunk is processed.
   auto fetch = [&](int c, Raw& r) {
     const int s = c * C, Lc = min(C, T - s);
-    r.lg = 0.f;
-    r.bt = 0.f;
-    if (lane < Lc) {
-      r.lg = logf(p.gamma[rowbase + s + lane]);
-      r.bt = p.beta[rowbase + s + lane];
-    }
+    const int jl = min(lane, Lc - 1);
+    r.lg = p.gamma[rowbase + s + jl];
+    r.bt = p.beta[rowbase + s + jl];
+    auto row = [&](int j) { return rowbase + s + min(j, Lc - 1); };
     if constexpr (BF16) {
       const uint16_t* Xg = static_cast<const uint16_t*>(X);
       const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
-      const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int q = 0; q < S::PPX; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = min(tid + q * S::THREADS, S::NPX - 1);
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
-        r.x[q].a = z;
-        r.x[q].b = z;
-        if (pc < S::NPX) {
-          if (2 * jp < Lc) r.x[q].a = *reinterpret_cast<const u16x8*>(Xg + (rowbase + s + 2 * jp) * D + 8 * c8);
-          if (2 * jp + 1 < Lc) r.x[q].b = *reinterpret_cast<const u16x8*>(Xg + (rowbase + s + 2 * jp + 1) * D + 8 * c8);
-        }
+        r.x[q].a = *reinterpret_cast<const u16x8*>(Xg + row(2 * jp) * D + 8 * c8);
+        r.x[q].b = *reinterpret_cast<const u16x8*>(Xg + row(2 * jp + 1) * D + 8 * c8);
       }
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = min(tid + q * S::THREADS, S::NPK - 1);
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
         const int col = (FULL ? 0 : 16 * mpart) + 8 * c8;
-        r.k[q].a = z;
-        r.k[q].b = z;
-        if (pc < S::NPK) {
-          if (2 * jp < Lc) r.k[q].a = *reinterpret_cast<const u16x8*>(Kg + (rowbase + s + 2 * jp) * D + col);
-          if (2 * jp + 1 < Lc) r.k[q].b = *reinterpret_cast<const u16x8*>(Kg + (rowbase + s + 2 * jp + 1) * D + col);
-        }
+        r.k[q].a = *reinterpret_cast<const u16x8*>(Kg + row(2 * jp) * D + col);
+        r.k[q].b = *reinterpret_cast<const u16x8*>(Kg + row(2 * jp + 1) * D + col);
       }
     } else {
       const float* Xg = static_cast<const float*>(X);
       const float* Kg = static_cast<const float*>(p.k);
 #pragma unroll
       for (int q = 0; q < S::PPX; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = min(tid + q * S::THREADS, S::NPX - 1);
         const int j = pc / (D / 4), c4 = pc % (D / 4);
-        r.x[q].a = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (pc < S::NPX && j < Lc) r.x[q].a = *reinterpret_cast<const f32x4*>(Xg + (rowbase + s + j) * D + 4 * c4);
+        r.x[q].a = *reinterpret_cast<const f32x4*>(Xg + row(j) * D + 4 * c4);
       }
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = min(tid + q * S::THREADS, S::NPK - 1);
         const int j = pc / (MROWS / 4), c4 = pc % (MROWS / 4);
         const int col = (FULL ? 0 : 16 * mpart) + 4 * c4;
-        r.k[q].a = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (pc < S::NPK && j < Lc) r.k[q].a = *reinterpret_cast<const f32x4*>(Kg + (rowbase + s + j) * D + col);
+        r.k[q].a = *reinterpret_cast<const f32x4*>(Kg + row(j) * D + col);
       }
     }
   };
 
-  Raw cur, nxt;
-  if (NC > 0) fetch(0, cur);
-
-  for (int c = 0; c < NC; ++c) {
-    if (c + 1 < NC) fetch(c + 1, nxt);
+  // A ring of DEPTH chunk buffers: chunk c + DEPTH - 1 is fetched while chunk
+  // c is processed, so each fetch has DEPTH - 1 chunk steps to land (three
+  // buffers for bf16 inputs; two for fp32, whose buffers are twice as large).
+  // The loop is unrolled by DEPTH so the buffers never move between
+  // registers (a move would wait for the fetch), and every fetch is
+  // unconditional (the chunk index is clamped; a fetch past the end is
+  // simply not used).
+  constexpr int DEPTH = BF16 ? 3 : 2;
+  Raw b0, b1, b2;
+  if (NC > 0) {
+    fetch(0, b0);
+    if constexpr (DEPTH == 3) fetch(min(1, NC - 1), b1);
+  }
+  auto step = [&](const int c, const Raw& cur, Raw& pre) {
+    fetch(min(c + DEPTH - 1, NC - 1), pre);
 
     // ---- snapshot of the state before chunk c ----------------------------------
     {
       const size_t snap = ((size_t)bh * NC + c) * D * D;
 #pragma unroll
       for (int ui = 0; ui < UPW; ++ui) {
-        const int u = wave + 4 * ui;
+        const int u = wave + S::WAVES * ui;
         if (u >= S::NU) continue;
         const int nt = unit_nt(u);
         if constexpr (BF16) {
@@ -223,7 +228,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
     }
 
     // ---- gates (every wave, in registers): w_j = beta_j prod_{i>j} gamma_i ------
-    float suf = cur.lg;  // inclusive suffix sum of log gamma
+    const int Lcur = min(C, T - c * C);
+    float suf = lane < Lcur ? logf(cur.lg) : 0.f;  // inclusive suffix sum of log gamma
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float t = __shfl_down(suf, o, 64);
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
     // sum over i > j; the shuffle runs with every lane active, then lane 63 drops it
     const float next = __shfl_down(suf, 1, 64);
     const float after = (lane < 63) ? next : 0.f;
-    const float wj = cur.bt * expf(after);                              // 0 past the chunk end
+    const float wj = lane < Lcur ? cur.bt * expf(after) : 0.f;          // 0 past the chunk end
     const float gamma_c = expf(__shfl(suf, 0, 64));
 
     // ---- stage operands (LDS is free once every wave finished chunk c-1) -------
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
       __bf16* XL = XH + D * AS;                       // lo part
 #pragma unroll
       for (int q = 0; q < S::PPX; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = tid + q * S::THREADS;
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
         // shuffles before any lane leaves: every lane of the wave participates
         const float w0 = __shfl(wj, (2 * jp) & 63, 64), w1 = __shfl(wj, (2 * jp + 1) & 63, 64);
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
       }
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = tid + q * S::THREADS;
         if (pc >= S::NPK) continue;
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
 #pragma unroll
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
       float* Xs = reinterpret_cast<float*>(lds_b);    // [CP][D] = w_j * X[j][n]
 #pragma unroll
       for (int q = 0; q < S::PPX; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = tid + q * S::THREADS;
         const int j = pc / (D / 4), c4 = pc % (D / 4);
         const float w = __shfl(wj, j & 63, 64);
         if (pc >= S::NPX) continue;
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
       }
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
-        const int pc = tid + q * kScanThreads;
+        const int pc = tid + q * S::THREADS;
         if (pc >= S::NPK) continue;
         const int j = pc / (MROWS / 4), c4 = pc % (MROWS / 4);
         *reinterpret_cast<f32x4*>(Ks + j * MROWS + 4 * c4) = cur.k[q].a;
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
     // ---- delta tiles and state update --------------------------------------------
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-      const int u = wave + 4 * ui;
+      const int u = wave + S::WAVES * ui;
       if (u >= S::NU) continue;
       const int nt = unit_nt(u);
 #pragma unroll
@@ -326,7 +332,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
         for (int i = 0; i < 4; ++i) st[ui][h][i] = gamma_c * st[ui][h][i] + acc[i];
       }
     }
-    if (c + 1 < NC) cur = nxt;
+  };
+  if constexpr (DEPTH == 3) {
+    for (int c = 0; c < NC; c += 3) {
+      step(c, b0, b2);
+      if (c + 1 < NC) step(c + 1, b1, b0);
+      if (c + 2 < NC) step(c + 2, b2, b1);
+    }
+  } else {
+    for (int c = 0; c < NC; c += 2) {
+      step(c, b0, b1);
+      if (c + 1 < NC) step(c + 1, b1, b0);
+    }
   }
 
   // ---- final state (fp32, row-major) ----------------------------------------------
@@ -335,7 +352,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanParams p) {
     float* base = fin + (size_t)bh * D * D;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-      const int u = wave + 4 * ui;
+      const int u = wave + S::WAVES * ui;
       if (u >= S::NU) continue;
       const int nt = unit_nt(u);
 #pragma unroll
@@ -357,7 +374,7 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t s) {
   constexpr int U = ScanShape<BF16, D, C, FULL>::U;
   const int groups = (p.BH + 7) / 8;
   const dim3 grid(groups * 8 * U);
-  hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL>), grid, dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL>), grid, dim3(ScanShape<BF16, D, C, FULL>::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
