@@ -226,9 +226,12 @@ void cg_bf16_kernel(CgParams p) {
   // the mask and packing of the scores (long finished by then), then the
   // intra-chunk MFMAs; the VALU work on acc comes after all of them, so no
   // instruction waits on an MFMA issued just before it.
+  // With LAM the boundary-state chains start from (Lambda / Gamma_t) .* u, so
+  // acc = (A_t / Gamma_t) u and the Lambda multiplies issue among the MFMAs.
   f32x4 acc[ND];
-  auto matvec = [&](auto wc, const bf16x8* ub) {
+  auto matvec = [&](auto wc, auto lamc, const bf16x8* ub, const f32x4* u, const f32x4* lt) {
     constexpr int w = decltype(wc)::value;
+    constexpr bool LAM = decltype(lamc)::value;
     f32x4 sc[w + 1];
 #pragma unroll
     for (int jt = 0; jt <= w; ++jt) {
@@ -238,7 +241,9 @@ void cg_bf16_kernel(CgParams p) {
     }
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) {
-      acc[nt] = mfma_bf16(mf[nt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (LAM) c0 = lt[nt] * u[nt];
+      acc[nt] = mfma_bf16(mf[nt][0], ub[0], c0);
 #pragma unroll
       for (int m = 1; m < NM; ++m) acc[nt] = mfma_bf16(mf[nt][m], ub[m], acc[nt]);
     }
@@ -295,12 +300,11 @@ void cg_bf16_kernel(CgParams p) {
       bf16x8 ub[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) ub[m] = pack8(pv[2 * m], pv[2 * m + 1]);
-      matvec(wc, ub);
-      // w = acc + (Lambda / Gamma_t) .* p and p.w, two independent chains
+      matvec(wc, std::true_type{}, ub, pv, lt);
+      // w = acc and p.w, two independent chains
       float pw0 = 0.f, pw1 = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
-        acc[a] += lt[a] * pv[a];
         pw0 += pv[a][0] * acc[a][0];
         pw1 += pv[a][1] * acc[a][1];
         pw0 += pv[a][2] * acc[a][2];
@@ -358,7 +362,7 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) xb[m] = pack8(x[2 * m], x[2 * m + 1]);
     pin_operands();
-    matvec(wc, xb);
+    matvec(wc, std::false_type{}, xb, x, x);
     if (tloc < Lc) {
 #pragma unroll
       for (int a = 0; a < ND; ++a)
