@@ -51,6 +51,9 @@ struct ScanShape {
   static constexpr int THREADS = FULL ? 512 : 256;
   static constexpr int WAVES = THREADS / 64;
   static constexpr int UPW = (NU + WAVES - 1) / WAVES; // units per wave
+  // every wave owns exactly UPW units (no guard, so no divergent branch
+  // in the chunk loop: a branch join there costs the loads' wait counts)
+  static constexpr bool EVEN = NU % WAVES == 0;
   // register prefetch: pieces of the chunk each thread loads
   static constexpr int NPX = BF16 ? (CP / 2) * (D / 8) : C * (D / 4);   // X pieces
   static constexpr int PPX = (NPX + THREADS - 1) / THREADS;
@@ -108,7 +111,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     for (int h = 0; h < TPU; ++h) {
       const int u = wave + S::WAVES * ui;
       st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < S::NU && init) {
+      if ((S::EVEN || u < S::NU) && init) {
         const int mt = unit_mt(u, h), nt = unit_nt(u);
         const float* base = init + (size_t)bh * D * D;
         if (which == 0) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 #pragma unroll
       for (int ui = 0; ui < UPW; ++ui) {
         const int u = wave + S::WAVES * ui;
-        if (u >= S::NU) continue;
+        if (!S::EVEN && u >= S::NU) continue;
         const int nt = unit_nt(u);
         if constexpr (BF16) {
           __bf16* dst = static_cast<__bf16*>(which ? p.gb : p.hb) + snap;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
         // shuffles before any lane leaves: every lane of the wave participates
         const float w0 = __shfl(wj, (2 * jp) & 63, 64), w1 = __shfl(wj, (2 * jp + 1) & 63, 64);
-        if (pc >= S::NPX) continue;
+        if (S::NPX % S::THREADS != 0 && pc >= S::NPX) continue;
         const float ww0 = (2 * jp < C) ? w0 : 0.f, ww1 = (2 * jp + 1 < C) ? w1 : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -268,7 +271,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
         const int pc = tid + q * S::THREADS;
-        if (pc >= S::NPK) continue;
+        if (S::NPK % S::THREADS != 0 && pc >= S::NPK) continue;
         const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -285,13 +288,13 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         const int pc = tid + q * S::THREADS;
         const int j = pc / (D / 4), c4 = pc % (D / 4);
         const float w = __shfl(wj, j & 63, 64);
-        if (pc >= S::NPX) continue;
+        if (S::NPX % S::THREADS != 0 && pc >= S::NPX) continue;
         *reinterpret_cast<f32x4*>(Xs + j * D + 4 * c4) = cur.x[q].a * w;
       }
 #pragma unroll
       for (int q = 0; q < S::PPK; ++q) {
         const int pc = tid + q * S::THREADS;
-        if (pc >= S::NPK) continue;
+        if (S::NPK % S::THREADS != 0 && pc >= S::NPK) continue;
         const int j = pc / (MROWS / 4), c4 = pc % (MROWS / 4);
         *reinterpret_cast<f32x4*>(Ks + j * MROWS + 4 * c4) = cur.k[q].a;
       }
@@ -302,7 +305,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
       const int u = wave + S::WAVES * ui;
-      if (u >= S::NU) continue;
+      if (!S::EVEN && u >= S::NU) continue;
       const int nt = unit_nt(u);
 #pragma unroll
       for (int h = 0; h < TPU; ++h) {
@@ -353,7 +356,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
       const int u = wave + S::WAVES * ui;
-      if (u >= S::NU) continue;
+      if (!S::EVEN && u >= S::NU) continue;
       const int nt = unit_nt(u);
 #pragma unroll
       for (int h = 0; h < TPU; ++h) {
