@@ -50,12 +50,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   __shared__ __attribute__((aligned(16))) float pb[NW][D];      // per-wave copy of p, then x
   __shared__ __attribute__((aligned(16))) float part[2][NW][D]; // per-wave column sums, double buffered
 
-  for (int i = tid; i < D; i += 64 * NW) {
-    ks[i] = load1<BF16>(p.k, (size_t)pair * D + i);
-    qs[i] = load1<BF16>(p.q, (size_t)pair * D + i);
-    vs[i] = load1<BF16>(p.v, (size_t)pair * D + i);
-    lam_s[i] = p.lam[(size_t)h * D + i];
-  }
+  // token vectors: one element per thread (index clamped, so the loads are
+  // unconditional and the state loads below go out without waiting on them)
+  static_assert(D <= 64 * NW, "one vector element per thread");
+  const int iv = min(tid, D - 1);
+  const float kv = load1<BF16>(p.k, (size_t)pair * D + iv);
+  const float qv = load1<BF16>(p.q, (size_t)pair * D + iv);
+  const float vv = load1<BF16>(p.v, (size_t)pair * D + iv);
+  const float lamv = p.lam[(size_t)h * D + iv];
   const float gam = p.gamma[pair], bet = p.beta[pair];
 
   // ---- H <- gamma H + beta (k k^T), kept in registers, written back --------------
@@ -70,6 +72,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   f32x4 hreg[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) hreg[i] = __builtin_nontemporal_load(at(Hb, i));
+  if (tid < D) {
+    ks[tid] = kv;
+    qs[tid] = qv;
+    vs[tid] = vv;
+    lam_s[tid] = lamv;
+  }
   __syncthreads();
   const f32x4 kq = *reinterpret_cast<const f32x4*>(&ks[4 * cq]);
 #pragma unroll
