@@ -54,7 +54,8 @@ size_t mesa_fwd_workspace_bytes(const mesa_fwd_desc* d) {
   const size_t nc = (size_t)(d->T + d->chunk - 1) / d->chunk;
   const size_t bh = (size_t)d->B * d->H;
   const bool bf16 = d->in_dtype == MESA_BF16;
-  return 2 * bh * nc * mesa::snapshot_bytes(bf16, d->dk) + (bf16 ? mesa::flag_bytes(bh * nc) : 0);
+  return 2 * bh * nc * mesa::snapshot_bytes(bf16, d->dk) + (bf16 ? mesa::flag_bytes(bh * nc) : 0) +
+         mesa::scan_segment_bytes((long long)bh, (int)nc, d->dk);
 }
 
 }  // extern "C"
@@ -88,6 +89,14 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
   void* gb = workspace ? static_cast<char*>(workspace) + snap : nullptr;
   int32_t* flags = (workspace && bf16) ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * snap)
                                        : nullptr;
+  // segment states of a split scan follow the snapshots and the flags
+  char* segbase = workspace ? static_cast<char*>(workspace) + 2 * snap + (bf16 ? mesa::flag_bytes((size_t)BH * NC) : 0)
+                            : nullptr;
+  const int NS = mesa::scan_segments(BH, NC, D);
+  float* seg_state = (NS > 1 && segbase) ? reinterpret_cast<float*>(segbase) : nullptr;
+  float* seg_decay = (NS > 1 && segbase)
+                         ? reinterpret_cast<float*>(segbase + (size_t)BH * 2 * (NS - 1) * D * D * 4)
+                         : nullptr;
 
   if ((phases & kScan) && (any_tokens || h_final || g_final)) {
     mesa::ScanParams sp{};
@@ -95,6 +104,8 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
     sp.h_final = h_final; sp.g_final = g_final;
     sp.hb = hb; sp.gb = gb;
     sp.BH = BH; sp.T = d->T; sp.NC = NC;
+    sp.NS = NS; sp.SEG = mesa::scan_segment_chunks(NC, NS);
+    sp.seg_state = seg_state; sp.seg_decay = seg_decay;
     if (mesa::launch_scan(bf16, D, C, sp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
   if ((phases & kSolve) && any_tokens) {

@@ -20,7 +20,37 @@ struct ScanParams {
   void* hb;              // [BH, NC, D*D] boundary snapshots of H (layout: see scan kernel)
   void* gb;              // [BH, NC, D*D] boundary snapshots of G
   int BH, T, NC;
+  // segmented walk (long sequences with few (b, h)): NS segments of SEG chunks
+  int SEG, NS;
+  float* seg_state;      // [BH, 2, NS-1, D*D]: segment totals, then carry-in states
+  float* seg_decay;      // [BH, NS-1]: product of gamma over each segment
 };
+
+// Segments per sequence for the state scan.  Whole-state workgroups (one per
+// CU) fill the GPU with one walk once 2*BH >= 256.  With fewer (b, h) and a
+// long sequence (>= 128 chunks) the whole-state walk is split into segments,
+// about 256 workgroups in all with at least 8 chunks each; shorter sequences
+// walk once in 16-row stripes (segmenting stripes does not pay: every stripe
+// stages the whole chunk).
+inline int scan_segments(long long BH, int NC, int D) {
+  (void)D;
+  if (2 * BH >= 256 || NC < 128) return 1;
+  long long ns = (256 + 2 * BH - 1) / (2 * BH);
+  if (ns > NC / 8) ns = NC / 8;
+  if (ns < 2) return 1;
+  const int seg = (int)((NC + ns - 1) / ns);
+  return (NC + seg - 1) / seg;
+}
+// whole-state workgroups (else 16-row stripes)
+inline bool scan_whole_state(long long BH, int NC, int D) { return 2 * BH >= 256 || scan_segments(BH, NC, D) > 1; }
+inline int scan_segment_chunks(int NC, int NS) { return (NC + NS - 1) / NS; }
+inline size_t scan_segment_bytes(long long BH, int NC, int D) {
+  const int ns = scan_segments(BH, NC, D);
+  if (ns <= 1) return 0;
+  const size_t st = (size_t)BH * 2 * (ns - 1) * D * D * 4;
+  const size_t dec = ((size_t)BH * (ns - 1) * 4 + 255) / 256 * 256;
+  return st + dec;
+}
 
 // Chunked CG solve + output.
 struct CgParams {

@@ -71,7 +71,9 @@ struct Piece<true> { u16x8 a, b; };   // two token rows (j0, j1), 8 columns each
 template <>
 struct Piece<false> { f32x4 a; };     // one token row, 4 columns
 
-template <bool BF16, int D, int C, bool FULL>
+// TOTALS: the first pass of a segmented walk -- each segment from a zero
+// state, no snapshots, the segment's total state and decay at the end.
+template <bool BF16, int D, int C, bool FULL, bool TOTALS>
 __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_kernel(ScanParams p) {
   using S = ScanShape<BF16, D, C, FULL>;
   constexpr int ND = S::ND, CP = S::CP, U = S::U, MROWS = S::MROWS, TPU = S::TPU, UPW = S::UPW;
@@ -80,15 +82,19 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
 
-  // XCD-aware decode: the U workgroups of one (b, h) share blockIdx % 8.
+  // XCD-aware decode: the workgroups of one (b, h) share blockIdx % 8.
+  // Within an XCD: (b, h) group, then segment, then unit.
+  const int NSP = TOTALS ? p.NS - 1 : p.NS;  // segments walked by this launch
   const int xcd = blockIdx.x & 7;
   const int local = blockIdx.x >> 3;
-  const int bh = (local / U) * 8 + xcd;
-  if (bh >= p.BH) return;
   const int u0 = local % U;
+  const int seg = (local / U) % NSP;
+  const int bh = (local / U / NSP) * 8 + xcd;
+  if (bh >= p.BH) return;
   const int which = FULL ? u0 : u0 / ND;   // 0: H, 1: G
   const int mpart = FULL ? 0 : u0 % ND;    // stripe (non-FULL)
   const int T = p.T, NC = p.NC;
+  const int cb = seg * p.SEG, ce = min(cb + p.SEG, NC);  // this segment's chunks
   const void* X = which ? p.v : p.k;      // the second factor of the chunk delta
   const size_t rowbase = (size_t)bh * T;
 
@@ -104,7 +110,12 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 
   // Running state: lane holds O[16 mt + 4 g + i][16 nt + tl], O = H (H) or G^T (G).
   f32x4 st[UPW][TPU];
-  const float* init = which ? p.g0 : p.h0;
+  // start state: h0/g0 for the first segment, the carry-in state for a later
+  // one (second pass), zero for a segment total
+  const float* init = TOTALS ? nullptr : (seg == 0 ? (which ? p.g0 : p.h0) : p.seg_state);
+  const size_t init_off = (TOTALS || seg == 0)
+                              ? (size_t)bh * D * D
+                              : (((size_t)bh * 2 + which) * (p.NS - 1) + (seg - 1)) * D * D;
 #pragma unroll
   for (int ui = 0; ui < UPW; ++ui)
 #pragma unroll
@@ -113,7 +124,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
       st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if ((S::EVEN || u < S::NU) && init) {
         const int mt = unit_mt(u, h), nt = unit_nt(u);
-        const float* base = init + (size_t)bh * D * D;
+        const float* base = init + init_off;
         if (which == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) st[ui][h][i] = base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl];
@@ -186,15 +197,16 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   // simply not used).
   constexpr int DEPTH = BF16 ? 3 : 2;
   Raw b0, b1, b2;
-  if (NC > 0) {
-    fetch(0, b0);
-    if constexpr (DEPTH == 3) fetch(min(1, NC - 1), b1);
+  if (ce > cb) {
+    fetch(cb, b0);
+    if constexpr (DEPTH == 3) fetch(min(cb + 1, ce - 1), b1);
   }
+  float seg_log = 0.f;  // sum of log gamma over the segment (wave-uniform)
   auto step = [&](const int c, const Raw& cur, Raw& pre) {
-    fetch(min(c + DEPTH - 1, NC - 1), pre);
+    fetch(min(c + DEPTH - 1, ce - 1), pre);
 
     // ---- snapshot of the state before chunk c ----------------------------------
-    {
+    if constexpr (!TOTALS) {
       const size_t snap = ((size_t)bh * NC + c) * D * D;
 #pragma unroll
       for (int ui = 0; ui < UPW; ++ui) {
@@ -242,7 +254,9 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     const float next = __shfl_down(suf, 1, 64);
     const float after = (lane < 63) ? next : 0.f;
     const float wj = lane < Lcur ? cur.bt * expf(after) : 0.f;          // 0 past the chunk end
-    const float gamma_c = expf(__shfl(suf, 0, 64));
+    const float sum_log = __shfl(suf, 0, 64);
+    const float gamma_c = expf(sum_log);
+    seg_log += sum_log;
 
     // ---- stage operands (LDS is free once every wave finished chunk c-1) -------
     __syncthreads();
@@ -337,22 +351,31 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     }
   };
   if constexpr (DEPTH == 3) {
-    for (int c = 0; c < NC; c += 3) {
+    for (int c = cb; c < ce; c += 3) {
       step(c, b0, b2);
-      if (c + 1 < NC) step(c + 1, b1, b0);
-      if (c + 2 < NC) step(c + 2, b2, b1);
+      if (c + 1 < ce) step(c + 1, b1, b0);
+      if (c + 2 < ce) step(c + 2, b2, b1);
     }
   } else {
-    for (int c = 0; c < NC; c += 2) {
+    for (int c = cb; c < ce; c += 2) {
       step(c, b0, b1);
-      if (c + 1 < NC) step(c + 1, b1, b0);
+      if (c + 1 < ce) step(c + 1, b1, b0);
     }
   }
 
-  // ---- final state (fp32, row-major) ----------------------------------------------
-  float* fin = which ? p.g_final : p.h_final;
+  // ---- final state (fp32, row-major): the sequence's, or a segment total ----------
+  float* fin;
+  size_t fin_off;
+  if constexpr (TOTALS) {
+    fin = p.seg_state;
+    fin_off = (((size_t)bh * 2 + which) * (p.NS - 1) + seg) * D * D;
+    if (which == 0 && u0 == 0 && tid == 0) p.seg_decay[(size_t)bh * (p.NS - 1) + seg] = expf(seg_log);
+  } else {
+    fin = seg == p.NS - 1 ? (which ? p.g_final : p.h_final) : nullptr;
+    fin_off = (size_t)bh * D * D;
+  }
   if (fin) {
-    float* base = fin + (size_t)bh * D * D;
+    float* base = fin + fin_off;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
       const int u = wave + S::WAVES * ui;
@@ -372,24 +395,58 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   }
 }
 
-template <bool BF16, int D, int C, bool FULL>
+// Carry pass of a segmented walk: for every state entry, fold the segment
+// totals in order, C_{s+1} = Gamma_s C_s + total_s (C_0 = h0 / g0 or 0), and
+// leave the carry-in state of segment s+1 where total_s was.
+__global__ __launch_bounds__(256) void scan_carry_kernel(ScanParams p, int D2) {
+  const int q4 = D2 / 4;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)p.BH * 2 * q4) return;
+  const int e = (int)(idx % q4);
+  const int which = (int)((idx / q4) % 2);
+  const int bh = (int)(idx / q4 / 2);
+  const float* init = which ? p.g0 : p.h0;
+  f32x4 c = init ? *reinterpret_cast<const f32x4*>(init + (size_t)bh * D2 + 4 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sg = 0; sg < p.NS - 1; ++sg) {
+    f32x4* t = reinterpret_cast<f32x4*>(p.seg_state + (((size_t)bh * 2 + which) * (p.NS - 1) + sg) * D2) + e;
+    c = p.seg_decay[(size_t)bh * (p.NS - 1) + sg] * c + *t;
+    *t = c;
+  }
+}
+
+template <bool BF16, int D, int C, bool FULL, bool TOTALS>
 hipError_t launch_scan_t(const ScanParams& p, hipStream_t s) {
   constexpr int U = ScanShape<BF16, D, C, FULL>::U;
   const int groups = (p.BH + 7) / 8;
-  const dim3 grid(groups * 8 * U);
-  hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL>), grid, dim3(ScanShape<BF16, D, C, FULL>::THREADS), 0, s, p);
+  const int nsp = TOTALS ? p.NS - 1 : p.NS;
+  const dim3 grid(groups * 8 * U * nsp);
+  hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL, TOTALS>), grid, dim3(ScanShape<BF16, D, C, FULL>::THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool BF16, int D, int C>
+hipError_t launch_scan_c(const ScanParams& p, hipStream_t s) {
+  // A whole state per workgroup when there are enough (b, h) slices to give
+  // every CU work, or when a long sequence is walked in segments (totals,
+  // carry, then the walk proper); otherwise one 16-row stripe per workgroup.
+  if (!scan_whole_state(p.BH, p.NC, D)) return launch_scan_t<BF16, D, C, false, false>(p, s);
+  if (p.NS > 1) {
+    hipError_t e = launch_scan_t<BF16, D, C, true, true>(p, s);
+    if (e != hipSuccess) return e;
+    const long long n = (long long)p.BH * 2 * (D * D / 4);
+    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D * D);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_scan_t<BF16, D, C, true, false>(p, s);
 }
 
 template <bool BF16, int D>
 hipError_t launch_scan_d(int C, const ScanParams& p, hipStream_t s) {
-  // A whole state per workgroup once there are enough (b, h) slices to give
-  // every CU work; otherwise one 16-row stripe per workgroup for parallelism.
-  const bool full = 2LL * p.BH >= 256;
   switch (C) {
-    case 16: return full ? launch_scan_t<BF16, D, 16, true>(p, s) : launch_scan_t<BF16, D, 16, false>(p, s);
-    case 32: return full ? launch_scan_t<BF16, D, 32, true>(p, s) : launch_scan_t<BF16, D, 32, false>(p, s);
-    case 64: return full ? launch_scan_t<BF16, D, 64, true>(p, s) : launch_scan_t<BF16, D, 64, false>(p, s);
+    case 16: return launch_scan_c<BF16, D, 16>(p, s);
+    case 32: return launch_scan_c<BF16, D, 32>(p, s);
+    case 64: return launch_scan_c<BF16, D, 64>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -56,6 +56,10 @@ def test_workspace_sizes():
     assert ws(desc(dk=64, dv=32)) == 0
     assert ws(desc(chunk=48)) == 0
     assert ws(desc(B=8, H=16, T=4096, dk=128, dv=128)) == 512 * 1024 * 1024 + 8192 * 4
+    # few (b, h) and a long sequence: the scan walks 8 segments of 64 chunks,
+    # + 7 carry-in states per (b, h, state) in fp32 and one decay per (b, h, segment)
+    assert ws(desc(B=1, H=16, T=32768, dk=128, dv=128)) == (
+        2 * 16 * 512 * 128 * 128 * 2 + 16 * 512 * 4 + 16 * 2 * 7 * 128 * 128 * 4 + 512)
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first

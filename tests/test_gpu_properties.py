@@ -227,3 +227,31 @@ def test_strong_decay_chunks(d, chunk):
         sl = slice(c * chunk, min((c + 1) * chunk, cfg.T))
         e = rel_l2(r["o"].reshape(2, cfg.T, d)[:, sl], o_ref[:, sl])
         assert e <= TOL["bf16"], (c, e)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 32)])
+def test_segmented_scan_with_initial_state(dtype, d, chunk):
+    """Few (b, h) and many chunks: the scan walks segments (totals, carry, walk).
+
+    Final states and sampled outputs against the oracle, starting from h0/g0.
+    """
+    T = 130 * chunk + 9  # 131 chunks (the last one ragged): long enough to be walked in segments
+    cfg = small_fwd(B=1, H=2, T=T, d=d, chunk=chunk, dtype=dtype, max_steps=6)
+    x = make_fwd_inputs(cfg)
+    rng = np.random.default_rng(11)
+    m = rng.standard_normal((1, 2, d, d)) / np.sqrt(d)
+    h0 = (m @ m.transpose(0, 1, 3, 2)).astype(np.float32)
+    h0 = (0.5 * (h0 + h0.transpose(0, 1, 3, 2))).astype(np.float32)
+    g0 = (rng.standard_normal((1, 2, d, d)) / np.sqrt(d)).astype(np.float32)
+    dv = dev_inputs(x)
+    r = fwd(dv, cfg, h0=torch.from_numpy(h0).cuda(), g0=torch.from_numpy(g0).cuda(), return_state=True)
+    from oracle import mesa_forward
+    at = np.zeros(T, bool)
+    at[np.random.default_rng(12).choice(T, 40, replace=False)] = True
+    at[-3:] = True
+    steps = r["steps"]
+    ref = mesa_forward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], max_steps=6, tol=0.0,
+                       h0=h0, g0=g0, forced_steps=steps, exact=False, solve_at=at)
+    assert rel_l2(r["h_final"], ref["H_final"]) < 1e-4
+    assert rel_l2(r["g_final"], ref["G_final"]) < 1e-4
+    assert rel_l2(r["o"][:, :, at], ref["o_cg"][:, :, at]) <= TOL[dtype]
