@@ -255,3 +255,20 @@ def test_segmented_scan_with_initial_state(dtype, d, chunk):
     assert rel_l2(r["h_final"], ref["H_final"]) < 1e-4
     assert rel_l2(r["g_final"], ref["G_final"]) < 1e-4
     assert rel_l2(r["o"][:, :, at], ref["o_cg"][:, :, at]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("f32", 32, 32), ("f32", 16, 16), ("bf16", 64, 64), ("bf16", 32, 16)])
+def test_many_heads_whole_state_scan(dtype, d, chunk):
+    """B*H >= 128: the scan gives each state a whole workgroup; sampled slices vs the oracle."""
+    cfg = small_fwd(B=2, H=64, T=3 * chunk + 5, d=d, chunk=chunk, dtype=dtype, max_steps=6)
+    x = make_fwd_inputs(cfg)
+    dv = dev_inputs(x)
+    r = fwd(dv, cfg, return_state=True)
+    idx = [0, 37, 64, 127]
+    refs = oracle_on_slices(x, idx, steps_gpu=r["steps"].reshape(128, -1)[idx])
+    o = r["o"].reshape(128, cfg.T, d)[idx]
+    assert rel_l2(o, np.stack([rr["o_cg"][0, 0] for rr in refs])) <= TOL[dtype]
+    hf = r["h_final"].reshape(128, d, d)[idx]
+    gf = r["g_final"].reshape(128, d, d)[idx]
+    assert rel_l2(hf, np.stack([rr["H_final"][0, 0] for rr in refs])) < 1e-5
+    assert rel_l2(gf, np.stack([rr["G_final"][0, 0] for rr in refs])) < 1e-5
