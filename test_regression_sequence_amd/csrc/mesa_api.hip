@@ -148,11 +148,13 @@ mesa_status mesa_fwd_solve(const mesa_fwd_desc* d, const void* q, const void* k,
                   steps, x_out, workspace, workspace_bytes, stream);
 }
 
-mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
-                             const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
-                             const float* beta, const float* lambda, float* h_state,
-                             float* g_state, float* o, int32_t* steps, float* x_out,
-                             int32_t max_steps, float tol, hipStream_t stream) {
+namespace {
+
+mesa_status decode_impl(bool symh, int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+                        const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
+                        const float* beta, const float* lambda, float* h_state, float* g_state,
+                        float* o, int32_t* steps, float* x_out, int32_t max_steps, float tol,
+                        hipStream_t stream) {
   if (N < 0 || H < 1 || dk < 1 || dv < 1 || max_steps < 0 || std::isnan(tol)) return MESA_ERR_INVALID_ARG;
   if (in_dtype != MESA_F32 && in_dtype != MESA_BF16) return MESA_ERR_INVALID_ARG;
   if (dk != dv || (dk != 64 && dk != 128)) return MESA_ERR_UNSUPPORTED;
@@ -169,8 +171,55 @@ mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const
   dp.h = h_state; dp.g = g_state; dp.o = o; dp.steps = steps; dp.x_out = x_out;
   dp.P = N * H; dp.H = H; dp.max_steps = max_steps;
   dp.tol2 = tol > 0.f ? tol * tol : -1.f;
-  if (mesa::launch_decode(in_dtype == MESA_BF16, dk, dp, stream) != hipSuccess) return MESA_ERR_HIP;
+  const hipError_t e = symh ? mesa::launch_decode_symh(in_dtype == MESA_BF16, dk, dp, stream)
+                            : mesa::launch_decode(in_dtype == MESA_BF16, dk, dp, stream);
+  return e == hipSuccess ? MESA_OK : MESA_ERR_HIP;
+}
+
+mesa_status sym_check(int32_t count, int32_t d, const float* a, const float* b) {
+  if (count < 0 || d < 1) return MESA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MESA_ERR_UNSUPPORTED;
+  if (count == 0) return MESA_OK;
+  if (!a || !b) return MESA_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b)) return MESA_ERR_ALIGNMENT;
   return MESA_OK;
+}
+
+}  // namespace
+
+mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+                             const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
+                             const float* beta, const float* lambda, float* h_state,
+                             float* g_state, float* o, int32_t* steps, float* x_out,
+                             int32_t max_steps, float tol, hipStream_t stream) {
+  return decode_impl(false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state, g_state, o,
+                     steps, x_out, max_steps, tol, stream);
+}
+
+mesa_status mesa_decode_step_symh(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+                                  const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
+                                  const float* beta, const float* lambda, float* h_sym,
+                                  float* g_state, float* o, int32_t* steps, float* x_out,
+                                  int32_t max_steps, float tol, hipStream_t stream) {
+  return decode_impl(true, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_sym, g_state, o,
+                     steps, x_out, max_steps, tol, stream);
+}
+
+size_t mesa_sym_state_floats(int32_t d) {
+  if (d != 64 && d != 128) return 0;
+  return mesa::sym_state_floats(d);
+}
+
+mesa_status mesa_sym_pack(int32_t count, int32_t d, const float* full, float* packed, hipStream_t stream) {
+  const mesa_status st = sym_check(count, d, full, packed);
+  if (st != MESA_OK || count == 0) return st;
+  return mesa::launch_sym_pack(d, count, full, packed, stream) == hipSuccess ? MESA_OK : MESA_ERR_HIP;
+}
+
+mesa_status mesa_sym_unpack(int32_t count, int32_t d, const float* packed, float* full, hipStream_t stream) {
+  const mesa_status st = sym_check(count, d, packed, full);
+  if (st != MESA_OK || count == 0) return st;
+  return mesa::launch_sym_unpack(d, count, packed, full, stream) == hipSuccess ? MESA_OK : MESA_ERR_HIP;
 }
 
 }  // extern "C"

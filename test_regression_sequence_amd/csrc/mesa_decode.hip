@@ -20,8 +20,9 @@
 //      so both dot products are wave-local and all waves take identical
 //      decisions.
 //   G: the same row segments; o = G x is reduced across the lanes of a row.
-// The update forms k_r*k_j before scaling, so an exactly symmetric H stays
-// exactly symmetric.
+// The update forms k_r*k_j before scaling and is one explicit FMA per element,
+// gamma*h + (beta*(k_r*k_j)), so an exactly symmetric H stays exactly
+// symmetric and every variant of the kernel rounds the same way.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -31,7 +32,19 @@ namespace {
 
 constexpr int kDecWaves = 4;
 
-template <bool BF16, int D>
+// row-major index of block (bi, bj), bi <= bj, in the upper triangle of an nb x nb grid
+__device__ __forceinline__ int sym_block(int nb, int bi, int bj) { return bi * nb - bi * (bi - 1) / 2 + (bj - bi); }
+
+// SYMH: H is stored packed as 16x16 blocks on and above the block diagonal
+// (row-major block order, each block row-major).  The workgroup streams the
+// stored blocks once, contiguously, into LDS; every thread then takes its
+// strip from there: on or above the diagonal straight out of its block, below
+// it transposed out of the mirror block (16-byte runs of that block's rows,
+// every 4x4 group transposed in registers).  The LDS copy swizzles 16-byte
+// slots so that both read patterns and the linear fill avoid bank conflicts,
+// and the CG buffers reuse its space.  Only threads of stored blocks write H
+// back.  The CG and G parts are unchanged.
+template <bool BF16, int D, bool SYMH>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) {
   constexpr int NW = kDecWaves;
   constexpr int Q = D / 4;                   // 16-byte column quads per row
@@ -46,9 +59,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   const int cq = lane % Q;                       // column quad
   const int row0 = (wave * TPR + lane / Q) * RPT;  // first row of this thread
 
+  constexpr int NB = D / 16, NBLK = NB * (NB + 1) / 2;  // packed H: blocks per side, stored blocks
+  constexpr int CG_LDS = 3 * NW * D;                       // floats of pb and part
+  constexpr int LDS_F = SYMH && NBLK * 256 > CG_LDS ? NBLK * 256 : CG_LDS;
   __shared__ float ks[D], qs[D], vs[D], lam_s[D];
-  __shared__ __attribute__((aligned(16))) float pb[NW][D];      // per-wave copy of p, then x
-  __shared__ __attribute__((aligned(16))) float part[2][NW][D]; // per-wave column sums, double buffered
+  __shared__ __attribute__((aligned(16))) float lds[LDS_F];  // packed H staging (SYMH), then pb and part
+  float(*pb)[D] = reinterpret_cast<float(*)[D]>(lds);             // per-wave copy of p, then x
+  float(*part2)[NW][D] = reinterpret_cast<float(*)[NW][D]>(lds + NW * D);  // per-wave column sums, double buffered
 
   // token vectors: one element per thread (index clamped, so the loads are
   // unconditional and the state loads below go out without waiting on them)
@@ -65,29 +82,78 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   // constant per row: lets every row share one address register.  The states
   // are touched once per step, so they stream with nontemporal hints (each
   // wave then covers its 16 KB of a state contiguously at full HBM rate).
-  char* Hb = reinterpret_cast<char*>(p.h + (size_t)pair * D * D);
   char* Gb = reinterpret_cast<char*>(p.g + (size_t)pair * D * D);
   const uint64_t voff = (uint32_t)((row0 * D + 4 * cq) * 4);
   auto at = [&](char* base, int i) { return reinterpret_cast<f32x4*>(base + voff + i * D * 4); };
   f32x4 hreg[RPT];
+  // full layout
+  char* Hb = reinterpret_cast<char*>(p.h + (size_t)pair * D * D);
+  // packed layout
+  const int bi = row0 >> 4, bj = cq >> 2, r0 = row0 & 15, cm = cq & 3;
+  const bool mirror = SYMH && bi > bj;
+  const int myblk = mirror ? sym_block(NB, bj, bi) : sym_block(NB, bi, bj);
+  f32x4* Hp = reinterpret_cast<f32x4*>(p.h + (size_t)pair * NBLK * 256);
+  // 16-byte slot of (row, column quad c4) of stored block blk in the LDS copy
+  auto slot = [](int blk, int row, int c4) {
+    return blk * 64 + (row >> 2) * 16 + (((row & 3) ^ (blk & 3)) << 2) + (c4 ^ ((row >> 2) & 3));
+  };
+  // this thread's j-th row segment: direct, or the transposed source in the mirror block
+  auto strip = [&](int j) {
+    return mirror ? slot(myblk, 4 * cm + (j & 3), (r0 >> 2) + (j >> 2)) : slot(myblk, r0 + j, cm);
+  };
+  auto transpose_groups = [&]() {  // mirror threads: out[4g+u][e] = in[4g+e][u]
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) hreg[i] = __builtin_nontemporal_load(at(Hb, i));
+    for (int g4 = 0; g4 < RPT / 4; ++g4) {
+      f32x4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[u][e] = mirror ? hreg[4 * g4 + e][u] : hreg[4 * g4 + u][e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hreg[4 * g4 + u] = t[u];
+    }
+  };
+  constexpr int NV = (NBLK * 64 + 64 * NW - 1) / (64 * NW);  // packed H: 16-byte loads per thread
+  f32x4 stage[SYMH ? NV : 1];
+  if constexpr (SYMH) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) stage[i] = Hp[min(tid + 64 * NW * i, NBLK * 64 - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) hreg[i] = __builtin_nontemporal_load(at(Hb, i));
+  }
   if (tid < D) {
     ks[tid] = kv;
     qs[tid] = qv;
     vs[tid] = vv;
     lam_s[tid] = lamv;
   }
-  __syncthreads();
+  if constexpr (SYMH) {
+    f32x4* hl = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int g = tid + 64 * NW * i;
+      if ((NBLK * 64) % (64 * NW) == 0 || g < NBLK * 64) hl[slot(g >> 6, (g >> 2) & 15, g & 3)] = stage[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) hreg[j] = hl[strip(j)];
+    transpose_groups();
+  }
+  __syncthreads();  // token vectors visible; packed H: LDS copy read before pb and part reuse it
   const f32x4 kq = *reinterpret_cast<const f32x4*>(&ks[4 * cq]);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float kr = ks[row0 + i];
     f32x4 hv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hv[e] = gam * hreg[i][e] + bet * (kr * kq[e]);
+    for (int e = 0; e < 4; ++e) hv[e] = __builtin_fmaf(gam, hreg[i][e], bet * (kr * kq[e]));
     hreg[i] = hv;
-    __builtin_nontemporal_store(hv, at(Hb, i));
+    if constexpr (SYMH) {
+      if (!mirror) __builtin_nontemporal_store(hv, Hp + myblk * 64 + (r0 + i) * 4 + cm);
+    } else {
+      __builtin_nontemporal_store(hv, at(Hb, i));
+    }
   }
 
   // ---- CG on (H + Lambda) x = q -------------------------------------------------------
@@ -133,7 +199,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
       const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
       acc[e] = __uint_as_float(b[0]) + __uint_as_float(b[1]);
     }
-    float(*pt)[D] = part[it & 1];
+    float(*pt)[D] = part2[it & 1];
     if (lane < Q) *reinterpret_cast<f32x4*>(&pt[wave][4 * cq]) = acc;
     __syncthreads();
     float wv[EPL];
@@ -176,7 +242,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
     const float bv = bet * vs[row];
     f32x4 gv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) gv[e] = gam * greg[i][e] + bv * kq[e];
+    for (int e = 0; e < 4; ++e) gv[e] = __builtin_fmaf(gam, greg[i][e], bv * kq[e]);
     __builtin_nontemporal_store(gv, at(Gb, i));
     const float s = group_sum<Q>(gv[0] * xq[0] + gv[1] * xq[1] + gv[2] * xq[2] + gv[3] * xq[3]);
     if (cq == 0) p.o[(size_t)pair * D + row] = s;
@@ -188,23 +254,32 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   if (tid == 0 && p.steps) p.steps[pair] = n;
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool SYMH>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<BF16, D>), dim3(p.P), dim3(64 * kDecWaves), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<BF16, D, SYMH>), dim3(p.P), dim3(64 * kDecWaves), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool SYMH>
+hipError_t launch_decode_s(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
+  if (bf16) {
+    if (D == 128) return launch_decode_t<true, 128, SYMH>(p, s);
+    if (D == 64) return launch_decode_t<true, 64, SYMH>(p, s);
+  } else {
+    if (D == 128) return launch_decode_t<false, 128, SYMH>(p, s);
+    if (D == 64) return launch_decode_t<false, 64, SYMH>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
-  if (bf16) {
-    if (D == 128) return launch_decode_t<true, 128>(p, s);
-    if (D == 64) return launch_decode_t<true, 64>(p, s);
-  } else {
-    if (D == 128) return launch_decode_t<false, 128>(p, s);
-    if (D == 64) return launch_decode_t<false, 64>(p, s);
-  }
-  return hipErrorInvalidValue;
+  return launch_decode_s<false>(bf16, D, p, s);
+}
+
+hipError_t launch_decode_symh(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
+  return launch_decode_s<true>(bf16, D, p, s);
 }
 
 }  // namespace mesa

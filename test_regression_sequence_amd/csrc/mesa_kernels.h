@@ -96,6 +96,11 @@ hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_cg_bf16(int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s);
+// decode with H in the blocked upper-triangular layout (DecodeParams::h packed)
+hipError_t launch_decode_symh(bool bf16, int D, const DecodeParams& p, hipStream_t s);
+hipError_t launch_sym_pack(int D, int count, const float* full, float* packed, hipStream_t s);
+hipError_t launch_sym_unpack(int D, int count, const float* packed, float* full, hipStream_t s);
+size_t sym_state_floats(int D);
 
 // Bytes of one (b, h, chunk) boundary snapshot of H (or of G).
 inline size_t snapshot_bytes(bool bf16, int D) { return (size_t)D * D * (bf16 ? 2 : 4); }

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "MesaError", "lib", "library_path", "FwdDesc", "MESA_F32", "MESA_BF16",
     "workspace_bytes", "fwd_chunked", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
-    "status_string",
+    "status_string", "sym_state_floats", "sym_pack", "sym_unpack", "decode_step_symh",
 ]
 
 MESA_F32 = 0
@@ -67,6 +67,14 @@ def lib() -> ctypes.CDLL:
         L.mesa_decode_step.restype = ctypes.c_int
         L.mesa_decode_step.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, P, P,
                                        P, P, I32, F, P]
+        L.mesa_decode_step_symh.restype = ctypes.c_int
+        L.mesa_decode_step_symh.argtypes = list(L.mesa_decode_step.argtypes)
+        L.mesa_sym_state_floats.restype = S
+        L.mesa_sym_state_floats.argtypes = [I32]
+        L.mesa_sym_pack.restype = ctypes.c_int
+        L.mesa_sym_pack.argtypes = [I32, I32, P, P, P]
+        L.mesa_sym_unpack.restype = ctypes.c_int
+        L.mesa_sym_unpack.argtypes = [I32, I32, P, P, P]
         _LIB = L
     return _LIB
 
@@ -193,9 +201,48 @@ def fwd_solve(q, k, v, gamma, beta, lam, *, chunk: int, max_steps: int, tol: flo
     _check(code_, "mesa_fwd_solve")
 
 
+def sym_state_floats(d: int) -> int:
+    """Floats of one H state in the blocked upper-triangular layout (d in {64, 128})."""
+    n = int(lib().mesa_sym_state_floats(int(d)))
+    if n == 0:
+        raise MesaError(f"no packed layout for d={d}", 2)
+    return n
+
+
+def sym_pack(full: torch.Tensor, stream=None) -> torch.Tensor:
+    """[..., d, d] fp32 symmetric states -> [..., sym_state_floats(d)] blocked upper triangle."""
+    d = full.shape[-1]
+    lead = full.shape[:-2]
+    count = int(full.numel() // (d * d))
+    _need(full, "full", tuple(lead) + (d, d), torch.float32)
+    out = torch.empty(tuple(lead) + (sym_state_floats(d),), device=full.device, dtype=torch.float32)
+    _check(lib().mesa_sym_pack(count, d, _ptr(full), _ptr(out), _stream(stream)), "mesa_sym_pack")
+    return out
+
+
+def sym_unpack(packed: torch.Tensor, d: int, stream=None) -> torch.Tensor:
+    """[..., sym_state_floats(d)] -> [..., d, d] fp32 (lower blocks mirrored)."""
+    n = sym_state_floats(d)
+    lead = packed.shape[:-1]
+    _need(packed, "packed", tuple(lead) + (n,), torch.float32)
+    count = int(packed.numel() // n)
+    out = torch.empty(tuple(lead) + (d, d), device=packed.device, dtype=torch.float32)
+    _check(lib().mesa_sym_unpack(count, d, _ptr(packed), _ptr(out), _stream(stream)), "mesa_sym_unpack")
+    return out
+
+
+def decode_step_symh(q, k, v, gamma, beta, lam, h_sym, g_state, *, max_steps: int = 32,
+                     tol: float = 1e-4, return_steps: bool = True, return_x: bool = False,
+                     out=None, stream=None) -> dict:
+    """decode_step with h_sym [N, H, sym_state_floats(d)] in the blocked layout (updated in place)."""
+    return decode_step(q, k, v, gamma, beta, lam, h_sym, g_state, max_steps=max_steps, tol=tol,
+                       return_steps=return_steps, return_x=return_x, out=out, stream=stream,
+                       _symh=True)
+
+
 def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int = 32,
                 tol: float = 1e-4, return_steps: bool = True, return_x: bool = False,
-                out=None, stream=None) -> dict:
+                out=None, stream=None, _symh: bool = False) -> dict:
     """One recurrent step; q, k, v [N, H, d]; h_state, g_state [N, H, d, d] fp32, updated in place."""
     N, H, d = q.shape
     code = _dtype_code(q)
@@ -204,7 +251,10 @@ def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int =
     _need(gamma, "gamma", (N, H), torch.float32)
     _need(beta, "beta", (N, H), torch.float32)
     _need(lam, "lam", (H, d), torch.float32)
-    _need(h_state, "h_state", (N, H, d, d), torch.float32)
+    if _symh:
+        _need(h_state, "h_sym", (N, H, sym_state_floats(d)), torch.float32)
+    else:
+        _need(h_state, "h_state", (N, H, d, d), torch.float32)
     _need(g_state, "g_state", (N, H, d, d), torch.float32)
     dev = q.device
     out = dict(out or {})
@@ -213,9 +263,10 @@ def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int =
         res["steps"] = out.get("steps") if out.get("steps") is not None else torch.empty((N, H), device=dev, dtype=torch.int32)
     if return_x:
         res["x"] = out.get("x") if out.get("x") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)
-    code_ = lib().mesa_decode_step(N, H, d, d, _ptr(q), _ptr(k), _ptr(v), code, _ptr(gamma), _ptr(beta),
-                                   _ptr(lam), _ptr(h_state), _ptr(g_state), _ptr(res["o"]),
-                                   _ptr(res.get("steps")), _ptr(res.get("x")), int(max_steps),
-                                   float(tol), _stream(stream))
-    _check(code_, "mesa_decode_step")
+    fn = lib().mesa_decode_step_symh if _symh else lib().mesa_decode_step
+    code_ = fn(N, H, d, d, _ptr(q), _ptr(k), _ptr(v), code, _ptr(gamma), _ptr(beta),
+               _ptr(lam), _ptr(h_state), _ptr(g_state), _ptr(res["o"]),
+               _ptr(res.get("steps")), _ptr(res.get("x")), int(max_steps),
+               float(tol), _stream(stream))
+    _check(code_, "mesa_decode_step_symh" if _symh else "mesa_decode_step")
     return res

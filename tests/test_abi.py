@@ -113,3 +113,19 @@ def test_decode_validation():
     assert call_dec(h=0) == 1
     assert call_dec(o=FAKE + 2) == 3
     assert call_dec(N=0) == 0  # nothing to do, nothing launched
+
+
+def test_packed_state_sizes_and_validation():
+    L = mesa.lib()
+    assert L.mesa_sym_state_floats(128) == 36 * 256
+    assert L.mesa_sym_state_floats(64) == 10 * 256
+    assert L.mesa_sym_state_floats(32) == 0
+    P = ctypes.c_void_p
+    assert L.mesa_sym_pack(4, 48, P(FAKE), P(FAKE), None) == 2
+    assert L.mesa_sym_pack(-1, 128, P(FAKE), P(FAKE), None) == 1
+    assert L.mesa_sym_pack(4, 128, None, P(FAKE), None) == 1
+    assert L.mesa_sym_unpack(4, 128, P(FAKE + 4), P(FAKE), None) == 3
+    assert L.mesa_sym_pack(0, 128, None, None, None) == 0
+    args = [P(FAKE)] * 3 + [1] + [P(FAKE)] * 8
+    assert L.mesa_decode_step_symh(2, 2, 96, 96, *args, 8, ctypes.c_float(1e-4), None) == 2
+    assert L.mesa_decode_step_symh(2, 2, 128, 128, *args, -1, ctypes.c_float(1e-4), None) == 1
