@@ -144,6 +144,7 @@ def bench_decode(cfg, steps, warmup):
     gs = [torch.from_numpy(x["g"]).to(dev) for _ in range(DECODE_STATE_COPIES)]
     o = torch.empty((cfg.N, cfg.H, cfg.d), device=dev, dtype=torch.float32)
     st = torch.empty((cfg.N, cfg.H), device=dev, dtype=torch.int32)
+    h_host, g_host = x["h"], x["g"]
     del x
     turn = [0]
 
@@ -185,6 +186,9 @@ def bench_decode(cfg, steps, warmup):
     ms_s = time_events(step_symh, steps)
     nbytes_s = pairs * decode_bytes_per_pair(cfg.d, in_bytes, mesa.sym_state_floats(cfg.d)) + cfg.H * cfg.d * 4
     gbs_s = nbytes_s / (ms_s * 1e-3) / 1e9
+    del hs_sym, gs
+    torch.cuda.empty_cache()
+    warm = bench_decode_warm(cfg, h_host, g_host, lam, in_bytes)
     return {
         "workload": f"decode step: {cfg.N} seqs x {cfg.H} heads, d={cfg.d}, fp32 states, "
                     f"{cfg.dtype} q/k/v, CG tol {cfg.tol:g} max {cfg.max_steps}",
@@ -206,6 +210,67 @@ def bench_decode(cfg, steps, warmup):
             "achieved_GBs": round(gbs_s, 1),
             "frac": round(gbs_s / PEAK_HBM_GBS, 4),
         },
+        "warm_start": warm,
+    }
+
+
+def bench_decode_warm(cfg, h_host, g_host, lam, in_bytes, T=8):
+    """Cold against warm-started CG over T consecutive tokens of related queries.
+
+    Both runs decode the same stream from the same states (full-layout H,
+    rotating over the state copies); the warm run starts every pair's CG at
+    its previous solution.  Step counts are averaged over tokens 1..T-1
+    (token 0 starts from zero in both)."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_decode_stream
+
+    dev = "cuda"
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    x = make_decode_stream(cfg, T)
+    tok = [{key: torch.from_numpy(np.ascontiguousarray(x[key][:, :, t])).to(dev).to(dt if key in ("q", "k", "v") else torch.float32)
+            for key in ("q", "k", "v", "gamma", "beta")} for t in range(T)]
+    del x
+    nc = DECODE_STATE_COPIES
+    o = torch.empty((cfg.N, cfg.H, cfg.d), device=dev, dtype=torch.float32)
+    st = torch.empty((nc, T, cfg.N, cfg.H), device=dev, dtype=torch.int32)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(warm):
+        hs = [torch.from_numpy(h_host).to(dev) for _ in range(nc)]
+        gs = [torch.from_numpy(g_host).to(dev) for _ in range(nc)]
+        xs = [torch.zeros((cfg.N, cfg.H, cfg.d), device=dev) for _ in range(nc)]
+        torch.cuda.synchronize()
+        e0.record()
+        for t in range(T):
+            a = tok[t]
+            for c in range(nc):
+                if warm:
+                    mesa.decode_step_warm(a["q"], a["k"], a["v"], a["gamma"], a["beta"], lam, hs[c], gs[c], xs[c],
+                                          max_steps=cfg.max_steps, tol=cfg.tol, out={"o": o, "steps": st[c, t]})
+                else:
+                    mesa.decode_step(a["q"], a["k"], a["v"], a["gamma"], a["beta"], lam, hs[c], gs[c],
+                                     max_steps=cfg.max_steps, tol=cfg.tol, out={"o": o, "steps": st[c, t]})
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (T * nc)
+        n = st[:, 1:].float().mean().item()
+        del hs, gs, xs
+        torch.cuda.empty_cache()
+        return ms, n
+
+    run(True)  # warm-up
+    ms_c, n_c = run(False)
+    ms_w, n_w = run(True)
+    pairs = cfg.N * cfg.H
+    nbytes = pairs * (decode_bytes_per_pair(cfg.d, in_bytes) + 2 * 4 * cfg.d) + cfg.H * cfg.d * 4
+    gbs = nbytes / (ms_w * 1e-3) / 1e9
+    return {
+        "stream": f"{T} tokens per pair; q, k per-dim AR(1) with lag-1 correlation 0.75, L2-normalised",
+        "cold": {"us_per_step": round(ms_c * 1e3, 2), "cg_steps_mean": round(n_c, 2)},
+        "warm": {"us_per_step": round(ms_w * 1e3, 2), "cg_steps_mean": round(n_w, 2),
+                 "bytes_per_step": int(nbytes), "achieved_GBs": round(gbs, 1),
+                 "frac": round(gbs / PEAK_HBM_GBS, 4)},
     }
 
 

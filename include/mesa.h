@@ -195,6 +195,31 @@ mesa_status mesa_decode_step_symh(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                   float* o, int32_t* steps, float* x_out,
                                   int32_t max_steps, float tol, hipStream_t stream);
 
+/* ---- warm-started decode step -----------------------------------------------
+ *
+ * The "significance" section of the MesaNet page names warm-starting the
+ * optimisation as a way to cut the solver's cost.  This step starts CG from a
+ * per-pair guess instead of 0 -- in decoding, the previous token's solution,
+ * which the step itself leaves behind:
+ *
+ *   x_state [N, H, dk] fp32, in/out (required): on entry the CG start x_0
+ *           (zeros give the cold start of mesa_decode_step), on return this
+ *           token's solution x_t, the next call's start.
+ *   h_packed 0: h_state is [N, H, dk, dk]; 1: h_state is [N, H,
+ *           mesa_sym_state_floats(dk)] in the blocked layout above.
+ *
+ * CG then begins from r_0 = q - (H_t + Lambda) x_0, tests the tolerance
+ * before every iteration as usual, and `steps` counts its iterations (the
+ * product A x_0 is one more, uncounted).  Everything else is as in
+ * mesa_decode_step.  Calls that share x_state must not overlap.
+ * Errors: MESA_ERR_INVALID_ARG for a NULL x_state or h_packed not 0/1. */
+mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                  const void* q, const void* k, const void* v, mesa_dtype in_dtype,
+                                  const float* gamma, const float* beta, const float* lambda,
+                                  float* h_state, int32_t h_packed, float* g_state, float* x_state,
+                                  float* o, int32_t* steps,
+                                  int32_t max_steps, float tol, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* mesa_status_string(mesa_status s);
 

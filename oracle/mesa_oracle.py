@@ -28,6 +28,12 @@ x_0 = 0 with the recursive residual, as in Saad, "Iterative Methods for Sparse
 Linear Systems", 2nd ed., Algorithm 6.18.  A token stops before an iteration
 when sqrt(rho) <= tol (tol > 0), when rho == 0, or when p.(A p) <= 0; a
 stopped token never restarts.  ``steps`` counts executed alpha updates.
+
+Warm start (the "significance" section names warm-started optimisation as a
+way to cut the solver's cost, without details): on request CG starts from a
+given x_0 with the residual r_0 = q - A x_0; in a sequence, token t starts from
+token t-1's CG result (token 0 from a given guess, else 0).  The product A x_0
+is not counted in ``steps``.
 """
 from __future__ import annotations
 
@@ -50,21 +56,28 @@ def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
 
 
 def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
-             forced_steps: np.ndarray | None = None, residuals: bool = False):
+             forced_steps: np.ndarray | None = None, residuals: bool = False,
+             x0: np.ndarray | None = None):
     """Batched conjugate gradient on A[s] x = q[s], fp64.
 
     A: [S, d, d] symmetric positive definite; q: [S, d].
     forced_steps: optional [S] ints -- run exactly that many iterations per
     system (the breakdown guard still applies) instead of the tolerance test.
+    x0: optional [S, d] initial guesses (default 0); the residual starts at
+    q - A x0.
     Returns (x [S, d], steps [S] int64); with ``residuals=True`` also the
     recursive residual norms ||r|| after the last executed iteration and
-    before it (equal to ||q|| for systems that ran no iteration).
+    before it (equal to ||r_0|| for systems that ran no iteration).
     """
     A = np.asarray(A, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
     S = q.shape[0]
-    x = np.zeros_like(q)
-    r = q.copy()
+    if x0 is None:
+        x = np.zeros_like(q)
+        r = q.copy()
+    else:
+        x = np.array(x0, dtype=np.float64).reshape(q.shape)
+        r = q - np.matmul(A, x[:, :, None])[:, :, 0]
     p = r.copy()
     rho = np.einsum("sd,sd->s", r, r)
     rho_prev = rho.copy()
@@ -109,7 +122,8 @@ def _flat(a, S, *tail):
 
 def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                  h0=None, g0=None, forced_steps=None, exact: bool = True,
-                 record_every: int | None = None, solve_at=None):
+                 record_every: int | None = None, solve_at=None,
+                 warm_start: bool = False, x_init=None):
     """Token-by-token Mesa layer over [B, H, T, d] inputs, fp64.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv]; gamma, beta: [B, H, T];
@@ -120,6 +134,8 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     solve_at: optional [T] bool -- solve and emit outputs only at these token
     positions (the state recurrence still runs over every token); outputs at
     other positions are left at zero.  Used to sample long sequences.
+    warm_start: start token t's CG from token t-1's CG result, token 0's from
+    x_init ([B, H, dk], default 0).  Needs every token solved (no solve_at).
 
     Returns a dict with o_cg, x_cg, steps, H_final, G_final (and o_exact,
     x_exact when ``exact``), shaped like the inputs.
@@ -138,6 +154,9 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     Hs = np.zeros((S, dk, dk)) if h0 is None else _flat(h0, S, dk, dk).copy()
     Gs = np.zeros((S, dv, dk)) if g0 is None else _flat(g0, S, dv, dk).copy()
     fs = None if forced_steps is None else np.asarray(forced_steps).reshape(S, T)
+    if warm_start and solve_at is not None:
+        raise ValueError("warm start needs every token solved")
+    x_prev = np.zeros((S, dk)) if x_init is None else _flat(x_init, S, dk).copy()
 
     o_cg = np.zeros((S, T, dv))
     x_cg = np.zeros((S, T, dk))
@@ -161,7 +180,9 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
             continue
         A = Hs + Lam
         xs, ns, rn, rp = cg_solve(A, qf[:, t], max_steps, tol,
-                                  None if fs is None else fs[:, t], residuals=True)
+                                  None if fs is None else fs[:, t], residuals=True,
+                                  x0=x_prev if warm_start else None)
+        x_prev = xs
         x_cg[:, t] = xs
         steps[:, t] = ns
         res_norm[:, t] = rn
@@ -191,11 +212,13 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
 
 
 def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: float,
-                     forced_steps=None, exact: bool = False):
+                     forced_steps=None, exact: bool = False, x0=None):
     """One recurrent step for N sequences x H heads, fp64.
 
     q, k: [N, H, dk]; v: [N, H, dv]; gamma, beta: [N, H]; lam: [H, dk] or
     [H, dk, dk]; h: [N, H, dk, dk]; g: [N, H, dv, dk] (not modified).
+    x0: optional [N, H, dk] warm start of the CG (the previous token's
+    solution); default: CG from 0.
     Returns dict(o, x, steps, h, g[, o_exact]) for the new token.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -206,7 +229,7 @@ def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: fl
                        max_steps=max_steps, tol=tol, h0=h, g0=g,
                        forced_steps=None if forced_steps is None
                        else np.asarray(forced_steps).reshape(N, Hh, 1),
-                       exact=exact)
+                       exact=exact, warm_start=x0 is not None, x_init=x0)
     out = dict(o=res["o_cg"][:, :, 0], x=res["x_cg"][:, :, 0], steps=res["steps"][:, :, 0],
                res_norm=res["res_norm"][:, :, 0], res_prev=res["res_prev"][:, :, 0],
                h=res["H_final"], g=res["G_final"])

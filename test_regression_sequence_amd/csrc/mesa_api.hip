@@ -150,7 +150,7 @@ mesa_status mesa_fwd_solve(const mesa_fwd_desc* d, const void* q, const void* k,
 
 namespace {
 
-mesa_status decode_impl(bool symh, int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+mesa_status decode_impl(bool symh, bool warm, int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
                         const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
                         const float* beta, const float* lambda, float* h_state, float* g_state,
                         float* o, int32_t* steps, float* x_out, int32_t max_steps, float tol,
@@ -160,7 +160,7 @@ mesa_status decode_impl(bool symh, int32_t N, int32_t H, int32_t dk, int32_t dv,
   if (dk != dv || (dk != 64 && dk != 128)) return MESA_ERR_UNSUPPORTED;
   if ((long long)N * H > (1LL << 31) - 1) return MESA_ERR_UNSUPPORTED;
   if (N == 0) return MESA_OK;
-  if (!q || !k || !v || !gamma || !beta || !lambda || !h_state || !g_state || !o)
+  if (!q || !k || !v || !gamma || !beta || !lambda || !h_state || !g_state || !o || (warm && !x_out))
     return MESA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, gamma, beta, lambda, h_state, g_state, o, steps, x_out};
   for (const void* ptr : ptrs)
@@ -169,10 +169,10 @@ mesa_status decode_impl(bool symh, int32_t N, int32_t H, int32_t dk, int32_t dv,
   mesa::DecodeParams dp{};
   dp.q = q; dp.k = k; dp.v = v; dp.gamma = gamma; dp.beta = beta; dp.lam = lambda;
   dp.h = h_state; dp.g = g_state; dp.o = o; dp.steps = steps; dp.x_out = x_out;
+  dp.x0 = warm ? x_out : nullptr;
   dp.P = N * H; dp.H = H; dp.max_steps = max_steps;
   dp.tol2 = tol > 0.f ? tol * tol : -1.f;
-  const hipError_t e = symh ? mesa::launch_decode_symh(in_dtype == MESA_BF16, dk, dp, stream)
-                            : mesa::launch_decode(in_dtype == MESA_BF16, dk, dp, stream);
+  const hipError_t e = mesa::launch_decode(in_dtype == MESA_BF16, dk, symh, warm, dp, stream);
   return e == hipSuccess ? MESA_OK : MESA_ERR_HIP;
 }
 
@@ -192,7 +192,7 @@ mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const
                              const float* beta, const float* lambda, float* h_state,
                              float* g_state, float* o, int32_t* steps, float* x_out,
                              int32_t max_steps, float tol, hipStream_t stream) {
-  return decode_impl(false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state, g_state, o,
+  return decode_impl(false, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state, g_state, o,
                      steps, x_out, max_steps, tol, stream);
 }
 
@@ -201,8 +201,18 @@ mesa_status mesa_decode_step_symh(int32_t N, int32_t H, int32_t dk, int32_t dv, 
                                   const float* beta, const float* lambda, float* h_sym,
                                   float* g_state, float* o, int32_t* steps, float* x_out,
                                   int32_t max_steps, float tol, hipStream_t stream) {
-  return decode_impl(true, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_sym, g_state, o,
+  return decode_impl(true, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_sym, g_state, o,
                      steps, x_out, max_steps, tol, stream);
+}
+
+mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+                                  const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
+                                  const float* beta, const float* lambda, float* h_state, int32_t h_packed,
+                                  float* g_state, float* x_state, float* o, int32_t* steps,
+                                  int32_t max_steps, float tol, hipStream_t stream) {
+  if (h_packed != 0 && h_packed != 1) return MESA_ERR_INVALID_ARG;
+  return decode_impl(h_packed == 1, true, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state,
+                     g_state, o, steps, x_state, max_steps, tol, stream);
 }
 
 size_t mesa_sym_state_floats(int32_t d) {

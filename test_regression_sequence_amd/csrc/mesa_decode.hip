@@ -20,6 +20,10 @@
 //      so both dot products are wave-local and all waves take identical
 //      decisions.
 //   G: the same row segments; o = G x is reduced across the lanes of a row.
+// WARM: CG starts from a given x_0 (the previous token's solution, kept per
+// pair by the caller) with r_0 = q - (H + Lambda) x_0, one more product with
+// H + Lambda that is not counted as a step; the solution is written back in
+// place of x_0.
 // The update forms k_r*k_j before scaling and is one explicit FMA per element,
 // gamma*h + (beta*(k_r*k_j)), so an exactly symmetric H stays exactly
 // symmetric and every variant of the kernel rounds the same way.
@@ -44,7 +48,7 @@ __device__ __forceinline__ int sym_block(int nb, int bi, int bj) { return bi * n
 // slots so that both read patterns and the linear fill avoid bank conflicts,
 // and the CG buffers reuse its space.  Only threads of stored blocks write H
 // back.  The CG and G parts are unchanged.
-template <bool BF16, int D, bool SYMH>
+template <bool BF16, int D, bool SYMH, bool WARM>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) {
   constexpr int NW = kDecWaves;
   constexpr int Q = D / 4;                   // 16-byte column quads per row
@@ -76,6 +80,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   const float vv = load1<BF16>(p.v, (size_t)pair * D + iv);
   const float lamv = p.lam[(size_t)h * D + iv];
   const float gam = p.gamma[pair], bet = p.beta[pair];
+  float x0v[WARM ? EPL : 1];  // warm start, in flight while H streams
+  if constexpr (WARM) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x0v[e] = p.x0[(size_t)pair * D + lane + 64 * e];
+  }
 
   // ---- H <- gamma H + beta (k k^T), kept in registers, written back --------------
   // wave-uniform base plus a 32-bit per-lane byte offset (row0, cq) plus a
@@ -159,35 +168,22 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   // ---- CG on (H + Lambda) x = q -------------------------------------------------------
   float xv[EPL], rv[EPL], pv[EPL], lv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    xv[e] = 0.f;
-    rv[e] = qs[lane + 64 * e];
-    pv[e] = rv[e];
-    lv[e] = lam_s[lane + 64 * e];
-  }
-  // identical in every lane by construction; taken from lane 0 so that the
-  // loop's exit tests are wave-uniform beyond doubt (a barrier is inside)
-  auto vsum = [&](const float* a, const float* b) {
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) s += a[e] * b[e];
-    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_sum(s))));
-  };
+  for (int e = 0; e < EPL; ++e) lv[e] = lam_s[lane + 64 * e];
   float* mypb = pb[wave];
-  float rho = vsum(rv, rv);
-  int n = 0;
-  for (int it = 0; it < p.max_steps; ++it) {
-    if (!(rho > 0.f && rho > p.tol2)) break;
-    // publish p to this wave's own LDS copy (read back by the same wave only)
+  // w = (H + Lambda) u for a vector u that every wave holds whole: this wave's
+  // rows give column sums for all columns, the waves' parts meet in part2[buf]
+  // at one barrier
+  auto apply_a = [&](const float(&u)[EPL], float(&w)[EPL], int buf) {
+    // publish u to this wave's own LDS copy (read back by the same wave only)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) mypb[lane + 64 * e] = pv[e];
+    for (int e = 0; e < EPL; ++e) mypb[lane + 64 * e] = u[e];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the writes above have landed
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i4 = 0; i4 < RPT / 4; ++i4) {
       const f32x4 pr = *reinterpret_cast<const f32x4*>(&mypb[row0 + 4 * i4]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc += hreg[4 * i4 + u] * pr[u];
+      for (int u4 = 0; u4 < 4; ++u4) acc += hreg[4 * i4 + u4] * pr[u4];
     }
     // combine the row groups of this wave: lanes l, l^32 (and l^16 when 4 groups)
 #pragma unroll
@@ -199,18 +195,50 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
       const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
       acc[e] = __uint_as_float(b[0]) + __uint_as_float(b[1]);
     }
-    float(*pt)[D] = part2[it & 1];
+    float(*pt)[D] = part2[buf];
     if (lane < Q) *reinterpret_cast<f32x4*>(&pt[wave][4 * cq]) = acc;
     __syncthreads();
-    float wv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int j = lane + 64 * e;
       float y = pt[0][j];
 #pragma unroll
       for (int q = 1; q < NW; ++q) y += pt[q][j];
-      wv[e] = y + lv[e] * pv[e];
+      w[e] = y + lv[e] * u[e];
     }
+  };
+  if constexpr (WARM) {
+    // the part buffer used here is next written two barriers later
+    float ax[EPL];
+    apply_a(x0v, ax, 1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      xv[e] = x0v[e];
+      rv[e] = qs[lane + 64 * e] - ax[e];
+      pv[e] = rv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      xv[e] = 0.f;
+      rv[e] = qs[lane + 64 * e];
+      pv[e] = rv[e];
+    }
+  }
+  // identical in every lane by construction; taken from lane 0 so that the
+  // loop's exit tests are wave-uniform beyond doubt (a barrier is inside)
+  auto vsum = [&](const float* a, const float* b) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s += a[e] * b[e];
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_sum(s))));
+  };
+  float rho = vsum(rv, rv);
+  int n = 0;
+  for (int it = 0; it < p.max_steps; ++it) {
+    if (!(rho > 0.f && rho > p.tol2)) break;
+    float wv[EPL];
+    apply_a(pv, wv, it & 1);
     const float pw = vsum(pv, wv);
     if (!(pw > 0.f)) break;
     const float alpha = rho / pw;
@@ -254,32 +282,29 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   if (tid == 0 && p.steps) p.steps[pair] = n;
 }
 
-template <bool BF16, int D, bool SYMH>
+template <bool BF16, int D, bool SYMH, bool WARM>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<BF16, D, SYMH>), dim3(p.P), dim3(64 * kDecWaves), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<BF16, D, SYMH, WARM>), dim3(p.P), dim3(64 * kDecWaves), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool SYMH>
+template <bool SYMH, bool WARM>
 hipError_t launch_decode_s(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
   if (bf16) {
-    if (D == 128) return launch_decode_t<true, 128, SYMH>(p, s);
-    if (D == 64) return launch_decode_t<true, 64, SYMH>(p, s);
+    if (D == 128) return launch_decode_t<true, 128, SYMH, WARM>(p, s);
+    if (D == 64) return launch_decode_t<true, 64, SYMH, WARM>(p, s);
   } else {
-    if (D == 128) return launch_decode_t<false, 128, SYMH>(p, s);
-    if (D == 64) return launch_decode_t<false, 64, SYMH>(p, s);
+    if (D == 128) return launch_decode_t<false, 128, SYMH, WARM>(p, s);
+    if (D == 64) return launch_decode_t<false, 64, SYMH, WARM>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
-  return launch_decode_s<false>(bf16, D, p, s);
-}
-
-hipError_t launch_decode_symh(bool bf16, int D, const DecodeParams& p, hipStream_t s) {
-  return launch_decode_s<true>(bf16, D, p, s);
+hipError_t launch_decode(bool bf16, int D, bool packed_h, bool warm, const DecodeParams& p, hipStream_t s) {
+  if (packed_h) return warm ? launch_decode_s<true, true>(bf16, D, p, s) : launch_decode_s<true, false>(bf16, D, p, s);
+  return warm ? launch_decode_s<false, true>(bf16, D, p, s) : launch_decode_s<false, false>(bf16, D, p, s);
 }
 
 }  // namespace mesa

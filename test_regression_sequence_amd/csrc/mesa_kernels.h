@@ -86,6 +86,7 @@ struct DecodeParams {
   float* o;              // [P, D]
   int32_t* steps;        // [P] or null
   float* x_out;          // [P, D] or null
+  const float* x0;       // [P, D] CG start (warm variant only; may alias x_out)
   int P, H, max_steps;
   float tol2;
 };
@@ -95,9 +96,9 @@ hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_cg_bf16(int D, int C, const CgParams& p, hipStream_t s);
 hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t s);
-hipError_t launch_decode(bool bf16, int D, const DecodeParams& p, hipStream_t s);
-// decode with H in the blocked upper-triangular layout (DecodeParams::h packed)
-hipError_t launch_decode_symh(bool bf16, int D, const DecodeParams& p, hipStream_t s);
+// packed_h: DecodeParams::h in the blocked upper-triangular layout;
+// warm: CG starts from DecodeParams::x0
+hipError_t launch_decode(bool bf16, int D, bool packed_h, bool warm, const DecodeParams& p, hipStream_t s);
 hipError_t launch_sym_pack(int D, int count, const float* full, float* packed, hipStream_t s);
 hipError_t launch_sym_unpack(int D, int count, const float* packed, float* full, hipStream_t s);
 size_t sym_state_floats(int D);

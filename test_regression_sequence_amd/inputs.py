@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
-    "make_decode_inputs", "round_to_bf16", "bf16_bits", "bits_to_f32",
+    "make_decode_inputs", "make_decode_stream", "round_to_bf16", "bf16_bits", "bits_to_f32",
 ]
 
 
@@ -261,6 +261,39 @@ def make_decode_inputs(cfg: DecodeConfig, block: int = 64) -> dict:
     if cfg.dtype == "bf16":
         out.update(q_bits=qb, k_bits=kb, v_bits=vb)
     return out
+
+
+def make_decode_stream(cfg: DecodeConfig, T: int, rho: float = 0.75) -> dict:
+    """T consecutive new tokens for the decode step, neighbouring queries and keys related.
+
+    Queries and keys follow a Gaussian AR(1) process per (pair, dim),
+    z_t = rho z_{t-1} + sqrt(1 - rho^2) eps_t, each token then L2-normalised:
+    consecutive tokens correlate like the outputs of a short causal filter
+    (rho = 0.75 is the lag-1 correlation of a 4-tap moving average of
+    independent vectors).  v ~ N(0, 1), gamma and beta as in
+    :func:`make_decode_inputs`, independent per token.  Stream:
+    ``default_rng([seed, 2])`` drawing z_0 and eps for q, then for k, then v,
+    u, beta.  Shapes: q, k, v ``[N, H, T, d]``; gamma, beta ``[N, H, T]``.
+    Lambda and the starting states are those of ``make_decode_inputs(cfg)``.
+    """
+    rng = np.random.default_rng([cfg.seed, 2])
+    shp = (cfg.N, cfg.H, T, cfg.d)
+
+    def ar1():
+        z = np.empty(shp)
+        z[:, :, 0] = rng.standard_normal(shp[:2] + (cfg.d,))
+        eps = rng.standard_normal((cfg.N, cfg.H, T - 1, cfg.d)) if T > 1 else None
+        for t in range(1, T):
+            z[:, :, t] = rho * z[:, :, t - 1] + np.sqrt(1.0 - rho * rho) * eps[:, :, t - 1]
+        return z / np.linalg.norm(z, axis=-1, keepdims=True)
+
+    q, _ = _finish(ar1(), cfg.dtype)
+    k, _ = _finish(ar1(), cfg.dtype)
+    v, _ = _finish(rng.standard_normal(shp), cfg.dtype)
+    u = rng.uniform(cfg.gamma_logit[0], cfg.gamma_logit[1], shp[:3])
+    gamma = (1.0 / (1.0 + np.exp(-u))).astype(np.float32)
+    beta = _beta(rng, cfg.beta_dist, shp[:3]).astype(np.float32)
+    return dict(q=q, k=k, v=v, gamma=gamma, beta=beta, cfg=cfg)
 
 
 def small_fwd(B=1, H=2, T=200, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0,

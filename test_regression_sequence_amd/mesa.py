@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
                                        P, P, I32, F, P]
         L.mesa_decode_step_symh.restype = ctypes.c_int
         L.mesa_decode_step_symh.argtypes = list(L.mesa_decode_step.argtypes)
+        L.mesa_decode_step_warm.restype = ctypes.c_int
+        L.mesa_decode_step_warm.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, I32,
+                                            P, P, P, P, I32, F, P]
         L.mesa_sym_state_floats.restype = S
         L.mesa_sym_state_floats.argtypes = [I32]
         L.mesa_sym_pack.restype = ctypes.c_int
@@ -269,4 +272,36 @@ def decode_step(q, k, v, gamma, beta, lam, h_state, g_state, *, max_steps: int =
                _ptr(res.get("steps")), _ptr(res.get("x")), int(max_steps),
                float(tol), _stream(stream))
     _check(code_, "mesa_decode_step_symh" if _symh else "mesa_decode_step")
+    return res
+
+
+def decode_step_warm(q, k, v, gamma, beta, lam, h_state, g_state, x_state, *, packed_h: bool = False,
+                     max_steps: int = 32, tol: float = 1e-4, return_steps: bool = True,
+                     out=None, stream=None) -> dict:
+    """decode_step with CG started from x_state [N, H, d] fp32, which is overwritten
+    with this token's solution (the next step's start).  h_state is [N, H, d, d], or
+    [N, H, sym_state_floats(d)] in the blocked layout when packed_h."""
+    N, H, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, H, d), q.dtype)
+    _need(gamma, "gamma", (N, H), torch.float32)
+    _need(beta, "beta", (N, H), torch.float32)
+    _need(lam, "lam", (H, d), torch.float32)
+    if packed_h:
+        _need(h_state, "h_sym", (N, H, sym_state_floats(d)), torch.float32)
+    else:
+        _need(h_state, "h_state", (N, H, d, d), torch.float32)
+    _need(g_state, "g_state", (N, H, d, d), torch.float32)
+    _need(x_state, "x_state", (N, H, d), torch.float32)
+    dev = q.device
+    out = dict(out or {})
+    res = {"o": out.get("o") if out.get("o") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)}
+    if return_steps:
+        res["steps"] = out.get("steps") if out.get("steps") is not None else torch.empty((N, H), device=dev, dtype=torch.int32)
+    code_ = lib().mesa_decode_step_warm(N, H, d, d, _ptr(q), _ptr(k), _ptr(v), code, _ptr(gamma), _ptr(beta),
+                                        _ptr(lam), _ptr(h_state), 1 if packed_h else 0, _ptr(g_state),
+                                        _ptr(x_state), _ptr(res["o"]), _ptr(res.get("steps")),
+                                        int(max_steps), float(tol), _stream(stream))
+    _check(code_, "mesa_decode_step_warm")
     return res

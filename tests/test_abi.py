@@ -129,3 +129,20 @@ def test_packed_state_sizes_and_validation():
     args = [P(FAKE)] * 3 + [1] + [P(FAKE)] * 8
     assert L.mesa_decode_step_symh(2, 2, 96, 96, *args, 8, ctypes.c_float(1e-4), None) == 2
     assert L.mesa_decode_step_symh(2, 2, 128, 128, *args, -1, ctypes.c_float(1e-4), None) == 1
+
+
+def test_warm_decode_validation():
+    L = mesa.lib()
+    P = ctypes.c_void_p
+
+    def call(h_packed=0, x_state=FAKE, dk=128, max_steps=8):
+        return L.mesa_decode_step_warm(2, 2, dk, dk, P(FAKE), P(FAKE), P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE),
+                                       P(FAKE), h_packed, P(FAKE), P(x_state) if x_state else None,
+                                       P(FAKE), None, max_steps, ctypes.c_float(1e-4), None)
+
+    assert call(x_state=0) == 1        # the start is required
+    assert call(h_packed=2) == 1
+    assert call(h_packed=-1) == 1
+    assert call(dk=96) == 2
+    assert call(max_steps=-1) == 1
+    assert call(x_state=FAKE + 4) == 3

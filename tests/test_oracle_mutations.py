@@ -38,6 +38,13 @@ MUTATIONS = {
     "tolerance_ignored": ("go = np.sqrt(rho) > tol", "go = np.ones(S, dtype=bool)"),
     "direction_not_updated": ("p = np.where(go[:, None], r + beta[:, None] * p, p)",
                               "p = np.where(go[:, None], r, p)"),
+    "warm_residual_not_shifted": ("r = q - np.matmul(A, x[:, :, None])[:, :, 0]", "r = q.copy()"),
+    "warm_guess_dropped": ("x = np.array(x0, dtype=np.float64).reshape(q.shape)",
+                           "x = np.zeros_like(q)"),
+    "warm_chain_not_advanced": ("        x_prev = xs\n", "\n"),
+    "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
+                                       ("            x_ex[:, t] = xe\n",
+                                        "            x_ex[:, t] = xe\n            x_prev = xe\n")],
 }
 
 
@@ -106,6 +113,27 @@ def run_pins(m):
                 break
     except Exception:
         failed.append("P5-crash")
+    # P4w: warm-started iterates are affine Krylov projections
+    xw = np.array([1, 0, -2, 1])
+    xq = [Fraction(int(z)) for z in xw]
+    for n in range(0, d + 1):
+        ref = np.array([float(z) for z in pins._krylov_iterate(Aq, qq, n, xq)])
+        x, steps = m.cg_solve(A[None].astype(float), qv[None].astype(float), n, 0.0,
+                              x0=xw[None].astype(float))
+        if pins.rel(x[0], ref) > 1e-9:
+            failed.append("P4w")
+            break
+    # chained warm start over a sequence (exact rationals)
+    saved = pins.mesa_forward
+    try:
+        pins.mesa_forward = m.mesa_forward
+        pins.test_p4w_warm_sequence_chains_previous_solution()
+    except AssertionError:
+        failed.append("P4w-seq")
+    except Exception:
+        failed.append("P4w-seq-crash")
+    finally:
+        pins.mesa_forward = saved
     # P7: tolerance stops before an iteration
     x, n = m.cg_solve(np.eye(3)[None] * 2.0, np.array([[1e-7, 0.0, 0.0]]), 10, 1e-6)
     if n[0] != 0:

@@ -183,18 +183,30 @@ def _frac_solve(M, b):
     return [A[i][n] / A[i][i] for i in range(n)]
 
 
-def _krylov_iterate(A, q, n):
-    """x_n = V (V^T A V)^{-1} V^T q, V = [q, Aq, ..., A^{n-1} q], exactly."""
+def _krylov_iterate(A, q, n, x0=None):
+    """The n-th CG iterate characterised without the CG recurrence, exactly.
+
+    From x0 = 0: x_n = V (V^T A V)^{-1} V^T q with V = [q, Aq, ..., A^{n-1} q],
+    the A-norm projection of the solution onto the Krylov space.  From a
+    guess x0: x_n = x0 + V (V^T A V)^{-1} V^T r0 with r0 = q - A x0 and V a
+    basis of K_n(A, r0), the projection onto the affine space x0 + K_n.
+    """
     d = len(q)
     matvec = lambda x: [sum(A[i][j] * x[j] for j in range(d)) for i in range(d)]
-    V = [list(q)]
+    if x0 is None:
+        x0 = [Fraction(0)] * d
+    Ax0 = matvec(x0)
+    r0 = [q[i] - Ax0[i] for i in range(d)]
+    if n == 0 or all(z == 0 for z in r0):
+        return list(x0)
+    V = [r0]
     for _ in range(n - 1):
         V.append(matvec(V[-1]))
     AV = [matvec(vv) for vv in V]
     M = [[sum(V[a][i] * AV[b][i] for i in range(d)) for b in range(n)] for a in range(n)]
-    rhs = [sum(V[a][i] * q[i] for i in range(d)) for a in range(n)]
+    rhs = [sum(V[a][i] * r0[i] for i in range(d)) for a in range(n)]
     c = _frac_solve(M, rhs)
-    return [sum(c[a] * V[a][i] for a in range(n)) for i in range(d)]
+    return [x0[i] + sum(c[a] * V[a][i] for a in range(n)) for i in range(d)]
 
 
 @pytest.mark.parametrize("seed,d", [(0, 3), (1, 4), (2, 5), (3, 6)])
@@ -211,6 +223,78 @@ def test_p4_cg_iterates_are_krylov_projections(seed, d):
         x, steps = cg_solve(A[None].astype(float), q[None].astype(float), n, 0.0)
         assert steps[0] == n
         assert rel(x[0], ref) < 1e-9, (n, x[0], ref)
+
+
+# ---------------------------------------------------------------------------
+# P4w, P3w, P7w: CG from a warm start
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,d", [(4, 3), (5, 4), (6, 5)])
+def test_p4w_warm_iterates_are_affine_krylov_projections(seed, d):
+    rng = np.random.default_rng(seed)
+    Mi = rng.integers(-3, 4, (d, d))
+    A = (Mi @ Mi.T + np.diag(rng.integers(1, 4, d))).astype(np.int64)
+    q = rng.integers(-4, 5, d).astype(np.int64)
+    x0 = rng.integers(-3, 4, d).astype(np.int64)
+    Aq = [[Fraction(int(a)) for a in row] for row in A]
+    qq = [Fraction(int(z)) for z in q]
+    xq = [Fraction(int(z)) for z in x0]
+    for n in range(0, d + 1):
+        ref = np.array([float(z) for z in _krylov_iterate(Aq, qq, n, xq)])
+        x, steps = cg_solve(A[None].astype(float), q[None].astype(float), n, 0.0,
+                            x0=x0[None].astype(float))
+        assert rel(x[0], ref) < 1e-9, (n, x[0], ref)
+
+
+def test_p3w_warm_start_d_steps_reach_the_solution():
+    rng = np.random.default_rng(16)
+    S, d = 6, 16
+    M = rng.standard_normal((S, d, d))
+    A = np.matmul(M, M.transpose(0, 2, 1)) / d + np.eye(d)
+    q = rng.standard_normal((S, d))
+    x0 = 3.0 * rng.standard_normal((S, d))
+    x, steps = cg_solve(A, q, d, 0.0, x0=x0)
+    ref = np.stack([np.linalg.solve(A[s], q[s]) for s in range(S)])
+    assert rel(x, ref) < 1e-10
+
+
+def test_p7w_exact_guess_takes_no_step():
+    A = np.eye(3)[None] * 2.0
+    q = np.array([[1.0, 0.0, 0.0]])
+    x0 = np.array([[0.5, 0.0, 0.0]])
+    for tol in (1e-6, 0.0):
+        x, n = cg_solve(A, q, 10, tol, x0=x0)
+        assert n[0] == 0 and np.array_equal(x, x0)
+
+
+def test_p4w_warm_sequence_chains_previous_solution():
+    """Token t starts from token t-1's n-step result: chained affine Krylov projections,
+    with the states, forget factors and outputs in exact rationals."""
+    rng = np.random.default_rng(17)
+    T, d, n = 5, 3, 2
+    ki = rng.integers(-2, 3, (T, d)); vi = rng.integers(-2, 3, (T, d)); qi = rng.integers(-3, 4, (T, d))
+    gnum = rng.integers(1, 4, T); bnum = rng.integers(1, 4, T); lnum = rng.integers(1, 4, d)
+    gam = [Fraction(int(a), 4) for a in gnum]       # in (0, 1)
+    bet = [Fraction(int(a), 2) for a in bnum]
+    lam = [Fraction(int(a), 2) for a in lnum]
+    x_init = [Fraction(int(a)) for a in rng.integers(-1, 2, d)]
+    Hq = [[Fraction(0)] * d for _ in range(d)]
+    Gq = [[Fraction(0)] * d for _ in range(d)]
+    xp = list(x_init)
+    ref_o = []
+    for t in range(T):
+        kk = [Fraction(int(a)) for a in ki[t]]; vv = [Fraction(int(a)) for a in vi[t]]
+        Hq = [[gam[t] * Hq[i][j] + bet[t] * kk[i] * kk[j] for j in range(d)] for i in range(d)]
+        Gq = [[gam[t] * Gq[i][j] + bet[t] * vv[i] * kk[j] for j in range(d)] for i in range(d)]
+        Aq = [[Hq[i][j] + (lam[i] if i == j else 0) for j in range(d)] for i in range(d)]
+        xp = _krylov_iterate(Aq, [Fraction(int(a)) for a in qi[t]], n, xp)
+        ref_o.append([float(sum(Gq[i][j] * xp[j] for j in range(d))) for i in range(d)])
+    res = mesa_forward(qi[None, None].astype(float), ki[None, None].astype(float),
+                       vi[None, None].astype(float),
+                       np.array([[[float(g) for g in gam]]]), np.array([[[float(b) for b in bet]]]),
+                       np.array([[float(l) for l in lam]]), max_steps=n, tol=0.0, exact=False,
+                       warm_start=True, x_init=np.array([[[float(a) for a in x_init]]]))
+    assert rel(res["o_cg"][0, 0], np.array(ref_o)) < 1e-10
 
 
 # ---------------------------------------------------------------------------
@@ -347,3 +431,18 @@ def test_decode_step_continues_forward():
                            pre["H_final"], pre["G_final"], max_steps=3, tol=0.0)
     assert rel(dec["o"], full["o_cg"][:, :, T]) < 1e-13
     assert rel(dec["h"], full["H_final"]) < 1e-14
+
+
+def test_decode_step_warm_continues_warm_forward():
+    rng = np.random.default_rng(18)
+    T, d = 7, 4
+    q, k, v, gamma, beta = rand_slice(rng, T + 1, d, d)
+    lam = rng.uniform(0.25, 1.0, (1, d))
+    full = mesa_forward(q, k, v, gamma, beta, lam, max_steps=2, tol=0.0, warm_start=True)
+    pre = mesa_forward(q[:, :, :T], k[:, :, :T], v[:, :, :T], gamma[:, :, :T], beta[:, :, :T],
+                       lam, max_steps=2, tol=0.0, warm_start=True)
+    dec = mesa_decode_step(q[:, :, T], k[:, :, T], v[:, :, T], gamma[:, :, T], beta[:, :, T], lam,
+                           pre["H_final"], pre["G_final"], max_steps=2, tol=0.0,
+                           x0=pre["x_cg"][:, :, T - 1])
+    assert rel(dec["o"], full["o_cg"][:, :, T]) < 1e-13
+    assert rel(dec["x"], full["x_cg"][:, :, T]) < 1e-13
