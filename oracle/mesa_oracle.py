@@ -39,7 +39,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full"]
+__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full", "qk_preprocess"]
 
 
 def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
@@ -236,3 +236,32 @@ def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: fl
     if exact:
         out["o_exact"] = res["o_exact"][:, :, 0]
     return out
+
+
+def qk_preprocess(x, w, hist=None, eps: float = 1e-6):
+    """Query/key preprocessing before the layer, fp64.
+
+    The architecture section has queries and keys normalised and convolved
+    with a small window before the Mesa layer.  Reading: a causal convolution
+    along time with its own taps per channel (depthwise), then L2
+    normalisation of each token vector, so the layer receives unit-norm
+    queries and keys:
+        y_t[j] = sum_{i < W} w[h, j, i] * x_{t-i}[j]
+        out_t  = y_t / max(||y_t||_2, eps)
+    x: [B, H, T, d] raw vectors; w: [H, d, W] taps (tap i weighs token t-i);
+    hist: optional [B, H, W-1, d] raw vectors before t = 0, oldest first
+    (default: zeros).  Returns (out [B, H, T, d], hist_out [B, H, W-1, d]:
+    the last W-1 raw vectors, oldest first -- the history of the next call).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, Hh, T, d = x.shape
+    W = w.shape[-1]
+    pre = np.zeros((B, Hh, W - 1, d)) if hist is None else np.asarray(hist, dtype=np.float64)
+    seq = np.concatenate([pre, x], axis=2)      # token t sits at index t + W - 1
+    y = np.zeros((B, Hh, T, d))
+    for i in range(W):
+        y += w[None, :, None, :, i] * seq[:, :, W - 1 - i:W - 1 - i + T]
+    nrm = np.linalg.norm(y, axis=-1, keepdims=True)
+    out = y / np.maximum(nrm, eps)
+    return out, seq[:, :, T:]

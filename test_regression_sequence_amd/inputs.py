@@ -35,7 +35,8 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
-    "make_decode_inputs", "make_decode_stream", "round_to_bf16", "bf16_bits", "bits_to_f32",
+    "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "round_to_bf16",
+    "bf16_bits", "bits_to_f32",
 ]
 
 
@@ -294,6 +295,29 @@ def make_decode_stream(cfg: DecodeConfig, T: int, rho: float = 0.75) -> dict:
     gamma = (1.0 / (1.0 + np.exp(-u))).astype(np.float32)
     beta = _beta(rng, cfg.beta_dist, shp[:3]).astype(np.float32)
     return dict(q=q, k=k, v=v, gamma=gamma, beta=beta, cfg=cfg)
+
+
+def make_preprocess_inputs(cfg: FwdConfig, window: int = 4) -> dict:
+    """Raw queries and keys, and convolution taps, for the query/key preprocessing.
+
+    Raw q, k ~ N(0, 1) (not normalised: the preprocessing normalises),
+    ``[B, H, T, d]`` in the configuration's dtype; taps wq, wk ``[H, d, window]``
+    fp32 ~ U(-1/sqrt(window), 1/sqrt(window)) (the usual initialisation of a
+    depthwise convolution); raw histories hq, hk ``[B, H, window-1, d]`` ~ N(0, 1)
+    for calls that continue a sequence.  Stream: ``default_rng([seed, 3])``
+    in the order q, k, wq, wk, hq, hk, drawn in fp32.
+    """
+    rng = np.random.default_rng([cfg.seed, 3])
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    q, _ = _finish(rng.standard_normal(shp, dtype=np.float32), cfg.dtype)
+    k, _ = _finish(rng.standard_normal(shp, dtype=np.float32), cfg.dtype)
+    a = 1.0 / np.sqrt(window)
+    wq = rng.uniform(-a, a, (cfg.H, cfg.d, window)).astype(np.float32)
+    wk = rng.uniform(-a, a, (cfg.H, cfg.d, window)).astype(np.float32)
+    hshp = (cfg.B, cfg.H, window - 1, cfg.d)
+    hq, _ = _finish(rng.standard_normal(hshp, dtype=np.float32), cfg.dtype)
+    hk, _ = _finish(rng.standard_normal(hshp, dtype=np.float32), cfg.dtype)
+    return dict(q=q, k=k, wq=wq, wk=wk, hq=hq, hk=hk, window=window, cfg=cfg)
 
 
 def small_fwd(B=1, H=2, T=200, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0,

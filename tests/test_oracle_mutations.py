@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import test_oracle_pins as pins
+import test_oracle_preprocess as prep
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "mesa_oracle.py")
@@ -42,6 +43,13 @@ MUTATIONS = {
     "warm_guess_dropped": ("x = np.array(x0, dtype=np.float64).reshape(q.shape)",
                            "x = np.zeros_like(q)"),
     "warm_chain_not_advanced": ("        x_prev = xs\n", "\n"),
+    "prep_taps_reversed": ("y += w[None, :, None, :, i] * seq", "y += w[None, :, None, :, W - 1 - i] * seq"),
+    "prep_history_reversed": ("seq = np.concatenate([pre, x], axis=2)",
+                              "seq = np.concatenate([pre[:, :, ::-1], x], axis=2)"),
+    "prep_norm_over_time": ("nrm = np.linalg.norm(y, axis=-1, keepdims=True)",
+                            "nrm = np.linalg.norm(y, axis=-2, keepdims=True)"),
+    "prep_history_out_shifted": ("return out, seq[:, :, T:]", "return out, seq[:, :, T - 1:-1]"),
+    "prep_current_token_dropped": ("for i in range(W):\n        y +=", "for i in range(1, W):\n        y +="),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
                                        ("            x_ex[:, t] = xe\n",
                                         "            x_ex[:, t] = xe\n            x_prev = xe\n")],
@@ -134,6 +142,19 @@ def run_pins(m):
         failed.append("P4w-seq-crash")
     finally:
         pins.mesa_forward = saved
+    # preprocessing against library convolution and normalisation
+    saved = prep.qk_preprocess
+    try:
+        prep.qk_preprocess = m.qk_preprocess
+        for fn in (lambda: prep.test_matches_library_convolution_and_normalisation(3),
+                   prep.test_short_sequences_carry_history_through):
+            try:
+                fn()
+            except AssertionError:
+                failed.append("prep")
+                break
+    finally:
+        prep.qk_preprocess = saved
     # P7: tolerance stops before an iteration
     x, n = m.cg_solve(np.eye(3)[None] * 2.0, np.array([[1e-7, 0.0, 0.0]]), 10, 1e-6)
     if n[0] != 0:
