@@ -274,6 +274,40 @@ def bench_decode_warm(cfg, h_host, g_host, lam, in_bytes, T=8):
     }
 
 
+def bench_preprocess(cfg, steps, warmup, window=4):
+    """Query/key preprocessing (causal depthwise convolution + L2 norm) at the layer
+    workload's shape: raw q, k read once, processed q, k written once."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_preprocess_inputs
+
+    x = make_preprocess_inputs(cfg, window)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(x["q"]).cuda().to(dt)
+    k = torch.from_numpy(x["k"]).cuda().to(dt)
+    wq = torch.from_numpy(x["wq"]).cuda()
+    wk = torch.from_numpy(x["wk"]).cuda()
+    del x
+    out = {"q": torch.empty_like(q), "k": torch.empty_like(k)}
+
+    def step():
+        mesa.qk_preprocess(q, k, wq, wk, out=out)
+
+    for _ in range(warmup):
+        step()
+    ms = time_events(step, steps)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    nbytes = 4 * cfg.B * cfg.H * cfg.T * cfg.d * esz + 2 * cfg.H * cfg.d * window * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"q/k preprocessing: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} {cfg.dtype}, window {window}",
+        "us_per_call": round(ms * 1e3, 2),
+        "bytes_per_call": int(nbytes),
+        "achieved_GBs": round(gbs, 1),
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+    }
+
+
 def kernel_source_digest(names=("mesa_cg_bf16.hip", "mesa_common.h", "mesa_kernels.h")) -> str:
     """sha256 over the sources of the CG kernel (ties a traffic record to one kernel version)."""
     import hashlib
@@ -430,6 +464,7 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = bench_decode(CONFIGS[5], args.steps, args.warmup)
+    line["preprocess"] = bench_preprocess(CONFIGS[args.workload], args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
     print(json.dumps(line), flush=True)

@@ -220,6 +220,37 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                   float* o, int32_t* steps,
                                   int32_t max_steps, float tol, hipStream_t stream);
 
+/* ---- query/key preprocessing -------------------------------------------------
+ *
+ * MesaNet page, "architecture" section: queries and keys are normalised and
+ * convolved with a small window before the Mesa layer.  Computed here as a
+ * causal depthwise convolution along time followed by L2 normalisation of
+ * every token vector (so the layer receives unit-norm queries and keys), for
+ * queries and keys in one call, each with its own taps:
+ *
+ *   y_t[j] = sum_{i < window} w[h][j][i] * x_{t-i}[j]
+ *   out_t  = y_t / max(||y_t||_2, eps)
+ *
+ *   q_raw, k_raw [B, H, T, d] dtype (raw projections)
+ *   w_q, w_k     [H, d, window] fp32; tap i weighs token t-i
+ *   q_hist, k_hist [B, H, window-1, d] dtype, or NULL: the raw vectors before
+ *                t = 0, oldest first (NULL: zeros -- a sequence start)
+ *   q_out, k_out [B, H, T, d] dtype (bf16 outputs are rounded to nearest even)
+ *   q_hist_out, k_hist_out [B, H, window-1, d] dtype, or NULL: the last
+ *                window-1 raw vectors of history + sequence, the next call's
+ *                history (also for T < window-1, and for a decode step, T = 1)
+ *
+ * Supported: d in {16, 64, 128}, 1 <= window <= 4, B*H <= 65535, eps > 0.
+ * Outputs may not overlap the raw inputs or histories (MESA_ERR_INVALID_ARG):
+ * every raw vector is read by up to `window` outputs.  Device pointers,
+ * 16-byte aligned; asynchronous on `stream`. */
+mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32_t window,
+                               mesa_dtype dtype, const void* q_raw, const void* k_raw,
+                               const float* w_q, const float* w_k,
+                               const void* q_hist, const void* k_hist, float eps,
+                               void* q_out, void* k_out, void* q_hist_out, void* k_hist_out,
+                               hipStream_t stream);
+
 /* Static text for a status code. */
 const char* mesa_status_string(mesa_status s);
 

@@ -215,6 +215,47 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv, 
                      g_state, o, steps, x_state, max_steps, tol, stream);
 }
 
+mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32_t window,
+                               mesa_dtype dtype, const void* q_raw, const void* k_raw,
+                               const float* w_q, const float* w_k, const void* q_hist,
+                               const void* k_hist, float eps, void* q_out, void* k_out,
+                               void* q_hist_out, void* k_hist_out, hipStream_t stream) {
+  if (B < 0 || H < 1 || T < 0 || window < 1 || !(eps > 0.f) || std::isinf(eps)) return MESA_ERR_INVALID_ARG;
+  if (dtype != MESA_F32 && dtype != MESA_BF16) return MESA_ERR_INVALID_ARG;
+  if ((d != 16 && d != 64 && d != 128) || window > 4) return MESA_ERR_UNSUPPORTED;
+  if ((long long)B * H > 65535) return MESA_ERR_UNSUPPORTED;
+  if (B == 0) return MESA_OK;
+  const size_t esz = dtype == MESA_BF16 ? 2 : 4;
+  const size_t seq_bytes = (size_t)B * H * T * d * esz;
+  const size_t hist_bytes = (size_t)B * H * (window - 1) * d * esz;
+  if ((T > 0 && (!q_raw || !k_raw || !q_out || !k_out)) || !w_q || !w_k) return MESA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_raw, k_raw, w_q, w_k, q_hist, k_hist, q_out, k_out, q_hist_out, k_hist_out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+  // outputs may not overlap the inputs they are computed from
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+  };
+  const void* ins[] = {q_raw, k_raw, q_hist, k_hist};
+  const size_t in_bytes[] = {seq_bytes, seq_bytes, hist_bytes, hist_bytes};
+  const void* outs[] = {q_out, k_out, q_hist_out, k_hist_out};
+  const size_t out_bytes[] = {seq_bytes, seq_bytes, hist_bytes, hist_bytes};
+  for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b)
+      if (overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return MESA_ERR_INVALID_ARG;
+
+  mesa::PrepParams pp{};
+  pp.x[0] = q_raw; pp.x[1] = k_raw; pp.w[0] = w_q; pp.w[1] = w_k;
+  pp.hist_in[0] = q_hist; pp.hist_in[1] = k_hist;
+  pp.out[0] = q_out; pp.out[1] = k_out;
+  pp.hist_out[0] = q_hist_out; pp.hist_out[1] = k_hist_out;
+  pp.BH = B * H; pp.H = H; pp.T = T; pp.W = window; pp.eps = eps;
+  return mesa::launch_qk_prep(dtype == MESA_BF16, d, pp, stream) == hipSuccess ? MESA_OK : MESA_ERR_HIP;
+}
+
 size_t mesa_sym_state_floats(int32_t d) {
   if (d != 64 && d != 128) return 0;
   return mesa::sym_state_floats(d);

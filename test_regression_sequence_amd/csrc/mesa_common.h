@@ -64,14 +64,14 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 // swaps of sum_lane_groups.  Every lane receives the bitwise-identical result.
 #define MESA_DPP_ADD(v, ctrl) \
   ((v) + __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), (ctrl), 0xF, 0xF, false)))
-// Sum over each aligned group of N consecutive lanes (N = 16, 32 or 64).
+// Sum over each aligned group of N consecutive lanes (N = 2, 4, ..., 64).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 16 || N == 32 || N == 64, "group of 16, 32 or 64 lanes");
-  v = MESA_DPP_ADD(v, 0xB1);   // quad_perm [1,0,3,2]: lane ^ 1
-  v = MESA_DPP_ADD(v, 0x4E);   // quad_perm [2,3,0,1]: lane ^ 2
-  v = MESA_DPP_ADD(v, 0x141);  // row_half_mirror: quad 0 <-> quad 1, quad 2 <-> quad 3
-  v = MESA_DPP_ADD(v, 0x140);  // row_mirror: half-row 0 <-> half-row 1
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group of 2^k lanes, k >= 1");
+  v = MESA_DPP_ADD(v, 0xB1);                          // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (N >= 4) v = MESA_DPP_ADD(v, 0x4E);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) v = MESA_DPP_ADD(v, 0x141);   // row_half_mirror: quad 0 <-> quad 1, quad 2 <-> quad 3
+  if constexpr (N >= 16) v = MESA_DPP_ADD(v, 0x140);  // row_mirror: half-row 0 <-> half-row 1
   if constexpr (N >= 32) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(a[0]) + __uint_as_float(a[1]);

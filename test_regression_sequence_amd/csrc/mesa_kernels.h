@@ -91,6 +91,17 @@ struct DecodeParams {
   float tol2;
 };
 
+// Query/key preprocessing: index 0 = queries, 1 = keys.
+struct PrepParams {
+  const void* x[2];        // raw [BH, T, D]
+  const float* w[2];       // taps [H, D, W]
+  const void* hist_in[2];  // [BH, W-1, D] or null (zeros)
+  void* out[2];            // [BH, T, D]
+  void* hist_out[2];       // [BH, W-1, D] or null
+  int BH, H, T, W;
+  float eps;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
@@ -99,6 +110,7 @@ hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t 
 // packed_h: DecodeParams::h in the blocked upper-triangular layout;
 // warm: CG starts from DecodeParams::x0
 hipError_t launch_decode(bool bf16, int D, bool packed_h, bool warm, const DecodeParams& p, hipStream_t s);
+hipError_t launch_qk_prep(bool bf16, int D, const PrepParams& p, hipStream_t s);
 hipError_t launch_sym_pack(int D, int count, const float* full, float* packed, hipStream_t s);
 hipError_t launch_sym_unpack(int D, int count, const float* packed, float* full, hipStream_t s);
 size_t sym_state_floats(int D);

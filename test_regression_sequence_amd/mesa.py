@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.mesa_decode_step_warm.restype = ctypes.c_int
         L.mesa_decode_step_warm.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, I32,
                                             P, P, P, P, I32, F, P]
+        L.mesa_qk_preprocess.restype = ctypes.c_int
+        L.mesa_qk_preprocess.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P, P, F,
+                                         P, P, P, P, P]
         L.mesa_sym_state_floats.restype = S
         L.mesa_sym_state_floats.argtypes = [I32]
         L.mesa_sym_pack.restype = ctypes.c_int
@@ -304,4 +307,35 @@ def decode_step_warm(q, k, v, gamma, beta, lam, h_state, g_state, x_state, *, pa
                                         _ptr(x_state), _ptr(res["o"]), _ptr(res.get("steps")),
                                         int(max_steps), float(tol), _stream(stream))
     _check(code_, "mesa_decode_step_warm")
+    return res
+
+
+def qk_preprocess(q_raw, k_raw, w_q, w_k, *, q_hist=None, k_hist=None, eps: float = 1e-6,
+                  return_history: bool = False, out=None, stream=None) -> dict:
+    """Causal depthwise convolution of raw q, k [B, H, T, d] along time with taps
+    w_q, w_k [H, d, W], then L2 normalisation per token.  q_hist, k_hist
+    [B, H, W-1, d]: raw vectors before t = 0 (None: zeros).  Returns q, k (and,
+    with return_history, the next call's histories q_hist, k_hist)."""
+    B, H, T, d = q_raw.shape
+    W = w_q.shape[-1]
+    code = _dtype_code(q_raw)
+    _need(q_raw, "q_raw", (B, H, T, d), q_raw.dtype)
+    _need(k_raw, "k_raw", (B, H, T, d), q_raw.dtype)
+    _need(w_q, "w_q", (H, d, W), torch.float32)
+    _need(w_k, "w_k", (H, d, W), torch.float32)
+    for name, t in (("q_hist", q_hist), ("k_hist", k_hist)):
+        if t is not None:
+            _need(t, name, (B, H, W - 1, d), q_raw.dtype)
+    out = dict(out or {})
+    dev = q_raw.device
+    res = {}
+    for key in ("q", "k"):
+        res[key] = out.get(key) if out.get(key) is not None else torch.empty((B, H, T, d), device=dev, dtype=q_raw.dtype)
+    if return_history:
+        for key in ("q_hist", "k_hist"):
+            res[key] = out.get(key) if out.get(key) is not None else torch.empty((B, H, W - 1, d), device=dev, dtype=q_raw.dtype)
+    code_ = lib().mesa_qk_preprocess(B, H, T, d, W, code, _ptr(q_raw), _ptr(k_raw), _ptr(w_q), _ptr(w_k),
+                                     _ptr(q_hist), _ptr(k_hist), float(eps), _ptr(res["q"]), _ptr(res["k"]),
+                                     _ptr(res.get("q_hist")), _ptr(res.get("k_hist")), _stream(stream))
+    _check(code_, "mesa_qk_preprocess")
     return res

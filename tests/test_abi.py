@@ -146,3 +146,30 @@ def test_warm_decode_validation():
     assert call(dk=96) == 2
     assert call(max_steps=-1) == 1
     assert call(x_state=FAKE + 4) == 3
+
+
+def test_preprocess_validation():
+    L = mesa.lib()
+    P = ctypes.c_void_p
+    A, Bp = 0x7F0000000000, 0x7F1000000000   # distinct 16-byte aligned fake ranges
+
+    def call(B=2, H=2, T=8, d=128, W=4, dtype=1, eps=1e-6, q=A, k=A + 0x100000, qo=Bp, ko=Bp + 0x100000,
+             wq=A + 0x200000, qh=0, qho=0):
+        return L.mesa_qk_preprocess(B, H, T, d, W, dtype, P(q) if q else None, P(k) if k else None,
+                                    P(wq) if wq else None, P(A + 0x300000), P(qh) if qh else None, None,
+                                    ctypes.c_float(eps), P(qo) if qo else None, P(ko) if ko else None,
+                                    P(qho) if qho else None, None, None)
+
+    assert call(d=96) == 2
+    assert call(W=5) == 2
+    assert call(W=0) == 1
+    assert call(T=-1) == 1
+    assert call(eps=0.0) == 1
+    assert call(dtype=3) == 1
+    assert call(q=0) == 1
+    assert call(wq=0) == 1
+    assert call(qo=Bp + 4) == 3
+    assert call(qo=A) == 1                   # output over the raw input
+    assert call(qo=A + 0x100000) == 1        # output over the other raw input
+    assert call(qh=Bp + 0x400000, qho=Bp + 0x400000) == 1  # history out over history in
+    assert call(B=0) == 0
