@@ -3,4 +3,4 @@
 Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py``.  It shares no code with the HIP path.
 """
-from .mesa_oracle import cg_solve, mesa_forward, mesa_decode_step, diag_or_full, qk_preprocess  # noqa: F401
+from .mesa_oracle import cg_solve, mesa_forward, mesa_decode_step, diag_or_full, qk_preprocess, mesa_backward  # noqa: F401

@@ -39,7 +39,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full", "qk_preprocess"]
+__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full", "qk_preprocess",
+           "mesa_backward"]
 
 
 def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
@@ -265,3 +266,119 @@ def qk_preprocess(x, w, hist=None, eps: float = 1e-6):
     nrm = np.linalg.norm(y, axis=-1, keepdims=True)
     out = y / np.maximum(nrm, eps)
     return out, seq[:, :, T:]
+
+
+def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
+                  h0=None, g0=None, dh_final=None, dg_final=None, forced_steps=None,
+                  adjoint_forced_steps=None, exact: bool = False, chunk: int = 64):
+    """Gradients of the layer by implicit differentiation of its solves, fp64.
+
+    The scalar differentiated is L = sum_t <d_o_t, o_t> + <dh_final, H_T> +
+    <dg_final, G_T> (H_T, G_T: the states after the last token).  Each
+    x_t = (H_t + Lambda)^{-1} q_t is treated as the solution of its system, so
+    with the adjoint y_t = (H_t + Lambda)^{-1} G_t^T d_o_t:
+        dL/dq_t = y_t,  dL/dH_t (local) = -y_t x_t^T,  dL/dG_t (local) = d_o_t x_t^T,
+        dL/dlambda = -sum_t y_t * x_t  (diagonal Lambda, summed over batch and time).
+    The state adjoints run backwards, Hhat_t = dH_t + gamma_{t+1} Hhat_{t+1}
+    (Hhat_T starts at dh_final; the same for G), and give
+        dk_t = beta_t ((Hhat_t + Hhat_t^T) k_t + Ghat_t^T v_t),  dv_t = beta_t Ghat_t k_t,
+        dbeta_t = k_t^T Hhat_t k_t + v_t^T Ghat_t k_t,
+        dgamma_t = <Hhat_t, H_{t-1}> + <Ghat_t, G_{t-1}>,
+        dh0 = gamma_0 Hhat_0 (symmetrised: h0 is a symmetric state),  dg0 = gamma_0 Ghat_0.
+    x_t and y_t come from exact solves (``exact``) or from the CG schedule:
+    x_t as in :func:`mesa_forward` (``forced_steps`` as there); y_t by CG with
+    the same max_steps, and the tolerance taken relative to ||G_t^T d_o_t||
+    (CG on the normalised right-hand side, rescaled), optionally forced to
+    ``adjoint_forced_steps`` [B, H, T].  The states are checkpointed every
+    ``chunk`` tokens and recomputed chunk by chunk on the way back.
+
+    Returns dict(dq, dk, dv [B,H,T,d], dgamma, dbeta [B,H,T], dlam [H,dk],
+    dh0 [B,H,dk,dk], dg0 [B,H,dv,dk], x, y [B,H,T,dk], adj_steps [B,H,T]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hh, T, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    S = B * Hh
+    qf, kf = _flat(q, S, T, dk), _flat(k, S, T, dk)
+    vf, of = _flat(v, S, T, dv), _flat(d_o, S, T, dv)
+    gf, bf = _flat(gamma, S, T), _flat(beta, S, T)
+    lam = np.asarray(lam, dtype=np.float64)
+    if lam.shape != (Hh, dk):
+        raise ValueError("the backward takes a diagonal Lambda [H, dk]")
+    fs = None if forced_steps is None else np.asarray(forced_steps).reshape(S, T)
+    fa = None if adjoint_forced_steps is None else np.asarray(adjoint_forced_steps).reshape(S, T)
+    out = {name: np.zeros((S, T, dd)) for name, dd in (("dq", dk), ("dk", dk), ("dv", dv),
+                                                         ("x", dk), ("y", dk))}
+    out.update(dgamma=np.zeros((S, T)), dbeta=np.zeros((S, T)), adj_steps=np.zeros((S, T), np.int64),
+               dh0=np.zeros((S, dk, dk)), dg0=np.zeros((S, dv, dk)))
+    dlam = np.zeros((Hh, dk))
+    NC = (T + chunk - 1) // chunk
+    for s_ in range(S):
+        h = s_ % Hh
+        Lam = np.diag(lam[h])
+        Hs = np.zeros((dk, dk)) if h0 is None else _flat(h0, S, dk, dk)[s_].copy()
+        Gs = np.zeros((dv, dk)) if g0 is None else _flat(g0, S, dv, dk)[s_].copy()
+
+        def step(Hm, Gm, t):
+            kt = kf[s_, t]
+            return (gf[s_, t] * Hm + bf[s_, t] * (kt[:, None] * kt[None, :]),
+                    gf[s_, t] * Gm + bf[s_, t] * (vf[s_, t][:, None] * kt[None, :]))
+
+        # forward: checkpoints at chunk starts, and the solutions x_t
+        ckpt = []
+        for t in range(T):
+            if t % chunk == 0:
+                ckpt.append((Hs.copy(), Gs.copy()))
+            Hs, Gs = step(Hs, Gs, t)
+            A = Hs + Lam
+            if exact:
+                xt = np.linalg.solve(A, qf[s_, t])
+            else:
+                xs_, _ = cg_solve(A[None], qf[s_, t][None], max_steps, tol,
+                                  None if fs is None else fs[s_, t:t + 1])
+                xt = xs_[0]
+            out["x"][s_, t] = xt
+        # backward, chunk by chunk from the end
+        Hhat = np.zeros((dk, dk)) if dh_final is None else _flat(dh_final, S, dk, dk)[s_].astype(np.float64).copy()
+        Ghat = np.zeros((dv, dk)) if dg_final is None else _flat(dg_final, S, dv, dk)[s_].astype(np.float64).copy()
+        for c in range(NC - 1, -1, -1):
+            t0, t1 = c * chunk, min(T, (c + 1) * chunk)
+            Hm, Gm = ckpt[c]
+            states = [(Hm, Gm)]                 # states[i] = (H, G) before token t0 + i
+            for t in range(t0, t1):
+                states.append(step(*states[-1], t))
+            for t in range(t1 - 1, t0 - 1, -1):
+                Ht, Gt = states[t - t0 + 1]
+                Hp, Gp = states[t - t0]
+                xt, kt, vt, dot = out["x"][s_, t], kf[s_, t], vf[s_, t], of[s_, t]
+                A = Ht + Lam
+                dxt = Gt.T @ dot
+                if exact:
+                    yt = np.linalg.solve(A, dxt)
+                    na = 0
+                else:
+                    nrm = np.linalg.norm(dxt)
+                    if nrm > 0:
+                        ys_, ns_ = cg_solve(A[None], (dxt / nrm)[None], max_steps, tol,
+                                            None if fa is None else fa[s_, t:t + 1])
+                        yt, na = ys_[0] * nrm, int(ns_[0])
+                    else:
+                        yt, na = np.zeros(dk), 0
+                out["y"][s_, t] = yt
+                out["adj_steps"][s_, t] = na
+                out["dq"][s_, t] = yt
+                dlam[h] -= yt * xt
+                Hhat = Hhat - np.outer(yt, xt)
+                Ghat = Ghat + np.outer(dot, xt)
+                bt = bf[s_, t]
+                out["dk"][s_, t] = bt * ((Hhat + Hhat.T) @ kt + Ghat.T @ vt)
+                out["dv"][s_, t] = bt * (Ghat @ kt)
+                out["dbeta"][s_, t] = kt @ Hhat @ kt + vt @ Ghat @ kt
+                out["dgamma"][s_, t] = np.sum(Hhat * Hp) + np.sum(Ghat * Gp)
+                Hhat = gf[s_, t] * Hhat
+                Ghat = gf[s_, t] * Ghat
+        out["dh0"][s_] = 0.5 * (Hhat + Hhat.T)
+        out["dg0"][s_] = Ghat
+    res = {key: val.reshape(B, Hh, *val.shape[1:]) for key, val in out.items()}
+    res["dlam"] = dlam
+    return res

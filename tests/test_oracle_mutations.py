@@ -12,6 +12,7 @@ import types
 import numpy as np
 import pytest
 
+import test_oracle_backward as bwd
 import test_oracle_pins as pins
 import test_oracle_preprocess as prep
 
@@ -50,6 +51,15 @@ MUTATIONS = {
                             "nrm = np.linalg.norm(y, axis=-2, keepdims=True)"),
     "prep_history_out_shifted": ("return out, seq[:, :, T:]", "return out, seq[:, :, T - 1:-1]"),
     "prep_current_token_dropped": ("for i in range(W):\n        y +=", "for i in range(1, W):\n        y +="),
+    "bwd_adjoint_previous_state": ("dxt = Gt.T @ dot", "dxt = Gp.T @ dot"),
+    "bwd_H_adjoint_sign": ("Hhat = Hhat - np.outer(yt, xt)", "Hhat = Hhat + np.outer(yt, xt)"),
+    "bwd_dk_one_sided": ("bt * ((Hhat + Hhat.T) @ kt", "bt * ((2 * Hhat) @ kt"),
+    "bwd_no_decay_on_G_adjoint": ("Ghat = gf[s_, t] * Ghat", "Ghat = Ghat"),
+    "bwd_dgamma_current_state": ("np.sum(Hhat * Hp) + np.sum(Ghat * Gp)", "np.sum(Hhat * Ht) + np.sum(Ghat * Gt)"),
+    "bwd_dbeta_without_G": ("kt @ Hhat @ kt + vt @ Ghat @ kt", "kt @ Hhat @ kt"),
+    "bwd_dlam_sign": ("dlam[h] -= yt * xt", "dlam[h] += yt * xt"),
+    "bwd_dq_is_solution": ('out["dq"][s_, t] = yt', 'out["dq"][s_, t] = xt'),
+    "bwd_dv_reads_solution": ('out["dv"][s_, t] = bt * (Ghat @ kt)', 'out["dv"][s_, t] = bt * (Ghat @ xt)'),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
                                        ("            x_ex[:, t] = xe\n",
                                         "            x_ex[:, t] = xe\n            x_prev = xe\n")],
@@ -155,6 +165,23 @@ def run_pins(m):
                 break
     finally:
         prep.qk_preprocess = saved
+    # backward: finite differences of the brute-force objective and of the forward
+    saved = (bwd.mesa_backward, bwd.mesa_forward)
+    try:
+        bwd.mesa_backward, bwd.mesa_forward = m.mesa_backward, m.mesa_forward
+        for fn in (lambda: bwd.test_gradients_match_finite_differences_of_the_objective(0, 1),
+                   bwd.test_state_gradients_match_finite_differences_of_the_forward,
+                   bwd.test_homogeneity_identities):
+            try:
+                fn()
+            except AssertionError:
+                failed.append("bwd")
+                break
+            except Exception:
+                failed.append("bwd-crash")
+                break
+    finally:
+        bwd.mesa_backward, bwd.mesa_forward = saved
     # P7: tolerance stops before an iteration
     x, n = m.cg_solve(np.eye(3)[None] * 2.0, np.array([[1e-7, 0.0, 0.0]]), 10, 1e-6)
     if n[0] != 0:
