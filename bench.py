@@ -26,6 +26,7 @@ intra-chunk products, nbar = (C+1)/2 keys on average):
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -274,6 +275,44 @@ def bench_decode_warm(cfg, h_host, g_host, lam, in_bytes, T=8):
     }
 
 
+def bench_backward(cfg, steps, warmup):
+    """The backward pass (implicit differentiation through both CG solves) at the
+    layer workload: one mesa_bwd_chunked call, the forward's x and o resident."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs, make_bwd_inputs
+
+    x = make_fwd_inputs(cfg)
+    g = make_bwd_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    gamma, beta, lam = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta", "lam"))
+    d_o = torch.from_numpy(g["d_o"]).cuda()
+    del x, g
+    f = mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                         return_x=True)
+    res = mesa.bwd_chunked(q, k, v, gamma, beta, lam, f["x"], d_o, chunk=cfg.chunk,
+                           max_steps=cfg.max_steps, tol=cfg.tol)
+    ws = torch.empty(int(mesa.lib().mesa_bwd_workspace_bytes(ctypes.byref(
+        mesa.make_desc(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, cfg.max_steps, cfg.tol, 1)))),
+        device="cuda", dtype=torch.uint8)
+
+    def step():
+        mesa.bwd_chunked(q, k, v, gamma, beta, lam, f["x"], d_o, chunk=cfg.chunk,
+                         max_steps=cfg.max_steps, tol=cfg.tol, out=res, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    ms = time_events(step, steps)
+    tokens = cfg.B * cfg.H * cfg.T
+    return {
+        "workload": f"backward: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} {cfg.dtype}, "
+                    f"{cfg.max_steps} CG steps per solve",
+        "ms_per_call": round(ms, 4),
+        "token_heads_per_s": round(tokens / (ms * 1e-3), 1),
+    }
+
+
 def bench_preprocess(cfg, steps, warmup, window=4):
     """Query/key preprocessing (causal depthwise convolution + L2 norm) at the layer
     workload's shape: raw q, k read once, processed q, k written once."""
@@ -465,6 +504,7 @@ def main():
     if not args.no_decode:
         line["decode"] = bench_decode(CONFIGS[5], args.steps, args.warmup)
     line["preprocess"] = bench_preprocess(CONFIGS[args.workload], args.steps, args.warmup)
+    line["backward"] = bench_backward(CONFIGS[args.workload], args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
     print(json.dumps(line), flush=True)

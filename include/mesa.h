@@ -220,6 +220,50 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                   float* o, int32_t* steps,
                                   int32_t max_steps, float tol, hipStream_t stream);
 
+/* ---- backward pass (training) -------------------------------------------------
+ *
+ * Gradients of a mesa_fwd_chunked call by implicit differentiation of its
+ * solves (MesaNet page, technical summary, "Mesa layer"; the layer is trained
+ * end to end).  The scalar differentiated is
+ *   L = sum_t <d_o_t, o_t> + <d_hfinal, H_T> + <d_gfinal, G_T>.
+ * Each x_t is treated as the solution of (H_t + Lambda) x_t = q_t; the adjoint
+ * systems (H_t + Lambda) y_t = G_t^T d_o_t are solved by the same CG (the
+ * descriptor's max_steps; its tol taken relative to ||G_t^T d_o_t||), and
+ *   dq_t = y_t,  dk_t = beta_t ((Hh_t + Hh_t^T) k_t + Gh_t^T v_t),  dv_t = beta_t Gh_t k_t,
+ *   dbeta_t = k_t^T Hh_t k_t + v_t^T Gh_t k_t,  dgamma_t = <Hh_t, H_{t-1}> + <Gh_t, G_{t-1}>,
+ *   dlambda = -sum_{b,t} y_t * x_t,  dh0 = sym(gamma_0 Hh_0),  dg0 = gamma_0 Gh_0,
+ * with Hh_t = -y_t x_t^T + gamma_{t+1} Hh_{t+1} (Hh_T = d_hfinal) and
+ * Gh_t = d_o_t x_t^T + gamma_{t+1} Gh_{t+1} (Gh_T = d_gfinal).
+ *
+ *   desc          the forward's descriptor; supported: bf16 inputs, dk == dv in
+ *                 {64, 128}, chunk 64 (else MESA_ERR_UNSUPPORTED)
+ *   q ... g0      the forward's inputs (h0, g0 may be NULL)
+ *   x             the forward's x_out, fp32 [B, H, T, d]
+ *   d_o           dL/do, fp32 [B, H, T, dv]
+ *   d_hfinal, d_gfinal  fp32 [B, H, d, d] or NULL (zero)
+ *   dq, dk, dv    fp32 [B, H, T, d] out;  dgamma, dbeta fp32 [B, H, T] out
+ *   dlambda       fp32 [H, dk] out (summed over batch and time)
+ *   dh0, dg0      fp32 [B, H, d, d] out or NULL; dh0 is symmetric (h0 is a
+ *                 symmetric state)
+ *   adj_steps     int32 [B, H, T] out or NULL: CG steps of the adjoint solves
+ *   workspace     mesa_bwd_workspace_bytes(desc) bytes (it recomputes the
+ *                 forward's boundary states; nothing from the forward call's
+ *                 workspace is needed)
+ * The products inside use bf16 operands with fp32 accumulation, like the
+ * forward's bf16 path.  Asynchronous on `stream`; device pointers, 16-byte
+ * aligned; validation failures write nothing. */
+size_t mesa_bwd_workspace_bytes(const mesa_fwd_desc* d);
+
+mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d,
+                             const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0,
+                             const float* x, const float* d_o,
+                             const float* d_hfinal, const float* d_gfinal,
+                             float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                             float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- query/key preprocessing -------------------------------------------------
  *
  * MesaNet page, "architecture" section: queries and keys are normalised and

@@ -215,6 +215,112 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv, 
                      g_state, o, steps, x_state, max_steps, tol, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+mesa_status check_bwd(const mesa_fwd_desc* d) {
+  const mesa_status st = check_desc(d);
+  if (st != MESA_OK) return st;
+  if (d->in_dtype != MESA_BF16 || (d->dk != 64 && d->dk != 128) || d->chunk != 64) return MESA_ERR_UNSUPPORTED;
+  return MESA_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct BwdLayout {
+  size_t fwd, rhs, nu, yn, oscr, snap, lam, total;
+};
+
+BwdLayout bwd_layout(const mesa_fwd_desc* d) {
+  BwdLayout L{};
+  const size_t BH = (size_t)d->B * d->H, T = (size_t)d->T, D = (size_t)d->dk;
+  const size_t NC = (T + d->chunk - 1) / d->chunk;
+  size_t off = align256(mesa_fwd_workspace_bytes(d));
+  L.fwd = 0;
+  L.rhs = off; off = align256(off + BH * T * D * 2);
+  L.nu = off; off = align256(off + BH * T * 4);
+  L.yn = off; off = align256(off + BH * T * D * 4);
+  L.oscr = off; off = align256(off + BH * T * D * 4);
+  L.snap = off; off = align256(off + 3 * BH * NC * D * D * 2);
+  L.lam = off; off = align256(off + BH * NC * D * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mesa_bwd_workspace_bytes(const mesa_fwd_desc* d) {
+  if (check_bwd(d) != MESA_OK) return 0;
+  return bwd_layout(d).total;
+}
+
+mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0, const float* x, const float* d_o,
+                             const float* d_hfinal, const float* d_gfinal,
+                             float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                             float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const mesa_status st = check_bwd(d);
+  if (st != MESA_OK) return st;
+  const bool any = d->T > 0;
+  if (!lambda || !dlambda) return MESA_ERR_INVALID_ARG;
+  if (any && (!q || !k || !v || !gamma || !beta || !x || !d_o || !dq || !dk || !dv || !dgamma || !dbeta))
+    return MESA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, gamma, beta, lambda, h0, g0, x, d_o, d_hfinal, d_gfinal,
+                        dq, dk, dv, dgamma, dbeta, dlambda, dh0, dg0, adj_steps, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+  const BwdLayout L = bwd_layout(d);
+  if (!workspace || workspace_bytes < L.total) return MESA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  const int D = d->dk, C = d->chunk, BH = d->B * d->H;
+  const int NC = (d->T + C - 1) / C;
+  // 1. the forward's boundary states, into the forward part of the workspace
+  if (any) {
+    const mesa_status s1 = fwd_impl(kScan, d, nullptr, k, v, gamma, beta, nullptr, h0, g0, nullptr, nullptr,
+                                    nullptr, nullptr, nullptr, ws, mesa_fwd_workspace_bytes(d), stream);
+    if (s1 != MESA_OK) return s1;
+  }
+  const size_t snap = (size_t)BH * NC * mesa::snapshot_bytes(true, D);
+  mesa::BwdParams bp{};
+  bp.k = k; bp.v = v; bp.gamma = gamma; bp.beta = beta;
+  bp.hb = ws; bp.gb = ws + snap;
+  bp.x = x; bp.d_o = d_o; bp.d_hfinal = d_hfinal; bp.d_gfinal = d_gfinal;
+  bp.rhs = ws + L.rhs;
+  bp.nu = reinterpret_cast<float*>(ws + L.nu);
+  bp.yn = reinterpret_cast<float*>(ws + L.yn);
+  const size_t sn = (size_t)BH * NC * D * D;
+  bp.snap_r = reinterpret_cast<uint16_t*>(ws + L.snap);
+  bp.snap_s = bp.snap_r + sn;
+  bp.snap_st = bp.snap_s + sn;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dbeta = dbeta; bp.dgamma = dgamma;
+  bp.lam_part = reinterpret_cast<float*>(ws + L.lam);
+  bp.dlam = dlambda; bp.dh0 = dh0; bp.dg0 = dg0;
+  bp.BH = BH; bp.H = d->H; bp.T = d->T; bp.NC = NC;
+  if (any) {
+    // 2. right-hand sides of the adjoint systems
+    if (mesa::launch_bwd(0, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
+    // 3. adjoint solves by the forward CG (read-out to scratch)
+    mesa::CgParams cp{};
+    cp.q = bp.rhs; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
+    cp.hb = bp.hb; cp.gb = bp.gb; cp.o = reinterpret_cast<float*>(ws + L.oscr); cp.steps = adj_steps;
+    cp.x_out = reinterpret_cast<float*>(ws + L.yn);
+    cp.unscaled = reinterpret_cast<int32_t*>(ws + 2 * snap);
+    cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
+    cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
+    if (mesa::launch_cg(true, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
+  }
+  // 4. adjoint scan (also the initial-state gradients); 5. per-token gradients
+  if ((any || dh0 || dg0) && mesa::launch_bwd(1, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
+  if (mesa::launch_bwd(2, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
+  return MESA_OK;
+}
+
 mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32_t window,
                                mesa_dtype dtype, const void* q_raw, const void* k_raw,
                                const float* w_q, const float* w_k, const void* q_hist,

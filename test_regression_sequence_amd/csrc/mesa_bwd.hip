@@ -1,0 +1,617 @@
+// Backward pass of the chunked Mesa layer by implicit differentiation of its
+// solves (MesaNet page, technical summary, "Mesa layer": CG query response and
+// chunk-parallel states; "architecture": the layer is trained end to end).
+//
+// With x_t the solution of (H_t + Lambda) x_t = q_t and o_t = G_t x_t, and
+// d_o the gradient arriving at o:
+//   dx_t = G_t^T d_o_t,            y_t = (H_t + Lambda)^{-1} dx_t   (adjoint solve)
+//   dq_t = y_t,   local state gradients  dH_t = -y_t x_t^T,  dG_t = d_o_t x_t^T,
+//   Hhat_t = dH_t + gamma_{t+1} Hhat_{t+1},  Ghat_t likewise (backward in time),
+//   dk_t = beta_t ((Hhat_t + Hhat_t^T) k_t + Ghat_t^T v_t),   dv_t = beta_t Ghat_t k_t,
+//   dbeta_t = k_t^T Hhat_t k_t + v_t^T Ghat_t k_t,   dlambda = -sum_t y_t * x_t.
+// The forget factors: gamma_t dgamma_t = <Hhat_t, H_t> + <Ghat_t, G_t> - beta_t dbeta_t
+// (= gamma_t (<Hhat_t, H_{t-1}> + <Ghat_t, G_{t-1}>)).  Inside a chunk with
+// boundary states Hb, Gb and arriving adjoints Rb (of H; Rs = Rb + Rb^T) and
+// S (of G), and b restarted at the chunk start s, <Hhat_t, H_t> is
+//   e^{b_e} <Rb, Hb>                                             (per chunk)
+// + sum_{j<=t} e^{b_e-b_j} beta_j k_j^T Rb k_j                    (prefix)
+// + sum_{t'>=t} e^{b_t'} <dH_t', Hb>                               (suffix)
+// + sum_{j<=t<=t'} e^{b_t'-b_j} beta_j <dH_t', k_j k_j^T>          (pairs)
+// and <Ghat_t, G_t> likewise; every factor is a decay <= 1 and nothing
+// accumulates across chunks (a cumulative sum of dL/db over the whole
+// sequence would cancel to O(1) out of O(T) terms).
+//
+// Kernels (chunks of C = 64 tokens; s..e the chunk, b restarted at s):
+//   bwd_dx_kernel    per chunk: dx = Gamma (d_O Gb) + (W o (d_O V^T)) K with
+//                    W_tj = e^{b_t-b_j} beta_j [j<=t]; writes dx/||dx|| (bf16)
+//                    and ||dx||, the right-hand sides of the adjoint CG (the
+//                    forward CG kernels, so the stopping test is relative).
+//   bwd_scan_kernel  per sequence, chunks backwards: the adjoints arriving at a
+//                    chunk's end, Rs = Hhat + Hhat^T and S = Ghat, stored per
+//                    chunk (bf16; S also transposed), then
+//                    Rs <- e^{b_e} Rs - sum_t w_t (y_t x_t^T + x_t y_t^T),
+//                    S  <- e^{b_e} S + sum_t w_t d_o_t x_t^T,  w_t = e^{b_t};
+//                    the final values give dh0 = Rs/2 and dg0 = S.
+//   bwd_grad_kernel  per chunk: Hhat_t, Ghat_t applied to k_t, v_t as
+//                    e^{b_e-b_t} (stored adjoint) k_t plus the chunk's own
+//                    reverse-causal terms, e.g. Ghat_t k_t gains
+//                    sum_{t'>=t} e^{b_t'-b_t} (x_t'.k_t) d_o_t'; the four parts of
+//                    dgamma above; writes dq, dk, dv, dbeta, dgamma and
+//                    per-chunk dlambda parts.
+//   bwd_lambda_kernel dlambda summed over batch and chunks.
+// Every chunk product is an MFMA 16x16x32 bf16 contraction with fp32
+// accumulation on tiles staged in LDS with the contraction index contiguous
+// (rows padded by 16 bytes, so the 16 rows an MFMA operand reads fall in
+// distinct banks); fp32 inputs (x, y, d_o) are rounded to bf16 for the
+// products only.
+#include "mesa_common.h"
+#include "mesa_kernels.h"
+
+namespace mesa {
+
+namespace {
+
+constexpr int kC = 64;          // tokens per chunk
+constexpr int kThreads = 256;   // 4 waves
+
+__device__ __forceinline__ uint16_t bf(float x) { return __builtin_bit_cast(uint16_t, f32_to_bf16(x)); }
+
+// acc (16x16 tile; lane l holds rows 4(l/16)+{0..3} of column l%16) +=
+// A[16][K] * Bt[16][K]^T, both bf16 in LDS with row strides lda, ldb.
+template <int K>
+__device__ __forceinline__ f32x4 mma(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, f32x4 acc) {
+  const int tl = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + tl * lda + 32 * kb + 8 * g);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + tl * ldb + 32 * kb + 8 * g);
+    acc = mfma_bf16(a, b, acc);
+  }
+  return acc;
+}
+
+// b_t (inclusive prefix of log gamma from the chunk start) and beta_t of a
+// chunk into LDS; tokens past Lc get gamma = 1, beta = 0.  Called by wave 0.
+__device__ __forceinline__ void chunk_gates(const float* gamma, const float* beta, size_t row0, int Lc,
+                                            float* bcum, float* betas) {
+  const int lane = threadIdx.x & 63;
+  float lg = 0.f, bt = 0.f;
+  if (lane < Lc) {
+    lg = logf(gamma[row0 + lane]);
+    bt = beta[row0 + lane];
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(lg, o, 64);
+    if (lane >= o) lg += t;
+  }
+  bcum[lane] = lg;
+  betas[lane] = bt;
+}
+
+// token-major [C][D] tile -> LDS bf16 [C][ld]; rows >= Lc are zero.
+template <int D>
+__device__ __forceinline__ void stage_rows_f32(uint16_t* dst, int ld, const float* src, int Lc,
+                                               const float* row_scale = nullptr) {
+  for (int idx = threadIdx.x; idx < kC * D / 4; idx += kThreads) {
+    const int t = idx / (D / 4), c4 = idx % (D / 4);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < Lc) {
+      v = *reinterpret_cast<const f32x4*>(src + (size_t)t * D + 4 * c4);
+      if (row_scale) v *= row_scale[t];
+    }
+    u16x4 o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = bf(v[u]);
+    *reinterpret_cast<u16x4*>(dst + t * ld + 4 * c4) = o;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_rows_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
+  for (int idx = threadIdx.x; idx < kC * D / 8; idx += kThreads) {
+    const int t = idx / (D / 8), c8 = idx % (D / 8);
+    u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (t < Lc) v = *reinterpret_cast<const u16x8*>(src + (size_t)t * D + 8 * c8);
+    *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = v;
+  }
+}
+
+// token-major [C][D] fp32 -> LDS bf16 transposed: dst[i * ld + col0 + t] = scale_t * src[t][i]
+template <int D>
+__device__ __forceinline__ void stage_cols_f32(uint16_t* dst, int ld, int col0, const float* src, int Lc,
+                                               const float* row_scale = nullptr, float sign = 1.f) {
+  for (int idx = threadIdx.x; idx < kC * D / 4; idx += kThreads) {
+    const int t = idx / (D / 4), c4 = idx % (D / 4);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < Lc) {
+      v = *reinterpret_cast<const f32x4*>(src + (size_t)t * D + 4 * c4);
+      v *= sign * (row_scale ? row_scale[t] : 1.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(v[u]);
+  }
+}
+
+// token-major [C][D] bf16 -> LDS transposed
+template <int D>
+__device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
+  for (int idx = threadIdx.x; idx < kC * D / 8; idx += kThreads) {
+    const int t = idx / (D / 8), c8 = idx % (D / 8);
+    u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (t < Lc) v = *reinterpret_cast<const u16x8*>(src + (size_t)t * D + 8 * c8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = v[u];
+  }
+}
+
+// A boundary snapshot in the scan's bf16 fragment order (fragment
+// f = nt*(D/32) + m, lane l: row 16nt + l%16, columns 32m + 4(l/16) + {0..3},
+// 32m + 16 + 4(l/16) + {0..3}) -> LDS row-major (TRANS: transposed).
+template <int D, bool TRANS>
+__device__ __forceinline__ void stage_snapshot(uint16_t* dst, int ld, const uint16_t* frag) {
+  constexpr int NM = D / 32;
+  for (int idx = threadIdx.x; idx < D * D / 8; idx += kThreads) {
+    const int f = idx >> 6, l = idx & 63;
+    const int n = 16 * (f / NM) + (l & 15);
+    const int c0 = 32 * (f % NM) + 4 * (l >> 4);
+    const u16x8 v = *reinterpret_cast<const u16x8*>(frag + (size_t)idx * 8);
+    if constexpr (TRANS) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        dst[(c0 + u) * ld + n] = v[u];
+        dst[(c0 + 16 + u) * ld + n] = v[4 + u];
+      }
+    } else {
+      *reinterpret_cast<u16x4*>(dst + n * ld + c0) = u16x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{v[4], v[5], v[6], v[7]};
+    }
+  }
+}
+
+// row-major [D][D] bf16 -> LDS [D][ld]
+template <int D>
+__device__ __forceinline__ void stage_square(uint16_t* dst, int ld, const uint16_t* src) {
+  for (int idx = threadIdx.x; idx < D * D / 8; idx += kThreads) {
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    *reinterpret_cast<u16x8*>(dst + r * ld + 8 * c8) = *reinterpret_cast<const u16x8*>(src + (size_t)idx * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dx_t = G_t^T d_o_t, normalised right-hand sides of the adjoint solves
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
+  constexpr int LD = D + 8, LC = kC + 8, NTL = D / 16;
+  constexpr int REG = (D * LD + kC * LD) > (kC * LC + D * LC) ? (D * LD + kC * LD) : (kC * LC + D * LC);
+  const int chunk = blockIdx.x, bh = chunk / p.NC, c = chunk % p.NC;
+  const int s = c * kC, Lc = min(kC, p.T - s);
+  const size_t row0 = (size_t)bh * p.T + s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
+
+  __shared__ float bcum[kC], betas[kC];
+  __shared__ __attribute__((aligned(16))) uint16_t sDO[kC * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sR[REG];
+  uint16_t* sGT = sR;               // Gb^T  [D][LD]
+  uint16_t* sV = sR + D * LD;       // V     [C][LD]
+  uint16_t* sS = sR;                // masked scores [C][LC]  (after Gb^T, V are consumed)
+  uint16_t* sKT = sR + kC * LC;     // K^T   [D][LC]
+
+  if (wave == 0) chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
+  stage_rows_f32<D>(sDO, LD, p.d_o + row0 * D, Lc);
+  stage_rows_bf16<D>(sV, LD, static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
+  stage_snapshot<D, true>(sGT, LD, static_cast<const uint16_t*>(p.gb) + (size_t)chunk * D * D);
+  __syncthreads();
+
+  f32x4 u[NTL], pp[4];
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt)
+    u[nt] = mma<D>(sDO + 16 * wave * LD, LD, sGT + 16 * nt * LD, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+    pp[jt] = mma<D>(sDO + 16 * wave * LD, LD, sV + 16 * jt * LD, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+  __syncthreads();  // Gb^T and V consumed
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * wave + 4 * g + i, j = 16 * jt + tl;
+      const float w = j <= t ? expf(bcum[t] - bcum[j]) * betas[j] : 0.f;
+      sS[t * LC + j] = bf(pp[jt][i] * w);
+    }
+  stage_cols_bf16<D>(sKT, LC, static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
+  __syncthreads();
+
+  f32x4 r[NTL];
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt)
+    r[nt] = mma<kC>(sS + 16 * wave * LC, LC, sKT + 16 * nt * LC, LC, f32x4{0.f, 0.f, 0.f, 0.f});
+
+  uint16_t* rhs = static_cast<uint16_t*>(p.rhs);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * wave + 4 * g + i;
+    const float gt = expf(bcum[t]);
+    float ss = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+      r[nt][i] = __builtin_fmaf(gt, u[nt][i], r[nt][i]);
+      ss = __builtin_fmaf(r[nt][i], r[nt][i], ss);
+    }
+    ss = group_sum<16>(ss);
+    const float nrm = sqrtf(ss);
+    const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+    if (t < Lc) {
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) rhs[(row0 + t) * D + 16 * nt + tl] = bf(r[nt][i] * inv);
+      if (tl == 0) p.nu[row0 + t] = nrm;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// adjoint scan, chunks backwards
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
+  constexpr int RW = D / 4, NRT = RW / 16, NCT = D / 16;
+  constexpr int L2 = 2 * kC + 8, LC = kC + 8;
+  const int bh = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
+
+  __shared__ float bcum[kC], betas[kC], wt[kC], nus[kC], nyw[kC];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[D * L2];  // [(-wY)^T | (-wX)^T]
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[D * L2];  // [X^T | Y^T]
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[D * LC];  // (w d_O)^T
+
+  f32x4 R[NRT][NCT], S[NRT][NCT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int row = RW * wave + 16 * rt + 4 * g + ii, col = 16 * ct + tl;
+        float rv = 0.f, sv = 0.f;
+        if (p.d_hfinal) {
+          const float* Dh = p.d_hfinal + (size_t)bh * D * D;
+          rv = Dh[row * D + col] + Dh[col * D + row];
+        }
+        if (p.d_gfinal) sv = p.d_gfinal[(size_t)bh * D * D + row * D + col];
+        R[rt][ct][ii] = rv;
+        S[rt][ct][ii] = sv;
+      }
+
+  for (int c = p.NC - 1; c >= 0; --c) {
+    const int chunk = bh * p.NC + c;
+    const int s = c * kC, Lc = min(kC, p.T - s);
+    const size_t row0 = (size_t)bh * p.T + s;
+    // the adjoints arriving at this chunk's end
+    uint16_t* snR = p.snap_r + (size_t)chunk * D * D;
+    uint16_t* snS = p.snap_s + (size_t)chunk * D * D;
+    uint16_t* snT = p.snap_st + (size_t)chunk * D * D;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int row = RW * wave + 16 * rt + 4 * g, col = 16 * ct + tl;
+        u16x4 st;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          snR[(row + ii) * D + col] = bf(R[rt][ct][ii]);
+          snS[(row + ii) * D + col] = bf(S[rt][ct][ii]);
+          st[ii] = bf(S[rt][ct][ii]);
+        }
+        *reinterpret_cast<u16x4*>(snT + col * D + row) = st;
+      }
+    if (wave == 0) {
+      chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
+      const float w = expf(bcum[lane]);
+      const float nu = lane < Lc ? p.nu[row0 + lane] : 0.f;
+      wt[lane] = w;
+      nus[lane] = nu;
+      nyw[lane] = -w * nu;
+    }
+    __syncthreads();
+    // y_t = nu_t * yn_t
+    stage_cols_f32<D>(sA1, L2, 0, p.yn + row0 * D, Lc, nyw);            // -(w Y)^T
+    stage_cols_f32<D>(sA1, L2, kC, p.x + row0 * D, Lc, wt, -1.f);       // -(w X)^T
+    stage_cols_f32<D>(sB1, L2, 0, p.x + row0 * D, Lc);                  // X^T
+    stage_cols_f32<D>(sB1, L2, kC, p.yn + row0 * D, Lc, nus);           // Y^T
+    stage_cols_f32<D>(sA2, LC, 0, p.d_o + row0 * D, Lc, wt);            // (w d_O)^T
+    __syncthreads();
+    const float decay = expf(bcum[kC - 1]);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        R[rt][ct] = mma<2 * kC>(sA1 + (RW * wave + 16 * rt) * L2, L2, sB1 + 16 * ct * L2, L2, R[rt][ct] * decay);
+        S[rt][ct] = mma<kC>(sA2 + (RW * wave + 16 * rt) * LC, LC, sB1 + 16 * ct * L2, L2, S[rt][ct] * decay);
+      }
+    __syncthreads();
+  }
+  // gradients of the initial states
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int row = RW * wave + 16 * rt + 4 * g + ii, col = 16 * ct + tl;
+        if (p.dh0) p.dh0[(size_t)bh * D * D + row * D + col] = 0.5f * R[rt][ct][ii];
+        if (p.dg0) p.dg0[(size_t)bh * D * D + row * D + col] = S[rt][ct][ii];
+      }
+}
+
+// ---------------------------------------------------------------------------------------
+// per-token gradients of a chunk
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
+  constexpr int LD = D + 8, L2 = 2 * kC + 8, LC = kC + 8, NTL = D / 16;
+  constexpr int R1A = 5 * kC * LD;                       // K, V, X, Y, d_O token-major
+  constexpr int R1B = 2 * kC * LD + D * L2 + D * LC;     // K, V, [Y^T | X^T], d_O^T
+  constexpr int R1 = R1A > R1B ? R1A : R1B;
+  const int chunk = blockIdx.x, bh = chunk / p.NC, c = chunk % p.NC;
+  const int h = bh % p.H;
+  const int s = c * kC, Lc = min(kC, p.T - s);
+  const size_t row0 = (size_t)bh * p.T + s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
+
+  __shared__ float bcum[kC], betas[kC], nus[kC];
+  __shared__ float ta[kC], tsuf[kC], trs[kC], tcol[4][kC], tdb[kC];  // dgamma parts per token
+  __shared__ float red[2][4];                                          // <Rs, Hb>, <S, Gb> per wave
+  __shared__ __attribute__((aligned(16))) uint16_t r1[R1];
+  __shared__ __attribute__((aligned(16))) uint16_t r2[D * LD];          // Hb, Gb, then Rs, S, S^T
+  __shared__ __attribute__((aligned(16))) uint16_t r3[kC * L2 + kC * LC];  // scores
+  uint16_t* sK = r1;
+  uint16_t* sV = r1 + kC * LD;
+  uint16_t* sX = r1 + 2 * kC * LD;
+  uint16_t* sY = r1 + 3 * kC * LD;
+  uint16_t* sDO = r1 + 4 * kC * LD;
+  uint16_t* sYX = r1 + 2 * kC * LD;             // [Y^T | X^T]  (after the scores)
+  uint16_t* sDOT = sYX + D * L2;                // d_O^T
+  uint16_t* sA3 = r3;                           // [-M o Pxk | -M o Pyk]
+  uint16_t* sMvd = r3 + kC * L2;                // M o Pvd
+  const size_t sn = (size_t)chunk * D * D;
+
+  if (wave == 0) {
+    chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
+    nus[lane] = lane < Lc ? p.nu[row0 + lane] : 0.f;
+  }
+  __syncthreads();
+  stage_rows_bf16<D>(sK, LD, static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
+  stage_rows_bf16<D>(sV, LD, static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
+  stage_rows_f32<D>(sX, LD, p.x + row0 * D, Lc);
+  stage_rows_f32<D>(sY, LD, p.yn + row0 * D, Lc, nus);
+  stage_rows_f32<D>(sDO, LD, p.d_o + row0 * D, Lc);
+  stage_snapshot<D, false>(r2, LD, static_cast<const uint16_t*>(p.hb) + sn);
+  __syncthreads();
+
+  const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int trow = 16 * wave;
+  // ---- dgamma: suffix terms e^{b_t}(<dH_t, Hb> + <dG_t, Gb>) and the per-chunk ones ------
+  float cpart[4];
+  {
+    f32x4 hx[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) hx[nt] = mma<D>(sX + trow * LD, LD, r2 + 16 * nt * LD, LD, z);  // Hb x_t
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = trow + 4 * g + i;
+      const float* yrow = p.yn + (row0 + min(t, Lc - 1)) * D;
+      float a = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(yrow[16 * nt + tl], hx[nt][i], a);
+      cpart[i] = -nus[t] * a;  // <dH_t, Hb> = -y_t^T Hb x_t
+    }
+    float rh = 0.f;
+    const uint16_t* rs = p.snap_r + sn;
+    for (int idx = threadIdx.x; idx < D * D; idx += kThreads)
+      rh = __builtin_fmaf(bf16_to_f32(rs[idx]), bf16_to_f32(r2[(idx / D) * LD + idx % D]), rh);
+    rh = wave_sum(rh);
+    if (lane == 0) red[0][wave] = rh;
+  }
+  __syncthreads();  // Hb consumed
+  stage_snapshot<D, false>(r2, LD, static_cast<const uint16_t*>(p.gb) + sn);
+  __syncthreads();
+  {
+    f32x4 gx[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) gx[nt] = mma<D>(sX + trow * LD, LD, r2 + 16 * nt * LD, LD, z);  // Gb x_t
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = trow + 4 * g + i;
+      const float* drow = p.d_o + (row0 + min(t, Lc - 1)) * D;
+      float a = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(drow[16 * nt + tl], gx[nt][i], a);
+      const float tot = group_sum<16>(cpart[i] + a);  // + <dG_t, Gb> = d_o_t^T Gb x_t
+      if (tl == 0) tsuf[t] = t < Lc ? expf(bcum[t]) * tot : 0.f;
+    }
+    float sg = 0.f;
+    const uint16_t* ss = p.snap_s + sn;
+    for (int idx = threadIdx.x; idx < D * D; idx += kThreads)
+      sg = __builtin_fmaf(bf16_to_f32(ss[idx]), bf16_to_f32(r2[(idx / D) * LD + idx % D]), sg);
+    sg = wave_sum(sg);
+    if (lane == 0) red[1][wave] = sg;
+  }
+  // ---- reverse-causal scores (t' >= t), masked and decayed ----------------------------
+  {
+    f32x4 pxk[4], pyk[4], pvd[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      pxk[jt] = mma<D>(sK + trow * LD, LD, sX + 16 * jt * LD, LD, z);   // k_t . x_t'
+      pyk[jt] = mma<D>(sK + trow * LD, LD, sY + 16 * jt * LD, LD, z);   // k_t . y_t'
+      pvd[jt] = mma<D>(sV + trow * LD, LD, sDO + 16 * jt * LD, LD, z);  // v_t . d_o_t'
+    }
+    // pairs j <= t': e^{b_t'-b_j} beta_j (<dH_t', k_j k_j^T> + <dG_t', v_j k_j^T>), row sums and column sums
+    float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, colacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = trow + 4 * g + i, tp = 16 * jt + tl;
+        const float m = tp >= t ? expf(bcum[tp] - bcum[t]) : 0.f;
+        sA3[t * L2 + tp] = bf(-m * pxk[jt][i]);
+        sA3[t * L2 + kC + tp] = bf(-m * pyk[jt][i]);
+        sMvd[t * LC + tp] = bf(m * pvd[jt][i]);
+        const float e = m * betas[t] * pxk[jt][i] * (pvd[jt][i] - pyk[jt][i]);
+        rowacc[i] += e;
+        colacc[jt] += e;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = group_sum<16>(rowacc[i]);
+      if (tl == 0) trs[trow + 4 * g + i] = r;
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const float cs = sum_lane_groups(colacc[jt]);
+      if (g == 0) tcol[wave][16 * jt + tl] = cs;
+    }
+  }
+  __syncthreads();  // X, Y, d_O token-major and Gb consumed
+  // ---- stored adjoints of the chunk's end, applied to k_t and v_t ---------------------
+  stage_square<D>(r2, LD, p.snap_r + sn);
+  stage_cols_f32<D>(sYX, L2, 0, p.yn + row0 * D, Lc, nus);      // Y^T
+  stage_cols_f32<D>(sYX, L2, kC, p.x + row0 * D, Lc);           // X^T
+  stage_cols_f32<D>(sDOT, LC, 0, p.d_o + row0 * D, Lc);         // d_O^T
+  __syncthreads();
+  f32x4 hk[NTL], gk[NTL], gtv[NTL];
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) hk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
+  __syncthreads();
+  stage_square<D>(r2, LD, p.snap_s + sn);
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) gk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
+  __syncthreads();
+  stage_square<D>(r2, LD, p.snap_st + sn);
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) gtv[nt] = mma<D>(sV + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = trow + 4 * g + i;
+    const float e = expf(bcum[kC - 1] - bcum[t]);
+    float kh = 0.f, vg = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+      hk[nt][i] *= e;
+      gk[nt][i] *= e;
+      gtv[nt][i] *= e;
+      const int col = 16 * nt + tl;
+      kh = __builtin_fmaf(bf16_to_f32(sK[t * LD + col]), hk[nt][i], kh);
+      vg = __builtin_fmaf(bf16_to_f32(sV[t * LD + col]), gk[nt][i], vg);
+    }
+    // dgamma prefix term: e^{b_e-b_t} beta_t (k_t^T Rb k_t + v_t^T S k_t), Rb = Rs/2 on k k^T
+    const float a = group_sum<16>(0.5f * kh + vg);
+    if (tl == 0) ta[t] = betas[t] * a;
+  }
+  // ---- the chunk's own reverse-causal terms ------------------------------------------
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) {
+    hk[nt] = mma<2 * kC>(sA3 + trow * L2, L2, sYX + 16 * nt * L2, L2, hk[nt]);
+    gk[nt] -= mma<kC>(sA3 + trow * L2, L2, sDOT + 16 * nt * LC, LC, z);
+    gtv[nt] = mma<kC>(sMvd + trow * LC, LC, sYX + 16 * nt * L2 + kC, L2, gtv[nt]);
+  }
+  // ---- outputs ------------------------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = trow + 4 * g + i;
+    const float bt = betas[t];
+    float kh = 0.f, vg = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+      const int col = 16 * nt + tl;
+      kh = __builtin_fmaf(bf16_to_f32(sK[t * LD + col]), hk[nt][i], kh);
+      vg = __builtin_fmaf(bf16_to_f32(sV[t * LD + col]), gk[nt][i], vg);
+    }
+    const float dbeta = group_sum<16>(0.5f * kh + vg);
+    if (t < Lc) {
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) {
+        const int col = 16 * nt + tl;
+        p.dk[(row0 + t) * D + col] = bt * (hk[nt][i] + gtv[nt][i]);
+        p.dv[(row0 + t) * D + col] = bt * gk[nt][i];
+      }
+      if (tl == 0) p.dbeta[row0 + t] = dbeta;
+    }
+    if (tl == 0) tdb[t] = dbeta;
+  }
+  __syncthreads();
+  // dgamma_t = (per-chunk + prefix + suffix + pair terms - beta_t dbeta_t) / gamma_t
+  if (wave == 0) {
+    float A = ta[lane], R = trs[lane], Sf = tsuf[lane];
+    const float cs = tcol[0][lane] + tcol[1][lane] + tcol[2][lane] + tcol[3][lane];
+    float Cl = cs;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float a2 = __shfl_up(A, o, 64), r2v = __shfl_up(R, o, 64), c2 = __shfl_up(Cl, o, 64);
+      const float s2 = __shfl_down(Sf, o, 64);
+      if (lane >= o) {
+        A += a2;
+        R += r2v;
+        Cl += c2;
+      }
+      if (lane + o < 64) Sf += s2;
+    }
+    // pairs j <= t <= t': sum_{u<=t} rowsum_u - sum_{u<t} colsum_u
+    const float pairs = R - (Cl - cs);
+    const float c1 = expf(bcum[kC - 1]) *
+                     (0.5f * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    if (lane < Lc) p.dgamma[row0 + lane] = (c1 + A + Sf + pairs - betas[lane] * tdb[lane]) / p.gamma[row0 + lane];
+  }
+  // dq = y; this chunk's part of dlambda = -sum_t y_t * x_t
+  for (int idx = threadIdx.x; idx < Lc * D; idx += kThreads) {
+    const int t = idx / D;
+    p.dq[(row0 + t) * D + idx % D] = nus[t] * p.yn[(row0 + t) * D + idx % D];
+  }
+  for (int i = threadIdx.x; i < D; i += kThreads) {
+    float acc = 0.f;
+    for (int t = 0; t < Lc; ++t) acc -= nus[t] * p.yn[(row0 + t) * D + i] * p.x[(row0 + t) * D + i];
+    p.lam_part[(size_t)chunk * D + i] = acc;
+  }
+  (void)h;
+}
+
+// dlambda[h][i] = sum over batch and chunks of the chunk parts
+__global__ __launch_bounds__(128) void bwd_lambda_kernel(BwdParams p, int D) {
+  const int h = blockIdx.x;
+  for (int i = threadIdx.x; i < D; i += 128) {
+    float acc = 0.f;
+    for (int b = 0; b < p.BH / p.H; ++b)
+      for (int c = 0; c < p.NC; ++c) acc += p.lam_part[((size_t)(b * p.H + h) * p.NC + c) * D + i];
+    p.dlam[h * D + i] = acc;
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
+  const dim3 chunks((unsigned)(p.BH * p.NC));
+  switch (phase) {
+    case 0: hipLaunchKernelGGL((bwd_dx_kernel<D>), chunks, dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)p.BH), dim3(kThreads), 0, s, p); break;
+    case 2:
+      if (p.NC > 0) {
+        hipLaunchKernelGGL((bwd_grad_kernel<D>), chunks, dim3(kThreads), 0, s, p);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      }
+      hipLaunchKernelGGL(bwd_lambda_kernel, dim3((unsigned)p.H), dim3(128), 0, s, p, D);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int phase, int D, const BwdParams& p, hipStream_t s) {
+  if (D == 128) return launch_bwd_d<128>(phase, p, s);
+  if (D == 64) return launch_bwd_d<64>(phase, p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mesa

@@ -102,6 +102,36 @@ struct PrepParams {
   float eps;
 };
 
+// Backward pass (bf16 inputs, chunk 64).
+struct BwdParams {
+  const void* k;            // [BH, T, D] bf16
+  const void* v;
+  const float* gamma;       // [BH, T]
+  const float* beta;
+  const void* hb;           // forward boundary snapshots (bf16 fragment order)
+  const void* gb;
+  const float* x;           // forward solutions [BH, T, D]
+  const float* d_o;         // dL/do
+  const float* d_hfinal;    // [BH, D, D] or null
+  const float* d_gfinal;
+  void* rhs;                // adjoint right-hand sides dx/||dx|| [BH, T, D] bf16
+  float* nu;                // ||dx|| [BH, T]
+  const float* yn;          // adjoint CG solutions for rhs [BH, T, D]
+  uint16_t* snap_r;         // per chunk: Hhat + Hhat^T, Ghat, Ghat^T at its end [BH*NC, D, D] bf16
+  uint16_t* snap_s;
+  uint16_t* snap_st;
+  float* dq;                // [BH, T, D]
+  float* dk;
+  float* dv;
+  float* dbeta;             // [BH, T]
+  float* dgamma;
+  float* lam_part;          // [BH*NC, D]
+  float* dlam;              // [H, D]
+  float* dh0;               // [BH, D, D] or null
+  float* dg0;
+  int BH, H, T, NC;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);
@@ -110,6 +140,8 @@ hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t 
 // packed_h: DecodeParams::h in the blocked upper-triangular layout;
 // warm: CG starts from DecodeParams::x0
 hipError_t launch_decode(bool bf16, int D, bool packed_h, bool warm, const DecodeParams& p, hipStream_t s);
+// phase 0: adjoint right-hand sides; 1: adjoint scan; 2: per-token gradients and dlambda
+hipError_t launch_bwd(int phase, int D, const BwdParams& p, hipStream_t s);
 hipError_t launch_qk_prep(bool bf16, int D, const PrepParams& p, hipStream_t s);
 hipError_t launch_sym_pack(int D, int count, const float* full, float* packed, hipStream_t s);
 hipError_t launch_sym_unpack(int D, int count, const float* packed, float* full, hipStream_t s);

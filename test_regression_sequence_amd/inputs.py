@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
-    "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "round_to_bf16",
+    "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs", "round_to_bf16",
     "bf16_bits", "bits_to_f32",
 ]
 
@@ -318,6 +318,26 @@ def make_preprocess_inputs(cfg: FwdConfig, window: int = 4) -> dict:
     hq, _ = _finish(rng.standard_normal(hshp, dtype=np.float32), cfg.dtype)
     hk, _ = _finish(rng.standard_normal(hshp, dtype=np.float32), cfg.dtype)
     return dict(q=q, k=k, wq=wq, wk=wk, hq=hq, hk=hk, window=window, cfg=cfg)
+
+
+def make_bwd_inputs(cfg: FwdConfig) -> dict:
+    """Upstream gradients and initial states for the backward pass.
+
+    d_o ~ N(0, 1) ``[B, H, T, d]``; d_hfinal, d_gfinal ~ N(0, 0.1^2)
+    ``[B, H, d, d]``; initial states h0 = M M^T / d (M ~ N(0, 1), symmetric
+    positive semi-definite) and g0 ~ N(0, 0.1^2).  All fp32.  Stream:
+    ``default_rng([seed, 4])`` in the order d_o, d_hfinal, d_gfinal, M, g0.
+    """
+    rng = np.random.default_rng([cfg.seed, 4])
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    d_o = rng.standard_normal((B, H, T, d), dtype=np.float32)
+    d_hfinal = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32)
+    d_gfinal = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32)
+    M = rng.standard_normal((B, H, d, d))
+    h0 = np.matmul(M, M.transpose(0, 1, 3, 2)) / d
+    h0 = (0.5 * (h0 + h0.transpose(0, 1, 3, 2))).astype(np.float32)
+    g0 = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32)
+    return dict(d_o=d_o, d_hfinal=d_hfinal, d_gfinal=d_gfinal, h0=h0, g0=g0)
 
 
 def small_fwd(B=1, H=2, T=200, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0,

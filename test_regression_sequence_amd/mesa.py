@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.mesa_decode_step_warm.restype = ctypes.c_int
         L.mesa_decode_step_warm.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, I32,
                                             P, P, P, P, I32, F, P]
+        L.mesa_bwd_workspace_bytes.restype = S
+        L.mesa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdDesc)]
+        L.mesa_bwd_chunked.restype = ctypes.c_int
+        L.mesa_bwd_chunked.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 21 + [P, S, P]
         L.mesa_qk_preprocess.restype = ctypes.c_int
         L.mesa_qk_preprocess.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P, P, F,
                                          P, P, P, P, P]
@@ -338,4 +342,52 @@ def qk_preprocess(q_raw, k_raw, w_q, w_k, *, q_hist=None, k_hist=None, eps: floa
                                      _ptr(q_hist), _ptr(k_hist), float(eps), _ptr(res["q"]), _ptr(res["k"]),
                                      _ptr(res.get("q_hist")), _ptr(res.get("k_hist")), _stream(stream))
     _check(code_, "mesa_qk_preprocess")
+    return res
+
+
+def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps: int = 30,
+                tol: float = 0.0, h0=None, g0=None, d_hfinal=None, d_gfinal=None,
+                state_grads: bool = False, return_steps: bool = False, out=None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Backward of fwd_chunked: x is the forward's solutions (its return_x output),
+    d_o [B, H, T, d] fp32 the gradient at o.  Returns dq, dk, dv [B, H, T, d],
+    dgamma, dbeta [B, H, T], dlam [H, d] (fp32) and, with state_grads, dh0, dg0."""
+    B, H, T, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (B, H, T, d), q.dtype)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(beta, "beta", (B, H, T), torch.float32)
+    _need(lam, "lam", (H, d), torch.float32)
+    for name, t in (("x", x), ("d_o", d_o)):
+        _need(t, name, (B, H, T, d), torch.float32)
+    for name, t in (("h0", h0), ("g0", g0), ("d_hfinal", d_hfinal), ("d_gfinal", d_gfinal)):
+        if t is not None:
+            _need(t, name, (B, H, d, d), torch.float32)
+    desc = make_desc(B, H, T, d, chunk, max_steps, tol, code)
+    L = lib()
+    need = int(L.mesa_bwd_workspace_bytes(ctypes.byref(desc)))
+    dev = q.device
+    out = dict(out or {})
+    f32 = torch.float32
+
+    def get(key, shape, dtype=f32):
+        return out.get(key) if out.get(key) is not None else torch.empty(shape, device=dev, dtype=dtype)
+
+    res = {key: get(key, (B, H, T, d)) for key in ("dq", "dk", "dv")}
+    res.update(dgamma=get("dgamma", (B, H, T)), dbeta=get("dbeta", (B, H, T)), dlam=get("dlam", (H, d)))
+    if state_grads:
+        res.update(dh0=get("dh0", (B, H, d, d)), dg0=get("dg0", (B, H, d, d)))
+    if return_steps:
+        res["adj_steps"] = get("adj_steps", (B, H, T), torch.int32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    wbytes = workspace.numel() * workspace.element_size()
+    code_ = L.mesa_bwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam),
+                               _ptr(h0), _ptr(g0), _ptr(x), _ptr(d_o), _ptr(d_hfinal), _ptr(d_gfinal),
+                               _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dgamma"]),
+                               _ptr(res["dbeta"]), _ptr(res["dlam"]), _ptr(res.get("dh0")), _ptr(res.get("dg0")),
+                               _ptr(res.get("adj_steps")), _ptr(workspace), ctypes.c_size_t(wbytes),
+                               _stream(stream))
+    _check(code_, "mesa_bwd_chunked")
     return res
