@@ -243,7 +243,7 @@ BwdLayout bwd_layout(const mesa_fwd_desc* d) {
   L.yn = off; off = align256(off + BH * T * D * 4);
   L.oscr = off; off = align256(off + BH * T * D * 4);
   L.snap = off; off = align256(off + 3 * BH * NC * D * D * 2);
-  L.lam = off; off = align256(off + BH * NC * D * 4);
+  L.lam = off; off = align256(off + BH * D * 4);
   L.total = off;
   return L;
 }

@@ -36,9 +36,9 @@
 //                    e^{b_e-b_t} (stored adjoint) k_t plus the chunk's own
 //                    reverse-causal terms, e.g. Ghat_t k_t gains
 //                    sum_{t'>=t} e^{b_t'-b_t} (x_t'.k_t) d_o_t'; the four parts of
-//                    dgamma above; writes dq, dk, dv, dbeta, dgamma and
-//                    per-chunk dlambda parts.
-//   bwd_lambda_kernel dlambda summed over batch and chunks.
+//                    dgamma above; writes dq, dk, dv, dbeta, dgamma.
+//   bwd_lambda_kernel dlambda summed over the batch (the scan sums each
+//                    sequence's -y_t * x_t while staging its chunks).
 // Every chunk product is an MFMA 16x16x32 bf16 contraction with fp32
 // accumulation on tiles staged in LDS with the contraction index contiguous
 // (rows padded by 16 bytes, so the 16 rows an MFMA operand reads fall in
@@ -89,59 +89,83 @@ __device__ __forceinline__ void chunk_gates(const float* gamma, const float* bet
   betas[lane] = bt;
 }
 
-// token-major [C][D] tile -> LDS bf16 [C][ld]; rows >= Lc are zero.
+// The staging helpers below load everything a thread moves into registers
+// before the first LDS write (compile-time trip counts), so a tile costs one
+// memory round trip.  Rows past Lc load row Lc-1 (every load is unconditional)
+// and are written as zeros.
+
+// token-major [C][D] fp32 tile -> LDS bf16 [C][ld], rows scaled by row_scale
 template <int D>
 __device__ __forceinline__ void stage_rows_f32(uint16_t* dst, int ld, const float* src, int Lc,
                                                const float* row_scale = nullptr) {
-  for (int idx = threadIdx.x; idx < kC * D / 4; idx += kThreads) {
-    const int t = idx / (D / 4), c4 = idx % (D / 4);
-    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < Lc) {
-      v = *reinterpret_cast<const f32x4*>(src + (size_t)t * D + 4 * c4);
-      if (row_scale) v *= row_scale[t];
-    }
+  constexpr int Q = D / 4, N = kC * Q / kThreads;
+  static_assert(kThreads % Q == 0 && N * kThreads == kC * Q, "whole quads per thread");
+  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+  f32x4 v[N];
+#pragma unroll
+  for (int it = 0; it < N; ++it)
+    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(t0 + it * (kThreads / Q), Lc - 1) * D + 4 * c4);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int t = t0 + it * (kThreads / Q);
+    const float sc = t < Lc ? (row_scale ? row_scale[t] : 1.f) : 0.f;
     u16x4 o;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = bf(v[u]);
+    for (int u = 0; u < 4; ++u) o[u] = bf(v[it][u] * sc);
     *reinterpret_cast<u16x4*>(dst + t * ld + 4 * c4) = o;
   }
 }
 
 template <int D>
 __device__ __forceinline__ void stage_rows_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
-  for (int idx = threadIdx.x; idx < kC * D / 8; idx += kThreads) {
-    const int t = idx / (D / 8), c8 = idx % (D / 8);
-    u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (t < Lc) v = *reinterpret_cast<const u16x8*>(src + (size_t)t * D + 8 * c8);
-    *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = v;
+  constexpr int E = D / 8, N = kC * E / kThreads;
+  static_assert(kThreads % E == 0 && N * kThreads == kC * E, "whole octets per thread");
+  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
+  u16x8 v[N];
+#pragma unroll
+  for (int it = 0; it < N; ++it)
+    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(t0 + it * (kThreads / E), Lc - 1) * D + 8 * c8);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int t = t0 + it * (kThreads / E);
+    const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = t < Lc ? v[it] : zero;
   }
 }
 
-// token-major [C][D] fp32 -> LDS bf16 transposed: dst[i * ld + col0 + t] = scale_t * src[t][i]
+// token-major [C][D] fp32 -> LDS bf16 transposed: dst[i * ld + col0 + t] = sign * scale_t * src[t][i]
 template <int D>
 __device__ __forceinline__ void stage_cols_f32(uint16_t* dst, int ld, int col0, const float* src, int Lc,
                                                const float* row_scale = nullptr, float sign = 1.f) {
-  for (int idx = threadIdx.x; idx < kC * D / 4; idx += kThreads) {
-    const int t = idx / (D / 4), c4 = idx % (D / 4);
-    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < Lc) {
-      v = *reinterpret_cast<const f32x4*>(src + (size_t)t * D + 4 * c4);
-      v *= sign * (row_scale ? row_scale[t] : 1.f);
-    }
+  constexpr int Q = D / 4, N = kC * Q / kThreads;
+  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+  f32x4 v[N];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(v[u]);
+  for (int it = 0; it < N; ++it)
+    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(t0 + it * (kThreads / Q), Lc - 1) * D + 4 * c4);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int t = t0 + it * (kThreads / Q);
+    const float sc = t < Lc ? sign * (row_scale ? row_scale[t] : 1.f) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(v[it][u] * sc);
   }
 }
 
 // token-major [C][D] bf16 -> LDS transposed
 template <int D>
 __device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
-  for (int idx = threadIdx.x; idx < kC * D / 8; idx += kThreads) {
-    const int t = idx / (D / 8), c8 = idx % (D / 8);
-    u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (t < Lc) v = *reinterpret_cast<const u16x8*>(src + (size_t)t * D + 8 * c8);
+  constexpr int E = D / 8, N = kC * E / kThreads;
+  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
+  u16x8 v[N];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = v[u];
+  for (int it = 0; it < N; ++it)
+    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(t0 + it * (kThreads / E), Lc - 1) * D + 8 * c8);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int t = t0 + it * (kThreads / E);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = t < Lc ? v[it][u] : uint16_t(0);
   }
 }
 
@@ -150,21 +174,26 @@ __device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uin
 // 32m + 16 + 4(l/16) + {0..3}) -> LDS row-major (TRANS: transposed).
 template <int D, bool TRANS>
 __device__ __forceinline__ void stage_snapshot(uint16_t* dst, int ld, const uint16_t* frag) {
-  constexpr int NM = D / 32;
-  for (int idx = threadIdx.x; idx < D * D / 8; idx += kThreads) {
+  constexpr int NM = D / 32, N = D * D / 8 / kThreads;
+  u16x8 v[N];
+#pragma unroll
+  for (int it = 0; it < N; ++it)
+    v[it] = *reinterpret_cast<const u16x8*>(frag + (size_t)(threadIdx.x + it * kThreads) * 8);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
     const int f = idx >> 6, l = idx & 63;
     const int n = 16 * (f / NM) + (l & 15);
     const int c0 = 32 * (f % NM) + 4 * (l >> 4);
-    const u16x8 v = *reinterpret_cast<const u16x8*>(frag + (size_t)idx * 8);
     if constexpr (TRANS) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        dst[(c0 + u) * ld + n] = v[u];
-        dst[(c0 + 16 + u) * ld + n] = v[4 + u];
+        dst[(c0 + u) * ld + n] = v[it][u];
+        dst[(c0 + 16 + u) * ld + n] = v[it][4 + u];
       }
     } else {
-      *reinterpret_cast<u16x4*>(dst + n * ld + c0) = u16x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{v[4], v[5], v[6], v[7]};
+      *reinterpret_cast<u16x4*>(dst + n * ld + c0) = u16x4{v[it][0], v[it][1], v[it][2], v[it][3]};
+      *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{v[it][4], v[it][5], v[it][6], v[it][7]};
     }
   }
 }
@@ -172,10 +201,34 @@ __device__ __forceinline__ void stage_snapshot(uint16_t* dst, int ld, const uint
 // row-major [D][D] bf16 -> LDS [D][ld]
 template <int D>
 __device__ __forceinline__ void stage_square(uint16_t* dst, int ld, const uint16_t* src) {
-  for (int idx = threadIdx.x; idx < D * D / 8; idx += kThreads) {
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
-    *reinterpret_cast<u16x8*>(dst + r * ld + 8 * c8) = *reinterpret_cast<const u16x8*>(src + (size_t)idx * 8);
+  constexpr int N = D * D / 8 / kThreads;
+  u16x8 v[N];
+#pragma unroll
+  for (int it = 0; it < N; ++it) v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)(threadIdx.x + it * kThreads) * 8);
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    *reinterpret_cast<u16x8*>(dst + (idx / (D / 8)) * ld + 8 * (idx % (D / 8))) = v[it];
   }
+}
+
+// <A, B> for a row-major [D][D] bf16 matrix in memory and one in LDS [D][ld]; the
+// calling thread's part (16-byte loads, all issued before the products).
+template <int D>
+__device__ __forceinline__ float square_dot(const uint16_t* a, const uint16_t* b, int ld) {
+  constexpr int N = D * D / 8 / kThreads;
+  u16x8 v[N];
+#pragma unroll
+  for (int it = 0; it < N; ++it) v[it] = *reinterpret_cast<const u16x8*>(a + (size_t)(threadIdx.x + it * kThreads) * 8);
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const u16x8 w = *reinterpret_cast<const u16x8*>(b + (idx / (D / 8)) * ld + 8 * (idx % (D / 8)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(v[it][u]), bf16_to_f32(w[u]), acc);
+  }
+  return acc;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -265,6 +318,10 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sB1[D * L2];  // [X^T | Y^T]
   __shared__ __attribute__((aligned(16))) uint16_t sA2[D * LC];  // (w d_O)^T
 
+  constexpr int Q = D / 4, NQ = kC * Q / kThreads;
+  const int qc = threadIdx.x % Q, qt0 = threadIdx.x / Q;   // this thread's dim quad and first token
+  f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
+  __shared__ __attribute__((aligned(16))) f32x4 lam_s[kThreads];
   f32x4 R[NRT][NCT], S[NRT][NCT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
@@ -314,11 +371,33 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       nyw[lane] = -w * nu;
     }
     __syncthreads();
-    // y_t = nu_t * yn_t
-    stage_cols_f32<D>(sA1, L2, 0, p.yn + row0 * D, Lc, nyw);            // -(w Y)^T
-    stage_cols_f32<D>(sA1, L2, kC, p.x + row0 * D, Lc, wt, -1.f);       // -(w X)^T
-    stage_cols_f32<D>(sB1, L2, 0, p.x + row0 * D, Lc);                  // X^T
-    stage_cols_f32<D>(sB1, L2, kC, p.yn + row0 * D, Lc, nus);           // Y^T
+    // y_t = nu_t * yn_t: -(w Y)^T, -(w X)^T into sA1, X^T, Y^T into sB1, and
+    // this thread's dims of dlambda = -sum_t y_t * x_t
+    {
+      f32x4 xv[NQ], yv[NQ];
+#pragma unroll
+      for (int it = 0; it < NQ; ++it) {
+        const size_t r = row0 + min(qt0 + it * (kThreads / Q), Lc - 1);
+        xv[it] = *reinterpret_cast<const f32x4*>(p.x + r * D + 4 * qc);
+        yv[it] = *reinterpret_cast<const f32x4*>(p.yn + r * D + 4 * qc);
+      }
+#pragma unroll
+      for (int it = 0; it < NQ; ++it) {
+        const int t = qt0 + it * (kThreads / Q);
+        const bool in = t < Lc;
+        const float w = in ? wt[t] : 0.f, nu = in ? nus[t] : 0.f, ex = in ? 1.f : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * qc + u;
+          const float xe = xv[it][u] * ex, ye = yv[it][u] * nu;
+          sA1[i * L2 + t] = bf(-w * ye);
+          sA1[i * L2 + kC + t] = bf(-w * xe);
+          sB1[i * L2 + t] = bf(xe);
+          sB1[i * L2 + kC + t] = bf(ye);
+          lam[u] = __builtin_fmaf(-ye, xe, lam[u]);
+        }
+      }
+    }
     stage_cols_f32<D>(sA2, LC, 0, p.d_o + row0 * D, Lc, wt);            // (w d_O)^T
     __syncthreads();
     const float decay = expf(bcum[kC - 1]);
@@ -330,6 +409,14 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
         S[rt][ct] = mma<kC>(sA2 + (RW * wave + 16 * rt) * LC, LC, sB1 + 16 * ct * L2, L2, S[rt][ct] * decay);
       }
     __syncthreads();
+  }
+  // this sequence's part of dlambda: the threads sharing a dim quad
+  lam_s[threadIdx.x] = lam;
+  __syncthreads();
+  if (threadIdx.x < Q) {
+    f32x4 acc = lam_s[threadIdx.x];
+    for (int r = 1; r < kThreads / Q; ++r) acc += lam_s[threadIdx.x + r * Q];
+    *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * threadIdx.x) = acc;
   }
   // gradients of the initial states
 #pragma unroll
@@ -406,11 +493,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(yrow[16 * nt + tl], hx[nt][i], a);
       cpart[i] = -nus[t] * a;  // <dH_t, Hb> = -y_t^T Hb x_t
     }
-    float rh = 0.f;
-    const uint16_t* rs = p.snap_r + sn;
-    for (int idx = threadIdx.x; idx < D * D; idx += kThreads)
-      rh = __builtin_fmaf(bf16_to_f32(rs[idx]), bf16_to_f32(r2[(idx / D) * LD + idx % D]), rh);
-    rh = wave_sum(rh);
+    const float rh = wave_sum(square_dot<D>(p.snap_r + sn, r2, LD));
     if (lane == 0) red[0][wave] = rh;
   }
   __syncthreads();  // Hb consumed
@@ -430,11 +513,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       const float tot = group_sum<16>(cpart[i] + a);  // + <dG_t, Gb> = d_o_t^T Gb x_t
       if (tl == 0) tsuf[t] = t < Lc ? expf(bcum[t]) * tot : 0.f;
     }
-    float sg = 0.f;
-    const uint16_t* ss = p.snap_s + sn;
-    for (int idx = threadIdx.x; idx < D * D; idx += kThreads)
-      sg = __builtin_fmaf(bf16_to_f32(ss[idx]), bf16_to_f32(r2[(idx / D) * LD + idx % D]), sg);
-    sg = wave_sum(sg);
+    const float sg = wave_sum(square_dot<D>(p.snap_s + sn, r2, LD));
     if (lane == 0) red[1][wave] = sg;
   }
   // ---- reverse-causal scores (t' >= t), masked and decayed ----------------------------
@@ -564,26 +643,30 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
                      (0.5f * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + red[1][0] + red[1][1] + red[1][2] + red[1][3]);
     if (lane < Lc) p.dgamma[row0 + lane] = (c1 + A + Sf + pairs - betas[lane] * tdb[lane]) / p.gamma[row0 + lane];
   }
-  // dq = y; this chunk's part of dlambda = -sum_t y_t * x_t
-  for (int idx = threadIdx.x; idx < Lc * D; idx += kThreads) {
-    const int t = idx / D;
-    p.dq[(row0 + t) * D + idx % D] = nus[t] * p.yn[(row0 + t) * D + idx % D];
-  }
-  for (int i = threadIdx.x; i < D; i += kThreads) {
-    float acc = 0.f;
-    for (int t = 0; t < Lc; ++t) acc -= nus[t] * p.yn[(row0 + t) * D + i] * p.x[(row0 + t) * D + i];
-    p.lam_part[(size_t)chunk * D + i] = acc;
+  // dq = y
+  {
+    constexpr int Q = D / 4, N = kC * Q / kThreads;
+    const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+    f32x4 yv[N];
+#pragma unroll
+    for (int it = 0; it < N; ++it)
+      yv[it] = *reinterpret_cast<const f32x4*>(p.yn + (row0 + min(t0 + it * (kThreads / Q), Lc - 1)) * D + 4 * c4);
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int t = t0 + it * (kThreads / Q);
+      if (t < Lc) *reinterpret_cast<f32x4*>(p.dq + (row0 + t) * D + 4 * c4) = yv[it] * nus[t];
+    }
   }
   (void)h;
 }
 
-// dlambda[h][i] = sum over batch and chunks of the chunk parts
+// dlambda[h][i] = sum over the batch of the sequences' parts
 __global__ __launch_bounds__(128) void bwd_lambda_kernel(BwdParams p, int D) {
   const int h = blockIdx.x;
   for (int i = threadIdx.x; i < D; i += 128) {
     float acc = 0.f;
-    for (int b = 0; b < p.BH / p.H; ++b)
-      for (int c = 0; c < p.NC; ++c) acc += p.lam_part[((size_t)(b * p.H + h) * p.NC + c) * D + i];
+    if (p.NC > 0)
+      for (int b = 0; b < p.BH / p.H; ++b) acc += p.lam_part[(size_t)(b * p.H + h) * D + i];
     p.dlam[h * D + i] = acc;
   }
 }

@@ -125,7 +125,7 @@ struct BwdParams {
   float* dv;
   float* dbeta;             // [BH, T]
   float* dgamma;
-  float* lam_part;          // [BH*NC, D]
+  float* lam_part;          // [BH, D]: -sum_t y_t * x_t per sequence
   float* dlam;              // [H, D]
   float* dh0;               // [BH, D, D] or null
   float* dg0;
