@@ -26,7 +26,9 @@
 //                    W_tj = e^{b_t-b_j} beta_j [j<=t]; writes dx/||dx|| (bf16)
 //                    and ||dx||, the right-hand sides of the adjoint CG (the
 //                    forward CG kernels, so the stopping test is relative).
-//   bwd_scan_kernel  per sequence, chunks backwards: the adjoints arriving at a
+//   bwd_scan_kernel  per stripe of 32 state rows of a sequence, chunks
+//                    backwards (the next chunk's x, y, d_o loaded while the
+//                    current one's products run): the adjoints arriving at a
 //                    chunk's end, Rs = Hhat + Hhat^T and S = Ghat, stored per
 //                    chunk (bf16; S also transposed), then
 //                    Rs <- e^{b_e} Rs - sum_t w_t (y_t x_t^T + x_t y_t^T),
@@ -304,24 +306,29 @@ __global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// adjoint scan, chunks backwards
+// adjoint scan, chunks backwards; a workgroup owns a stripe of 32 state rows
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
-  constexpr int RW = D / 4, NRT = RW / 16, NCT = D / 16;
+  constexpr int SR = 32, NSTR = D / SR;          // state rows per workgroup, stripes per sequence
+  constexpr int CW = D / 4, NCT = CW / 16;       // state columns per wave, their 16-column tiles
+  constexpr int NRT = SR / 16;
   constexpr int L2 = 2 * kC + 8, LC = kC + 8;
-  const int bh = blockIdx.x;
+  constexpr int Q = D / 4, NQ = kC * Q / kThreads;   // dim quads per row, (token, quad) items per thread
+  constexpr int SQ = SR / 4, ND = kC * SQ / kThreads;  // the same for the stripe's dims (d_o)
+  static_assert(ND >= 1 && ND * kThreads == kC * SQ, "stripe items per thread");
+  const int bh = blockIdx.x / NSTR, stripe = blockIdx.x % NSTR, r0 = SR * stripe;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
+  const int qc = threadIdx.x % Q, qt0 = threadIdx.x / Q;           // dim quad, first token
+  const bool own = 4 * qc >= r0 && 4 * qc < r0 + SR;               // quad inside the stripe
+  const int dq = threadIdx.x % SQ, dt0 = threadIdx.x / SQ;         // d_o: stripe quad, first token
 
-  __shared__ float bcum[kC], betas[kC], wt[kC], nus[kC], nyw[kC];
-  __shared__ __attribute__((aligned(16))) uint16_t sA1[D * L2];  // [(-wY)^T | (-wX)^T]
-  __shared__ __attribute__((aligned(16))) uint16_t sB1[D * L2];  // [X^T | Y^T]
-  __shared__ __attribute__((aligned(16))) uint16_t sA2[D * LC];  // (w d_O)^T
-
-  constexpr int Q = D / 4, NQ = kC * Q / kThreads;
-  const int qc = threadIdx.x % Q, qt0 = threadIdx.x / Q;   // this thread's dim quad and first token
-  f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
+  __shared__ float bcum[kC], betas[kC], wt[kC], nus[kC];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[SR * L2];  // [(-wY)^T | (-wX)^T], stripe rows
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[D * L2];   // [X^T | Y^T], all dims
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[SR * LC];  // (w d_O)^T, stripe rows
   __shared__ __attribute__((aligned(16))) f32x4 lam_s[kThreads];
+
   f32x4 R[NRT][NCT], S[NRT][NCT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int row = RW * wave + 16 * rt + 4 * g + ii, col = 16 * ct + tl;
+        const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
         float rv = 0.f, sv = 0.f;
         if (p.d_hfinal) {
           const float* Dh = p.d_hfinal + (size_t)bh * D * D;
@@ -339,6 +346,26 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
         R[rt][ct][ii] = rv;
         S[rt][ct][ii] = sv;
       }
+
+  // x, y (all dims) and d_o (stripe dims) of a chunk, into registers
+  f32x4 xv[NQ], yv[NQ], dv[ND];
+  auto fetch = [&](int c) {
+    const int Lc = min(kC, p.T - c * kC);
+    const size_t row0 = (size_t)bh * p.T + c * kC;
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const size_t r = row0 + min(qt0 + it * (kThreads / Q), Lc - 1);
+      xv[it] = *reinterpret_cast<const f32x4*>(p.x + r * D + 4 * qc);
+      yv[it] = *reinterpret_cast<const f32x4*>(p.yn + r * D + 4 * qc);
+    }
+#pragma unroll
+    for (int it = 0; it < ND; ++it) {
+      const size_t r = row0 + min(dt0 + it * (kThreads / SQ), Lc - 1);
+      dv[it] = *reinterpret_cast<const f32x4*>(p.d_o + r * D + r0 + 4 * dq);
+    }
+  };
+  f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.NC > 0) fetch(p.NC - 1);
 
   for (int c = p.NC - 1; c >= 0; --c) {
     const int chunk = bh * p.NC + c;
@@ -352,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const int row = RW * wave + 16 * rt + 4 * g, col = 16 * ct + tl;
+        const int row = r0 + 16 * rt + 4 * g, col = CW * wave + 16 * ct + tl;
         u16x4 st;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -364,59 +391,59 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       }
     if (wave == 0) {
       chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
-      const float w = expf(bcum[lane]);
-      const float nu = lane < Lc ? p.nu[row0 + lane] : 0.f;
-      wt[lane] = w;
-      nus[lane] = nu;
-      nyw[lane] = -w * nu;
+      wt[lane] = expf(bcum[lane]);
+      nus[lane] = lane < Lc ? p.nu[row0 + lane] : 0.f;
     }
     __syncthreads();
-    // y_t = nu_t * yn_t: -(w Y)^T, -(w X)^T into sA1, X^T, Y^T into sB1, and
-    // this thread's dims of dlambda = -sum_t y_t * x_t
-    {
-      f32x4 xv[NQ], yv[NQ];
+    // y_t = nu_t * yn_t: X^T, Y^T into sB1; -(w Y)^T, -(w X)^T of the stripe into sA1;
+    // stripe 0 also sums this thread's dims of dlambda = -sum_t y_t * x_t
 #pragma unroll
-      for (int it = 0; it < NQ; ++it) {
-        const size_t r = row0 + min(qt0 + it * (kThreads / Q), Lc - 1);
-        xv[it] = *reinterpret_cast<const f32x4*>(p.x + r * D + 4 * qc);
-        yv[it] = *reinterpret_cast<const f32x4*>(p.yn + r * D + 4 * qc);
-      }
+    for (int it = 0; it < NQ; ++it) {
+      const int t = qt0 + it * (kThreads / Q);
+      const bool in = t < Lc;
+      const float w = in ? wt[t] : 0.f, nu = in ? nus[t] : 0.f, ex = in ? 1.f : 0.f;
 #pragma unroll
-      for (int it = 0; it < NQ; ++it) {
-        const int t = qt0 + it * (kThreads / Q);
-        const bool in = t < Lc;
-        const float w = in ? wt[t] : 0.f, nu = in ? nus[t] : 0.f, ex = in ? 1.f : 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * qc + u;
-          const float xe = xv[it][u] * ex, ye = yv[it][u] * nu;
-          sA1[i * L2 + t] = bf(-w * ye);
-          sA1[i * L2 + kC + t] = bf(-w * xe);
-          sB1[i * L2 + t] = bf(xe);
-          sB1[i * L2 + kC + t] = bf(ye);
-          lam[u] = __builtin_fmaf(-ye, xe, lam[u]);
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * qc + u;
+        const float xe = xv[it][u] * ex, ye = yv[it][u] * nu;
+        sB1[i * L2 + t] = bf(xe);
+        sB1[i * L2 + kC + t] = bf(ye);
+        if (own) {
+          sA1[(i - r0) * L2 + t] = bf(-w * ye);
+          sA1[(i - r0) * L2 + kC + t] = bf(-w * xe);
         }
+        if (stripe == 0) lam[u] = __builtin_fmaf(-ye, xe, lam[u]);
       }
     }
-    stage_cols_f32<D>(sA2, LC, 0, p.d_o + row0 * D, Lc, wt);            // (w d_O)^T
+#pragma unroll
+    for (int it = 0; it < ND; ++it) {
+      const int t = dt0 + it * (kThreads / SQ);
+      const float w = t < Lc ? wt[t] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sA2[(4 * dq + u) * LC + t] = bf(w * dv[it][u]);
+    }
+    if (c > 0) fetch(c - 1);  // the next chunk's loads fly during this chunk's products
     __syncthreads();
     const float decay = expf(bcum[kC - 1]);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        R[rt][ct] = mma<2 * kC>(sA1 + (RW * wave + 16 * rt) * L2, L2, sB1 + 16 * ct * L2, L2, R[rt][ct] * decay);
-        S[rt][ct] = mma<kC>(sA2 + (RW * wave + 16 * rt) * LC, LC, sB1 + 16 * ct * L2, L2, S[rt][ct] * decay);
+        const uint16_t* bt = sB1 + (CW * wave + 16 * ct) * L2;
+        R[rt][ct] = mma<2 * kC>(sA1 + 16 * rt * L2, L2, bt, L2, R[rt][ct] * decay);
+        S[rt][ct] = mma<kC>(sA2 + 16 * rt * LC, LC, bt, L2, S[rt][ct] * decay);
       }
     __syncthreads();
   }
   // this sequence's part of dlambda: the threads sharing a dim quad
-  lam_s[threadIdx.x] = lam;
-  __syncthreads();
-  if (threadIdx.x < Q) {
-    f32x4 acc = lam_s[threadIdx.x];
-    for (int r = 1; r < kThreads / Q; ++r) acc += lam_s[threadIdx.x + r * Q];
-    *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * threadIdx.x) = acc;
+  if (stripe == 0) {
+    lam_s[threadIdx.x] = lam;
+    __syncthreads();
+    if (threadIdx.x < Q) {
+      f32x4 acc = lam_s[threadIdx.x];
+      for (int r = 1; r < kThreads / Q; ++r) acc += lam_s[threadIdx.x + r * Q];
+      *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * threadIdx.x) = acc;
+    }
   }
   // gradients of the initial states
 #pragma unroll
@@ -425,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int row = RW * wave + 16 * rt + 4 * g + ii, col = 16 * ct + tl;
+        const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
         if (p.dh0) p.dh0[(size_t)bh * D * D + row * D + col] = 0.5f * R[rt][ct][ii];
         if (p.dg0) p.dg0[(size_t)bh * D * D + row * D + col] = S[rt][ct][ii];
       }
@@ -676,7 +703,7 @@ hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
   const dim3 chunks((unsigned)(p.BH * p.NC));
   switch (phase) {
     case 0: hipLaunchKernelGGL((bwd_dx_kernel<D>), chunks, dim3(kThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)p.BH), dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)(p.BH * (D / 32))), dim3(kThreads), 0, s, p); break;
     case 2:
       if (p.NC > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<D>), chunks, dim3(kThreads), 0, s, p);
