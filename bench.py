@@ -347,7 +347,7 @@ def bench_preprocess(cfg, steps, warmup, window=4):
     }
 
 
-def kernel_source_digest(names=("mesa_cg_bf16.hip", "mesa_common.h", "mesa_kernels.h")) -> str:
+def kernel_source_digest(names=("mesa_cg_bf16.hip", "mesa_common.h")) -> str:
     """sha256 over the sources of the CG kernel (ties a traffic record to one kernel version)."""
     import hashlib
     h = hashlib.sha256()
@@ -453,8 +453,13 @@ def main():
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
         return
     mesa.lib()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     cfg = CONFIGS[args.workload]
     fw = bench_forward(cfg, args.steps, args.warmup)
+    log(f"forward: {fw['ms']:.4f} ms per call")
     tokens = cfg.B * cfg.H * cfg.T
     n_avg = fw["steps_mean"]
     f = flops_per_token(cfg.d, cfg.chunk, n_avg)
@@ -503,10 +508,14 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = bench_decode(CONFIGS[5], args.steps, args.warmup)
+        log(f"decode: {line['decode']['us_per_step']} us per step")
     line["preprocess"] = bench_preprocess(CONFIGS[args.workload], args.steps, args.warmup)
+    log(f"preprocess: {line['preprocess']['us_per_call']} us per call")
     line["backward"] = bench_backward(CONFIGS[args.workload], args.steps, args.warmup)
+    log(f"backward: {line['backward']['ms_per_call']} ms per call")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
+        log("cpu baseline done")
     print(json.dumps(line), flush=True)
 
 
