@@ -135,37 +135,50 @@ __device__ __forceinline__ void stage_rows_bf16(uint16_t* dst, int ld, const uin
   }
 }
 
+// Transposed staging: 8 neighbouring lanes take 8 consecutive tokens of one
+// group of dims, so their LDS writes form 16-byte runs of a row (at most
+// 2-way bank conflicts), while a wave instruction still reads 8 token rows x
+// 128 contiguous bytes.  Thread mapping for quads (Q = D/4 groups of 4 dims):
+// quad (tid/8) % Q, tokens tid%8 + 8 (blk + (32/Q) it), blk = (tid/8) / Q.
+template <int D>
+struct ColMap {
+  static constexpr int Q = D / 4, BLKS = 32 / Q, N = kC * Q / kThreads;
+  __device__ static int quad() { return (threadIdx.x >> 3) % Q; }
+  __device__ static int tok(int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / Q + BLKS * it); }
+};
+
 // token-major [C][D] fp32 -> LDS bf16 transposed: dst[i * ld + col0 + t] = sign * scale_t * src[t][i]
 template <int D>
 __device__ __forceinline__ void stage_cols_f32(uint16_t* dst, int ld, int col0, const float* src, int Lc,
                                                const float* row_scale = nullptr, float sign = 1.f) {
-  constexpr int Q = D / 4, N = kC * Q / kThreads;
-  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
-  f32x4 v[N];
+  using M = ColMap<D>;
+  const int c4 = M::quad();
+  f32x4 v[M::N];
 #pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(t0 + it * (kThreads / Q), Lc - 1) * D + 4 * c4);
+  for (int it = 0; it < M::N; ++it)
+    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(M::tok(it), Lc - 1) * D + 4 * c4);
 #pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int t = t0 + it * (kThreads / Q);
+  for (int it = 0; it < M::N; ++it) {
+    const int t = M::tok(it);
     const float sc = t < Lc ? sign * (row_scale ? row_scale[t] : 1.f) : 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(v[it][u] * sc);
   }
 }
 
-// token-major [C][D] bf16 -> LDS transposed
+// token-major [C][D] bf16 -> LDS transposed (octets of 8 dims; same token-contiguous lane groups)
 template <int D>
 __device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
-  constexpr int E = D / 8, N = kC * E / kThreads;
-  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
+  constexpr int E = D / 8, BLKS = 32 / E, N = kC * E / kThreads;
+  const int c8 = (threadIdx.x >> 3) % E;
+  auto tok = [&](int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / E + BLKS * it); };
   u16x8 v[N];
 #pragma unroll
   for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(t0 + it * (kThreads / E), Lc - 1) * D + 8 * c8);
+    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(tok(it), Lc - 1) * D + 8 * c8);
 #pragma unroll
   for (int it = 0; it < N; ++it) {
-    const int t = t0 + it * (kThreads / E);
+    const int t = tok(it);
 #pragma unroll
     for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = t < Lc ? v[it][u] : uint16_t(0);
   }
@@ -314,14 +327,16 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   constexpr int CW = D / 4, NCT = CW / 16;       // state columns per wave, their 16-column tiles
   constexpr int NRT = SR / 16;
   constexpr int L2 = 2 * kC + 8, LC = kC + 8;
-  constexpr int Q = D / 4, NQ = kC * Q / kThreads;   // dim quads per row, (token, quad) items per thread
-  constexpr int SQ = SR / 4, ND = kC * SQ / kThreads;  // the same for the stripe's dims (d_o)
+  using M = ColMap<D>;                            // x, y: all dims; token-contiguous lane groups
+  constexpr int Q = M::Q, NQ = M::N;
+  constexpr int SQ = SR / 4, ND = kC * SQ / kThreads;  // d_o: the stripe's dims
   static_assert(ND >= 1 && ND * kThreads == kC * SQ, "stripe items per thread");
   const int bh = blockIdx.x / NSTR, stripe = blockIdx.x % NSTR, r0 = SR * stripe;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
-  const int qc = threadIdx.x % Q, qt0 = threadIdx.x / Q;           // dim quad, first token
+  const int qc = M::quad();                                        // this thread's dim quad
   const bool own = 4 * qc >= r0 && 4 * qc < r0 + SR;               // quad inside the stripe
-  const int dq = threadIdx.x % SQ, dt0 = threadIdx.x / SQ;         // d_o: stripe quad, first token
+  const int dq = (threadIdx.x >> 3) % SQ;                          // d_o: stripe quad
+  auto dtok = [&](int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / SQ + (kThreads / 8 / SQ) * it); };
 
   __shared__ float bcum[kC], betas[kC], wt[kC], nus[kC];
   __shared__ __attribute__((aligned(16))) uint16_t sA1[SR * L2];  // [(-wY)^T | (-wX)^T], stripe rows
@@ -347,21 +362,28 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
         S[rt][ct][ii] = sv;
       }
 
-  // x, y (all dims) and d_o (stripe dims) of a chunk, into registers
+  // x, y (all dims), d_o (stripe dims) and the gates of a chunk, into registers
   f32x4 xv[NQ], yv[NQ], dv[ND];
+  float gam_n = 1.f, bet_n = 0.f, nu_n = 0.f;  // wave 0: one token per lane
   auto fetch = [&](int c) {
     const int Lc = min(kC, p.T - c * kC);
     const size_t row0 = (size_t)bh * p.T + c * kC;
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-      const size_t r = row0 + min(qt0 + it * (kThreads / Q), Lc - 1);
+      const size_t r = row0 + min(M::tok(it), Lc - 1);
       xv[it] = *reinterpret_cast<const f32x4*>(p.x + r * D + 4 * qc);
       yv[it] = *reinterpret_cast<const f32x4*>(p.yn + r * D + 4 * qc);
     }
 #pragma unroll
     for (int it = 0; it < ND; ++it) {
-      const size_t r = row0 + min(dt0 + it * (kThreads / SQ), Lc - 1);
+      const size_t r = row0 + min(dtok(it), Lc - 1);
       dv[it] = *reinterpret_cast<const f32x4*>(p.d_o + r * D + r0 + 4 * dq);
+    }
+    if (wave == 0) {
+      const size_t r = row0 + min(lane, Lc - 1);
+      gam_n = p.gamma[r];
+      bet_n = p.beta[r];
+      nu_n = p.nu[r];
     }
   };
   f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -390,16 +412,23 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
         *reinterpret_cast<u16x4*>(snT + col * D + row) = st;
       }
     if (wave == 0) {
-      chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
-      wt[lane] = expf(bcum[lane]);
-      nus[lane] = lane < Lc ? p.nu[row0 + lane] : 0.f;
+      float lg = lane < Lc ? logf(gam_n) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(lg, o, 64);
+        if (lane >= o) lg += t;
+      }
+      bcum[lane] = lg;
+      betas[lane] = lane < Lc ? bet_n : 0.f;
+      wt[lane] = expf(lg);
+      nus[lane] = lane < Lc ? nu_n : 0.f;
     }
     __syncthreads();
     // y_t = nu_t * yn_t: X^T, Y^T into sB1; -(w Y)^T, -(w X)^T of the stripe into sA1;
     // stripe 0 also sums this thread's dims of dlambda = -sum_t y_t * x_t
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-      const int t = qt0 + it * (kThreads / Q);
+      const int t = M::tok(it);
       const bool in = t < Lc;
       const float w = in ? wt[t] : 0.f, nu = in ? nus[t] : 0.f, ex = in ? 1.f : 0.f;
 #pragma unroll
@@ -417,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int it = 0; it < ND; ++it) {
-      const int t = dt0 + it * (kThreads / SQ);
+      const int t = dtok(it);
       const float w = t < Lc ? wt[t] : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) sA2[(4 * dq + u) * LC + t] = bf(w * dv[it][u]);
@@ -440,8 +469,9 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     lam_s[threadIdx.x] = lam;
     __syncthreads();
     if (threadIdx.x < Q) {
-      f32x4 acc = lam_s[threadIdx.x];
-      for (int r = 1; r < kThreads / Q; ++r) acc += lam_s[threadIdx.x + r * Q];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < kThreads; ++r)
+        if (((r >> 3) % Q) == (int)threadIdx.x) acc += lam_s[r];
       *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * threadIdx.x) = acc;
     }
   }
