@@ -229,7 +229,7 @@ mesa_status check_bwd(const mesa_fwd_desc* d) {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct BwdLayout {
-  size_t fwd, rhs, nu, yn, oscr, snap, lam, total;
+  size_t fwd, rhs, nu, yn, snap, lam, total;
 };
 
 BwdLayout bwd_layout(const mesa_fwd_desc* d) {
@@ -241,7 +241,6 @@ BwdLayout bwd_layout(const mesa_fwd_desc* d) {
   L.rhs = off; off = align256(off + BH * T * D * 2);
   L.nu = off; off = align256(off + BH * T * 4);
   L.yn = off; off = align256(off + BH * T * D * 4);
-  L.oscr = off; off = align256(off + BH * T * D * 4);
   L.snap = off; off = align256(off + 3 * BH * NC * D * D * 2);
   L.lam = off; off = align256(off + BH * D * 4);
   L.total = off;
@@ -305,10 +304,10 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
   if (any) {
     // 2. right-hand sides of the adjoint systems
     if (mesa::launch_bwd(0, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
-    // 3. adjoint solves by the forward CG (read-out to scratch)
+    // 3. adjoint solves by the forward CG (solutions only)
     mesa::CgParams cp{};
     cp.q = bp.rhs; cp.k = k; cp.v = v; cp.gamma = gamma; cp.beta = beta; cp.lam = lambda;
-    cp.hb = bp.hb; cp.gb = bp.gb; cp.o = reinterpret_cast<float*>(ws + L.oscr); cp.steps = adj_steps;
+    cp.hb = bp.hb; cp.gb = bp.gb; cp.o = nullptr; cp.steps = adj_steps;
     cp.x_out = reinterpret_cast<float*>(ws + L.yn);
     cp.unscaled = reinterpret_cast<int32_t*>(ws + 2 * snap);
     cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;

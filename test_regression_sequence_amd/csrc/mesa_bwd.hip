@@ -25,7 +25,8 @@
 //   bwd_dx_kernel    per chunk: dx = Gamma (d_O Gb) + (W o (d_O V^T)) K with
 //                    W_tj = e^{b_t-b_j} beta_j [j<=t]; writes dx/||dx|| (bf16)
 //                    and ||dx||, the right-hand sides of the adjoint CG (the
-//                    forward CG kernels, so the stopping test is relative).
+//                    forward CG kernels without their read-out; normalised
+//                    right-hand sides make the stopping test relative).
 //   bwd_scan_kernel  per stripe of 32 state rows of a sequence, chunks
 //                    backwards (the next chunk's x, y, d_o loaded while the
 //                    current one's products run): the adjoints arriving at a

@@ -378,6 +378,7 @@ void cg_bf16_kernel(CgParams p) {
   };
 
   for_tiles(solve_tile);
+  if (!p.o) return;  // solutions only (the backward's adjoint solves)
 
   // Gb and the (weighted) value columns replace Hb and the key columns (the
   // key rows stay: the scores of x are against the keys).

@@ -280,7 +280,8 @@ void cg_bf16_unscaled_kernel(CgParams p) {
 
     // ---- read-out o_t = Gamma_t Gb x_t + sum_j W_tj (k_j . x_t) v_j ------------------
     // Gb and the value columns replace Hb and the key columns (the key rows stay:
-    // the scores of x are against the keys).
+    // the scores of x are against the keys).  No read-out without o (solutions only).
+    if (p.o) {
     load_state(p.gb);
     {
       bf16x8 vr[NW][NM];
@@ -306,6 +307,7 @@ void cg_bf16_unscaled_kernel(CgParams p) {
         for (int a = 0; a < ND; ++a)
           *reinterpret_cast<f32x4*>(p.o + (row0 + tloc) * D + 16 * a + 4 * g) = acc[a];
       }
+    }
     }
     __syncthreads();  // the next chunk rewrites the gates and Lambda in LDS
   }

@@ -62,7 +62,7 @@ struct CgParams {
   const float* lam;      // [H, D]
   const void* hb;        // snapshots written by the scan
   const void* gb;
-  float* o;              // [BH, T, D]
+  float* o;              // [BH, T, D]; null on the bf16 path: solutions only, no read-out
   int32_t* steps;        // [BH, T] or null
   float* x_out;          // [BH, T, D] or null
   int32_t* unscaled;     // [BH, NC] bf16 path: chunks left to the unscaled kernel
