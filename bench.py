@@ -172,6 +172,20 @@ def bench_decode(cfg, steps, warmup):
     nbytes = pairs * decode_bytes_per_pair(cfg.d, in_bytes) + cfg.H * cfg.d * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
 
+    # the same step with a full symmetric positive definite Lambda per head
+    from test_regression_sequence_amd.inputs import make_full_lambda
+    lam_full = torch.from_numpy(make_full_lambda(cfg.H, cfg.d, cfg.seed)).to(dev)
+
+    def step_lfull():
+        i = next_copy()
+        mesa.decode_step_ex(q, k, v, gamma, beta, lam_full, hs_full[i], gs[i], max_steps=cfg.max_steps,
+                            tol=cfg.tol, out={"o": o, "steps": st})
+
+    for _ in range(max(1, warmup)):
+        step_lfull()
+    ms_lf = time_events(step_lfull, steps)
+    n_lf = st.cpu().numpy()
+
     # the same step with H in the packed-symmetric layout (blocked upper triangle)
     hs_sym = [mesa.sym_pack(h) for h in hs_full]
     del hs_full
@@ -203,6 +217,13 @@ def bench_decode(cfg, steps, warmup):
         "cg_steps_first_call_mean": round(float(n_first.mean()), 2),
         "cg_steps_mean": round(float(n.mean()), 2),
         "state_copies": DECODE_STATE_COPIES,
+        "full_lambda": {
+            "lambda": "full symmetric positive definite per head (read through the cache, shared by the sequences)",
+            "us_per_step": round(ms_lf * 1e3, 2),
+            "achieved_GBs": round(nbytes / (ms_lf * 1e-3) / 1e9, 1),
+            "frac": round(nbytes / (ms_lf * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "cg_steps_mean": round(float(n_lf.mean()), 2),
+        },
         "packed_h": {
             "layout": "H as 16x16 blocks on and above the block diagonal (36 of 64 at d=128)",
             "us_per_step": round(ms_s * 1e3, 2),

@@ -264,6 +264,31 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d,
                              float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- general decode step --------------------------------------------------------
+ *
+ * Every decode variant in one call, with the Lambda of the pages' objective
+ * either diagonal or a full symmetric positive definite matrix per head
+ * ("technical summary / Mesa layer": Lambda is a symmetric positive definite
+ * regulariser):
+ *
+ *   lambda       [H, dk] fp32 (lambda_full = 0: the diagonal) or
+ *                [H, dk, dk] fp32 (lambda_full = 1: symmetric positive definite,
+ *                row-major; the kernel relies on its symmetry)
+ *   h_packed     0: h_state [N, H, dk, dk]; 1: [N, H, mesa_sym_state_floats(dk)]
+ *   x_state      [N, H, dk] fp32 in/out, or NULL: as in mesa_decode_step_warm
+ *                (CG starts at x_state and leaves the solution there), or a
+ *                cold start from 0
+ *   x_out        [N, H, dk] fp32 out or NULL (cold start only)
+ * Everything else as in mesa_decode_step.  Errors: MESA_ERR_INVALID_ARG for
+ * flags other than 0/1, or x_out given together with x_state. */
+mesa_status mesa_decode_step_ex(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                const void* q, const void* k, const void* v, mesa_dtype in_dtype,
+                                const float* gamma, const float* beta,
+                                const float* lambda, int32_t lambda_full,
+                                float* h_state, int32_t h_packed, float* g_state, float* x_state,
+                                float* o, int32_t* steps, float* x_out,
+                                int32_t max_steps, float tol, hipStream_t stream);
+
 /* ---- query/key preprocessing -------------------------------------------------
  *
  * MesaNet page, "architecture" section: queries and keys are normalised and

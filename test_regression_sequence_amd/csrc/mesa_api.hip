@@ -150,7 +150,7 @@ mesa_status mesa_fwd_solve(const mesa_fwd_desc* d, const void* q, const void* k,
 
 namespace {
 
-mesa_status decode_impl(bool symh, bool warm, int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
+mesa_status decode_impl(bool symh, bool warm, bool lam_full, int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q,
                         const void* k, const void* v, mesa_dtype in_dtype, const float* gamma,
                         const float* beta, const float* lambda, float* h_state, float* g_state,
                         float* o, int32_t* steps, float* x_out, int32_t max_steps, float tol,
@@ -170,6 +170,7 @@ mesa_status decode_impl(bool symh, bool warm, int32_t N, int32_t H, int32_t dk, 
   dp.q = q; dp.k = k; dp.v = v; dp.gamma = gamma; dp.beta = beta; dp.lam = lambda;
   dp.h = h_state; dp.g = g_state; dp.o = o; dp.steps = steps; dp.x_out = x_out;
   dp.x0 = warm ? x_out : nullptr;
+  dp.lam_full = lam_full ? 1 : 0;
   dp.P = N * H; dp.H = H; dp.max_steps = max_steps;
   dp.tol2 = tol > 0.f ? tol * tol : -1.f;
   const hipError_t e = mesa::launch_decode(in_dtype == MESA_BF16, dk, symh, warm, dp, stream);
@@ -192,7 +193,7 @@ mesa_status mesa_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, const
                              const float* beta, const float* lambda, float* h_state,
                              float* g_state, float* o, int32_t* steps, float* x_out,
                              int32_t max_steps, float tol, hipStream_t stream) {
-  return decode_impl(false, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state, g_state, o,
+  return decode_impl(false, false, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state, g_state, o,
                      steps, x_out, max_steps, tol, stream);
 }
 
@@ -201,7 +202,7 @@ mesa_status mesa_decode_step_symh(int32_t N, int32_t H, int32_t dk, int32_t dv, 
                                   const float* beta, const float* lambda, float* h_sym,
                                   float* g_state, float* o, int32_t* steps, float* x_out,
                                   int32_t max_steps, float tol, hipStream_t stream) {
-  return decode_impl(true, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_sym, g_state, o,
+  return decode_impl(true, false, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_sym, g_state, o,
                      steps, x_out, max_steps, tol, stream);
 }
 
@@ -211,8 +212,20 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv, 
                                   float* g_state, float* x_state, float* o, int32_t* steps,
                                   int32_t max_steps, float tol, hipStream_t stream) {
   if (h_packed != 0 && h_packed != 1) return MESA_ERR_INVALID_ARG;
-  return decode_impl(h_packed == 1, true, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state,
+  return decode_impl(h_packed == 1, true, false, N, H, dk, dv, q, k, v, in_dtype, gamma, beta, lambda, h_state,
                      g_state, o, steps, x_state, max_steps, tol, stream);
+}
+
+mesa_status mesa_decode_step_ex(int32_t N, int32_t H, int32_t dk, int32_t dv, const void* q, const void* k,
+                                const void* v, mesa_dtype in_dtype, const float* gamma, const float* beta,
+                                const float* lambda, int32_t lambda_full, float* h_state, int32_t h_packed,
+                                float* g_state, float* x_state, float* o, int32_t* steps, float* x_out,
+                                int32_t max_steps, float tol, hipStream_t stream) {
+  if (h_packed != 0 && h_packed != 1) return MESA_ERR_INVALID_ARG;
+  if (lambda_full != 0 && lambda_full != 1) return MESA_ERR_INVALID_ARG;
+  if (x_state && x_out) return MESA_ERR_INVALID_ARG;  // a warm step returns its solution in x_state
+  return decode_impl(h_packed == 1, x_state != nullptr, lambda_full == 1, N, H, dk, dv, q, k, v, in_dtype, gamma,
+                     beta, lambda, h_state, g_state, o, steps, x_state ? x_state : x_out, max_steps, tol, stream);
 }
 
 }  // extern "C"

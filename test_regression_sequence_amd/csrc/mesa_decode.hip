@@ -24,6 +24,10 @@
 // pair by the caller) with r_0 = q - (H + Lambda) x_0, one more product with
 // H + Lambda that is not counted as a step; the solution is written back in
 // place of x_0.
+// A full symmetric positive definite Lambda (DecodeParams::lam_full, [H, D, D])
+// is added to the register copy of H after H is written back, so the CG runs
+// on H + Lambda directly; the per-head Lambda is shared by all sequences of a
+// head and read through the cache.
 // The update forms k_r*k_j before scaling and is one explicit FMA per element,
 // gamma*h + (beta*(k_r*k_j)), so an exactly symmetric H stays exactly
 // symmetric and every variant of the kernel rounds the same way.
@@ -166,9 +170,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   }
 
   // ---- CG on (H + Lambda) x = q -------------------------------------------------------
+  const bool lam_full = p.lam_full != 0;
+  if (lam_full) {
+    const char* Lb = reinterpret_cast<const char*>(p.lam + (size_t)h * D * D);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) hreg[i] += *reinterpret_cast<const f32x4*>(Lb + voff + i * D * 4);
+  }
   float xv[EPL], rv[EPL], pv[EPL], lv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) lv[e] = lam_s[lane + 64 * e];
+  for (int e = 0; e < EPL; ++e) lv[e] = lam_full ? 0.f : lam_s[lane + 64 * e];
   float* mypb = pb[wave];
   // w = (H + Lambda) u for a vector u that every wave holds whole: this wave's
   // rows give column sums for all columns, the waves' parts meet in part2[buf]

@@ -80,7 +80,7 @@ struct DecodeParams {
   const void* v;
   const float* gamma;    // [P]
   const float* beta;
-  const float* lam;      // [H, D]
+  const float* lam;      // [H, D] diagonal, or [H, D, D] with lam_full
   float* h;              // [P, D, D] in/out
   float* g;              // [P, D, D] in/out
   float* o;              // [P, D]
@@ -89,6 +89,7 @@ struct DecodeParams {
   const float* x0;       // [P, D] CG start (warm variant only; may alias x_out)
   int P, H, max_steps;
   float tol2;
+  int lam_full;          // lam is a full symmetric matrix per head
 };
 
 // Query/key preprocessing: index 0 = queries, 1 = keys.

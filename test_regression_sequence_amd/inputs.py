@@ -35,7 +35,8 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
-    "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs", "round_to_bf16",
+    "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs",
+    "make_full_lambda", "round_to_bf16",
     "bf16_bits", "bits_to_f32",
 ]
 
@@ -338,6 +339,24 @@ def make_bwd_inputs(cfg: FwdConfig) -> dict:
     h0 = (0.5 * (h0 + h0.transpose(0, 1, 3, 2))).astype(np.float32)
     g0 = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32)
     return dict(d_o=d_o, d_hfinal=d_hfinal, d_gfinal=d_gfinal, h0=h0, g0=g0)
+
+
+def make_full_lambda(H: int, d: int, seed: int) -> np.ndarray:
+    """A full symmetric positive definite Lambda per head, ``[H, d, d]`` fp32.
+
+    Lambda = 0.5 M M^T / d + diag(u), M ~ N(0, 1), u ~ U(0.25, 1): the
+    diagonal distribution of the workloads plus a random positive semi-definite
+    coupling, symmetrised after the fp32 cast.  Stream ``default_rng([seed, 5])``
+    in the order M, u.
+    """
+    rng = np.random.default_rng([seed, 5])
+    M = rng.standard_normal((H, d, d))
+    u = rng.uniform(0.25, 1.0, (H, d))
+    lam = 0.5 * np.matmul(M, M.transpose(0, 2, 1)) / d
+    idx = np.arange(d)
+    lam[:, idx, idx] += u
+    lam = lam.astype(np.float32)
+    return (0.5 * (lam + lam.transpose(0, 2, 1))).astype(np.float32)
 
 
 def small_fwd(B=1, H=2, T=200, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0,

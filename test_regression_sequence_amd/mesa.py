@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.mesa_decode_step_warm.restype = ctypes.c_int
         L.mesa_decode_step_warm.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, P, I32,
                                             P, P, P, P, I32, F, P]
+        L.mesa_decode_step_ex.restype = ctypes.c_int
+        L.mesa_decode_step_ex.argtypes = [I32, I32, I32, I32, P, P, P, ctypes.c_int, P, P, P, I32, P, I32,
+                                          P, P, P, P, P, I32, F, P]
         L.mesa_bwd_workspace_bytes.restype = S
         L.mesa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdDesc)]
         L.mesa_bwd_chunked.restype = ctypes.c_int
@@ -390,4 +393,37 @@ def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps
                                _ptr(res.get("adj_steps")), _ptr(workspace), ctypes.c_size_t(wbytes),
                                _stream(stream))
     _check(code_, "mesa_bwd_chunked")
+    return res
+
+
+def decode_step_ex(q, k, v, gamma, beta, lam, h_state, g_state, *, x_state=None, packed_h: bool = False,
+                   max_steps: int = 32, tol: float = 1e-4, return_steps: bool = True, return_x: bool = False,
+                   out=None, stream=None) -> dict:
+    """The general decode step: lam [H, d] (diagonal) or [H, d, d] (full symmetric
+    positive definite); h_state full or packed (packed_h); x_state [N, H, d] for a
+    warm start (overwritten with the solution) or None for a cold start."""
+    N, H, d = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, H, d), q.dtype)
+    _need(gamma, "gamma", (N, H), torch.float32)
+    _need(beta, "beta", (N, H), torch.float32)
+    full = lam.dim() == 3
+    _need(lam, "lam", (H, d, d) if full else (H, d), torch.float32)
+    _need(h_state, "h_state", (N, H, sym_state_floats(d)) if packed_h else (N, H, d, d), torch.float32)
+    _need(g_state, "g_state", (N, H, d, d), torch.float32)
+    if x_state is not None:
+        _need(x_state, "x_state", (N, H, d), torch.float32)
+    dev = q.device
+    out = dict(out or {})
+    res = {"o": out.get("o") if out.get("o") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)}
+    if return_steps:
+        res["steps"] = out.get("steps") if out.get("steps") is not None else torch.empty((N, H), device=dev, dtype=torch.int32)
+    if return_x and x_state is None:
+        res["x"] = out.get("x") if out.get("x") is not None else torch.empty((N, H, d), device=dev, dtype=torch.float32)
+    code_ = lib().mesa_decode_step_ex(N, H, d, d, _ptr(q), _ptr(k), _ptr(v), code, _ptr(gamma), _ptr(beta),
+                                      _ptr(lam), 1 if full else 0, _ptr(h_state), 1 if packed_h else 0,
+                                      _ptr(g_state), _ptr(x_state), _ptr(res["o"]), _ptr(res.get("steps")),
+                                      _ptr(res.get("x")), int(max_steps), float(tol), _stream(stream))
+    _check(code_, "mesa_decode_step_ex")
     return res

@@ -173,3 +173,18 @@ def test_preprocess_validation():
     assert call(qo=A + 0x100000) == 1        # output over the other raw input
     assert call(qh=Bp + 0x400000, qho=Bp + 0x400000) == 1  # history out over history in
     assert call(B=0) == 0
+
+
+def test_general_decode_validation():
+    L = mesa.lib()
+    P = ctypes.c_void_p
+
+    def call(lam_full=0, h_packed=0, x_state=0, x_out=0):
+        return L.mesa_decode_step_ex(2, 2, 128, 128, P(FAKE), P(FAKE), P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE),
+                                     lam_full, P(FAKE), h_packed, P(FAKE), P(x_state) if x_state else None,
+                                     P(FAKE), None, P(x_out) if x_out else None, 8, ctypes.c_float(1e-4), None)
+
+    assert call(lam_full=2) == 1
+    assert call(h_packed=3) == 1
+    assert call(x_state=FAKE, x_out=FAKE) == 1
+    assert call(x_state=FAKE + 4) == 3
