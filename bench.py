@@ -310,26 +310,28 @@ def bench_backward(cfg, steps, warmup):
     gamma, beta, lam = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta", "lam"))
     d_o = torch.from_numpy(g["d_o"]).cuda()
     del x, g
+    ws = torch.empty(mesa.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, cfg.max_steps, cfg.tol),
+                     device="cuda", dtype=torch.uint8)
+    # the forward runs with the backward's workspace and leaves its boundary states there
     f = mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
-                         return_x=True)
+                         return_x=True, workspace=ws)
     res = mesa.bwd_chunked(q, k, v, gamma, beta, lam, f["x"], d_o, chunk=cfg.chunk,
-                           max_steps=cfg.max_steps, tol=cfg.tol)
-    ws = torch.empty(int(mesa.lib().mesa_bwd_workspace_bytes(ctypes.byref(
-        mesa.make_desc(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, cfg.max_steps, cfg.tol, 1)))),
-        device="cuda", dtype=torch.uint8)
+                           max_steps=cfg.max_steps, tol=cfg.tol, workspace=ws, states_in_workspace=True)
 
-    def step():
-        mesa.bwd_chunked(q, k, v, gamma, beta, lam, f["x"], d_o, chunk=cfg.chunk,
-                         max_steps=cfg.max_steps, tol=cfg.tol, out=res, workspace=ws)
+    def step(kept):
+        mesa.bwd_chunked(q, k, v, gamma, beta, lam, f["x"], d_o, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                         tol=cfg.tol, out=res, workspace=ws, states_in_workspace=kept)
 
     for _ in range(warmup):
-        step()
-    ms = time_events(step, steps)
+        step(True)
+    ms_kept = time_events(lambda: step(True), steps)
+    ms = time_events(lambda: step(False), steps)
     tokens = cfg.B * cfg.H * cfg.T
     return {
         "workload": f"backward: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} {cfg.dtype}, "
                     f"{cfg.max_steps} CG steps per solve",
         "ms_per_call": round(ms, 4),
+        "ms_per_call_states_kept": round(ms_kept, 4),
         "token_heads_per_s": round(tokens / (ms * 1e-3), 1),
     }
 

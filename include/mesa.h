@@ -246,9 +246,13 @@ mesa_status mesa_decode_step_warm(int32_t N, int32_t H, int32_t dk, int32_t dv,
  *   dh0, dg0      fp32 [B, H, d, d] out or NULL; dh0 is symmetric (h0 is a
  *                 symmetric state)
  *   adj_steps     int32 [B, H, T] out or NULL: CG steps of the adjoint solves
- *   workspace     mesa_bwd_workspace_bytes(desc) bytes (it recomputes the
- *                 forward's boundary states; nothing from the forward call's
- *                 workspace is needed)
+ *   states_in_workspace  0: the call recomputes the forward's boundary
+ *                 states; 1: the forward call ran with this same workspace
+ *                 (its first mesa_fwd_workspace_bytes(desc) bytes are the
+ *                 forward's workspace layout) and the states it left there
+ *                 are used (same descriptor, same k, v, gamma, beta, h0, g0)
+ *   workspace     mesa_bwd_workspace_bytes(desc) bytes, which is at least
+ *                 mesa_fwd_workspace_bytes(desc)
  * The products inside use bf16 operands with fp32 accumulation, like the
  * forward's bf16 path.  Asynchronous on `stream`; device pointers, 16-byte
  * aligned; validation failures write nothing. */
@@ -262,6 +266,7 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d,
                              const float* d_hfinal, const float* d_gfinal,
                              float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
                              float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                             int32_t states_in_workspace,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- general decode step --------------------------------------------------------

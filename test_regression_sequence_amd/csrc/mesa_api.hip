@@ -275,9 +275,11 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
                              const float* d_hfinal, const float* d_gfinal,
                              float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
                              float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             int32_t states_in_workspace, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   const mesa_status st = check_bwd(d);
   if (st != MESA_OK) return st;
+  if (states_in_workspace != 0 && states_in_workspace != 1) return MESA_ERR_INVALID_ARG;
   const bool any = d->T > 0;
   if (!lambda || !dlambda) return MESA_ERR_INVALID_ARG;
   if (any && (!q || !k || !v || !gamma || !beta || !x || !d_o || !dq || !dk || !dv || !dgamma || !dbeta))
@@ -293,7 +295,8 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
   const int D = d->dk, C = d->chunk, BH = d->B * d->H;
   const int NC = (d->T + C - 1) / C;
   // 1. the forward's boundary states, into the forward part of the workspace
-  if (any) {
+  //    (unless the forward call left them there)
+  if (any && !states_in_workspace) {
     const mesa_status s1 = fwd_impl(kScan, d, nullptr, k, v, gamma, beta, nullptr, h0, g0, nullptr, nullptr,
                                     nullptr, nullptr, nullptr, ws, mesa_fwd_workspace_bytes(d), stream);
     if (s1 != MESA_OK) return s1;

@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.mesa_bwd_workspace_bytes.restype = S
         L.mesa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdDesc)]
         L.mesa_bwd_chunked.restype = ctypes.c_int
-        L.mesa_bwd_chunked.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 21 + [P, S, P]
+        L.mesa_bwd_chunked.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 21 + [I32, P, S, P]
         L.mesa_qk_preprocess.restype = ctypes.c_int
         L.mesa_qk_preprocess.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P, P, F,
                                          P, P, P, P, P]
@@ -348,13 +348,22 @@ def qk_preprocess(q_raw, k_raw, w_q, w_k, *, q_hist=None, k_hist=None, eps: floa
     return res
 
 
+def bwd_workspace_bytes(B, H, T, d, chunk, max_steps, tol, dtype_code=1) -> int:
+    """Bytes of the backward's workspace (also a valid forward workspace)."""
+    desc = make_desc(B, H, T, d, chunk, max_steps, tol, dtype_code)
+    return int(lib().mesa_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
 def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps: int = 30,
                 tol: float = 0.0, h0=None, g0=None, d_hfinal=None, d_gfinal=None,
                 state_grads: bool = False, return_steps: bool = False, out=None,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                workspace: Optional[torch.Tensor] = None, states_in_workspace: bool = False,
+                stream=None) -> dict:
     """Backward of fwd_chunked: x is the forward's solutions (its return_x output),
     d_o [B, H, T, d] fp32 the gradient at o.  Returns dq, dk, dv [B, H, T, d],
-    dgamma, dbeta [B, H, T], dlam [H, d] (fp32) and, with state_grads, dh0, dg0."""
+    dgamma, dbeta [B, H, T], dlam [H, d] (fp32) and, with state_grads, dh0, dg0.
+    states_in_workspace: the forward ran with ``workspace`` (bwd_workspace_bytes
+    long) and left its boundary states there, so they are not recomputed."""
     B, H, T, d = q.shape
     code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -390,8 +399,8 @@ def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps
                                _ptr(h0), _ptr(g0), _ptr(x), _ptr(d_o), _ptr(d_hfinal), _ptr(d_gfinal),
                                _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dgamma"]),
                                _ptr(res["dbeta"]), _ptr(res["dlam"]), _ptr(res.get("dh0")), _ptr(res.get("dg0")),
-                               _ptr(res.get("adj_steps")), _ptr(workspace), ctypes.c_size_t(wbytes),
-                               _stream(stream))
+                               _ptr(res.get("adj_steps")), 1 if states_in_workspace else 0, _ptr(workspace),
+                               ctypes.c_size_t(wbytes), _stream(stream))
     _check(code_, "mesa_bwd_chunked")
     return res
 

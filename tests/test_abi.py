@@ -188,3 +188,33 @@ def test_general_decode_validation():
     assert call(h_packed=3) == 1
     assert call(x_state=FAKE, x_out=FAKE) == 1
     assert call(x_state=FAKE + 4) == 3
+
+
+def test_backward_validation():
+    L = mesa.lib()
+    P = ctypes.c_void_p
+    desc = mesa.make_desc(2, 2, 128, 128, 64, 8, 0.0, 1)
+    need = L.mesa_bwd_workspace_bytes(ctypes.byref(desc))
+    assert need >= L.mesa_fwd_workspace_bytes(ctypes.byref(desc))
+    assert L.mesa_bwd_workspace_bytes(ctypes.byref(mesa.make_desc(2, 2, 128, 128, 64, 8, 0.0, 0))) == 0  # fp32
+    assert L.mesa_bwd_workspace_bytes(ctypes.byref(mesa.make_desc(2, 2, 128, 128, 32, 8, 0.0, 1))) == 0  # chunk 32
+
+    def call(desc=desc, flag=0, ws_bytes=need, lam=FAKE, ws=FAKE):
+        ptrs = [P(FAKE)] * 21
+        ptrs[5] = P(lam) if lam else None
+        ptrs[6] = None   # h0
+        ptrs[7] = None   # g0
+        ptrs[10] = None  # d_hfinal
+        ptrs[11] = None  # d_gfinal
+        ptrs[18] = None  # dh0
+        ptrs[19] = None  # dg0
+        ptrs[20] = None  # adj_steps
+        return L.mesa_bwd_chunked(ctypes.byref(desc), *ptrs, flag, P(ws) if ws else None,
+                                  ctypes.c_size_t(ws_bytes), None)
+
+    assert call(flag=2) == 1
+    assert call(lam=0) == 1
+    assert call(ws_bytes=need - 1) == 4
+    assert call(ws=0) == 4
+    assert call(desc=mesa.make_desc(2, 2, 128, 96, 64, 8, 0.0, 1)) == 2
+    assert call(ws=FAKE + 4) == 3

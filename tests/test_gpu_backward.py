@@ -111,3 +111,23 @@ def test_lm_workload_sampled_slice():
     errs = {n: rel_l2(b[n][bi:bi + 1, hi:hi + 1].cpu().numpy(), ref[n])
             for n in ("dq", "dk", "dv", "dgamma", "dbeta")}
     assert all(e <= 2e-2 for e in errs.values()), errs
+
+
+def test_states_kept_from_the_forward_match_recomputed_states():
+    cfg = small_fwd(B=2, H=2, T=200, d=128, chunk=64, dtype="bf16", max_steps=10)
+    x = make_fwd_inputs(cfg)
+    g = make_bwd_inputs(cfg)
+    a = dev_inputs(x)
+    d_o = torch.from_numpy(g["d_o"]).cuda()
+    h0, g0 = torch.from_numpy(g["h0"]).cuda(), torch.from_numpy(g["g0"]).cuda()
+    ws = torch.empty(mesa.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, cfg.max_steps, cfg.tol),
+                     device="cuda", dtype=torch.uint8)
+    f = mesa.fwd_chunked(a["q"], a["k"], a["v"], a["gamma"], a["beta"], a["lam"], chunk=cfg.chunk,
+                         max_steps=cfg.max_steps, tol=cfg.tol, h0=h0, g0=g0, return_x=True, workspace=ws)
+    kw = dict(chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol, h0=h0, g0=g0, state_grads=True)
+    kept = mesa.bwd_chunked(a["q"], a["k"], a["v"], a["gamma"], a["beta"], a["lam"], f["x"], d_o,
+                            workspace=ws, states_in_workspace=True, **kw)
+    fresh = mesa.bwd_chunked(a["q"], a["k"], a["v"], a["gamma"], a["beta"], a["lam"], f["x"], d_o, **kw)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(kept[n], fresh[n]), n
