@@ -247,6 +247,130 @@ __device__ __forceinline__ float square_dot(const uint16_t* a, const uint16_t* b
   return acc;
 }
 
+// Split staging for the gradient kernel: the load halves return registers, so a
+// kernel can issue the loads of several tiles (or of a later phase) at once and
+// write LDS afterwards.  Mappings and row handling as in the helpers above.
+template <int D>
+struct TileF32 { f32x4 v[kC * D / 4 / kThreads]; };
+template <int D>
+struct TileB16 { u16x8 v[kC * D / 8 / kThreads]; };
+template <int D>
+struct ColsF32 { f32x4 v[ColMap<D>::N]; };
+template <int D>
+struct Square { u16x8 v[D * D / 8 / kThreads]; };
+
+template <int D>
+__device__ __forceinline__ TileF32<D> load_tile_f32(const float* src, int Lc) {
+  constexpr int Q = D / 4;
+  TileF32<D> r;
+  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+#pragma unroll
+  for (int it = 0; it < kC * Q / kThreads; ++it)
+    r.v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(t0 + it * (kThreads / Q), Lc - 1) * D + 4 * c4);
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void put_tile_f32(uint16_t* dst, int ld, const TileF32<D>& r, int Lc) {
+  constexpr int Q = D / 4;
+  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+#pragma unroll
+  for (int it = 0; it < kC * Q / kThreads; ++it) {
+    const int t = t0 + it * (kThreads / Q);
+    const float sc = t < Lc ? 1.f : 0.f;
+    u16x4 o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = bf(r.v[it][u] * sc);
+    *reinterpret_cast<u16x4*>(dst + t * ld + 4 * c4) = o;
+  }
+}
+template <int D>
+__device__ __forceinline__ TileB16<D> load_tile_b16(const uint16_t* src, int Lc) {
+  constexpr int E = D / 8;
+  TileB16<D> r;
+  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
+#pragma unroll
+  for (int it = 0; it < kC * E / kThreads; ++it)
+    r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(t0 + it * (kThreads / E), Lc - 1) * D + 8 * c8);
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void put_tile_b16(uint16_t* dst, int ld, const TileB16<D>& r, int Lc) {
+  constexpr int E = D / 8;
+  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
+#pragma unroll
+  for (int it = 0; it < kC * E / kThreads; ++it) {
+    const int t = t0 + it * (kThreads / E);
+    const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = t < Lc ? r.v[it] : zero;
+  }
+}
+template <int D>
+__device__ __forceinline__ ColsF32<D> load_cols_f32(const float* src, int Lc) {
+  using M = ColMap<D>;
+  ColsF32<D> r;
+#pragma unroll
+  for (int it = 0; it < M::N; ++it)
+    r.v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(M::tok(it), Lc - 1) * D + 4 * M::quad());
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void put_cols_f32(uint16_t* dst, int ld, int col0, const ColsF32<D>& r, int Lc,
+                                             const float* row_scale = nullptr) {
+  using M = ColMap<D>;
+  const int c4 = M::quad();
+#pragma unroll
+  for (int it = 0; it < M::N; ++it) {
+    const int t = M::tok(it);
+    const float sc = t < Lc ? (row_scale ? row_scale[t] : 1.f) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(r.v[it][u] * sc);
+  }
+}
+template <int D>
+__device__ __forceinline__ Square<D> load_square(const uint16_t* src) {
+  Square<D> r;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it)
+    r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)(threadIdx.x + it * kThreads) * 8);
+  return r;
+}
+// a row-major square into LDS [D][ld]
+template <int D>
+__device__ __forceinline__ void put_square(uint16_t* dst, int ld, const Square<D>& r) {
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    *reinterpret_cast<u16x8*>(dst + (idx / (D / 8)) * ld + 8 * (idx % (D / 8))) = r.v[it];
+  }
+}
+// a boundary snapshot in fragment order into LDS row-major [D][ld]
+template <int D>
+__device__ __forceinline__ void put_frag(uint16_t* dst, int ld, const Square<D>& r) {
+  constexpr int NM = D / 32;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const int f = idx >> 6, l = idx & 63;
+    const int n = 16 * (f / NM) + (l & 15);
+    const int c0 = 32 * (f % NM) + 4 * (l >> 4);
+    *reinterpret_cast<u16x4*>(dst + n * ld + c0) = u16x4{r.v[it][0], r.v[it][1], r.v[it][2], r.v[it][3]};
+    *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{r.v[it][4], r.v[it][5], r.v[it][6], r.v[it][7]};
+  }
+}
+// <A, B> for a row-major square held in registers and one in LDS [D][ld]; this thread's part
+template <int D>
+__device__ __forceinline__ float dot_square(const Square<D>& a, const uint16_t* b, int ld) {
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const u16x8 w = *reinterpret_cast<const u16x8*>(b + (idx / (D / 8)) * ld + 8 * (idx % (D / 8)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(a.v[it][u]), bf16_to_f32(w[u]), acc);
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------------------------------
 // dx_t = G_t^T d_o_t, normalised right-hand sides of the adjoint solves
 // ---------------------------------------------------------------------------------------
@@ -521,22 +645,40 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
   uint16_t* sMvd = r3 + kC * L2;                // M o Pvd
   const size_t sn = (size_t)chunk * D * D;
 
+  // ---- every load of the first phase at once; wave 0 forms the gates meanwhile ----------
+  const TileB16<D> kt = load_tile_b16<D>(static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
+  const TileB16<D> vt = load_tile_b16<D>(static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
+  const TileF32<D> xt = load_tile_f32<D>(p.x + row0 * D, Lc);
+  const TileF32<D> yt = load_tile_f32<D>(p.yn + row0 * D, Lc);   // y / ||dx||: scaled where used
+  const TileF32<D> dt = load_tile_f32<D>(p.d_o + row0 * D, Lc);
+  const Square<D> hbs = load_square<D>(static_cast<const uint16_t*>(p.hb) + sn);
   if (wave == 0) {
     chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
     nus[lane] = lane < Lc ? p.nu[row0 + lane] : 0.f;
   }
+  put_tile_b16<D>(sK, LD, kt, Lc);
+  put_tile_b16<D>(sV, LD, vt, Lc);
+  put_tile_f32<D>(sX, LD, xt, Lc);
+  put_tile_f32<D>(sY, LD, yt, Lc);
+  put_tile_f32<D>(sDO, LD, dt, Lc);
+  put_frag<D>(r2, LD, hbs);
   __syncthreads();
-  stage_rows_bf16<D>(sK, LD, static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
-  stage_rows_bf16<D>(sV, LD, static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
-  stage_rows_f32<D>(sX, LD, p.x + row0 * D, Lc);
-  stage_rows_f32<D>(sY, LD, p.yn + row0 * D, Lc, nus);
-  stage_rows_f32<D>(sDO, LD, p.d_o + row0 * D, Lc);
-  stage_snapshot<D, false>(r2, LD, static_cast<const uint16_t*>(p.hb) + sn);
-  __syncthreads();
+  // dq = y
+  {
+    constexpr int Q = D / 4;
+    const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
+#pragma unroll
+    for (int it = 0; it < kC * Q / kThreads; ++it) {
+      const int t = t0 + it * (kThreads / Q);
+      if (t < Lc) *reinterpret_cast<f32x4*>(p.dq + (row0 + t) * D + 4 * c4) = yt.v[it] * nus[t];
+    }
+  }
 
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const int trow = 16 * wave;
   // ---- dgamma: suffix terms e^{b_t}(<dH_t, Hb> + <dG_t, Gb>) and the per-chunk ones ------
+  const Square<D> gbs = load_square<D>(static_cast<const uint16_t*>(p.gb) + sn);  // next phase
+  const Square<D> sqs = load_square<D>(p.snap_s + sn);                             // S: <S, Gb>, then staged
   float cpart[4];
   {
     f32x4 hx[NTL];
@@ -555,8 +697,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
     if (lane == 0) red[0][wave] = rh;
   }
   __syncthreads();  // Hb consumed
-  stage_snapshot<D, false>(r2, LD, static_cast<const uint16_t*>(p.gb) + sn);
+  put_frag<D>(r2, LD, gbs);
   __syncthreads();
+  const Square<D> rss = load_square<D>(p.snap_r + sn);  // Rs, staged after the scores
   {
     f32x4 gx[NTL];
 #pragma unroll
@@ -571,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       const float tot = group_sum<16>(cpart[i] + a);  // + <dG_t, Gb> = d_o_t^T Gb x_t
       if (tl == 0) tsuf[t] = t < Lc ? expf(bcum[t]) * tot : 0.f;
     }
-    const float sg = wave_sum(square_dot<D>(p.snap_s + sn, r2, LD));
+    const float sg = wave_sum(dot_square<D>(sqs, r2, LD));
     if (lane == 0) red[1][wave] = sg;
   }
   // ---- reverse-causal scores (t' >= t), masked and decayed ----------------------------
@@ -580,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       pxk[jt] = mma<D>(sK + trow * LD, LD, sX + 16 * jt * LD, LD, z);   // k_t . x_t'
-      pyk[jt] = mma<D>(sK + trow * LD, LD, sY + 16 * jt * LD, LD, z);   // k_t . y_t'
+      pyk[jt] = mma<D>(sK + trow * LD, LD, sY + 16 * jt * LD, LD, z);   // k_t . y_t' / ||dx_t'||
       pvd[jt] = mma<D>(sV + trow * LD, LD, sDO + 16 * jt * LD, LD, z);  // v_t . d_o_t'
     }
     // pairs j <= t': e^{b_t'-b_j} beta_j (<dH_t', k_j k_j^T> + <dG_t', v_j k_j^T>), row sums and column sums
@@ -591,6 +734,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) {
         const int t = trow + 4 * g + i, tp = 16 * jt + tl;
         const float m = tp >= t ? expf(bcum[tp] - bcum[t]) : 0.f;
+        pyk[jt][i] *= nus[tp];
         sA3[t * L2 + tp] = bf(-m * pxk[jt][i]);
         sA3[t * L2 + kC + tp] = bf(-m * pyk[jt][i]);
         sMvd[t * LC + tp] = bf(m * pvd[jt][i]);
@@ -609,23 +753,28 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       if (g == 0) tcol[wave][16 * jt + tl] = cs;
     }
   }
+  // the transposed tiles: loads issued before the barrier
+  const ColsF32<D> ycol = load_cols_f32<D>(p.yn + row0 * D, Lc);
+  const ColsF32<D> xcol = load_cols_f32<D>(p.x + row0 * D, Lc);
+  const ColsF32<D> dcol = load_cols_f32<D>(p.d_o + row0 * D, Lc);
   __syncthreads();  // X, Y, d_O token-major and Gb consumed
   // ---- stored adjoints of the chunk's end, applied to k_t and v_t ---------------------
-  stage_square<D>(r2, LD, p.snap_r + sn);
-  stage_cols_f32<D>(sYX, L2, 0, p.yn + row0 * D, Lc, nus);      // Y^T
-  stage_cols_f32<D>(sYX, L2, kC, p.x + row0 * D, Lc);           // X^T
-  stage_cols_f32<D>(sDOT, LC, 0, p.d_o + row0 * D, Lc);         // d_O^T
+  put_square<D>(r2, LD, rss);
+  put_cols_f32<D>(sYX, L2, 0, ycol, Lc, nus);      // Y^T
+  put_cols_f32<D>(sYX, L2, kC, xcol, Lc);          // X^T
+  put_cols_f32<D>(sDOT, LC, 0, dcol, Lc);          // d_O^T
   __syncthreads();
+  const Square<D> sts = load_square<D>(p.snap_st + sn);
   f32x4 hk[NTL], gk[NTL], gtv[NTL];
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) hk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  stage_square<D>(r2, LD, p.snap_s + sn);
+  put_square<D>(r2, LD, sqs);
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  stage_square<D>(r2, LD, p.snap_st + sn);
+  put_square<D>(r2, LD, sts);
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gtv[nt] = mma<D>(sV + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
@@ -700,20 +849,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
     const float c1 = expf(bcum[kC - 1]) *
                      (0.5f * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + red[1][0] + red[1][1] + red[1][2] + red[1][3]);
     if (lane < Lc) p.dgamma[row0 + lane] = (c1 + A + Sf + pairs - betas[lane] * tdb[lane]) / p.gamma[row0 + lane];
-  }
-  // dq = y
-  {
-    constexpr int Q = D / 4, N = kC * Q / kThreads;
-    const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
-    f32x4 yv[N];
-#pragma unroll
-    for (int it = 0; it < N; ++it)
-      yv[it] = *reinterpret_cast<const f32x4*>(p.yn + (row0 + min(t0 + it * (kThreads / Q), Lc - 1)) * D + 4 * c4);
-#pragma unroll
-    for (int it = 0; it < N; ++it) {
-      const int t = t0 + it * (kThreads / Q);
-      if (t < Lc) *reinterpret_cast<f32x4*>(p.dq + (row0 + t) * D + 4 * c4) = yv[it] * nus[t];
-    }
   }
   (void)h;
 }
