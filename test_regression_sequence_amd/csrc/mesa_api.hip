@@ -254,7 +254,7 @@ BwdLayout bwd_layout(const mesa_fwd_desc* d) {
   L.rhs = off; off = align256(off + BH * T * D * 2);
   L.nu = off; off = align256(off + BH * T * 4);
   L.yn = off; off = align256(off + BH * T * D * 4);
-  L.snap = off; off = align256(off + 3 * BH * NC * D * D * 2);
+  L.snap = off; off = align256(off + 2 * BH * NC * D * D * 2);
   L.lam = off; off = align256(off + BH * D * 4);
   L.total = off;
   return L;
@@ -312,7 +312,6 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
   const size_t sn = (size_t)BH * NC * D * D;
   bp.snap_r = reinterpret_cast<uint16_t*>(ws + L.snap);
   bp.snap_s = bp.snap_r + sn;
-  bp.snap_st = bp.snap_s + sn;
   bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dbeta = dbeta; bp.dgamma = dgamma;
   bp.lam_part = reinterpret_cast<float*>(ws + L.lam);
   bp.dlam = dlambda; bp.dh0 = dh0; bp.dg0 = dg0;

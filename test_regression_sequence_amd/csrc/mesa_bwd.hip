@@ -31,7 +31,7 @@
 //                    backwards (the next chunk's x, y, d_o loaded while the
 //                    current one's products run): the adjoints arriving at a
 //                    chunk's end, Rs = Hhat + Hhat^T and S = Ghat, stored per
-//                    chunk (bf16; S also transposed), then
+//                    chunk (bf16), then
 //                    Rs <- e^{b_e} Rs - sum_t w_t (y_t x_t^T + x_t y_t^T),
 //                    S  <- e^{b_e} S + sum_t w_t d_o_t x_t^T,  w_t = e^{b_t};
 //                    the final values give dh0 = Rs/2 and dg0 = S.
@@ -357,6 +357,57 @@ __device__ __forceinline__ void put_frag(uint16_t* dst, int ld, const Square<D>&
     *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{r.v[it][4], r.v[it][5], r.v[it][6], r.v[it][7]};
   }
 }
+// The same pieces in another order, for a square that is also written transposed: per wave
+// and step, 32 consecutive rows by two adjacent 8-column pieces, so a half-wave's 2-byte
+// transposed writes land in 16 distinct dwords of one row run (no bank conflicts).
+template <int D>
+struct TMap {
+  static_assert(D % 32 == 0, "32-row blocks");
+  static constexpr int RB = D / 32;
+  __device__ static int blk(int it) { return (threadIdx.x >> 6) + (kThreads / 64) * it; }
+  __device__ static int row(int it) { return 32 * (blk(it) % RB) + (threadIdx.x & 31); }
+  __device__ static int c8(int it) { return 2 * (blk(it) / RB) + ((threadIdx.x >> 5) & 1); }
+};
+template <int D>
+__device__ __forceinline__ Square<D> load_square_t(const uint16_t* src) {
+  using M = TMap<D>;
+  Square<D> r;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it)
+    r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)M::row(it) * D + 8 * M::c8(it));
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void put_square_t(uint16_t* dst, int ld, const Square<D>& r) {
+  using M = TMap<D>;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it)
+    *reinterpret_cast<u16x8*>(dst + M::row(it) * ld + 8 * M::c8(it)) = r.v[it];
+}
+// the transpose: dst[c][r] = square[r][c]
+template <int D>
+__device__ __forceinline__ void put_transposed_t(uint16_t* dst, int ld, const Square<D>& r) {
+  using M = TMap<D>;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const int row = M::row(it), c0 = 8 * M::c8(it);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[(c0 + u) * ld + row] = r.v[it][u];
+  }
+}
+template <int D>
+__device__ __forceinline__ float dot_square_t(const Square<D>& a, const uint16_t* b, int ld) {
+  using M = TMap<D>;
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const u16x8 w = *reinterpret_cast<const u16x8*>(b + M::row(it) * ld + 8 * M::c8(it));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(a.v[it][u]), bf16_to_f32(w[u]), acc);
+  }
+  return acc;
+}
+
 // <A, B> for a row-major square held in registers and one in LDS [D][ld]; this thread's part
 template <int D>
 __device__ __forceinline__ float dot_square(const Square<D>& a, const uint16_t* b, int ld) {
@@ -521,20 +572,16 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     // the adjoints arriving at this chunk's end
     uint16_t* snR = p.snap_r + (size_t)chunk * D * D;
     uint16_t* snS = p.snap_s + (size_t)chunk * D * D;
-    uint16_t* snT = p.snap_st + (size_t)chunk * D * D;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const int row = r0 + 16 * rt + 4 * g, col = CW * wave + 16 * ct + tl;
-        u16x4 st;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           snR[(row + ii) * D + col] = bf(R[rt][ct][ii]);
           snS[(row + ii) * D + col] = bf(S[rt][ct][ii]);
-          st[ii] = bf(S[rt][ct][ii]);
         }
-        *reinterpret_cast<u16x4*>(snT + col * D + row) = st;
       }
     if (wave == 0) {
       float lg = lane < Lc ? logf(gam_n) : 0.f;
@@ -678,7 +725,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
   const int trow = 16 * wave;
   // ---- dgamma: suffix terms e^{b_t}(<dH_t, Hb> + <dG_t, Gb>) and the per-chunk ones ------
   const Square<D> gbs = load_square<D>(static_cast<const uint16_t*>(p.gb) + sn);  // next phase
-  const Square<D> sqs = load_square<D>(p.snap_s + sn);                             // S: <S, Gb>, then staged
+  const Square<D> rss = load_square<D>(p.snap_r + sn);                             // Rs: <Rs, Hb>, then staged
+  const Square<D> sqs = load_square_t<D>(p.snap_s + sn);                           // S: <S, Gb>, then staged
   float cpart[4];
   {
     f32x4 hx[NTL];
@@ -687,19 +735,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = trow + 4 * g + i;
-      const float* yrow = p.yn + (row0 + min(t, Lc - 1)) * D;
       float a = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(yrow[16 * nt + tl], hx[nt][i], a);
+      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(bf16_to_f32(sY[t * LD + 16 * nt + tl]), hx[nt][i], a);
       cpart[i] = -nus[t] * a;  // <dH_t, Hb> = -y_t^T Hb x_t
     }
-    const float rh = wave_sum(square_dot<D>(p.snap_r + sn, r2, LD));
+    const float rh = wave_sum(dot_square<D>(rss, r2, LD));
     if (lane == 0) red[0][wave] = rh;
   }
   __syncthreads();  // Hb consumed
   put_frag<D>(r2, LD, gbs);
   __syncthreads();
-  const Square<D> rss = load_square<D>(p.snap_r + sn);  // Rs, staged after the scores
   {
     f32x4 gx[NTL];
 #pragma unroll
@@ -707,14 +753,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = trow + 4 * g + i;
-      const float* drow = p.d_o + (row0 + min(t, Lc - 1)) * D;
       float a = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(drow[16 * nt + tl], gx[nt][i], a);
+      for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(bf16_to_f32(sDO[t * LD + 16 * nt + tl]), gx[nt][i], a);
       const float tot = group_sum<16>(cpart[i] + a);  // + <dG_t, Gb> = d_o_t^T Gb x_t
       if (tl == 0) tsuf[t] = t < Lc ? expf(bcum[t]) * tot : 0.f;
     }
-    const float sg = wave_sum(dot_square<D>(sqs, r2, LD));
+    const float sg = wave_sum(dot_square_t<D>(sqs, r2, LD));
     if (lane == 0) red[1][wave] = sg;
   }
   // ---- reverse-causal scores (t' >= t), masked and decayed ----------------------------
@@ -753,28 +798,41 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       if (g == 0) tcol[wave][16 * jt + tl] = cs;
     }
   }
-  // the transposed tiles: loads issued before the barrier
-  const ColsF32<D> ycol = load_cols_f32<D>(p.yn + row0 * D, Lc);
-  const ColsF32<D> xcol = load_cols_f32<D>(p.x + row0 * D, Lc);
-  const ColsF32<D> dcol = load_cols_f32<D>(p.d_o + row0 * D, Lc);
+  // the transposed tiles come from the token-major ones in LDS: read here, written
+  // over them after the barrier
+  using CM = ColMap<D>;
+  u16x4 ycol[CM::N], xcol[CM::N], dcol[CM::N];
+#pragma unroll
+  for (int it = 0; it < CM::N; ++it) {
+    const int o = CM::tok(it) * LD + 4 * CM::quad();
+    ycol[it] = *reinterpret_cast<const u16x4*>(sY + o);
+    xcol[it] = *reinterpret_cast<const u16x4*>(sX + o);
+    dcol[it] = *reinterpret_cast<const u16x4*>(sDO + o);
+  }
   __syncthreads();  // X, Y, d_O token-major and Gb consumed
   // ---- stored adjoints of the chunk's end, applied to k_t and v_t ---------------------
   put_square<D>(r2, LD, rss);
-  put_cols_f32<D>(sYX, L2, 0, ycol, Lc, nus);      // Y^T
-  put_cols_f32<D>(sYX, L2, kC, xcol, Lc);          // X^T
-  put_cols_f32<D>(sDOT, LC, 0, dcol, Lc);          // d_O^T
+#pragma unroll
+  for (int it = 0; it < CM::N; ++it) {
+    const int t = CM::tok(it), i0 = 4 * CM::quad();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sYX[(i0 + u) * L2 + t] = bf(nus[t] * bf16_to_f32(ycol[it][u]));  // Y^T
+      sYX[(i0 + u) * L2 + kC + t] = xcol[it][u];                        // X^T
+      sDOT[(i0 + u) * LC + t] = dcol[it][u];                            // d_O^T
+    }
+  }
   __syncthreads();
-  const Square<D> sts = load_square<D>(p.snap_st + sn);
   f32x4 hk[NTL], gk[NTL], gtv[NTL];
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) hk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  put_square<D>(r2, LD, sqs);
+  put_square_t<D>(r2, LD, sqs);
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  put_square<D>(r2, LD, sts);
+  put_transposed_t<D>(r2, LD, sqs);  // S^T, from the S held in registers
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gtv[nt] = mma<D>(sV + trow * LD, LD, r2 + 16 * nt * LD, LD, z);

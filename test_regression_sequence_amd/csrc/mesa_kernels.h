@@ -118,9 +118,8 @@ struct BwdParams {
   void* rhs;                // adjoint right-hand sides dx/||dx|| [BH, T, D] bf16
   float* nu;                // ||dx|| [BH, T]
   const float* yn;          // adjoint CG solutions for rhs [BH, T, D]
-  uint16_t* snap_r;         // per chunk: Hhat + Hhat^T, Ghat, Ghat^T at its end [BH*NC, D, D] bf16
+  uint16_t* snap_r;         // per chunk: Hhat + Hhat^T and Ghat at its end [BH*NC, D, D] bf16
   uint16_t* snap_s;
-  uint16_t* snap_st;
   float* dq;                // [BH, T, D]
   float* dk;
   float* dv;
