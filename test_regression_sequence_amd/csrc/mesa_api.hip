@@ -242,7 +242,8 @@ mesa_status check_bwd(const mesa_fwd_desc* d) {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct BwdLayout {
-  size_t fwd, rhs, nu, yn, snap, lam, total;
+  size_t fwd, rhs, nu, yn, snap, lam, seg, segdec, total;
+  int NS, SEG;
 };
 
 BwdLayout bwd_layout(const mesa_fwd_desc* d) {
@@ -255,7 +256,11 @@ BwdLayout bwd_layout(const mesa_fwd_desc* d) {
   L.nu = off; off = align256(off + BH * T * 4);
   L.yn = off; off = align256(off + BH * T * D * 4);
   L.snap = off; off = align256(off + 2 * BH * NC * D * D * 2);
-  L.lam = off; off = align256(off + BH * D * 4);
+  L.NS = mesa::bwd_scan_segments((long long)BH, (int)NC, (int)D);
+  L.SEG = NC > 0 ? (int)((NC + L.NS - 1) / L.NS) : 0;
+  L.lam = off; off = align256(off + BH * L.NS * D * 4);
+  L.seg = off; off = align256(off + BH * 2 * (L.NS - 1) * D * D * 4);
+  L.segdec = off; off = align256(off + BH * (L.NS - 1) * 4);
   L.total = off;
   return L;
 }
@@ -315,7 +320,9 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
   bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dbeta = dbeta; bp.dgamma = dgamma;
   bp.lam_part = reinterpret_cast<float*>(ws + L.lam);
   bp.dlam = dlambda; bp.dh0 = dh0; bp.dg0 = dg0;
-  bp.BH = BH; bp.H = d->H; bp.T = d->T; bp.NC = NC;
+  bp.seg_state = reinterpret_cast<float*>(ws + L.seg);
+  bp.seg_decay = reinterpret_cast<float*>(ws + L.segdec);
+  bp.BH = BH; bp.H = d->H; bp.T = d->T; bp.NC = NC; bp.NS = L.NS; bp.SEG = L.SEG;
   if (any) {
     // 2. right-hand sides of the adjoint systems
     if (mesa::launch_bwd(0, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;

@@ -495,9 +495,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// adjoint scan, chunks backwards; a workgroup owns a stripe of 32 state rows
+// adjoint scan, chunks backwards; a workgroup owns a stripe of 32 state rows of one
+// sequence segment.  With TOTALS it walks segment s >= 1 from a zero state and leaves
+// the segment's total and decay for the carry pass; otherwise it walks segment s from
+// its carry-in state (the final-state adjoint for the last segment), storing snapshots.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool TOTALS>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   constexpr int SR = 32, NSTR = D / SR;          // state rows per workgroup, stripes per sequence
   constexpr int CW = D / 4, NCT = CW / 16;       // state columns per wave, their 16-column tiles
@@ -507,7 +510,17 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   constexpr int Q = M::Q, NQ = M::N;
   constexpr int SQ = SR / 4, ND = kC * SQ / kThreads;  // d_o: the stripe's dims
   static_assert(ND >= 1 && ND * kThreads == kC * SQ, "stripe items per thread");
-  const int bh = blockIdx.x / NSTR, stripe = blockIdx.x % NSTR, r0 = SR * stripe;
+  // XCD-aware decode: the stripes of one (sequence, segment) share blockIdx % 8 and are
+  // dispatched side by side, so the chunk's x and y tiles they all read come through
+  // one L2
+  const int NSP = TOTALS ? p.NS - 1 : p.NS;  // segments walked by this launch
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int stripe = local % NSTR, r0 = SR * stripe;
+  const int sg = (local / NSTR) % NSP + (TOTALS ? 1 : 0);
+  const int bh = (local / NSTR / NSP) * 8 + xcd;
+  if (bh >= p.BH) return;
+  const int cb = sg * p.SEG, ce = min(cb + p.SEG, p.NC);  // this segment's chunks
+  const size_t D2 = (size_t)D * D;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
   const int qc = M::quad();                                        // this thread's dim quad
   const bool own = 4 * qc >= r0 && 4 * qc < r0 + SR;               // quad inside the stripe
@@ -520,6 +533,11 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sA2[SR * LC];  // (w d_O)^T, stripe rows
   __shared__ __attribute__((aligned(16))) f32x4 lam_s[kThreads];
 
+  // start state: zero for a segment total, the final-state adjoint for the last
+  // segment, the carry-in state for an earlier one
+  const bool from_final = !TOTALS && sg == p.NS - 1;
+  const float* carry_r = (!TOTALS && !from_final) ? p.seg_state + (((size_t)bh * 2) * (p.NS - 1) + sg) * D2 : nullptr;
+  const float* carry_s = carry_r ? carry_r + (size_t)(p.NS - 1) * D2 : nullptr;
   f32x4 R[NRT][NCT], S[NRT][NCT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
@@ -529,11 +547,16 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       for (int ii = 0; ii < 4; ++ii) {
         const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
         float rv = 0.f, sv = 0.f;
-        if (p.d_hfinal) {
-          const float* Dh = p.d_hfinal + (size_t)bh * D * D;
-          rv = Dh[row * D + col] + Dh[col * D + row];
+        if (from_final) {
+          if (p.d_hfinal) {
+            const float* Dh = p.d_hfinal + (size_t)bh * D2;
+            rv = Dh[row * D + col] + Dh[col * D + row];
+          }
+          if (p.d_gfinal) sv = p.d_gfinal[(size_t)bh * D2 + row * D + col];
+        } else if (carry_r) {
+          rv = carry_r[row * D + col];
+          sv = carry_s[row * D + col];
         }
-        if (p.d_gfinal) sv = p.d_gfinal[(size_t)bh * D * D + row * D + col];
         R[rt][ct][ii] = rv;
         S[rt][ct][ii] = sv;
       }
@@ -563,26 +586,28 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     }
   };
   f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p.NC > 0) fetch(p.NC - 1);
+  float logdec = 0.f;  // the segment's total log decay
+  if (ce > cb) fetch(ce - 1);
 
-  for (int c = p.NC - 1; c >= 0; --c) {
+  for (int c = ce - 1; c >= cb; --c) {
     const int chunk = bh * p.NC + c;
     const int s = c * kC, Lc = min(kC, p.T - s);
-    const size_t row0 = (size_t)bh * p.T + s;
-    // the adjoints arriving at this chunk's end
-    uint16_t* snR = p.snap_r + (size_t)chunk * D * D;
-    uint16_t* snS = p.snap_s + (size_t)chunk * D * D;
+    if constexpr (!TOTALS) {
+      // the adjoints arriving at this chunk's end
+      uint16_t* snR = p.snap_r + (size_t)chunk * D2;
+      uint16_t* snS = p.snap_s + (size_t)chunk * D2;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int row = r0 + 16 * rt + 4 * g, col = CW * wave + 16 * ct + tl;
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int row = r0 + 16 * rt + 4 * g, col = CW * wave + 16 * ct + tl;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          snR[(row + ii) * D + col] = bf(R[rt][ct][ii]);
-          snS[(row + ii) * D + col] = bf(S[rt][ct][ii]);
+          for (int ii = 0; ii < 4; ++ii) {
+            snR[(row + ii) * D + col] = bf(R[rt][ct][ii]);
+            snS[(row + ii) * D + col] = bf(S[rt][ct][ii]);
+          }
         }
-      }
+    }
     if (wave == 0) {
       float lg = lane < Lc ? logf(gam_n) : 0.f;
 #pragma unroll
@@ -613,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
           sA1[(i - r0) * L2 + t] = bf(-w * ye);
           sA1[(i - r0) * L2 + kC + t] = bf(-w * xe);
         }
-        if (stripe == 0) lam[u] = __builtin_fmaf(-ye, xe, lam[u]);
+        if (!TOTALS && stripe == 0) lam[u] = __builtin_fmaf(-ye, xe, lam[u]);
       }
     }
 #pragma unroll
@@ -623,8 +648,9 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) sA2[(4 * dq + u) * LC + t] = bf(w * dv[it][u]);
     }
-    if (c > 0) fetch(c - 1);  // the next chunk's loads fly during this chunk's products
+    if (c > cb) fetch(c - 1);  // the next chunk's loads fly during this chunk's products
     __syncthreads();
+    logdec += bcum[kC - 1];
     const float decay = expf(bcum[kC - 1]);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
@@ -636,7 +662,24 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       }
     __syncthreads();
   }
-  // this sequence's part of dlambda: the threads sharing a dim quad
+  if constexpr (TOTALS) {
+    // the segment's total from a zero start, and its decay, for the carry pass
+    float* tr = p.seg_state + (((size_t)bh * 2) * (p.NS - 1) + sg - 1) * D2;
+    float* ts = tr + (size_t)(p.NS - 1) * D2;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
+          tr[row * D + col] = R[rt][ct][ii];
+          ts[row * D + col] = S[rt][ct][ii];
+        }
+    if (stripe == 0 && threadIdx.x == 0) p.seg_decay[(size_t)bh * (p.NS - 1) + sg - 1] = expf(logdec);
+    return;
+  }
+  // this segment's part of dlambda: the threads sharing a dim quad
   if (stripe == 0) {
     lam_s[threadIdx.x] = lam;
     __syncthreads();
@@ -644,20 +687,42 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int r = 0; r < kThreads; ++r)
         if (((r >> 3) % Q) == (int)threadIdx.x) acc += lam_s[r];
-      *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * threadIdx.x) = acc;
+      *reinterpret_cast<f32x4*>(p.lam_part + ((size_t)bh * p.NS + sg) * D + 4 * threadIdx.x) = acc;
     }
   }
   // gradients of the initial states
+  if (sg == 0) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
-        if (p.dh0) p.dh0[(size_t)bh * D * D + row * D + col] = 0.5f * R[rt][ct][ii];
-        if (p.dg0) p.dg0[(size_t)bh * D * D + row * D + col] = S[rt][ct][ii];
-      }
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
+          if (p.dh0) p.dh0[(size_t)bh * D2 + row * D + col] = 0.5f * R[rt][ct][ii];
+          if (p.dg0) p.dg0[(size_t)bh * D2 + row * D + col] = S[rt][ct][ii];
+        }
+  }
+}
+
+// Carry pass of a segmented adjoint scan, backwards over the segments: C_{NS-1} is the
+// final-state adjoint and C_{s-1} = Gamma_s C_s + total_s, left in the slot where
+// total_s was (the carry-in state of segment s-1).
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdParams p, int D) {
+  const size_t D2 = (size_t)D * D;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)p.BH * 2 * (long long)D2) return;
+  const int e = (int)(idx % D2), which = (int)((idx / D2) % 2);
+  const int bh = (int)(idx / D2 / 2);
+  const int row = e / D, col = e % D;
+  float c = 0.f;
+  if (which == 0 && p.d_hfinal) c = p.d_hfinal[bh * D2 + row * D + col] + p.d_hfinal[bh * D2 + col * D + row];
+  if (which == 1 && p.d_gfinal) c = p.d_gfinal[bh * D2 + e];
+  for (int sg = p.NS - 1; sg >= 1; --sg) {
+    float* t = p.seg_state + (((size_t)bh * 2 + which) * (p.NS - 1) + sg - 1) * D2 + e;
+    c = __builtin_fmaf(p.seg_decay[(size_t)bh * (p.NS - 1) + sg - 1], c, *t);
+    *t = c;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -917,7 +982,8 @@ __global__ __launch_bounds__(128) void bwd_lambda_kernel(BwdParams p, int D) {
   for (int i = threadIdx.x; i < D; i += 128) {
     float acc = 0.f;
     if (p.NC > 0)
-      for (int b = 0; b < p.BH / p.H; ++b) acc += p.lam_part[(size_t)(b * p.H + h) * D + i];
+      for (int b = 0; b < p.BH / p.H; ++b)
+        for (int sg = 0; sg < p.NS; ++sg) acc += p.lam_part[((size_t)(b * p.H + h) * p.NS + sg) * D + i];
     p.dlam[h * D + i] = acc;
   }
 }
@@ -927,7 +993,19 @@ hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
   const dim3 chunks((unsigned)(p.BH * p.NC));
   switch (phase) {
     case 0: hipLaunchKernelGGL((bwd_dx_kernel<D>), chunks, dim3(kThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)(p.BH * (D / 32))), dim3(kThreads), 0, s, p); break;
+    case 1: {
+      // (sequence, stripe) units padded to whole groups of 8 sequences (one per XCD)
+      const unsigned units = (unsigned)((p.BH + 7) / 8 * 8 * (D / 32));
+      if (p.NS > 1) {
+        hipLaunchKernelGGL((bwd_scan_kernel<D, true>), dim3(units * (unsigned)(p.NS - 1)), dim3(kThreads), 0, s, p);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        const long long n = (long long)p.BH * 2 * D * D;
+        hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      }
+      hipLaunchKernelGGL((bwd_scan_kernel<D, false>), dim3(units * (unsigned)p.NS), dim3(kThreads), 0, s, p);
+      break;
+    }
     case 2:
       if (p.NC > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<D>), chunks, dim3(kThreads), 0, s, p);

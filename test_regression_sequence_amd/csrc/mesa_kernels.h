@@ -125,12 +125,28 @@ struct BwdParams {
   float* dv;
   float* dbeta;             // [BH, T]
   float* dgamma;
-  float* lam_part;          // [BH, D]: -sum_t y_t * x_t per sequence
+  float* lam_part;          // [BH, NS, D]: -sum_t y_t * x_t per sequence segment
   float* dlam;              // [H, D]
   float* dh0;               // [BH, D, D] or null
   float* dg0;
-  int BH, H, T, NC;
+  // adjoint scan of a long sequence in NS segments of SEG chunks (NS = 1: one walk)
+  float* seg_state;         // [BH, 2, NS-1, D*D]: segment totals, then carry-in states
+  float* seg_decay;         // [BH, NS-1]: total decay of segments 1..NS-1
+  int BH, H, T, NC, NS, SEG;
 };
+
+// Segments of the adjoint scan: a sequence is split when there are too few
+// (sequence, 32-row stripe) units to fill the chip (two resident workgroups per CU)
+// and the sequence is long.
+inline int bwd_scan_segments(long long BH, int NC, int D) {
+  const long long units = BH * (D / 32);
+  if (units >= 256 || NC < 128) return 1;
+  long long ns = (512 + units - 1) / units;
+  if (ns > NC / 16) ns = NC / 16;
+  if (ns < 2) return 1;
+  const int seg = (int)((NC + ns - 1) / ns);
+  return (NC + seg - 1) / seg;
+}
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);

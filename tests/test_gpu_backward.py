@@ -72,6 +72,22 @@ def test_gradients_match_oracle(d, T, max_steps, tol, with_states):
         assert gpu["adj_steps"].max() <= max_steps and gpu["adj_steps"].min() >= 1
 
 
+@pytest.mark.parametrize("H,d", [(2, 64), (1, 128)])
+def test_long_sequence_walked_in_segments(H, d):
+    """Few sequences, 129 chunks: the adjoint scan splits each sequence into 8
+    segments (segment totals, a carry pass, then the walk proper).  Slow decay
+    (gamma in (0.99988, 0.999994)) keeps the final-state adjoints and the carries
+    between segments far from zero, so a wrong carry shows in every gradient."""
+    cfg = small_fwd(B=1, H=H, T=8192 + 100, d=d, chunk=64, dtype="bf16", max_steps=6, tol=0.0,
+                    gamma_logit=(9.0, 12.0))
+    x = make_fwd_inputs(cfg)
+    g = make_bwd_inputs(cfg)
+    gpu = run_gpu(cfg, x, g, True)
+    ref = run_oracle(cfg, x, g, gpu, True)
+    errs = {n: rel_l2(gpu[n], ref[n]) for n in NAMES}
+    assert all(e <= 2e-2 for e in errs.values()), errs
+
+
 def test_empty_sequence_passes_final_state_gradients_through():
     cfg = small_fwd(B=1, H=2, T=0, d=64, chunk=64, dtype="bf16", max_steps=8, tol=0.0)
     g = make_bwd_inputs(cfg)
