@@ -94,29 +94,34 @@ def bench_forward(cfg, steps, warmup):
     out = {"o": o, "steps": st}
     kw = dict(chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol, workspace=ws, out=out)
 
-    def step():
-        mesa.fwd_chunked(q, k, v, gamma, beta, lam, **kw)
+    # One step is the forward's two entry points back to back on the current
+    # stream -- the state scan, then the CG solve and read-out -- which are the
+    # kernels one mesa_fwd_chunked call launches.  An event between the two, in
+    # every timed step, gives each kernel's duration over the timed region
+    # itself (the solve's pair also brackets its 4.5 us strong-decay check).
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mesa.fwd_scan(k, v, gamma, beta, chunk=cfg.chunk, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        mesa.fwd_solve(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                       tol=cfg.tol, workspace=ws, o=o, steps=st)
+        if ev is not None:
+            ev[2].record()
 
     for _ in range(warmup):
         step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(step, steps)
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
-
-    # per-kernel durations: events around each of the two launches, same stream
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    scan_ms, cg_ms = [], []
-    for _ in range(max(3, steps // 2)):
-        ev[0].record()
-        mesa.fwd_scan(k, v, gamma, beta, chunk=cfg.chunk, workspace=ws)
-        ev[1].record()
-        mesa.fwd_solve(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps,
-                       tol=cfg.tol, workspace=ws, o=o, steps=st)
-        ev[2].record()
-        torch.cuda.synchronize()
-        scan_ms.append(ev[0].elapsed_time(ev[1]))
-        cg_ms.append(ev[1].elapsed_time(ev[2]))
+    ms = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    cg_ms = [e[1].elapsed_time(e[2]) for e in evs]
     n = st.cpu().numpy()
     return dict(ms=ms, wall_ms=wall, scan_ms=float(np.mean(scan_ms)), cg_ms=float(np.mean(cg_ms)),
                 steps_mean=float(n.mean()), steps_max=int(n.max()), x=x)
