@@ -6,8 +6,9 @@
 // solve (H + Lambda) x = q by conjugate gradient (fixed steps or residual
 // test), emit o = G x.  The step is bound by streaming H and G through HBM
 // (2 * 4 * d^2 bytes read and written per (sequence, head) pair); the CG
-// iterations run on the register-resident H, and with few registers per wave
-// several pairs share each CU, so one pair's solve overlaps others' streams.
+// iterations run on the register-resident H while G's loads are in flight,
+// and two pairs share each CU, so one pair's solve overlaps the other's
+// streams.
 //
 // One workgroup of NW = 4 waves per pair; both states move as 16-byte row
 // segments, every wave instruction covering 1 KB of contiguous memory.
@@ -169,6 +170,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
     }
   }
 
+  // G's loads go out now and land during the solve: waiting for them after it
+  // would leave every pair's G round trip exposed
+  f32x4 greg[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) greg[i] = __builtin_nontemporal_load(at(Gb, i));
   // ---- CG on (H + Lambda) x = q -------------------------------------------------------
   const bool lam_full = p.lam_full != 0;
   if (lam_full) {
@@ -270,9 +276,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   __builtin_amdgcn_s_waitcnt(0xc07f);
 
   // ---- G <- gamma G + beta (v k^T); o = G x ------------------------------------------
-  f32x4 greg[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) greg[i] = __builtin_nontemporal_load(at(Gb, i));
   const f32x4 xq = *reinterpret_cast<const f32x4*>(&mypb[4 * cq]);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
