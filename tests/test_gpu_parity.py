@@ -14,7 +14,7 @@ import torch
 from helpers import dev_inputs, oracle_on_slices, rel_l2
 from test_regression_sequence_amd import mesa
 from test_regression_sequence_amd.inputs import (
-    CONFIGS, make_decode_inputs, make_fwd_inputs, select_slices, small_fwd,
+    CONFIGS, make_bwd_inputs, make_decode_inputs, make_fwd_inputs, select_slices, small_fwd,
 )
 
 pytestmark = pytest.mark.gpu
@@ -197,3 +197,40 @@ def test_small_fixed_steps(dtype, d, chunk, T):
     assert rel_l2(gpu["h_final"].reshape(2, d, d), Hr) < st_tol
     assert rel_l2(gpu["g_final"].reshape(2, d, d), Gr) < st_tol
     assert rel_l2(gpu["x"].reshape(2, T, d), np.stack([r["x_cg"][0, 0] for r in refs])) < TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# the state scan with a whole state per workgroup (B*H >= 128), every slice
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,T", [(64, 200), (128, 130)])
+def test_whole_state_scan_every_slice(d, T):
+    """B*H = 128 (two whole-state workgroups per (b, h)): every slice's final
+    states against the oracle's recurrence, from given initial states, and the
+    outputs of the first and last slices (they read every boundary snapshot of
+    their sequence)."""
+    cfg = small_fwd(B=4, H=32, T=T, d=d, chunk=64, dtype="bf16", max_steps=6)
+    x = make_fwd_inputs(cfg)
+    init = make_bwd_inputs(cfg)  # initial states: h0 = M M^T / d (valid, PSD), g0 ~ N(0, 0.1^2)
+    h0, g0 = init["h0"], init["g0"]
+    gpu = run_fwd(x, return_state=True, h0=torch.from_numpy(h0).cuda(), g0=torch.from_numpy(g0).cuda())
+    from oracle import mesa_forward
+    S = cfg.B * cfg.H
+    Hg, Gg = gpu["h_final"].reshape(S, d, d), gpu["g_final"].reshape(S, d, d)
+    eh, eg = [], []
+    for i in range(S):
+        b, hh = divmod(i, cfg.H)
+        r = mesa_forward(x["q"][b:b + 1, hh:hh + 1], x["k"][b:b + 1, hh:hh + 1], x["v"][b:b + 1, hh:hh + 1],
+                         x["gamma"][b:b + 1, hh:hh + 1], x["beta"][b:b + 1, hh:hh + 1], x["lam"][hh:hh + 1],
+                         max_steps=cfg.max_steps, tol=cfg.tol, h0=h0[b:b + 1, hh:hh + 1],
+                         g0=g0[b:b + 1, hh:hh + 1], exact=False, solve_at=np.zeros(T, bool))
+        eh.append(rel_l2(Hg[i], r["H_final"][0, 0]))
+        eg.append(rel_l2(Gg[i], r["G_final"][0, 0]))
+    assert max(eh) < 1e-4 and max(eg) < 1e-4, (max(eh), max(eg))
+    for i in (0, S - 1):
+        b, hh = divmod(i, cfg.H)
+        r = mesa_forward(x["q"][b:b + 1, hh:hh + 1], x["k"][b:b + 1, hh:hh + 1], x["v"][b:b + 1, hh:hh + 1],
+                         x["gamma"][b:b + 1, hh:hh + 1], x["beta"][b:b + 1, hh:hh + 1], x["lam"][hh:hh + 1],
+                         max_steps=cfg.max_steps, tol=cfg.tol, h0=h0[b:b + 1, hh:hh + 1],
+                         g0=g0[b:b + 1, hh:hh + 1], exact=False, forced_steps=gpu["steps"][b:b + 1, hh:hh + 1])
+        assert rel_l2(gpu["o"][b, hh], r["o_cg"][0, 0]) <= TOL["bf16"]
