@@ -220,33 +220,13 @@ void cg_bf16_kernel(CgParams p) {
 
   // ---- per-tile machinery ----------------------------------------------------------
 
-  // acc[nt] <- Mb U^T + Y^T S^T with S^T the causal key scores of the tile's
-  // tokens (the weights sit in the key columns; only the diagonal block needs
-  // the mask j <= t).  Issue order: score MFMAs, boundary-state MFMAs, then
-  // the mask and packing of the scores (long finished by then), then the
-  // intra-chunk MFMAs; the VALU work on acc comes after all of them, so no
-  // instruction waits on an MFMA issued just before it.
-  // With LAM the boundary-state chains start from (Lambda / Gamma_t) .* u, so
-  // acc = (A_t / Gamma_t) u and the Lambda multiplies issue among the MFMAs.
+  // The causal part of a tile's product: with the score tiles sc[jt] of its
+  // tokens against key tile jt (jt <= w), mask the diagonal block (j <= t),
+  // pack the scores to bf16 and add Y^T S^T to acc[nt] (the key weights sit in
+  // the key columns).
   f32x4 acc[ND];
-  auto matvec = [&](auto wc, auto lamc, const bf16x8* ub, const f32x4* u, const f32x4* lt) {
+  auto add_intra = [&](auto wc, f32x4* sc) {
     constexpr int w = decltype(wc)::value;
-    constexpr bool LAM = decltype(lamc)::value;
-    f32x4 sc[w + 1];
-#pragma unroll
-    for (int jt = 0; jt <= w; ++jt) {
-      sc[jt] = mfma_bf16(kr[jt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int m = 1; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < ND; ++nt) {
-      f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (LAM) c0 = lt[nt] * u[nt];
-      acc[nt] = mfma_bf16(mf[nt][0], ub[0], c0);
-#pragma unroll
-      for (int m = 1; m < NM; ++m) acc[nt] = mfma_bf16(mf[nt][m], ub[m], acc[nt]);
-    }
 #pragma unroll
     for (int jt = 0; jt <= w; ++jt) asm volatile("" : "+v"(sc[jt]));
     bf16x8 sb[w / 2 + 1];
@@ -261,6 +241,26 @@ void cg_bf16_kernel(CgParams p) {
     for (int mj = 0; mj <= w / 2; ++mj)
 #pragma unroll
       for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(kc[nt][mj], sb[mj], acc[nt]);
+  };
+  // acc[nt] <- Mb u + Y^T S^T for a bf16 vector u given as k-blocks ub (the
+  // read-out): score MFMAs, boundary-state MFMAs, then the masked scores'
+  // MFMAs, so no instruction waits on an MFMA issued just before it
+  auto matvec = [&](auto wc, const bf16x8* ub) {
+    constexpr int w = decltype(wc)::value;
+    f32x4 sc[w + 1];
+#pragma unroll
+    for (int jt = 0; jt <= w; ++jt) {
+      sc[jt] = mfma_bf16(kr[jt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int m = 1; m < NM; ++m) sc[jt] = mfma_bf16(kr[jt][m], ub[m], sc[jt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt) {
+      acc[nt] = mfma_bf16(mf[nt][0], ub[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int m = 1; m < NM; ++m) acc[nt] = mfma_bf16(mf[nt][m], ub[m], acc[nt]);
+    }
+    add_intra(wc, sc);
 #pragma unroll
     for (int nt = 0; nt < ND; ++nt) asm volatile("" : "+v"(acc[nt]));
   };
@@ -293,18 +293,41 @@ void cg_bf16_kernel(CgParams p) {
     rho = sum_lane_groups(rho);
     int n = 0;
     bool stopped = false;
+    // the previous step's alpha and beta: its x step and the new direction are
+    // formed block by block at the top of the next iteration, among its MFMAs
+    float alpha_p = 0.f, beta_p = 0.f;
     for (int it = 0; it < p.max_steps; ++it) {
       const bool active = !stopped && rho > 0.f && rho > p.tol2;
       if (!__any(active)) break;
       pin_operands();
-      bf16x8 ub[NM];
+      // per k-block m (the dims of pv[2m], pv[2m+1]): x += alpha_p p, then
+      // p = r + beta_p p in place (three-operand FMA: the two-address form would
+      // tie the result to r, which stays live), its bf16 copy, and every MFMA
+      // that reads that copy -- so block m+1's vector work issues while block
+      // m's MFMAs run
+      f32x4 sc[w + 1];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) ub[m] = pack8(pv[2 * m], pv[2 * m + 1]);
-      matvec(wc, std::true_type{}, ub, pv, lt);
-      // w = acc and p.w, two independent chains
+      for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int a = 2 * m + hh;
+          x[a] += alpha_p * pv[a];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) asm("v_fma_f32 %0, %1, %0, %2" : "+v"(pv[a][i]) : "v"(beta_p), "v"(r[a][i]));
+        }
+        const bf16x8 ub = pack8(pv[2 * m], pv[2 * m + 1]);
+#pragma unroll
+        for (int jt = 0; jt <= w; ++jt) sc[jt] = mfma_bf16(kr[jt][m], ub, m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[jt]);
+#pragma unroll
+        for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(mf[nt][m], ub, m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt]);
+      }
+      add_intra(wc, sc);
+      // + (Lambda / Gamma_t) p, then w = acc and p.w (two independent chains)
       float pw0 = 0.f, pw1 = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][i] = __builtin_fmaf(lt[a][i], pv[a][i], acc[a][i]);
         pw0 += pv[a][0] * acc[a][0];
         pw1 += pv[a][1] * acc[a][1];
         pw0 += pv[a][2] * acc[a][2];
@@ -317,7 +340,6 @@ void cg_bf16_kernel(CgParams p) {
       float rr0 = 0.f, rr1 = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
-        x[a] += alpha * pv[a];
         r[a] -= alpha * acc[a];
         rr0 += r[a][0] * r[a][0];
         rr1 += r[a][1] * r[a][1];
@@ -328,15 +350,14 @@ void cg_bf16_kernel(CgParams p) {
       // a stopped token keeps x and r (alpha = 0); its direction becomes r,
       // which stays finite and is never used again
       const float bet = ok ? rr * __builtin_amdgcn_rcpf(rho) : 0.f;
-      // p <- r + bet p in place (three-operand FMA; the two-address form would
-      // tie the result to r, which stays live, and cost a copy per element)
-#pragma unroll
-      for (int a = 0; a < ND; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) asm("v_fma_f32 %0, %1, %0, %2" : "+v"(pv[a][i]) : "v"(bet), "v"(r[a][i]));
+      alpha_p = alpha;
+      beta_p = bet;
       rho = ok ? rr : rho;
       n += ok ? 1 : 0;
     }
+    // the last step's x update
+#pragma unroll
+    for (int a = 0; a < ND; ++a) x[a] += alpha_p * pv[a];
 #pragma unroll
     for (int a = 0; a < ND; ++a) xs[(w * ND + a) * 64 + lane] = x[a];
     if (valid) {
@@ -362,7 +383,7 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) xb[m] = pack8(x[2 * m], x[2 * m + 1]);
     pin_operands();
-    matvec(wc, std::false_type{}, xb, x, x);
+    matvec(wc, xb);
     if (tloc < Lc) {
 #pragma unroll
       for (int a = 0; a < ND; ++a)
