@@ -28,7 +28,8 @@
 // A full symmetric positive definite Lambda (DecodeParams::lam_full, [H, D, D])
 // is added to the register copy of H after H is written back, so the CG runs
 // on H + Lambda directly; the per-head Lambda is shared by all sequences of a
-// head and read through the cache.
+// head and read through the cache, each thread's strip of it loaded together
+// with the state.
 // The update forms k_r*k_j before scaling and is one explicit FMA per element,
 // gamma*h + (beta*(k_r*k_j)), so an exactly symmetric H stays exactly
 // symmetric and every variant of the kernel rounds the same way.
@@ -136,6 +137,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) hreg[i] = __builtin_nontemporal_load(at(Hb, i));
   }
+  // a full Lambda: this thread's strip of it, in flight with the state
+  const bool lam_full = p.lam_full != 0;
+  f32x4 lreg[RPT];
+  if (lam_full) {
+    const char* Lb = reinterpret_cast<const char*>(p.lam + (size_t)h * D * D);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) lreg[i] = *reinterpret_cast<const f32x4*>(Lb + voff + i * D * 4);
+  }
   if (tid < D) {
     ks[tid] = kv;
     qs[tid] = qv;
@@ -176,11 +185,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) greg[i] = __builtin_nontemporal_load(at(Gb, i));
   // ---- CG on (H + Lambda) x = q -------------------------------------------------------
-  const bool lam_full = p.lam_full != 0;
   if (lam_full) {
-    const char* Lb = reinterpret_cast<const char*>(p.lam + (size_t)h * D * D);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) hreg[i] += *reinterpret_cast<const f32x4*>(Lb + voff + i * D * 4);
+    for (int i = 0; i < RPT; ++i) hreg[i] += lreg[i];
   }
   float xv[EPL], rv[EPL], pv[EPL], lv[EPL];
 #pragma unroll
