@@ -34,7 +34,10 @@
 //                    chunk (bf16), then
 //                    Rs <- e^{b_e} Rs - sum_t w_t (y_t x_t^T + x_t y_t^T),
 //                    S  <- e^{b_e} S + sum_t w_t d_o_t x_t^T,  w_t = e^{b_t};
-//                    the final values give dh0 = Rs/2 and dg0 = S.
+//                    the final values give dh0 = Rs/2 and dg0 = S.  The
+//                    update is linear in (Rs, S), so a long sequence is
+//                    walked in segments: totals from zero, a carry pass
+//                    (bwd_carry_kernel), then each segment from its carry-in.
 //   bwd_grad_kernel  per chunk: Hhat_t, Ghat_t applied to k_t, v_t as
 //                    e^{b_e-b_t} (stored adjoint) k_t plus the chunk's own
 //                    reverse-causal terms, e.g. Ghat_t k_t gains
