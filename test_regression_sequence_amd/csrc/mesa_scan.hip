@@ -18,7 +18,8 @@
 // workgroups per (b, h); the launch picks the split that fills the GPU and
 // maps the workgroups of one (b, h) onto one XCD (they share the chunk's keys
 // in that XCD's L2).  The keys, values and gates of the chunk after next are
-// loaded into registers while the current chunk is processed.  The chunk delta
+// loaded into registers while the current chunk is processed, and the staged
+// operands alternate between two LDS buffers, so a chunk costs one barrier.  The chunk delta
 // K^T diag(w) X is an MFMA contraction over the chunk's tokens: bf16 MFMA for
 // bf16 inputs with the scaled operand split into bf16 hi + lo parts (so the
 // carried fp32 state does not pick up a bf16 rounding of beta*tail*x), fp32
@@ -98,8 +99,9 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   const void* X = which ? p.v : p.k;      // the second factor of the chunk delta
   const size_t rowbase = (size_t)bh * T;
 
-  __shared__ __attribute__((aligned(16))) char lds_a[S::LDS_A];
-  __shared__ __attribute__((aligned(16))) char lds_b[S::LDS_B];
+  // operand staging, double-buffered by chunk parity: one barrier per chunk
+  __shared__ __attribute__((aligned(16))) char lds_a2[2][S::LDS_A];
+  __shared__ __attribute__((aligned(16))) char lds_b2[2][S::LDS_B];
 
   // ---- ownership: unit list of this wave ----------------------------------------
   auto unit_mt = [&](int u, int h) -> int {
@@ -258,8 +260,10 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     const float gamma_c = expf(sum_log);
     seg_log += sum_log;
 
-    // ---- stage operands (LDS is free once every wave finished chunk c-1) -------
-    __syncthreads();
+    // ---- stage operands into the buffer of chunk parity c & 1: every wave
+    // finished chunk c-2's products, which read it, before chunk c-1's barrier
+    char* lds_a = lds_a2[c & 1];
+    char* lds_b = lds_b2[c & 1];
     if constexpr (BF16) {
       __bf16* KT = reinterpret_cast<__bf16*>(lds_a);  // [MROWS][AS]: K^T rows of the owned stripe
       __bf16* XH = reinterpret_cast<__bf16*>(lds_b);  // [D][AS]: (w .* X)^T, hi part
