@@ -530,7 +530,6 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   const int dq = (threadIdx.x >> 3) % SQ;                          // d_o: stripe quad
   auto dtok = [&](int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / SQ + (kThreads / 8 / SQ) * it); };
 
-  __shared__ float bcum[kC], betas[kC], wt[kC], nus[kC];
   __shared__ __attribute__((aligned(16))) uint16_t sA1[SR * L2];  // [(-wY)^T | (-wX)^T], stripe rows
   __shared__ __attribute__((aligned(16))) uint16_t sB1[D * L2];   // [X^T | Y^T], all dims
   __shared__ __attribute__((aligned(16))) uint16_t sA2[SR * LC];  // (w d_O)^T, stripe rows
@@ -566,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
 
   // x, y (all dims), d_o (stripe dims) and the gates of a chunk, into registers
   f32x4 xv[NQ], yv[NQ], dv[ND];
-  float gam_n = 1.f, bet_n = 0.f, nu_n = 0.f;  // wave 0: one token per lane
+  float gam_n = 1.f, nu_n = 0.f;  // one token per lane, in every wave
   auto fetch = [&](int c) {
     const int Lc = min(kC, p.T - c * kC);
     const size_t row0 = (size_t)bh * p.T + c * kC;
@@ -581,10 +580,9 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       const size_t r = row0 + min(dtok(it), Lc - 1);
       dv[it] = *reinterpret_cast<const f32x4*>(p.d_o + r * D + r0 + 4 * dq);
     }
-    if (wave == 0) {
+    {
       const size_t r = row0 + min(lane, Lc - 1);
       gam_n = p.gamma[r];
-      bet_n = p.beta[r];
       nu_n = p.nu[r];
     }
   };
@@ -611,26 +609,24 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
           }
         }
     }
-    if (wave == 0) {
-      float lg = lane < Lc ? logf(gam_n) : 0.f;
+    // the gates, in every wave (lane = token): no barrier between them and the staging
+    float lg = lane < Lc ? logf(gam_n) : 0.f;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(lg, o, 64);
-        if (lane >= o) lg += t;
-      }
-      bcum[lane] = lg;
-      betas[lane] = lane < Lc ? bet_n : 0.f;
-      wt[lane] = expf(lg);
-      nus[lane] = lane < Lc ? nu_n : 0.f;
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(lg, o, 64);
+      if (lane >= o) lg += t;
     }
-    __syncthreads();
+    const float wt_l = expf(lg);
+    const float nu_l = lane < Lc ? nu_n : 0.f;
+    const float blast = __shfl(lg, 63, 64);  // the chunk's total log decay
     // y_t = nu_t * yn_t: X^T, Y^T into sB1; -(w Y)^T, -(w X)^T of the stripe into sA1;
     // stripe 0 also sums this thread's dims of dlambda = -sum_t y_t * x_t
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int t = M::tok(it);
       const bool in = t < Lc;
-      const float w = in ? wt[t] : 0.f, nu = in ? nus[t] : 0.f, ex = in ? 1.f : 0.f;
+      const float wsh = __shfl(wt_l, t, 64), nsh = __shfl(nu_l, t, 64);
+      const float w = in ? wsh : 0.f, nu = in ? nsh : 0.f, ex = in ? 1.f : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = 4 * qc + u;
@@ -647,14 +643,15 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
 #pragma unroll
     for (int it = 0; it < ND; ++it) {
       const int t = dtok(it);
-      const float w = t < Lc ? wt[t] : 0.f;
+      const float wsh = __shfl(wt_l, t, 64);
+      const float w = t < Lc ? wsh : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) sA2[(4 * dq + u) * LC + t] = bf(w * dv[it][u]);
     }
     if (c > cb) fetch(c - 1);  // the next chunk's loads fly during this chunk's products
     __syncthreads();
-    logdec += bcum[kC - 1];
-    const float decay = expf(bcum[kC - 1]);
+    logdec += blast;
+    const float decay = expf(blast);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
