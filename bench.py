@@ -420,6 +420,28 @@ def calibrate_copy(mib: int, reps: int):
                       "bytes_written_per_launch": 4 * n, "launches": reps}), flush=True)
 
 
+def measure_copy_bw(mib: int = 512, copies: int = 3, reps: int = 10) -> float:
+    """Read + write rate (GB/s) of a plain device copy, over three rotating
+    buffer pairs so that no copy finds its source in the last-level cache: the
+    practical HBM rate the memory-bound kernels are compared with."""
+    import itertools
+    import torch
+    n = mib * (1 << 20) // 4
+    src = [torch.ones(n, device="cuda") for _ in range(copies)]
+    dst = [torch.empty(n, device="cuda") for _ in range(copies)]
+    ctr = itertools.count()
+
+    def one():
+        i = next(ctr) % copies
+        dst[i].copy_(src[i])
+
+    for _ in range(copies):
+        one()
+    ms = time_events(one, reps)
+    del src, dst
+    return 2 * 4 * n / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(x, slices: int, tokens: int):
     from threadpoolctl import threadpool_limits
     from oracle import mesa_forward
@@ -534,10 +556,17 @@ def main():
         "fwd_frac_of_mfma_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(fw["wall_ms"], 4),
     }
+    copy_gbs = measure_copy_bw()
+    line["measured_peaks"] = {"torch_copy_GBs": round(copy_gbs, 1),
+                              "note": "torch device copy of 512 MiB (read + write bytes), three rotating "
+                                      "buffer pairs: a reference rate, not a ceiling"}
+    log(f"device copy: {copy_gbs:.0f} GB/s")
     if not args.no_decode:
         line["decode"] = bench_decode(CONFIGS[5], args.steps, args.warmup)
+        line["decode"]["vs_torch_copy"] = round(line["decode"]["achieved_GBs"] / copy_gbs, 4)
         log(f"decode: {line['decode']['us_per_step']} us per step")
     line["preprocess"] = bench_preprocess(CONFIGS[args.workload], args.steps, args.warmup)
+    line["preprocess"]["vs_torch_copy"] = round(line["preprocess"]["achieved_GBs"] / copy_gbs, 4)
     log(f"preprocess: {line['preprocess']['us_per_call']} us per call")
     line["backward"] = bench_backward(CONFIGS[args.workload], args.steps, args.warmup)
     log(f"backward: {line['backward']['ms_per_call']} ms per call")
