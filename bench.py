@@ -480,7 +480,7 @@ def main():
                     help="forward workload: 2 (d=64), 3 (d=128, default), 4 (T=32768, dynamic CG)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-slices", type=int, default=2)
+    ap.add_argument("--cpu-slices", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
