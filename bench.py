@@ -488,7 +488,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Mesa layer's (b, h) slices shard across GPUs "
-              "with no communication, and this build runs and reports a single MI355X. "
+              "with no communication, and this benchmark runs and reports a single MI355X. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
