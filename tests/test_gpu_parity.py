@@ -234,3 +234,22 @@ def test_whole_state_scan_every_slice(d, T):
                          max_steps=cfg.max_steps, tol=cfg.tol, h0=h0[b:b + 1, hh:hh + 1],
                          g0=g0[b:b + 1, hh:hh + 1], exact=False, forced_steps=gpu["steps"][b:b + 1, hh:hh + 1])
         assert rel_l2(gpu["o"][b, hh], r["o_cg"][0, 0]) <= TOL["bf16"]
+
+
+def test_whole_state_scan_ragged_group_of_sequences():
+    """B*H = 131 (not a multiple of the 8 XCDs the scan groups sequences by):
+    the padded group's workgroups must leave every real slice's states right."""
+    cfg = small_fwd(B=1, H=131, T=70, d=64, chunk=64, dtype="bf16", max_steps=5)
+    x = make_fwd_inputs(cfg)
+    gpu = run_fwd(x, return_state=True)
+    from oracle import mesa_forward
+    d, S = cfg.d, cfg.H
+    Hg, Gg = gpu["h_final"].reshape(S, d, d), gpu["g_final"].reshape(S, d, d)
+    for hh in (0, 7, 8, 127, 128, 130):
+        r = mesa_forward(x["q"][:, hh:hh + 1], x["k"][:, hh:hh + 1], x["v"][:, hh:hh + 1],
+                         x["gamma"][:, hh:hh + 1], x["beta"][:, hh:hh + 1], x["lam"][hh:hh + 1],
+                         max_steps=cfg.max_steps, tol=cfg.tol, exact=False,
+                         forced_steps=gpu["steps"][:, hh:hh + 1])
+        assert rel_l2(Hg[hh], r["H_final"][0, 0]) < 1e-4, hh
+        assert rel_l2(Gg[hh], r["G_final"][0, 0]) < 1e-4, hh
+        assert rel_l2(gpu["o"][0, hh], r["o_cg"][0, 0]) <= TOL["bf16"], hh
