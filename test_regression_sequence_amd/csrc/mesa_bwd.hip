@@ -151,25 +151,6 @@ struct ColMap {
   __device__ static int tok(int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / Q + BLKS * it); }
 };
 
-// token-major [C][D] fp32 -> LDS bf16 transposed: dst[i * ld + col0 + t] = sign * scale_t * src[t][i]
-template <int D>
-__device__ __forceinline__ void stage_cols_f32(uint16_t* dst, int ld, int col0, const float* src, int Lc,
-                                               const float* row_scale = nullptr, float sign = 1.f) {
-  using M = ColMap<D>;
-  const int c4 = M::quad();
-  f32x4 v[M::N];
-#pragma unroll
-  for (int it = 0; it < M::N; ++it)
-    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(M::tok(it), Lc - 1) * D + 4 * c4);
-#pragma unroll
-  for (int it = 0; it < M::N; ++it) {
-    const int t = M::tok(it);
-    const float sc = t < Lc ? sign * (row_scale ? row_scale[t] : 1.f) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(v[it][u] * sc);
-  }
-}
-
 // token-major [C][D] bf16 -> LDS transposed (octets of 8 dims; same token-contiguous lane groups)
 template <int D>
 __device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
@@ -217,39 +198,6 @@ __device__ __forceinline__ void stage_snapshot(uint16_t* dst, int ld, const uint
   }
 }
 
-// row-major [D][D] bf16 -> LDS [D][ld]
-template <int D>
-__device__ __forceinline__ void stage_square(uint16_t* dst, int ld, const uint16_t* src) {
-  constexpr int N = D * D / 8 / kThreads;
-  u16x8 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it) v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)(threadIdx.x + it * kThreads) * 8);
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int idx = threadIdx.x + it * kThreads;
-    *reinterpret_cast<u16x8*>(dst + (idx / (D / 8)) * ld + 8 * (idx % (D / 8))) = v[it];
-  }
-}
-
-// <A, B> for a row-major [D][D] bf16 matrix in memory and one in LDS [D][ld]; the
-// calling thread's part (16-byte loads, all issued before the products).
-template <int D>
-__device__ __forceinline__ float square_dot(const uint16_t* a, const uint16_t* b, int ld) {
-  constexpr int N = D * D / 8 / kThreads;
-  u16x8 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it) v[it] = *reinterpret_cast<const u16x8*>(a + (size_t)(threadIdx.x + it * kThreads) * 8);
-  float acc = 0.f;
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int idx = threadIdx.x + it * kThreads;
-    const u16x8 w = *reinterpret_cast<const u16x8*>(b + (idx / (D / 8)) * ld + 8 * (idx % (D / 8)));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(v[it][u]), bf16_to_f32(w[u]), acc);
-  }
-  return acc;
-}
-
 // Split staging for the gradient kernel: the load halves return registers, so a
 // kernel can issue the loads of several tiles (or of a later phase) at once and
 // write LDS afterwards.  Mappings and row handling as in the helpers above.
@@ -257,8 +205,6 @@ template <int D>
 struct TileF32 { f32x4 v[kC * D / 4 / kThreads]; };
 template <int D>
 struct TileB16 { u16x8 v[kC * D / 8 / kThreads]; };
-template <int D>
-struct ColsF32 { f32x4 v[ColMap<D>::N]; };
 template <int D>
 struct Square { u16x8 v[D * D / 8 / kThreads]; };
 
@@ -305,28 +251,6 @@ __device__ __forceinline__ void put_tile_b16(uint16_t* dst, int ld, const TileB1
     const int t = t0 + it * (kThreads / E);
     const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = t < Lc ? r.v[it] : zero;
-  }
-}
-template <int D>
-__device__ __forceinline__ ColsF32<D> load_cols_f32(const float* src, int Lc) {
-  using M = ColMap<D>;
-  ColsF32<D> r;
-#pragma unroll
-  for (int it = 0; it < M::N; ++it)
-    r.v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(M::tok(it), Lc - 1) * D + 4 * M::quad());
-  return r;
-}
-template <int D>
-__device__ __forceinline__ void put_cols_f32(uint16_t* dst, int ld, int col0, const ColsF32<D>& r, int Lc,
-                                             const float* row_scale = nullptr) {
-  using M = ColMap<D>;
-  const int c4 = M::quad();
-#pragma unroll
-  for (int it = 0; it < M::N; ++it) {
-    const int t = M::tok(it);
-    const float sc = t < Lc ? (row_scale ? row_scale[t] : 1.f) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dst[(4 * c4 + u) * ld + col0 + t] = bf(r.v[it][u] * sc);
   }
 }
 template <int D>
