@@ -203,11 +203,8 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     fetch(cb, b0);
     if constexpr (DEPTH == 3) fetch(min(cb + 1, ce - 1), b1);
   }
-  float seg_log = 0.f;  // sum of log gamma over the segment (wave-uniform)
-  auto step = [&](const int c, const Raw& cur, Raw& pre) {
-    fetch(min(c + DEPTH - 1, ce - 1), pre);
-
-    // ---- snapshot of the state before chunk c ----------------------------------
+  // ---- the bf16 snapshot of the current state as the state before chunk c ------
+  auto store_snapshot = [&](const int c) {
     if constexpr (!TOTALS) {
       const size_t snap = ((size_t)bh * NC + c) * D * D;
 #pragma unroll
@@ -243,6 +240,16 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         }
       }
     }
+  };
+  if constexpr (FULL)
+    if (ce > cb) store_snapshot(cb);
+  float seg_log = 0.f;  // sum of log gamma over the segment (wave-uniform)
+  auto step = [&](const int c, const Raw& cur, Raw& pre) {
+    fetch(min(c + DEPTH - 1, ce - 1), pre);
+
+    // the state before chunk c (stripes: stored here; whole or segment
+    // states: stored right after chunk c-1's update, see below)
+    if constexpr (!FULL) store_snapshot(c);
 
     // ---- gates (every wave, in registers): w_j = beta_j prod_{i>j} gamma_i ------
     const int Lcur = min(C, T - c * C);
@@ -353,6 +360,12 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         for (int i = 0; i < 4; ++i) st[ui][h][i] = gamma_c * st[ui][h][i] + acc[i];
       }
     }
+    // whole or segment states: the state before chunk c+1 goes out now, so its
+    // stores drain while the next chunk is fetched, gated and staged (measured
+    // about 20 % faster than storing it at the top of the next step, at 128
+    // sequences of 64 chunks; the stripe walks are not faster this way)
+    if constexpr (FULL)
+      if (c + 1 < ce) store_snapshot(c + 1);
   };
   if constexpr (DEPTH == 3) {
     for (int c = cb; c < ce; c += 3) {
