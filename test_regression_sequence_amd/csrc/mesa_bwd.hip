@@ -518,19 +518,35 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     const int chunk = bh * p.NC + c;
     const int s = c * kC, Lc = min(kC, p.T - s);
     if constexpr (!TOTALS) {
-      // the adjoints arriving at this chunk's end
+      // the adjoints arriving at this chunk's end.  A 4x4 transpose inside each
+      // lane quad (two DPP butterfly stages) turns a lane's 4 rows of one
+      // column into 4 consecutive columns of one row: one 8-byte store each.
       uint16_t* snR = p.snap_r + (size_t)chunk * D2;
       uint16_t* snS = p.snap_s + (size_t)chunk * D2;
+      const int qb = tl & 3;  // position in the lane quad
+      auto quad_transpose = [&](f32x4 x) {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x[i ^ 1]), 0xB1, 0xF, 0xF, false));
+          y[i] = ((i & 1) == (qb & 1)) ? x[i] : t;
+        }
+        f32x4 z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(y[i ^ 2]), 0x4E, 0xF, 0xF, false));
+          z[i] = ((i & 2) == (qb & 2)) ? y[i] : t;
+        }
+        return z;
+      };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const int row = r0 + 16 * rt + 4 * g, col = CW * wave + 16 * ct + tl;
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            snR[(row + ii) * D + col] = bf(R[rt][ct][ii]);
-            snS[(row + ii) * D + col] = bf(S[rt][ct][ii]);
-          }
+          const int row = r0 + 16 * rt + 4 * g + qb, col = CW * wave + 16 * ct + (tl & ~3);
+          const f32x4 zr = quad_transpose(R[rt][ct]), zs = quad_transpose(S[rt][ct]);
+          *reinterpret_cast<u16x4*>(snR + (size_t)row * D + col) = u16x4{bf(zr[0]), bf(zr[1]), bf(zr[2]), bf(zr[3])};
+          *reinterpret_cast<u16x4*>(snS + (size_t)row * D + col) = u16x4{bf(zs[0]), bf(zs[1]), bf(zs[2]), bf(zs[3])};
         }
     }
     // the gates, in every wave (lane = token): no barrier between them and the staging
