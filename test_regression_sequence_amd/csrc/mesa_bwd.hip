@@ -62,6 +62,27 @@ constexpr int kThreads = 256;   // 4 waves
 
 __device__ __forceinline__ uint16_t bf(float x) { return __builtin_bit_cast(uint16_t, f32_to_bf16(x)); }
 
+// 4x4 transpose inside each lane quad by two DPP butterfly stages: lane b of a
+// quad holding x[i] = M[b][i] returns M[i][b].  Applied to an MFMA result tile
+// (a lane's 4 rows of one column), it gives a lane 4 consecutive columns of
+// one row, so the tile goes out as one 8-byte store per lane.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+  const int qb = threadIdx.x & 3;
+  f32x4 y, z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x[i ^ 1]), 0xB1, 0xF, 0xF, false));
+    y[i] = ((i & 1) == (qb & 1)) ? x[i] : t;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(y[i ^ 2]), 0x4E, 0xF, 0xF, false));
+    z[i] = ((i & 2) == (qb & 2)) ? y[i] : t;
+  }
+  return z;
+}
+__device__ __forceinline__ u16x4 bf4(f32x4 v) { return u16x4{bf(v[0]), bf(v[1]), bf(v[2]), bf(v[3])}; }
+
 // acc (16x16 tile; lane l holds rows 4(l/16)+{0..3} of column l%16) +=
 // A[16][K] * Bt[16][K]^T, both bf16 in LDS with row strides lda, ldb.
 template <int K>
@@ -413,11 +434,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
     ss = group_sum<16>(ss);
     const float nrm = sqrtf(ss);
     const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
-    if (t < Lc) {
 #pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) rhs[(row0 + t) * D + 16 * nt + tl] = bf(r[nt][i] * inv);
-      if (tl == 0) p.nu[row0 + t] = nrm;
-    }
+    for (int nt = 0; nt < NTL; ++nt) r[nt][i] *= inv;
+    if (t < Lc && tl == 0) p.nu[row0 + t] = nrm;
+  }
+  // token 16 wave + 4g + (lane quad position), dims 16nt + 4(tl/4) + {0..3}
+  const int tq = 16 * wave + 4 * g + (tl & 3);
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) {
+    const f32x4 z = quad_transpose(r[nt]);
+    if (tq < Lc) *reinterpret_cast<u16x4*>(rhs + (row0 + tq) * D + 16 * nt + (tl & ~3)) = bf4(z);
   }
 }
 
@@ -518,35 +544,18 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
     const int chunk = bh * p.NC + c;
     const int s = c * kC, Lc = min(kC, p.T - s);
     if constexpr (!TOTALS) {
-      // the adjoints arriving at this chunk's end.  A 4x4 transpose inside each
-      // lane quad (two DPP butterfly stages) turns a lane's 4 rows of one
-      // column into 4 consecutive columns of one row: one 8-byte store each.
+      // the adjoints arriving at this chunk's end, one 8-byte store per tile and lane
       uint16_t* snR = p.snap_r + (size_t)chunk * D2;
       uint16_t* snS = p.snap_s + (size_t)chunk * D2;
       const int qb = tl & 3;  // position in the lane quad
-      auto quad_transpose = [&](f32x4 x) {
-        f32x4 y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x[i ^ 1]), 0xB1, 0xF, 0xF, false));
-          y[i] = ((i & 1) == (qb & 1)) ? x[i] : t;
-        }
-        f32x4 z;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float t = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(y[i ^ 2]), 0x4E, 0xF, 0xF, false));
-          z[i] = ((i & 2) == (qb & 2)) ? y[i] : t;
-        }
-        return z;
-      };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const int row = r0 + 16 * rt + 4 * g + qb, col = CW * wave + 16 * ct + (tl & ~3);
           const f32x4 zr = quad_transpose(R[rt][ct]), zs = quad_transpose(S[rt][ct]);
-          *reinterpret_cast<u16x4*>(snR + (size_t)row * D + col) = u16x4{bf(zr[0]), bf(zr[1]), bf(zr[2]), bf(zr[3])};
-          *reinterpret_cast<u16x4*>(snS + (size_t)row * D + col) = u16x4{bf(zs[0]), bf(zs[1]), bf(zs[2]), bf(zs[3])};
+          *reinterpret_cast<u16x4*>(snR + (size_t)row * D + col) = bf4(zr);
+          *reinterpret_cast<u16x4*>(snS + (size_t)row * D + col) = bf4(zs);
         }
     }
     // the gates, in every wave (lane = token): no barrier between them and the staging
