@@ -522,7 +522,7 @@ def main():
         traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
     line = {
-        "metric": "Mesa fwd tokens/s (B*H*T/s) at d=128",
+        "metric": f"Mesa fwd tokens/s (B*H*T/s) at d={cfg.d}",
         "value": round(tokens / (fw["ms"] * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
