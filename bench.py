@@ -341,6 +341,46 @@ def bench_backward(cfg, steps, warmup):
     }
 
 
+def bench_forward_full_lambda(cfg, steps, warmup):
+    """The forward with a full symmetric positive definite Lambda per head: one
+    mesa_fwd_chunked_ex call (scan, CG solve with the extra d x d product, read-out)."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs, make_full_lambda
+
+    x = make_fwd_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    gamma, beta = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta"))
+    lam = torch.from_numpy(make_full_lambda(cfg.H, cfg.d, cfg.seed)).cuda()
+    del x
+    ws = torch.empty(mesa.workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, dtype=dt), device="cuda",
+                     dtype=torch.uint8)
+    res = mesa.fwd_chunked_ex(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                              workspace=ws)
+
+    def step():
+        mesa.fwd_chunked_ex(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                            workspace=ws, out=res)
+
+    for _ in range(warmup):
+        step()
+    ms = time_events(step, steps)
+    n_avg = float(res["steps"].float().mean().item())
+    tokens = cfg.B * cfg.H * cfg.T
+    # counted flops: the diagonal forward's plus the full Lambda's product per CG iteration
+    f = flops_per_token(cfg.d, cfg.chunk, n_avg)["total"] + n_avg * 2 * cfg.d * cfg.d
+    tflops = f * tokens / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"forward with a full SPD Lambda per head: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
+                    f"{cfg.dtype}, chunk {cfg.chunk}, cg_steps_mean {n_avg:.1f}",
+        "ms_per_call": round(ms, 4),
+        "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "counted_TFLOPs": round(tflops, 2),
+        "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def bench_preprocess(cfg, steps, warmup, window=4):
     """Query/key preprocessing (causal depthwise convolution + L2 norm) at the layer
     workload's shape: raw q, k read once, processed q, k written once."""
@@ -570,6 +610,10 @@ def main():
     log(f"preprocess: {line['preprocess']['us_per_call']} us per call")
     line["backward"] = bench_backward(CONFIGS[args.workload], args.steps, args.warmup)
     log(f"backward: {line['backward']['ms_per_call']} ms per call")
+    cfg_w = CONFIGS[args.workload]
+    if cfg_w.dtype == "bf16" and cfg_w.chunk == 64 and cfg_w.d in (64, 128):
+        line["forward_full_lambda"] = bench_forward_full_lambda(cfg_w, args.steps, args.warmup)
+        log(f"forward, full Lambda: {line['forward_full_lambda']['ms_per_call']} ms per call")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
         log("cpu baseline done")

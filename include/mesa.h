@@ -117,6 +117,31 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* mesa_fwd_chunked with the regulariser given either as before or as a full
+ * matrix per head (MesaNet page, technical summary, "Mesa layer": Lambda is a
+ * symmetric positive definite regulariser of the objective).
+ *
+ *   lambda_full = 0: lambda [H, dk] fp32, the diagonal, exactly as
+ *                    mesa_fwd_chunked (the same kernels run).
+ *   lambda_full = 1: lambda [H, dk, dk] fp32, row-major, symmetric positive
+ *                    definite (not checked: an indefinite matrix gives CG
+ *                    breakdowns, reported as tokens that stop early).  The
+ *                    matrix is rounded to bf16 for its MFMA products.
+ *                    Supported for in_dtype MESA_BF16, chunk 64 and
+ *                    dk = dv in {64, 128}; other descriptors return
+ *                    MESA_ERR_UNSUPPORTED and launch nothing.
+ *
+ * Every other argument, the workspace and the error behaviour are those of
+ * mesa_fwd_chunked. */
+mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d,
+                                const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, const float* lambda,
+                                int32_t lambda_full, const float* h0, const float* g0,
+                                float* o, float* h_final, float* g_final,
+                                int32_t* steps, float* x_out,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* The two phases of mesa_fwd_chunked, for callers that want them apart
  * (e.g. building decode states from a prompt without solving, or timing).
  *

@@ -68,9 +68,12 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
                      const void* v, const float* gamma, const float* beta, const float* lambda,
                      const float* h0, const float* g0, float* o, float* h_final, float* g_final,
                      int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool lam_full = false) {
   const mesa_status st = check_desc(d);
   if (st != MESA_OK) return st;
+  // a full Lambda is taken by the bf16 kernels at chunk 64, d 64 or 128
+  if (lam_full && (d->in_dtype != MESA_BF16 || d->chunk != 64 || (d->dk != 64 && d->dk != 128)))
+    return MESA_ERR_UNSUPPORTED;
   const bool any_tokens = d->T > 0;
   if (any_tokens && (!k || !v || !gamma || !beta)) return MESA_ERR_INVALID_ARG;
   if (any_tokens && (phases & kSolve) && (!q || !lambda || !o)) return MESA_ERR_INVALID_ARG;
@@ -114,6 +117,7 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
     cp.hb = hb; cp.gb = gb; cp.o = o; cp.steps = steps; cp.x_out = x_out; cp.unscaled = flags;
     cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
     cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
+    cp.lam_full = lam_full ? 1 : 0;
     if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
   return MESA_OK;
@@ -130,6 +134,15 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
                              size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                   steps, x_out, workspace, workspace_bytes, stream);
+}
+
+mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, const float* lambda,
+                                int32_t lambda_full, const float* h0, const float* g0, float* o,
+                                float* h_final, float* g_final, int32_t* steps, float* x_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
+                  steps, x_out, workspace, workspace_bytes, stream, lambda_full != 0);
 }
 
 mesa_status mesa_fwd_scan(const mesa_fwd_desc* d, const void* k, const void* v, const float* gamma,

@@ -46,6 +46,13 @@
 // batch; the column fragments are then formed from the (weighted) row
 // fragments by an exact MFMA transpose, so the CG loop touches no global
 // memory.  MFMA accumulators stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
+//
+// Lambda is diagonal, or (LF) a full symmetric positive definite matrix per
+// head (the page calls the regulariser symmetric positive definite).  The
+// full matrix enters as one more d x d MFMA operand, (Lambda / Gamma_t) p =
+// Lambda (e^{-b_t} p): its bf16 fragments sit in LDS, since the AGPRs already
+// hold Hb and the keys, and the B operand is the search direction scaled per
+// token.
 #include <type_traits>
 
 #include "mesa_common.h"
@@ -58,7 +65,7 @@ namespace {
 template <int W>
 using tile_c = std::integral_constant<int, W>;
 
-template <int D, int C>
+template <int D, int C, bool LF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_kernel(CgParams p) {
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
@@ -70,7 +77,8 @@ void cg_bf16_kernel(CgParams p) {
   const int T = p.T, s = c * C, Lc = min(C, T - s);
   const size_t row0 = (size_t)bh * T + s;
 
-  __shared__ f32x4 xs[NW * ND * 64];   // solutions xh of the tiles, [tile][a][lane]
+  __shared__ bf16x8 xs[NW * NM * 64];  // solutions xh of the tiles as bf16, [tile][m][lane]
+  __shared__ bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
   __shared__ float lam_s[D];
   __shared__ float bcum[C];
   __shared__ float betas[C];
@@ -177,6 +185,17 @@ void cg_bf16_kernel(CgParams p) {
     for (int a = 0; a < ND; ++a) qraw[a] = *reinterpret_cast<const u16x4*>(Qg + (row0 + tq) * D + 16 * a + 4 * g);
   };
 
+  if constexpr (LF) {
+    // Lambda[16nt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}] of the head, rounded to
+    // bf16; every lane writes and later reads only its own slots
+    const float* L = p.lam + (size_t)h * D * D;
+#pragma unroll 4
+    for (int f = 0; f < ND * NM; ++f) {
+      const int nt = f / NM, m = f % NM;
+      const float* src = L + (size_t)(16 * nt + tl) * D + 32 * m + 4 * g;
+      lamf[f * 64 + lane] = pack8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 16));
+    }
+  }
   // gates first: their prefix scan overlaps the state and key loads
   {
     float lg = 0.f, bt = 0.f;
@@ -187,7 +206,7 @@ void cg_bf16_kernel(CgParams p) {
     }
 #pragma unroll
     for (int i = 0; i < (D + 63) / 64; ++i)
-      lam_v[i] = (lane + 64 * i < D) ? p.lam[(size_t)h * D + lane + 64 * i] : 0.f;
+      lam_v[i] = (!LF && lane + 64 * i < D) ? p.lam[(size_t)h * D + lane + 64 * i] : 0.f;
     load_state(p.hb);
     load_rows(Kg, kr);
     fetch_q(0);
@@ -270,10 +289,11 @@ void cg_bf16_kernel(CgParams p) {
     constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
     const bool valid = tloc < Lc;
-    // Lambda / Gamma_t of the lane's token, held for the whole loop
-    f32x4 lt[ND];
-    {
-      const float lscale = expf(-bcum[tloc]);
+    // 1 / Gamma_t of the lane's token, and Lambda / Gamma_t for a diagonal
+    // Lambda, held for the whole loop
+    const float lscale = expf(-bcum[tloc]);
+    f32x4 lt[LF ? 1 : ND];
+    if constexpr (!LF) {
 #pragma unroll
       for (int a = 0; a < ND; ++a) lt[a] = *reinterpret_cast<const f32x4*>(&lam_s[16 * a + 4 * g]) * lscale;
     }
@@ -320,14 +340,23 @@ void cg_bf16_kernel(CgParams p) {
         for (int jt = 0; jt <= w; ++jt) sc[jt] = mfma_bf16(kr[jt][m], ub, m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[jt]);
 #pragma unroll
         for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(mf[nt][m], ub, m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt]);
+        if constexpr (LF) {
+          // + Lambda (e^{-b_t} p) over the dims of block m
+          const bf16x8 us = pack8(pv[2 * m] * lscale, pv[2 * m + 1] * lscale);
+#pragma unroll
+          for (int nt = 0; nt < ND; ++nt) acc[nt] = mfma_bf16(lamf[(nt * NM + m) * 64 + lane], us, acc[nt]);
+        }
       }
       add_intra(wc, sc);
-      // + (Lambda / Gamma_t) p, then w = acc and p.w (two independent chains)
+      // + (Lambda / Gamma_t) p for a diagonal Lambda, then w = acc and p.w (two
+      // independent chains)
       float pw0 = 0.f, pw1 = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
+        if constexpr (!LF) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[a][i] = __builtin_fmaf(lt[a][i], pv[a][i], acc[a][i]);
+          for (int i = 0; i < 4; ++i) acc[a][i] = __builtin_fmaf(lt[a][i], pv[a][i], acc[a][i]);
+        }
         pw0 += pv[a][0] * acc[a][0];
         pw1 += pv[a][1] * acc[a][1];
         pw0 += pv[a][2] * acc[a][2];
@@ -359,7 +388,7 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
     for (int a = 0; a < ND; ++a) x[a] += alpha_p * pv[a];
 #pragma unroll
-    for (int a = 0; a < ND; ++a) xs[(w * ND + a) * 64 + lane] = x[a];
+    for (int m = 0; m < NM; ++m) xs[(w * NM + m) * 64 + lane] = pack8(x[2 * m], x[2 * m + 1]);
     if (valid) {
       if (p.x_out) {
         // x = xh / Gamma_t
@@ -376,12 +405,9 @@ void cg_bf16_kernel(CgParams p) {
   auto readout_tile = [&](auto wc) {
     constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
-    f32x4 x[ND];
-#pragma unroll
-    for (int a = 0; a < ND; ++a) x[a] = xs[(w * ND + a) * 64 + lane];
     bf16x8 xb[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) xb[m] = pack8(x[2 * m], x[2 * m + 1]);
+    for (int m = 0; m < NM; ++m) xb[m] = xs[(w * NM + m) * 64 + lane];
     pin_operands();
     matvec(wc, xb);
     if (tloc < Lc) {
@@ -415,10 +441,10 @@ void cg_bf16_kernel(CgParams p) {
   for_tiles(readout_tile);
 }
 
-template <int D, int C>
+template <int D, int C, bool LF = false>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((long long)p.BH * p.NC));
-  hipLaunchKernelGGL((cg_bf16_kernel<D, C>), grid, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_cg_bf16_unscaled(D, C, p, s);
@@ -437,6 +463,12 @@ hipError_t launch_d(int C, const CgParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_cg_bf16(int D, int C, const CgParams& p, hipStream_t s) {
+  if (p.lam_full) {
+    if (C != 64) return hipErrorInvalidValue;
+    if (D == 64) return launch_t<64, 64, true>(p, s);
+    if (D == 128) return launch_t<128, 64, true>(p, s);
+    return hipErrorInvalidValue;
+  }
   switch (D) {
     case 32: return launch_d<32>(C, p, s);
     case 64: return launch_d<64>(C, p, s);

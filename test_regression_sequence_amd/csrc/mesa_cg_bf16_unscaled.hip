@@ -16,7 +16,9 @@
 // formed by an exact MFMA transpose), CG of the NW = C/16 token tiles one
 // after another, solutions parked in LDS, read-out with Gb and value columns.
 // Register layout (lane l, tl = l%16, g = l/16): CG vectors of token 16w + tl
-// keep dims 16a + 4g + {0..3} as f32x4 v[a].
+// keep dims 16a + 4g + {0..3} as f32x4 v[a].  A full symmetric positive
+// definite Lambda (LF) enters as one more MFMA operand, its bf16 fragments in
+// LDS, applied to the bf16 search direction.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -26,7 +28,7 @@ namespace {
 
 constexpr int kChunksPerWave = 8;
 
-template <int D, int C>
+template <int D, int C, bool LF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_unscaled_kernel(CgParams p) {
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
@@ -39,6 +41,7 @@ void cg_bf16_unscaled_kernel(CgParams p) {
 
   __shared__ f32x4 xs[NW * ND * 64];   // solutions of the tiles, [tile][a][lane]
   __shared__ float lam_s[D];
+  __shared__ bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
   __shared__ float bcum[C];
   __shared__ float betas[C];
 
@@ -140,7 +143,19 @@ void cg_bf16_unscaled_kernel(CgParams p) {
         bcum[lane] = lg;
         betas[lane] = bt;
       }
-      for (int i = lane; i < D; i += 64) lam_s[i] = p.lam[(size_t)h * D + i];
+      if constexpr (LF) {
+        // Lambda[16nt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}] of the head as bf16;
+        // every lane writes and later reads only its own slots
+        const float* L = p.lam + (size_t)h * D * D;
+#pragma unroll 4
+        for (int f = 0; f < ND * NM; ++f) {
+          const int nt = f / NM, m = f % NM;
+          const float* src = L + (size_t)(16 * nt + tl) * D + 32 * m + 4 * g;
+          lamf[f * 64 + lane] = pack8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 16));
+        }
+      } else {
+        for (int i = lane; i < D; i += 64) lam_s[i] = p.lam[(size_t)h * D + i];
+      }
     }
     __syncthreads();
     columns_from_rows(kr);
@@ -184,7 +199,14 @@ void cg_bf16_unscaled_kernel(CgParams p) {
         for (int m = 1; m < NM; ++m) t = mfma_bf16(mf[nt][m], ub[m], t);
         asm volatile("" : "+v"(t));
         acc[nt] = t * Gam;
-        if (with_lambda) acc[nt] += *reinterpret_cast<const f32x4*>(&lam_s[16 * nt + 4 * g]) * u[nt];
+        if constexpr (LF) {
+          if (with_lambda) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[nt] = mfma_bf16(lamf[(nt * NM + m) * 64 + lane], ub[m], acc[nt]);
+          }
+        } else {
+          if (with_lambda) acc[nt] += *reinterpret_cast<const f32x4*>(&lam_s[16 * nt + 4 * g]) * u[nt];
+        }
       }
 #pragma unroll
       for (int mj = 0; mj < NMJ; ++mj) {
@@ -313,11 +335,11 @@ void cg_bf16_unscaled_kernel(CgParams p) {
   }
 }
 
-template <int D, int C>
+template <int D, int C, bool LF = false>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
   const long long chunks = (long long)p.BH * p.NC;
   const dim3 grid((unsigned)((chunks + kChunksPerWave - 1) / kChunksPerWave));
-  hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C>), grid, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -334,6 +356,12 @@ hipError_t launch_d(int C, const CgParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_cg_bf16_unscaled(int D, int C, const CgParams& p, hipStream_t s) {
+  if (p.lam_full) {
+    if (C != 64) return hipErrorInvalidValue;
+    if (D == 64) return launch_t<64, 64, true>(p, s);
+    if (D == 128) return launch_t<128, 64, true>(p, s);
+    return hipErrorInvalidValue;
+  }
   switch (D) {
     case 32: return launch_d<32>(C, p, s);
     case 64: return launch_d<64>(C, p, s);

@@ -59,7 +59,7 @@ struct CgParams {
   const void* v;
   const float* gamma;    // [BH, T]
   const float* beta;
-  const float* lam;      // [H, D]
+  const float* lam;      // [H, D] diagonal, or [H, D, D] with lam_full
   const void* hb;        // snapshots written by the scan
   const void* gb;
   float* o;              // [BH, T, D]; null on the bf16 path: solutions only, no read-out
@@ -68,6 +68,7 @@ struct CgParams {
   int32_t* unscaled;     // [BH, NC] bf16 path: chunks left to the unscaled kernel
   int BH, H, T, NC, max_steps;
   float tol2;            // tol*tol, or -1 for the fixed-step mode
+  int lam_full;          // lam is a full symmetric matrix per head (bf16 path, chunk 64, D 64 or 128)
 };
 
 // Largest total decay -sum(log gamma) of a chunk that the scaled bf16 CG kernel

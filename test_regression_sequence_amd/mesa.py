@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.mesa_fwd_chunked.restype = ctypes.c_int
         L.mesa_fwd_chunked.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        P, S, P]
+        L.mesa_fwd_chunked_ex.restype = ctypes.c_int
+        L.mesa_fwd_chunked_ex.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, I32, P, P, P, P, P, P,
+                                          P, P, S, P]
         L.mesa_fwd_scan.restype = ctypes.c_int
         L.mesa_fwd_scan.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, S, P]
         L.mesa_fwd_solve.restype = ctypes.c_int
@@ -155,13 +158,33 @@ def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 
     ``steps`` [B, H, T] int32, ``x`` [B, H, T, d], ``h_final``, ``g_final``.
     ``out`` may pass preallocated result tensors (same keys).
     """
+    return _fwd(False, q, k, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, return_state=return_state, return_steps=return_steps, return_x=return_x,
+                out=out, workspace=workspace, stream=stream)
+
+
+def fwd_chunked_ex(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
+                   tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
+                   return_steps: bool = True, return_x: bool = False, out=None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """``fwd_chunked`` with ``lam`` either the diagonal [H, d] or a full
+    symmetric positive definite matrix per head [H, d, d] (fp32, row-major);
+    the full form needs bf16 inputs, chunk 64 and d in {64, 128}."""
+    return _fwd(True, q, k, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, return_state=return_state, return_steps=return_steps, return_x=return_x,
+                out=out, workspace=workspace, stream=stream)
+
+
+def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, return_state,
+         return_steps, return_x, out, workspace, stream) -> dict:
     B, H, T, d = q.shape
     code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, (B, H, T, d), q.dtype)
     _need(gamma, "gamma", (B, H, T), torch.float32)
     _need(beta, "beta", (B, H, T), torch.float32)
-    _need(lam, "lam", (H, d), torch.float32)
+    lam_full = ex and lam.dim() == 3
+    _need(lam, "lam", (H, d, d) if lam_full else (H, d), torch.float32)
     for name, t in (("h0", h0), ("g0", g0)):
         if t is not None:
             _need(t, name, (B, H, d, d), torch.float32)
@@ -182,11 +205,16 @@ def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    code_ = L.mesa_fwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
-                               _ptr(lam), _ptr(h0), _ptr(g0), _ptr(res["o"]), _ptr(res.get("h_final")),
-                               _ptr(res.get("g_final")), _ptr(res.get("steps")), _ptr(res.get("x")),
-                               _ptr(workspace), ctypes.c_size_t(wbytes), _stream(stream))
-    _check(code_, "mesa_fwd_chunked")
+    rest = (_ptr(h0), _ptr(g0), _ptr(res["o"]), _ptr(res.get("h_final")), _ptr(res.get("g_final")),
+            _ptr(res.get("steps")), _ptr(res.get("x")), _ptr(workspace), ctypes.c_size_t(wbytes),
+            _stream(stream))
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam))
+    if ex:
+        code_ = L.mesa_fwd_chunked_ex(*head, 1 if lam_full else 0, *rest)
+        _check(code_, "mesa_fwd_chunked_ex")
+    else:
+        code_ = L.mesa_fwd_chunked(*head, *rest)
+        _check(code_, "mesa_fwd_chunked")
     return res
 
 

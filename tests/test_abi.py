@@ -83,6 +83,31 @@ def test_fwd_rejects_bad_descriptors(kw, expect):
     assert call_fwd(desc(**kw)) == expect
 
 
+def call_fwd_ex(d, lam_full, q=FAKE, lam=FAKE, o=FAKE, workspace=FAKE, wbytes=1 << 40):
+    P = ctypes.c_void_p
+    return mesa.lib().mesa_fwd_chunked_ex(ctypes.byref(d), P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(lam),
+                                          lam_full, None, None, P(o), None, None, None, None, P(workspace),
+                                          ctypes.c_size_t(wbytes), None)
+
+
+def test_full_lambda_forward_scope_and_validation():
+    # the full-Lambda forward takes bf16 inputs, chunk 64 and d in {64, 128};
+    # every other descriptor is rejected before any launch
+    assert call_fwd_ex(desc(in_dtype=mesa.MESA_F32), 1) == 2
+    assert call_fwd_ex(desc(chunk=32), 1) == 2
+    assert call_fwd_ex(desc(dk=32, dv=32), 1) == 2
+    # the descriptor rules and pointer checks of mesa_fwd_chunked still come first
+    assert call_fwd_ex(desc(B=0), 1) == 1
+    assert call_fwd_ex(desc(dk=48, dv=48), 1) == 2
+    assert call_fwd_ex(desc(), 1, q=0) == 1
+    assert call_fwd_ex(desc(), 1, lam=0) == 1
+    assert call_fwd_ex(desc(), 1, o=FAKE + 4) == 3
+    assert call_fwd_ex(desc(), 1, wbytes=16) == 4
+    # lambda_full = 0 keeps the diagonal forward's scope (fp32 and chunk 32 allowed)
+    assert call_fwd_ex(desc(in_dtype=mesa.MESA_F32), 0, q=0) == 1
+    assert call_fwd_ex(desc(chunk=32), 0, wbytes=16) == 4
+
+
 def test_fwd_rejects_missing_pointers_alignment_and_workspace():
     d = desc()
     assert call_fwd(d, q=0) == 1
