@@ -52,7 +52,8 @@
 // full matrix enters as one more d x d MFMA operand, (Lambda / Gamma_t) p =
 // Lambda (e^{-b_t} p): its bf16 fragments sit in LDS, since the AGPRs already
 // hold Hb and the keys, and the B operand is the search direction scaled per
-// token.
+// token.  Two chunks of one sequence share a workgroup (one wave each) and one
+// copy of Lambda, so that four waves still fit a CU's LDS.
 #include <type_traits>
 
 #include "mesa_common.h"
@@ -66,22 +67,39 @@ template <int W>
 using tile_c = std::integral_constant<int, W>;
 
 template <int D, int C, bool LF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(LF ? 128 : 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_kernel(CgParams p) {
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
+  constexpr int NWV = LF ? 2 : 1;  // waves (chunks) per workgroup
 
-  const int lane = threadIdx.x, tl = lane & 15, g = lane >> 4;
-  const int chunk = blockIdx.x;
-  const int bh = chunk / p.NC, c = chunk % p.NC;
+  const int lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
+  const int wv = NWV > 1 ? (int)(threadIdx.x >> 6) : 0;
+  int bh, c;
+  if constexpr (NWV > 1) {
+    // chunks 2i and 2i+1 of sequence bh; past an odd chunk count the second
+    // wave only helps to stage Lambda (its loads repeat the last chunk's)
+    const int ncp = (p.NC + 1) / 2;
+    bh = blockIdx.x / ncp;
+    c = 2 * (blockIdx.x % ncp) + wv;
+  } else {
+    bh = blockIdx.x / p.NC;
+    c = blockIdx.x % p.NC;
+  }
+  const bool has_chunk = c < p.NC;
+  if (!has_chunk) c = p.NC - 1;
+  const int chunk = bh * p.NC + c;
   const int h = bh % p.H;
   const int T = p.T, s = c * C, Lc = min(C, T - s);
   const size_t row0 = (size_t)bh * T + s;
 
-  __shared__ bf16x8 xs[NW * NM * 64];  // solutions xh of the tiles as bf16, [tile][m][lane]
+  __shared__ bf16x8 xs_[NWV][NW * NM * 64];  // solutions xh of the tiles as bf16, [tile][m][lane]
   __shared__ bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
   __shared__ float lam_s[D];
-  __shared__ float bcum[C];
-  __shared__ float betas[C];
+  __shared__ float bcum_[NWV][C];
+  __shared__ float betas_[NWV][C];
+  bf16x8* const xs = xs_[wv];
+  float* const bcum = bcum_[wv];
+  float* const betas = betas_[wv];
 
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v);
@@ -187,10 +205,11 @@ void cg_bf16_kernel(CgParams p) {
 
   if constexpr (LF) {
     // Lambda[16nt+tl][32m+4g+{0..3}, 32m+16+4g+{0..3}] of the head, rounded to
-    // bf16; every lane writes and later reads only its own slots
+    // bf16; the two waves stage alternate fragments (the barrier below
+    // publishes them), and a lane reads only its own slots
     const float* L = p.lam + (size_t)h * D * D;
 #pragma unroll 4
-    for (int f = 0; f < ND * NM; ++f) {
+    for (int f = wv; f < ND * NM; f += NWV) {
       const int nt = f / NM, m = f % NM;
       const float* src = L + (size_t)(16 * nt + tl) * D + 32 * m + 4 * g;
       lamf[f * 64 + lane] = pack8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 16));
@@ -225,6 +244,7 @@ void cg_bf16_kernel(CgParams p) {
       if (lane + 64 * i < D) lam_s[lane + 64 * i] = lam_v[i];
   }
   __syncthreads();
+  if (!has_chunk) return;
   // the chunk's total decay decides the form (wave-uniform); a chunk left to
   // the unscaled kernel is flagged for it
   const bool scaled = __builtin_amdgcn_readfirstlane(bcum[Lc - 1] >= -kMaxScaledDecay ? 1 : 0) != 0;
@@ -443,8 +463,9 @@ void cg_bf16_kernel(CgParams p) {
 
 template <int D, int C, bool LF = false>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((long long)p.BH * p.NC));
-  hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
+  // LF: two chunks of one sequence per two-wave workgroup
+  const dim3 grid((unsigned)((long long)p.BH * (LF ? (p.NC + 1) / 2 : p.NC)));
+  hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(LF ? 128 : 64), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_cg_bf16_unscaled(D, C, p, s);
