@@ -124,9 +124,11 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
  *   lambda_full = 0: lambda [H, dk] fp32, the diagonal, exactly as
  *                    mesa_fwd_chunked (the same kernels run).
  *   lambda_full = 1: lambda [H, dk, dk] fp32, row-major, symmetric positive
- *                    definite (not checked: an indefinite matrix gives CG
- *                    breakdowns, reported as tokens that stop early).  The
- *                    matrix is rounded to bf16 for its MFMA products.
+ *                    definite.  This is not checked: with an indefinite
+ *                    matrix a token can meet p.Ap <= 0, and CG's breakdown
+ *                    rule stops it there, as for any token.  The matrix is
+ *                    rounded to bf16 for its MFMA products; lambda is only
+ *                    read.
  *                    Supported for in_dtype MESA_BF16, chunk 64 and
  *                    dk = dv in {64, 128}; other descriptors return
  *                    MESA_ERR_UNSUPPORTED and launch nothing.
