@@ -278,7 +278,9 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
     x_t = (H_t + Lambda)^{-1} q_t is treated as the solution of its system, so
     with the adjoint y_t = (H_t + Lambda)^{-1} G_t^T d_o_t:
         dL/dq_t = y_t,  dL/dH_t (local) = -y_t x_t^T,  dL/dG_t (local) = d_o_t x_t^T,
-        dL/dlambda = -sum_t y_t * x_t  (diagonal Lambda, summed over batch and time).
+        dL/dlambda = -sum_t y_t * x_t  (diagonal Lambda [H, dk], summed over batch and time),
+        dL/dLambda = -sum_t y_t x_t^T  (a full Lambda [H, dk, dk]: the partial derivative
+                     of each entry, not symmetrised; its diagonal is the diagonal case).
     The state adjoints run backwards, Hhat_t = dH_t + gamma_{t+1} Hhat_{t+1}
     (Hhat_T starts at dh_final; the same for G), and give
         dk_t = beta_t ((Hhat_t + Hhat_t^T) k_t + Ghat_t^T v_t),  dv_t = beta_t Ghat_t k_t,
@@ -292,7 +294,7 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
     ``adjoint_forced_steps`` [B, H, T].  The states are checkpointed every
     ``chunk`` tokens and recomputed chunk by chunk on the way back.
 
-    Returns dict(dq, dk, dv [B,H,T,d], dgamma, dbeta [B,H,T], dlam [H,dk],
+    Returns dict(dq, dk, dv [B,H,T,d], dgamma, dbeta [B,H,T], dlam [H,dk] or [H,dk,dk],
     dh0 [B,H,dk,dk], dg0 [B,H,dv,dk], x, y [B,H,T,dk], adj_steps [B,H,T]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -303,19 +305,20 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
     vf, of = _flat(v, S, T, dv), _flat(d_o, S, T, dv)
     gf, bf = _flat(gamma, S, T), _flat(beta, S, T)
     lam = np.asarray(lam, dtype=np.float64)
-    if lam.shape != (Hh, dk):
-        raise ValueError("the backward takes a diagonal Lambda [H, dk]")
+    full = lam.shape == (Hh, dk, dk)
+    if not full and lam.shape != (Hh, dk):
+        raise ValueError("the backward takes Lambda as a diagonal [H, dk] or a full [H, dk, dk]")
     fs = None if forced_steps is None else np.asarray(forced_steps).reshape(S, T)
     fa = None if adjoint_forced_steps is None else np.asarray(adjoint_forced_steps).reshape(S, T)
     out = {name: np.zeros((S, T, dd)) for name, dd in (("dq", dk), ("dk", dk), ("dv", dv),
                                                          ("x", dk), ("y", dk))}
     out.update(dgamma=np.zeros((S, T)), dbeta=np.zeros((S, T)), adj_steps=np.zeros((S, T), np.int64),
                dh0=np.zeros((S, dk, dk)), dg0=np.zeros((S, dv, dk)))
-    dlam = np.zeros((Hh, dk))
+    dlam = np.zeros((Hh, dk, dk) if full else (Hh, dk))
     NC = (T + chunk - 1) // chunk
     for s_ in range(S):
         h = s_ % Hh
-        Lam = np.diag(lam[h])
+        Lam = lam[h] if full else np.diag(lam[h])
         Hs = np.zeros((dk, dk)) if h0 is None else _flat(h0, S, dk, dk)[s_].copy()
         Gs = np.zeros((dv, dk)) if g0 is None else _flat(g0, S, dv, dk)[s_].copy()
 
@@ -367,7 +370,10 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
                 out["y"][s_, t] = yt
                 out["adj_steps"][s_, t] = na
                 out["dq"][s_, t] = yt
-                dlam[h] -= yt * xt
+                if full:
+                    dlam[h] -= np.outer(yt, xt)
+                else:
+                    dlam[h] -= yt * xt
                 Hhat = Hhat - np.outer(yt, xt)
                 Ghat = Ghat + np.outer(dot, xt)
                 bt = bf[s_, t]

@@ -64,6 +64,61 @@ def test_gradients_match_finite_differences_of_the_objective(seed, H):
         assert pins.rel(g[name], ref) < 1e-6, name
 
 
+def full_lambda(rng, H, dk):
+    M = rng.standard_normal((H, dk, dk))
+    return 0.3 * M @ M.transpose(0, 2, 1) / dk + np.stack([np.diag(rng.uniform(0.3, 1.2, dk)) for _ in range(H)])
+
+
+def test_full_lambda_gradient_along_symmetric_directions_matches_the_objective():
+    """A full SPD Lambda: <dLambda, E> for symmetric directions E against central
+    differences of the brute-force objective (which depends on Lambda's
+    symmetric part only)."""
+    q, k, v, gamma, beta, _, d_o = tiny(6, H=2)
+    lam = full_lambda(np.random.default_rng(7), 2, 3)
+    g = mesa_backward(q, k, v, gamma, beta, lam, d_o, max_steps=0, tol=0.0, exact=True, chunk=2)
+    assert g["dlam"].shape == (2, 3, 3)
+
+    def loss():
+        return sum(float(np.sum(d_o[0, h] * pins.brute_force_objective(q[0, h], k[0, h], v[0, h], gamma[0, h],
+                                                                       beta[0, h], lam[h])))
+                   for h in range(2))
+
+    eps = 1e-6
+    for h in range(2):
+        for i in range(3):
+            for j in range(i, 3):
+                E = np.zeros_like(lam)
+                E[h, i, j] += 1.0
+                E[h, j, i] += 1.0 if i != j else 0.0
+                lam += eps * E
+                fp = loss()
+                lam -= 2 * eps * E
+                fm = loss()
+                lam += eps * E
+                assert abs(np.sum(g["dlam"] * E) - (fp - fm) / (2 * eps)) < 1e-6 * (1 + abs(fp)), (h, i, j)
+
+
+def test_full_lambda_gradient_is_the_partial_derivative_of_each_entry():
+    """Every entry on its own (a non-symmetric perturbation of the solves):
+    dLambda = -sum_t y_t x_t^T against central differences of the exact
+    forward; a diagonal Lambda's gradient is the diagonal of the full one."""
+    q, k, v, gamma, beta, lamd, d_o = tiny(8)
+    lam = full_lambda(np.random.default_rng(9), 1, 3)
+    g = mesa_backward(q, k, v, gamma, beta, lam, d_o, max_steps=0, tol=0.0, exact=True, chunk=2)
+
+    def loss():
+        r = mesa_forward(q, k, v, gamma, beta, lam, max_steps=0, tol=0.0, exact=True)
+        return float(np.sum(d_o * r["o_exact"]))
+
+    assert pins.rel(g["dlam"], fd_grad(loss, lam)) < 1e-6
+    gd = mesa_backward(q, k, v, gamma, beta, lamd, d_o, max_steps=4, tol=0.0, chunk=2)
+    gf = mesa_backward(q, k, v, gamma, beta, np.stack([np.diag(r) for r in lamd]), d_o, max_steps=4, tol=0.0,
+                       chunk=2)
+    assert np.allclose(gd["dlam"], np.diagonal(gf["dlam"], axis1=1, axis2=2), rtol=1e-12, atol=1e-12)
+    for name in ("dq", "dk", "dv", "dgamma", "dbeta"):
+        assert np.allclose(gd[name], gf[name], rtol=1e-12, atol=1e-12), name
+
+
 def test_state_gradients_match_finite_differences_of_the_forward():
     q, k, v, gamma, beta, lam, d_o = tiny(2, dv=3)
     rng = np.random.default_rng(3)
