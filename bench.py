@@ -371,6 +371,22 @@ def bench_forward_full_lambda(cfg, steps, warmup):
     # counted flops: the diagonal forward's plus the full Lambda's product per CG iteration
     f = flops_per_token(cfg.d, cfg.chunk, n_avg)["total"] + n_avg * 2 * cfg.d * cfg.d
     tflops = f * tokens / (ms * 1e-3) / 1e12
+    # the backward with the same Lambda (adjoint solves with the full matrix, dLambda [H, d, d])
+    x = mesa.fwd_chunked_ex(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                            return_x=True)["x"]
+    d_o = torch.randn(x.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(cfg.seed))
+    wsb = torch.empty(mesa.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, cfg.max_steps, cfg.tol),
+                      device="cuda", dtype=torch.uint8)
+    gres = mesa.bwd_chunked_ex(q, k, v, gamma, beta, lam, x, d_o, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                               tol=cfg.tol, workspace=wsb)
+
+    def bstep():
+        mesa.bwd_chunked_ex(q, k, v, gamma, beta, lam, x, d_o, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                            tol=cfg.tol, workspace=wsb, out=gres)
+
+    for _ in range(warmup):
+        bstep()
+    ms_b = time_events(bstep, steps)
     return {
         "workload": f"forward with a full SPD Lambda per head: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
                     f"{cfg.dtype}, chunk {cfg.chunk}, cg_steps_mean {n_avg:.1f}",
@@ -378,6 +394,7 @@ def bench_forward_full_lambda(cfg, steps, warmup):
         "tokens_per_s": round(tokens / (ms * 1e-3), 1),
         "counted_TFLOPs": round(tflops, 2),
         "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "backward_ms_per_call": round(ms_b, 4),
     }
 
 

@@ -296,6 +296,30 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d,
                              int32_t states_in_workspace,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* mesa_bwd_chunked with Lambda either diagonal (lambda_full = 0: exactly
+ * mesa_bwd_chunked) or a full symmetric positive definite matrix per head
+ * (lambda_full = 1; MesaNet page, technical summary, "Mesa layer": Lambda is
+ * a symmetric positive definite regulariser):
+ *   lambda   fp32 [H, dk, dk] in, the matrix of the forward call
+ *            (mesa_fwd_chunked_ex with lambda_full = 1)
+ *   dlambda  fp32 [H, dk, dk] out: -sum_{b,t} y_t x_t^T, the partial
+ *            derivative of each entry of the solves' matrix (not
+ *            symmetrised; a caller that ties Lambda_ij to Lambda_ji adds the
+ *            transpose).  Its diagonal is the diagonal case's dlambda.
+ * The adjoint solves take the full matrix like the forward's.  Descriptors,
+ * workspace (mesa_bwd_workspace_bytes) and errors are those of
+ * mesa_bwd_chunked; lambda_full other than 0 or 1 is MESA_ERR_INVALID_ARG. */
+mesa_status mesa_bwd_chunked_ex(const mesa_fwd_desc* d,
+                                const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, const float* lambda,
+                                int32_t lambda_full, const float* h0, const float* g0,
+                                const float* x, const float* d_o,
+                                const float* d_hfinal, const float* d_gfinal,
+                                float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                                float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                                int32_t states_in_workspace,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- general decode step --------------------------------------------------------
  *
  * Every decode variant in one call, with the Lambda of the pages' objective

@@ -255,7 +255,7 @@ mesa_status check_bwd(const mesa_fwd_desc* d) {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct BwdLayout {
-  size_t fwd, rhs, nu, yn, snap, lam, seg, segdec, total;
+  size_t fwd, rhs, nu, yn, snap, lam, seg, segdec, lamf, total;
   int NS, SEG;
 };
 
@@ -274,6 +274,7 @@ BwdLayout bwd_layout(const mesa_fwd_desc* d) {
   L.lam = off; off = align256(off + BH * L.NS * D * 4);
   L.seg = off; off = align256(off + BH * 2 * (L.NS - 1) * D * D * 4);
   L.segdec = off; off = align256(off + BH * (L.NS - 1) * 4);
+  L.lamf = off; off = align256(off + (size_t)d->H * mesa::kLamSplits * D * D * 4);  // full-Lambda partial sums
   L.total = off;
   return L;
 }
@@ -287,14 +288,18 @@ size_t mesa_bwd_workspace_bytes(const mesa_fwd_desc* d) {
   return bwd_layout(d).total;
 }
 
-mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
-                             const float* gamma, const float* beta, const float* lambda,
-                             const float* h0, const float* g0, const float* x, const float* d_o,
-                             const float* d_hfinal, const float* d_gfinal,
-                             float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
-                             float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
-                             int32_t states_in_workspace, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+mesa_status bwd_impl(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta, const float* lambda, bool lam_full,
+                     const float* h0, const float* g0, const float* x, const float* d_o,
+                     const float* d_hfinal, const float* d_gfinal,
+                     float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                     float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                     int32_t states_in_workspace, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   const mesa_status st = check_bwd(d);
   if (st != MESA_OK) return st;
   if (states_in_workspace != 0 && states_in_workspace != 1) return MESA_ERR_INVALID_ARG;
@@ -336,6 +341,8 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
   bp.seg_state = reinterpret_cast<float*>(ws + L.seg);
   bp.seg_decay = reinterpret_cast<float*>(ws + L.segdec);
   bp.BH = BH; bp.H = d->H; bp.T = d->T; bp.NC = NC; bp.NS = L.NS; bp.SEG = L.SEG;
+  bp.lam_full = lam_full ? 1 : 0;
+  bp.lam_full_part = reinterpret_cast<float*>(ws + L.lamf);
   if (any) {
     // 2. right-hand sides of the adjoint systems
     if (mesa::launch_bwd(0, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
@@ -347,12 +354,44 @@ mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
     cp.unscaled = reinterpret_cast<int32_t*>(ws + 2 * snap);
     cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
     cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
+    cp.lam_full = lam_full ? 1 : 0;
     if (mesa::launch_cg(true, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
-  // 4. adjoint scan (also the initial-state gradients); 5. per-token gradients
+  // 4. adjoint scan (also the initial-state gradients); 5. per-token gradients and dlambda
   if ((any || dh0 || dg0) && mesa::launch_bwd(1, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
   if (mesa::launch_bwd(2, D, bp, stream) != hipSuccess) return MESA_ERR_HIP;
   return MESA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mesa_status mesa_bwd_chunked(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* lambda,
+                             const float* h0, const float* g0, const float* x, const float* d_o,
+                             const float* d_hfinal, const float* d_gfinal,
+                             float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                             float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                             int32_t states_in_workspace, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return bwd_impl(d, q, k, v, gamma, beta, lambda, false, h0, g0, x, d_o, d_hfinal, d_gfinal, dq, dk, dv,
+                  dgamma, dbeta, dlambda, dh0, dg0, adj_steps, states_in_workspace, workspace,
+                  workspace_bytes, stream);
+}
+
+mesa_status mesa_bwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, const float* lambda,
+                                int32_t lambda_full, const float* h0, const float* g0, const float* x,
+                                const float* d_o, const float* d_hfinal, const float* d_gfinal,
+                                float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                                float* dlambda, float* dh0, float* dg0, int32_t* adj_steps,
+                                int32_t states_in_workspace, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (lambda_full != 0 && lambda_full != 1) return MESA_ERR_INVALID_ARG;
+  return bwd_impl(d, q, k, v, gamma, beta, lambda, lambda_full == 1, h0, g0, x, d_o, d_hfinal, d_gfinal, dq,
+                  dk, dv, dgamma, dbeta, dlambda, dh0, dg0, adj_steps, states_in_workspace, workspace,
+                  workspace_bytes, stream);
 }
 
 mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32_t window,

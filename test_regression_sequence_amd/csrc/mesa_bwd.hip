@@ -45,6 +45,10 @@
 //                    dgamma above; writes dq, dk, dv, dbeta, dgamma.
 //   bwd_lambda_kernel dlambda summed over the batch (the scan sums each
 //                    sequence's -y_t * x_t while staging its chunks).
+//   bwd_lamfull_*    a full Lambda: dLambda = -sum_{b,t} y_t x_t^T per head,
+//                    the partial derivative of each entry of the solves' matrix
+//                    (fp32 products over 64-row tiles staged in LDS, in row
+//                    splits, then the splits summed).
 // Every chunk product is an MFMA 16x16x32 bf16 contraction with fp32
 // accumulation on tiles staged in LDS with the contraction index contiguous
 // (rows padded by 16 bytes, so the 16 rows an MFMA operand reads fall in
@@ -937,6 +941,68 @@ __global__ __launch_bounds__(128) void bwd_lambda_kernel(BwdParams p, int D) {
   }
 }
 
+// Partial sums of -y_t x_t^T over one split of the (b, t) rows of head h, for
+// one 64 x 64 block (rows i of y, columns j of x).  y_t = nu_t * yn_t.  Each of
+// the 256 threads owns a 4 x 4 patch; rows come through LDS in tiles of 64.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_lamfull_part_kernel(BwdParams p) {
+  constexpr int NB = D / 64;  // 64-wide blocks per side
+  const int sp = blockIdx.x % kLamSplits;
+  const int blk = (blockIdx.x / kLamSplits) % (NB * NB);
+  const int h = blockIdx.x / (kLamSplits * NB * NB);
+  const int ib = blk / NB, jb = blk % NB;
+  const int B = p.BH / p.H;
+  const long long R = (long long)B * p.T;  // rows (b, t) of head h
+  const long long r_lo = R * sp / kLamSplits, r_hi = R * (sp + 1) / kLamSplits;
+  __shared__ f32x4 Ys[64][16];
+  __shared__ f32x4 Xs[64][16];
+  const int tid = threadIdx.x;
+  const int pi = tid / 16, pj = tid % 16;  // patch rows 4pi.., cols 4pj..
+  f32x4 acc[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                  f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (long long r0 = r_lo; r0 < r_hi; r0 += 64) {
+    // stage 64 rows: thread tid loads quads (tid % 16) of rows tid / 16 + 16 u
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int rr = tid / 16 + 16 * u;
+      const long long r = r0 + rr;
+      f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f}, xv = yv;
+      if (r < r_hi) {
+        const int b = (int)(r / p.T), t = (int)(r % p.T);
+        const size_t row = (size_t)(b * p.H + h) * p.T + t;
+        yv = *reinterpret_cast<const f32x4*>(p.yn + row * D + 64 * ib + 4 * pj) * p.nu[row];
+        xv = *reinterpret_cast<const f32x4*>(p.x + row * D + 64 * jb + 4 * pj);
+      }
+      Ys[rr][pj] = yv;
+      Xs[rr][pj] = xv;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int rr = 0; rr < 64; ++rr) {
+      const f32x4 yv = Ys[rr][pi];
+      const f32x4 xv = Xs[rr][pj];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a] += yv[a] * xv;
+    }
+    __syncthreads();
+  }
+  float* out = p.lam_full_part + ((size_t)h * kLamSplits + sp) * D * D;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    *reinterpret_cast<f32x4*>(out + (size_t)(64 * ib + 4 * pi + a) * D + 64 * jb + 4 * pj) = -acc[a];
+}
+
+// dLambda[h] = sum of the splits' partial sums
+__global__ __launch_bounds__(256) void bwd_lamfull_sum_kernel(BwdParams p, int D) {
+  const size_t n = (size_t)D * D;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;  // element of all heads
+  if (e >= (size_t)p.H * n) return;
+  const size_t h = e / n, ij = e % n;
+  float acc = 0.f;
+  for (int sp = 0; sp < kLamSplits; ++sp) acc += p.lam_full_part[(h * kLamSplits + sp) * n + ij];
+  p.dlam[e] = acc;
+}
+
 template <int D>
 hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
   const dim3 chunks((unsigned)(p.BH * p.NC));
@@ -960,7 +1026,16 @@ hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
         hipLaunchKernelGGL((bwd_grad_kernel<D>), chunks, dim3(kThreads), 0, s, p);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       }
-      hipLaunchKernelGGL(bwd_lambda_kernel, dim3((unsigned)p.H), dim3(128), 0, s, p, D);
+      if (p.lam_full) {
+        constexpr int NB = D / 64;
+        hipLaunchKernelGGL((bwd_lamfull_part_kernel<D>), dim3((unsigned)(p.H * NB * NB * kLamSplits)), dim3(256), 0,
+                           s, p);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        const size_t n = (size_t)p.H * D * D;
+        hipLaunchKernelGGL(bwd_lamfull_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, D);
+      } else {
+        hipLaunchKernelGGL(bwd_lambda_kernel, dim3((unsigned)p.H), dim3(128), 0, s, p, D);
+      }
       break;
     default: return hipErrorInvalidValue;
   }

@@ -134,7 +134,13 @@ struct BwdParams {
   float* seg_state;         // [BH, 2, NS-1, D*D]: segment totals, then carry-in states
   float* seg_decay;         // [BH, NS-1]: total decay of segments 1..NS-1
   int BH, H, T, NC, NS, SEG;
+  // a full Lambda: dlam is [H, D, D], summed from kLamSplits partial sums per head
+  int lam_full;
+  float* lam_full_part;     // [H, kLamSplits, D, D]
 };
+
+// Row splits of the full-Lambda gradient -sum_{b,t} y_t x_t^T per head.
+constexpr int kLamSplits = 32;
 
 // Segments of the adjoint scan: a sequence is split when there are too few
 // (sequence, 32-row stripe) units to fill the chip (two resident workgroups per CU)

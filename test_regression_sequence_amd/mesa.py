@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.mesa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdDesc)]
         L.mesa_bwd_chunked.restype = ctypes.c_int
         L.mesa_bwd_chunked.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 21 + [I32, P, S, P]
+        L.mesa_bwd_chunked_ex.restype = ctypes.c_int
+        L.mesa_bwd_chunked_ex.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 6 + [I32] + [P] * 15 + [I32, P, S, P]
         L.mesa_qk_preprocess.restype = ctypes.c_int
         L.mesa_qk_preprocess.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P, P, F,
                                          P, P, P, P, P]
@@ -392,13 +394,36 @@ def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps
     dgamma, dbeta [B, H, T], dlam [H, d] (fp32) and, with state_grads, dh0, dg0.
     states_in_workspace: the forward ran with ``workspace`` (bwd_workspace_bytes
     long) and left its boundary states there, so they are not recomputed."""
+    return _bwd(False, q, k, v, gamma, beta, lam, x, d_o, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, d_hfinal=d_hfinal, d_gfinal=d_gfinal, state_grads=state_grads,
+                return_steps=return_steps, out=out, workspace=workspace,
+                states_in_workspace=states_in_workspace, stream=stream)
+
+
+def bwd_chunked_ex(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps: int = 30,
+                   tol: float = 0.0, h0=None, g0=None, d_hfinal=None, d_gfinal=None,
+                   state_grads: bool = False, return_steps: bool = False, out=None,
+                   workspace: Optional[torch.Tensor] = None, states_in_workspace: bool = False,
+                   stream=None) -> dict:
+    """``bwd_chunked`` with ``lam`` the diagonal [H, d] or a full symmetric positive
+    definite matrix per head [H, d, d]; with the full form ``dlam`` is [H, d, d],
+    the partial derivative of each entry (-sum_t y_t x_t^T)."""
+    return _bwd(True, q, k, v, gamma, beta, lam, x, d_o, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, d_hfinal=d_hfinal, d_gfinal=d_gfinal, state_grads=state_grads,
+                return_steps=return_steps, out=out, workspace=workspace,
+                states_in_workspace=states_in_workspace, stream=stream)
+
+
+def _bwd(ex: bool, q, k, v, gamma, beta, lam, x, d_o, *, chunk, max_steps, tol, h0, g0, d_hfinal, d_gfinal,
+         state_grads, return_steps, out, workspace, states_in_workspace, stream) -> dict:
     B, H, T, d = q.shape
     code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, (B, H, T, d), q.dtype)
     _need(gamma, "gamma", (B, H, T), torch.float32)
     _need(beta, "beta", (B, H, T), torch.float32)
-    _need(lam, "lam", (H, d), torch.float32)
+    lam_full = ex and lam.dim() == 3
+    _need(lam, "lam", (H, d, d) if lam_full else (H, d), torch.float32)
     for name, t in (("x", x), ("d_o", d_o)):
         _need(t, name, (B, H, T, d), torch.float32)
     for name, t in (("h0", h0), ("g0", g0), ("d_hfinal", d_hfinal), ("d_gfinal", d_gfinal)):
@@ -415,7 +440,7 @@ def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps
         return out.get(key) if out.get(key) is not None else torch.empty(shape, device=dev, dtype=dtype)
 
     res = {key: get(key, (B, H, T, d)) for key in ("dq", "dk", "dv")}
-    res.update(dgamma=get("dgamma", (B, H, T)), dbeta=get("dbeta", (B, H, T)), dlam=get("dlam", (H, d)))
+    res.update(dgamma=get("dgamma", (B, H, T)), dbeta=get("dbeta", (B, H, T)), dlam=get("dlam", (H, d, d) if lam_full else (H, d)))
     if state_grads:
         res.update(dh0=get("dh0", (B, H, d, d)), dg0=get("dg0", (B, H, d, d)))
     if return_steps:
@@ -423,13 +448,18 @@ def bwd_chunked(q, k, v, gamma, beta, lam, x, d_o, *, chunk: int = 64, max_steps
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
     wbytes = workspace.numel() * workspace.element_size()
-    code_ = L.mesa_bwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam),
-                               _ptr(h0), _ptr(g0), _ptr(x), _ptr(d_o), _ptr(d_hfinal), _ptr(d_gfinal),
-                               _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dgamma"]),
-                               _ptr(res["dbeta"]), _ptr(res["dlam"]), _ptr(res.get("dh0")), _ptr(res.get("dg0")),
-                               _ptr(res.get("adj_steps")), 1 if states_in_workspace else 0, _ptr(workspace),
-                               ctypes.c_size_t(wbytes), _stream(stream))
-    _check(code_, "mesa_bwd_chunked")
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam))
+    rest = (_ptr(h0), _ptr(g0), _ptr(x), _ptr(d_o), _ptr(d_hfinal), _ptr(d_gfinal),
+            _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dgamma"]),
+            _ptr(res["dbeta"]), _ptr(res["dlam"]), _ptr(res.get("dh0")), _ptr(res.get("dg0")),
+            _ptr(res.get("adj_steps")), 1 if states_in_workspace else 0, _ptr(workspace),
+            ctypes.c_size_t(wbytes), _stream(stream))
+    if ex:
+        code_ = L.mesa_bwd_chunked_ex(*head, 1 if lam_full else 0, *rest)
+        _check(code_, "mesa_bwd_chunked_ex")
+    else:
+        code_ = L.mesa_bwd_chunked(*head, *rest)
+        _check(code_, "mesa_bwd_chunked")
     return res
 
 

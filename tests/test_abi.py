@@ -173,6 +173,30 @@ def test_warm_decode_validation():
     assert call(x_state=FAKE + 4) == 3
 
 
+def test_backward_full_lambda_validation():
+    L = mesa.lib()
+    P = ctypes.c_void_p
+    desc = mesa.make_desc(2, 2, 128, 128, 64, 8, 0.0, 1)
+    need = L.mesa_bwd_workspace_bytes(ctypes.byref(desc))
+
+    def call(desc=desc, lam_full=1, ws_bytes=need, dlam=FAKE):
+        ptrs = [P(FAKE)] * 21
+        ptrs[6] = ptrs[7] = ptrs[10] = ptrs[11] = None          # h0, g0, d_hfinal, d_gfinal
+        ptrs[17] = P(dlam) if dlam else None
+        ptrs[18] = ptrs[19] = ptrs[20] = None                    # dh0, dg0, adj_steps
+        return L.mesa_bwd_chunked_ex(ctypes.byref(desc), *ptrs[:6], lam_full, *ptrs[6:], 0, P(FAKE),
+                                     ctypes.c_size_t(ws_bytes), None)
+
+    assert call(lam_full=2) == 1
+    assert call(lam_full=-1) == 1
+    assert call(dlam=0) == 1
+    assert call(dlam=FAKE + 4) == 3
+    assert call(ws_bytes=need - 1) == 4
+    assert call(desc=mesa.make_desc(2, 2, 128, 128, 64, 8, 0.0, 0)) == 2   # fp32 inputs
+    assert call(desc=mesa.make_desc(2, 2, 128, 128, 32, 8, 0.0, 1)) == 2   # chunk 32
+    assert call(desc=mesa.make_desc(2, 2, 128, 32, 64, 8, 0.0, 1)) == 2    # d 32
+
+
 def test_preprocess_validation():
     L = mesa.lib()
     P = ctypes.c_void_p
