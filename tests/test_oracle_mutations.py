@@ -58,6 +58,9 @@ MUTATIONS = {
     "bwd_dgamma_current_state": ("np.sum(Hhat * Hp) + np.sum(Ghat * Gp)", "np.sum(Hhat * Ht) + np.sum(Ghat * Gt)"),
     "bwd_dbeta_without_G": ("kt @ Hhat @ kt + vt @ Ghat @ kt", "kt @ Hhat @ kt"),
     "bwd_dlam_sign": ("dlam[h] -= yt * xt", "dlam[h] += yt * xt"),
+    "bwd_full_dlam_transposed": ("dlam[h] -= np.outer(yt, xt)", "dlam[h] -= np.outer(xt, yt)"),
+    "bwd_full_lambda_read_as_diagonal": ("Lam = lam[h] if full else np.diag(lam[h])",
+                                         "Lam = np.diag(np.diagonal(lam[h])) if full else np.diag(lam[h])"),
     "bwd_dq_is_solution": ('out["dq"][s_, t] = yt', 'out["dq"][s_, t] = xt'),
     "bwd_dv_reads_solution": ('out["dv"][s_, t] = bt * (Ghat @ kt)', 'out["dv"][s_, t] = bt * (Ghat @ xt)'),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
@@ -171,7 +174,9 @@ def run_pins(m):
         bwd.mesa_backward, bwd.mesa_forward = m.mesa_backward, m.mesa_forward
         for fn in (lambda: bwd.test_gradients_match_finite_differences_of_the_objective(0, 1),
                    bwd.test_state_gradients_match_finite_differences_of_the_forward,
-                   bwd.test_homogeneity_identities):
+                   bwd.test_homogeneity_identities,
+                   bwd.test_full_lambda_gradient_along_symmetric_directions_matches_the_objective,
+                   bwd.test_full_lambda_gradient_is_the_partial_derivative_of_each_entry):
             try:
                 fn()
             except AssertionError:
