@@ -21,7 +21,10 @@ Training", technical summary, "Mesa layer" section):
 
 This file runs that recurrence token by token with explicit H_t and G_t, and
 solves every system twice: by the CG schedule (the result the GPU path must
-match) and exactly (``numpy.linalg.solve``, the definition).
+match) and exactly, by a Cholesky factorisation (the definition).  The same
+section makes Lambda symmetric positive definite, so every H_t + Lambda is SPD;
+the factorisation fails loudly on any system that is not, which makes every
+exact solve also a check of that property.
 
 CG variant (the pages say only "CG"): Hestenes-Stiefel conjugate gradient from
 x_0 = 0 with the recursive residual, as in Saad, "Iterative Methods for Sparse
@@ -39,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["cg_solve", "mesa_forward", "mesa_decode_step", "diag_or_full", "qk_preprocess",
+__all__ = ["cg_solve", "cholesky_solve", "mesa_forward", "mesa_decode_step", "diag_or_full", "qk_preprocess",
            "mesa_backward"]
 
 
@@ -117,6 +120,21 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
     return x, steps
 
 
+def cholesky_solve(A: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Exact solve of the SPD systems A[s] x = b[s] by Cholesky, fp64.
+
+    A: [S, d, d]; b: [S, d].  ``scipy.linalg.cho_factor`` raises
+    ``numpy.linalg.LinAlgError`` when a system is not positive definite.
+    """
+    from scipy.linalg import cho_factor, cho_solve
+    A = np.asarray(A, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    x = np.empty_like(b)
+    for s in range(A.shape[0]):
+        x[s] = cho_solve(cho_factor(A[s], lower=True), b[s])
+    return x
+
+
 def _flat(a, S, *tail):
     return np.asarray(a, dtype=np.float64).reshape(S, *tail)
 
@@ -190,7 +208,7 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
         res_prev[:, t] = rp
         o_cg[:, t] = np.matmul(Gs, xs[:, :, None])[:, :, 0]
         if exact:
-            xe = np.linalg.solve(A, qf[:, t][:, :, None])[:, :, 0]
+            xe = cholesky_solve(A, qf[:, t])
             x_ex[:, t] = xe
             o_ex[:, t] = np.matmul(Gs, xe[:, :, None])[:, :, 0]
         if record_every and ((t + 1) % record_every == 0 or t == T - 1):
@@ -335,7 +353,7 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
             Hs, Gs = step(Hs, Gs, t)
             A = Hs + Lam
             if exact:
-                xt = np.linalg.solve(A, qf[s_, t])
+                xt = cholesky_solve(A[None], qf[s_, t][None])[0]
             else:
                 xs_, _ = cg_solve(A[None], qf[s_, t][None], max_steps, tol,
                                   None if fs is None else fs[s_, t:t + 1])
@@ -357,7 +375,7 @@ def mesa_backward(q, k, v, gamma, beta, lam, d_o, *, max_steps: int, tol: float,
                 A = Ht + Lam
                 dxt = Gt.T @ dot
                 if exact:
-                    yt = np.linalg.solve(A, dxt)
+                    yt = cholesky_solve(A[None], dxt[None])[0]
                     na = 0
                 else:
                     nrm = np.linalg.norm(dxt)

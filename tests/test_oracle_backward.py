@@ -106,9 +106,19 @@ def test_full_lambda_gradient_is_the_partial_derivative_of_each_entry():
     lam = full_lambda(np.random.default_rng(9), 1, 3)
     g = mesa_backward(q, k, v, gamma, beta, lam, d_o, max_steps=0, tol=0.0, exact=True, chunk=2)
 
+    T = q.shape[2]
+
     def loss():
-        r = mesa_forward(q, k, v, gamma, beta, lam, max_steps=0, tol=0.0, exact=True)
-        return float(np.sum(d_o * r["o_exact"]))
+        # sum_t d_o_t . G_t (H_t + Lambda)^{-1} q_t with the states assembled from the
+        # forget weights and a general (LU) solve: a non-symmetric perturbation of one
+        # entry is a different system, which a symmetric factorisation cannot represent
+        tot = 0.0
+        for t in range(T):
+            z = [pins.zeta(gamma[0, 0], beta[0, 0], t, j) for j in range(t + 1)]
+            Ht = sum(zj * np.outer(k[0, 0, j], k[0, 0, j]) for j, zj in enumerate(z))
+            Gt = sum(zj * np.outer(v[0, 0, j], k[0, 0, j]) for j, zj in enumerate(z))
+            tot += float(d_o[0, 0, t] @ (Gt @ np.linalg.solve(Ht + lam[0], q[0, 0, t])))
+        return tot
 
     assert pins.rel(g["dlam"], fd_grad(loss, lam)) < 1e-6
     gd = mesa_backward(q, k, v, gamma, beta, lamd, d_o, max_steps=4, tol=0.0, chunk=2)

@@ -63,6 +63,17 @@ MUTATIONS = {
                                          "Lam = np.diag(np.diagonal(lam[h])) if full else np.diag(lam[h])"),
     "bwd_dq_is_solution": ('out["dq"][s_, t] = yt', 'out["dq"][s_, t] = xt'),
     "bwd_dv_reads_solution": ('out["dv"][s_, t] = bt * (Ghat @ kt)', 'out["dv"][s_, t] = bt * (Ghat @ xt)'),
+    "forced_steps_one_extra": ("go = it < forced_steps", "go = it <= forced_steps"),
+    "forced_steps_ignored": ("            go = it < forced_steps\n", "            go = np.ones(S, dtype=bool)\n"),
+    "forced_steps_as_a_cap": ("            go = it < forced_steps\n",
+                              "            go = (it < forced_steps) & ((np.sqrt(rho) > tol) if tol > 0 else True)\n"),
+    "solve_at_skips_state_update": (
+        "        Hs = g_t * Hs + b_t * (kt[:, :, None] * kt[:, None, :])\n",
+        "        Hs = (g_t * Hs + b_t * (kt[:, :, None] * kt[:, None, :])) if (solve_at is None or solve_at[t]) else Hs\n"),
+    "solve_at_shifted": ("if solve_at is not None and not solve_at[t]:",
+                         "if solve_at is not None and not solve_at[max(t - 1, 0)]:"),
+    "exact_solve_wrong_triangle": ("cho_solve(cho_factor(A[s], lower=True), b[s])",
+                                   "cho_solve((np.linalg.cholesky(A[s]), False), b[s])"),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
                                        ("            x_ex[:, t] = xe\n",
                                         "            x_ex[:, t] = xe\n            x_prev = xe\n")],
@@ -187,6 +198,21 @@ def run_pins(m):
                 break
     finally:
         bwd.mesa_backward, bwd.mesa_forward = saved
+    # forced step counts and solving at selected tokens
+    saved = (pins.mesa_forward, pins.cg_solve)
+    try:
+        pins.mesa_forward, pins.cg_solve = m.mesa_forward, m.cg_solve
+        for tag, fn in (("forced", pins.test_forced_counts_are_krylov_projections_per_system),
+                        ("forced-free", pins.test_forced_counts_reproduce_free_runs_bitwise),
+                        ("solve_at", pins.test_solve_at_matches_the_objective_and_the_full_run)):
+            try:
+                fn()
+            except AssertionError:
+                failed.append(tag)
+            except Exception:
+                failed.append(tag + "-crash")
+    finally:
+        pins.mesa_forward, pins.cg_solve = saved
     # P7: tolerance stops before an iteration
     x, n = m.cg_solve(np.eye(3)[None] * 2.0, np.array([[1e-7, 0.0, 0.0]]), 10, 1e-6)
     if n[0] != 0:

@@ -155,15 +155,35 @@ def test_p2_cross_state_orientation():
 # P3: finite termination on the configurations' own distributions
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [16, 32])
-def test_p3_d_steps_equal_exact_solve(d):
+LM_DIST = dict(lam=("uniform", 0.25, 1.0), gamma_logit=(2.0, 6.0), beta=("uniform", 0.0, 1.0))
+LONG_DIST = dict(lam=("const", 0.25), gamma_logit=(4.0, 9.0), beta=("beta", 5.0, 1.0))
+
+
+@pytest.mark.parametrize("d,dist", [(16, "lm"), (32, "lm"), (64, "lm"), (128, "lm"), (128, "long")])
+def test_p3_d_steps_equal_exact_solve(d, dist):
+    """d CG steps reproduce the Cholesky solve, at the head dims of the workloads
+    and on their distributions (language-model gates; near-one gates with
+    Beta(5,1) writes and Lambda = 0.25 I)."""
     from test_regression_sequence_amd.inputs import small_fwd, make_fwd_inputs
-    cfg = small_fwd(B=1, H=2, T=48, d=d, chunk=16, dtype="f32", max_steps=d)
+    cfg = small_fwd(B=1, H=2, T=48, d=d, chunk=16, dtype="f32", max_steps=d,
+                    **(LM_DIST if dist == "lm" else LONG_DIST))
     x = make_fwd_inputs(cfg)
     res = mesa_forward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"],
                        max_steps=d, tol=0.0)
     assert rel(res["o_cg"], res["o_exact"]) < 1e-10
     assert rel(res["x_cg"], res["x_exact"]) < 1e-10
+
+
+def test_exact_solve_rejects_a_system_that_is_not_positive_definite():
+    """The exact solve is a Cholesky factorisation: a Lambda that makes H_t + Lambda
+    indefinite (outside the pages' SPD regulariser) raises instead of solving."""
+    rng = np.random.default_rng(19)
+    q, k, v, gamma, beta = rand_slice(rng, 5, 4, 3)
+    lam = np.array([[0.5, 0.5, -50.0, 0.5]])
+    with pytest.raises(np.linalg.LinAlgError):
+        mesa_forward(q, k, v, gamma, beta, lam, max_steps=2, tol=0.0, exact=True)
+    # the CG schedule alone does not factorise, so it still runs
+    mesa_forward(q, k, v, gamma, beta, lam, max_steps=2, tol=0.0, exact=False)
 
 
 # ---------------------------------------------------------------------------
@@ -223,6 +243,95 @@ def test_p4_cg_iterates_are_krylov_projections(seed, d):
         x, steps = cg_solve(A[None].astype(float), q[None].astype(float), n, 0.0)
         assert steps[0] == n
         assert rel(x[0], ref) < 1e-9, (n, x[0], ref)
+
+
+# ---------------------------------------------------------------------------
+# forced step counts (the mode every dynamic-CG parity check runs the oracle in)
+# ---------------------------------------------------------------------------
+
+def test_forced_counts_are_krylov_projections_per_system(seed=20, d=5):
+    """Each system of a batch, forced to its own count n_s below the cap, lands on
+    its n_s-th A-norm Krylov projection (exact rationals); no system runs past
+    its count and none stops short."""
+    rng = np.random.default_rng(seed)
+    S = 6
+    As, qs, Aq, qq = [], [], [], []
+    for _ in range(S):
+        Mi = rng.integers(-3, 4, (d, d))
+        A = (Mi @ Mi.T + np.diag(rng.integers(1, 4, d))).astype(np.int64)
+        qv = rng.integers(-4, 5, d).astype(np.int64)
+        qv[0] = qv[0] if qv[0] != 0 else 1
+        As.append(A); qs.append(qv)
+        Aq.append([[Fraction(int(a)) for a in row] for row in A])
+        qq.append([Fraction(int(z)) for z in qv])
+    forced = np.array([0, 1, 2, 3, 4, 2])
+    x, steps = cg_solve(np.stack(As).astype(float), np.stack(qs).astype(float), d + 3, 0.0,
+                        forced_steps=forced)
+    assert np.array_equal(steps, forced)
+    for s_ in range(S):
+        ref = np.array([float(z) for z in _krylov_iterate(Aq[s_], qq[s_], int(forced[s_]))])
+        assert rel(x[s_], ref) < 1e-9, (s_, forced[s_])
+    # the tolerance plays no part once counts are forced
+    x2, steps2 = cg_solve(np.stack(As).astype(float), np.stack(qs).astype(float), d + 3, 1e3,
+                          forced_steps=forced)
+    assert np.array_equal(steps2, forced) and np.array_equal(x2, x)
+
+
+def test_forced_counts_reproduce_free_runs_bitwise(seed=21):
+    """Forcing every token to n equals the fixed-step mode at n; forcing the
+    counts a tolerance run chose reproduces that run's x and o bit for bit."""
+    rng = np.random.default_rng(seed)
+    T, d = 14, 16
+    q, k, v, gamma, beta = rand_slice(rng, T, d, d, gamma_lo=0.8)
+    lam = rng.uniform(0.25, 1.0, (1, d))
+    for n in (1, 3, 5):
+        fixed = mesa_forward(q, k, v, gamma, beta, lam, max_steps=n, tol=0.0, exact=False)
+        forced = mesa_forward(q, k, v, gamma, beta, lam, max_steps=n + 4, tol=0.0, exact=False,
+                              forced_steps=np.full((1, 1, T), n))
+        assert np.array_equal(forced["o_cg"], fixed["o_cg"])
+        assert np.array_equal(forced["x_cg"], fixed["x_cg"])
+        assert np.all(forced["steps"] == n)
+    free = mesa_forward(q, k, v, gamma, beta, lam, max_steps=12, tol=1e-3, exact=False)
+    assert len(np.unique(free["steps"])) > 3 and free["steps"].max() == 12
+    again = mesa_forward(q, k, v, gamma, beta, lam, max_steps=12, tol=1e-3, exact=False,
+                         forced_steps=free["steps"])
+    for key in ("o_cg", "x_cg", "steps", "res_norm", "res_prev"):
+        assert np.array_equal(again[key], free[key]), key
+
+
+# ---------------------------------------------------------------------------
+# solving at selected tokens only (how long sequences are sampled)
+# ---------------------------------------------------------------------------
+
+def test_solve_at_matches_the_objective_and_the_full_run(seed=22):
+    """Outputs at the selected tokens are the objective's minimiser (brute force)
+    and the full run's outputs bit for bit; other tokens stay zero; the states
+    still absorb every token."""
+    rng = np.random.default_rng(seed)
+    T, dk, dv = 11, 4, 3
+    q, k, v, gamma, beta = rand_slice(rng, T, dk, dv)
+    lam = rng.uniform(0.3, 1.2, (1, dk))
+    at = np.zeros(T, bool)
+    at[[0, 3, 4, 9]] = True
+    part = mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0, solve_at=at,
+                        record_every=2)
+    full = mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0, record_every=2)
+    ref = brute_force_objective(q[0, 0], k[0, 0], v[0, 0], gamma[0, 0], beta[0, 0], np.diag(lam[0]))
+    assert rel(part["o_exact"][0, 0][at], ref[at]) < 1e-10
+    for key in ("o_cg", "x_cg", "o_exact", "steps"):
+        assert np.array_equal(part[key][0, 0][at], full[key][0, 0][at]), key
+        assert np.all(part[key][0, 0][~at] == 0), key
+    assert np.array_equal(part["H_final"], full["H_final"])
+    assert np.array_equal(part["G_final"], full["G_final"])
+    assert [t for t, _, _ in part["states"]] == [t for t, _, _ in full["states"]]
+    for (_, Hp, Gp), (_, Hf, Gf) in zip(part["states"], full["states"]):
+        assert np.array_equal(Hp, Hf) and np.array_equal(Gp, Gf)
+    # no token solved: the final states are the weighted sums of the whole prefix
+    none = mesa_forward(q, k, v, gamma, beta, lam, max_steps=dk, tol=0.0, solve_at=np.zeros(T, bool))
+    direct = sum(zeta(gamma[0, 0], beta[0, 0], T - 1, j) * np.outer(v[0, 0, j], k[0, 0, j])
+                 for j in range(T))
+    assert rel(none["G_final"][0, 0], direct) < 1e-12
+    assert np.all(none["o_cg"] == 0)
 
 
 # ---------------------------------------------------------------------------
