@@ -133,7 +133,9 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
  *                    dk = dv in {64, 128}; other descriptors return
  *                    MESA_ERR_UNSUPPORTED and launch nothing.
  *
- * Every other argument, the workspace and the error behaviour are those of
+ * Any other value of lambda_full returns MESA_ERR_INVALID_ARG and launches
+ * nothing, as in mesa_bwd_chunked_ex and mesa_decode_step_ex.  Every other
+ * argument, the workspace and the error behaviour are those of
  * mesa_fwd_chunked. */
 mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d,
                                 const void* q, const void* k, const void* v,

@@ -61,7 +61,7 @@ def diag_or_full(lam: np.ndarray, H: int, d: int) -> np.ndarray:
 
 def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
              forced_steps: np.ndarray | None = None, residuals: bool = False,
-             x0: np.ndarray | None = None):
+             x0: np.ndarray | None = None, history: bool = False):
     """Batched conjugate gradient on A[s] x = q[s], fp64.
 
     A: [S, d, d] symmetric positive definite; q: [S, d].
@@ -71,7 +71,9 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
     q - A x0.
     Returns (x [S, d], steps [S] int64); with ``residuals=True`` also the
     recursive residual norms ||r|| after the last executed iteration and
-    before it (equal to ||r_0|| for systems that ran no iteration).
+    before it (equal to ||r_0|| for systems that ran no iteration); with
+    ``history=True`` also [S, max_steps + 1] norms ||r_n|| after each executed
+    iteration n (column 0: ||r_0||; NaN past a system's last iteration).
     """
     A = np.asarray(A, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
@@ -87,6 +89,8 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
     rho_prev = rho.copy()
     steps = np.zeros(S, dtype=np.int64)
     stopped = np.zeros(S, dtype=bool)
+    hist = np.full((S, int(max_steps) + 1), np.nan)
+    hist[:, 0] = np.sqrt(rho)
     if forced_steps is not None:
         forced_steps = np.asarray(forced_steps).reshape(S)
     for it in range(int(max_steps)):
@@ -115,9 +119,13 @@ def cg_solve(A: np.ndarray, q: np.ndarray, max_steps: int, tol: float,
         rho_prev = np.where(go, rho, rho_prev)
         rho = np.where(go, rho_new, rho)
         steps += go
+        hist[go, it + 1] = np.sqrt(rho_new[go])
+    out = (x, steps)
     if residuals:
-        return x, steps, np.sqrt(rho), np.sqrt(rho_prev)
-    return x, steps
+        out += (np.sqrt(rho), np.sqrt(rho_prev))
+    if history:
+        out += (hist,)
+    return out
 
 
 def cholesky_solve(A: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -142,7 +150,7 @@ def _flat(a, S, *tail):
 def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                  h0=None, g0=None, forced_steps=None, exact: bool = True,
                  record_every: int | None = None, solve_at=None,
-                 warm_start: bool = False, x_init=None):
+                 warm_start: bool = False, x_init=None, residual_history: bool = False):
     """Token-by-token Mesa layer over [B, H, T, d] inputs, fp64.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv]; gamma, beta: [B, H, T];
@@ -155,6 +163,9 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     other positions are left at zero.  Used to sample long sequences.
     warm_start: start token t's CG from token t-1's CG result, token 0's from
     x_init ([B, H, dk], default 0).  Needs every token solved (no solve_at).
+    residual_history: also return ``res_hist`` [B, H, T, max_steps + 1], each
+    solved token's recursive residual norm after every CG iteration (see
+    :func:`cg_solve`; zero rows at tokens not solved).
 
     Returns a dict with o_cg, x_cg, steps, H_final, G_final (and o_exact,
     x_exact when ``exact``), shaped like the inputs.
@@ -182,6 +193,7 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     steps = np.zeros((S, T), dtype=np.int64)
     res_norm = np.zeros((S, T))
     res_prev = np.zeros((S, T))
+    res_hist = np.zeros((S, T, int(max_steps) + 1)) if residual_history else None
     o_ex = np.zeros((S, T, dv)) if exact else None
     x_ex = np.zeros((S, T, dk)) if exact else None
     states = []
@@ -198,9 +210,11 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                                Gs.reshape(B, Hh, dv, dk).copy()))
             continue
         A = Hs + Lam
-        xs, ns, rn, rp = cg_solve(A, qf[:, t], max_steps, tol,
-                                  None if fs is None else fs[:, t], residuals=True,
-                                  x0=x_prev if warm_start else None)
+        xs, ns, rn, rp, rh = cg_solve(A, qf[:, t], max_steps, tol,
+                                      None if fs is None else fs[:, t], residuals=True,
+                                      x0=x_prev if warm_start else None, history=True)
+        if residual_history:
+            res_hist[:, t] = rh
         x_prev = xs
         x_cg[:, t] = xs
         steps[:, t] = ns
@@ -224,6 +238,8 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
         G_final=Gs.reshape(B, Hh, dv, dk),
         states=states,
     )
+    if residual_history:
+        out["res_hist"] = res_hist.reshape(B, Hh, T, -1)
     if exact:
         out["o_exact"] = o_ex.reshape(B, Hh, T, dv)
         out["x_exact"] = x_ex.reshape(B, Hh, T, dk)
@@ -248,10 +264,10 @@ def mesa_decode_step(q, k, v, gamma, beta, lam, h, g, *, max_steps: int, tol: fl
                        max_steps=max_steps, tol=tol, h0=h, g0=g,
                        forced_steps=None if forced_steps is None
                        else np.asarray(forced_steps).reshape(N, Hh, 1),
-                       exact=exact, warm_start=x0 is not None, x_init=x0)
+                       exact=exact, warm_start=x0 is not None, x_init=x0, residual_history=True)
     out = dict(o=res["o_cg"][:, :, 0], x=res["x_cg"][:, :, 0], steps=res["steps"][:, :, 0],
                res_norm=res["res_norm"][:, :, 0], res_prev=res["res_prev"][:, :, 0],
-               h=res["H_final"], g=res["G_final"])
+               res_hist=res["res_hist"][:, :, 0], h=res["H_final"], g=res["G_final"])
     if exact:
         out["o_exact"] = res["o_exact"][:, :, 0]
     return out

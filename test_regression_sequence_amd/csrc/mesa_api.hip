@@ -141,6 +141,7 @@ mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const voi
                                 int32_t lambda_full, const float* h0, const float* g0, float* o,
                                 float* h_final, float* g_final, int32_t* steps, float* x_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (lambda_full != 0 && lambda_full != 1) return MESA_ERR_INVALID_ARG;
   return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                   steps, x_out, workspace, workspace_bytes, stream, lambda_full != 0);
 }

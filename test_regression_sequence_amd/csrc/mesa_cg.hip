@@ -1,4 +1,5 @@
-// Chunked conjugate-gradient solve and read-out of the Mesa layer.
+// Chunked conjugate-gradient solve and read-out of the Mesa layer, fp32
+// inputs (fp32 MFMA).  bf16 inputs take the tuned kernels of mesa_cg_bf16.hip.
 //
 // MesaNet page, technical summary, "Mesa layer" section: the optimal query
 // response x_t = (H_t + Lambda)^{-1} q_t is found by conjugate gradient, the
@@ -15,14 +16,12 @@
 // One workgroup per chunk, one wave per 16 tokens; the waves never
 // synchronise inside the CG loop (every token's iteration touches only its
 // own vectors and read-only chunk data), so each wave leaves the loop as soon
-// as its 16 tokens have stopped.  All matrix products run on MFMA in a
-// transposed orientation: the per-token vectors are the B operand, so lane l
-// of a wave holds token 16w + l%16 and dims 16a + 4(l/16) + {0..3} of every
-// CG vector, MFMA results land directly in that layout, and the CG scalars
-// need only a 4-lane reduction.  The bf16 path permutes the contraction
-// index of each 16x16x32 MFMA so that this register layout feeds it without
-// any data movement; A operands are the boundary state (registers) and the
-// chunk's keys in LDS.
+// as its 16 tokens have stopped.  All matrix products run on 16x16x4 fp32
+// MFMA in a transposed orientation: the per-token vectors are the B operand,
+// so lane l of a wave holds token 16w + l%16 and dims 16a + 4(l/16) + {0..3}
+// of every CG vector, MFMA results land directly in that layout, and the CG
+// scalars need only a 4-lane reduction.  The boundary state and the chunk's
+// keys and values sit in LDS.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -30,21 +29,8 @@ namespace mesa {
 
 namespace {
 
-template <bool BF16, int D, int C>
-struct CgLds;
-
 template <int D, int C>
-struct CgLds<true, D, C> {
-  static constexpr int CP = (C < 32) ? 32 : C;
-  static constexpr int KS = D + 8;     // row stride of Ks (elements)
-  static constexpr int TS = CP + 8;    // row stride of KT, VT
-  __bf16 Ks[C * KS];                   // K chunk, [token][dim]
-  __bf16 KT[D * TS];                   // K chunk, [dim][token]
-  __bf16 VT[D * TS];                   // V chunk, [dim][token]
-};
-
-template <int D, int C>
-struct CgLds<false, D, C> {
+struct CgLds {
   static constexpr int S = D + 1;
   float M[D * S];                      // Hb during CG, Gb for the read-out, [row][col]
   float Ks[C * S];                     // K chunk [token][dim]
@@ -55,12 +41,11 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-template <bool BF16, int D, int C>
+template <int D, int C>
 __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
   constexpr int ND = D / 16;   // dim tiles
   constexpr int NW = C / 16;   // waves = token tiles
-  constexpr int NM = ND / 2;   // bf16 k-blocks over dims (pairs of dim tiles)
-  using L = CgLds<BF16, D, C>;
+  using L = CgLds<D, C>;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
@@ -92,34 +77,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
     }
   }
 
-  // ---- stage the chunk's keys and values --------------------------------------
-  if constexpr (BF16) {
-    constexpr int CP = L::CP, KS = L::KS, TS = L::TS;
-    const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
-    const uint16_t* Vg = static_cast<const uint16_t*>(p.v);
-    for (int pc = tid; pc < (CP / 2) * (D / 8); pc += 64 * NW) {
-      const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
-      const int j0 = 2 * jp, j1 = j0 + 1;
-      const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      u16x8 k0 = z, k1 = z, v0 = z, v1 = z;
-      if (j0 < Lc) {
-        k0 = *reinterpret_cast<const u16x8*>(Kg + (row0 + j0) * D + 8 * c8);
-        v0 = *reinterpret_cast<const u16x8*>(Vg + (row0 + j0) * D + 8 * c8);
-      }
-      if (j1 < Lc) {
-        k1 = *reinterpret_cast<const u16x8*>(Kg + (row0 + j1) * D + 8 * c8);
-        v1 = *reinterpret_cast<const u16x8*>(Vg + (row0 + j1) * D + 8 * c8);
-      }
-      if (j0 < C) *reinterpret_cast<u16x8*>(&lds.Ks[j0 * KS + 8 * c8]) = k0;
-      if (j1 < C) *reinterpret_cast<u16x8*>(&lds.Ks[j1 * KS + 8 * c8]) = k1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int n = 8 * c8 + e;
-        *reinterpret_cast<uint32_t*>(&lds.KT[n * TS + j0]) = (uint32_t)k0[e] | ((uint32_t)k1[e] << 16);
-        *reinterpret_cast<uint32_t*>(&lds.VT[n * TS + j0]) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
-      }
-    }
-  } else {
+  // ---- stage the chunk's keys, values and boundary state ----------------------
+  {
     constexpr int S = L::S;
     const float* Kg = static_cast<const float*>(p.k);
     const float* Vg = static_cast<const float*>(p.v);
@@ -148,101 +107,46 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
 #pragma unroll
   for (int a = 0; a < ND; ++a) {
     lam[a] = *reinterpret_cast<const f32x4*>(p.lam + (size_t)h * D + 16 * a + 4 * g);
-    r[a] = valid ? load4<BF16>(p.q, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+    r[a] = valid ? load4<false>(p.q, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
     x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     pv[a] = r[a];
-  }
-
-  // boundary state as MFMA A operand (bf16 path: registers)
-  bf16x8 mfrag[BF16 ? ND : 1][BF16 ? NM : 1];
-  if constexpr (BF16) {
-    const bf16x8* Hf = static_cast<const bf16x8*>(p.hb) + ((size_t)bh * p.NC + c) * (D * D / 8);
-#pragma unroll
-    for (int nt = 0; nt < ND; ++nt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) mfrag[nt][m] = Hf[(nt * NM + m) * 64 + lane];
   }
 
   // y <- A y-operand: Gamma_t * Mb u + (sum_j W_tj (k_j.u) Y_j) for u = src
   // (Mb = Hb or Gb, Y = K or V); returns through out[].
   auto chunk_product = [&](const f32x4* src, f32x4* out, bool use_values) {
     f32x4 sc[NW];
-    if constexpr (BF16) {
-      constexpr int KS = L::KS, TS = L::TS;
-      bf16x8 ub[NM];
+    constexpr int S = L::S;
 #pragma unroll
-      for (int m = 0; m < NM; ++m) ub[m] = pack8(src[2 * m], src[2 * m + 1]);
+    for (int nt = 0; nt < ND; ++nt) {
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < ND; ++nt) {
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < ND; ++a)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) t = mfma_bf16(mfrag[nt][m], ub[m], t);
-        out[nt] = t * Gam;
-      }
-#pragma unroll
-      for (int jt = 0; jt < NW; ++jt) {
-        if (jt > w) continue;
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const __bf16* row = &lds.Ks[(16 * jt + tl) * KS + 32 * m + 4 * g];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          t = mfma_bf16(a, ub[m], t);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] *= W[jt][i];
-        sc[jt] = t;
-      }
-      const __bf16* Y = use_values ? lds.VT : lds.KT;
-#pragma unroll
-      for (int mj = 0; mj < (NW + 1) / 2; ++mj) {
-        if (2 * mj > w) continue;
-        const f32x4 hi = (2 * mj + 1 <= w && 2 * mj + 1 < NW) ? sc[(2 * mj + 1) % NW] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16x8 sb = pack8(sc[2 * mj], hi);
-#pragma unroll
-        for (int nt = 0; nt < ND; ++nt) {
-          const __bf16* row = &Y[(16 * nt + tl) * TS + 32 * mj + 4 * g];
-          const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(row);
-          const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(row + 16);
-          const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          out[nt] = mfma_bf16(a, sb, out[nt]);
-        }
-      }
-    } else {
-      constexpr int S = L::S;
-#pragma unroll
-      for (int nt = 0; nt < ND; ++nt) {
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int a = 0; a < ND; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t = mfma_f32(lds.M[(16 * nt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
-        out[nt] = t * Gam;
-      }
-#pragma unroll
-      for (int jt = 0; jt < NW; ++jt) {
-        if (jt > w) continue;
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int a = 0; a < ND; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t = mfma_f32(lds.Ks[(16 * jt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] *= W[jt][i];
-        sc[jt] = t;
-      }
-      const float* Y = use_values ? lds.Vs : lds.Ks;
-#pragma unroll
-      for (int nt = 0; nt < ND; ++nt)
-#pragma unroll
-        for (int jt = 0; jt < NW; ++jt) {
-          if (jt > w) continue;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[nt] = mfma_f32(Y[(16 * jt + 4 * g + i) * S + 16 * nt + tl], sc[jt][i], out[nt]);
-        }
+        for (int i = 0; i < 4; ++i) t = mfma_f32(lds.M[(16 * nt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
+      out[nt] = t * Gam;
     }
+#pragma unroll
+    for (int jt = 0; jt < NW; ++jt) {
+      if (jt > w) continue;
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int a = 0; a < ND; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t = mfma_f32(lds.Ks[(16 * jt + tl) * S + 16 * a + 4 * g + i], src[a][i], t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] *= W[jt][i];
+      sc[jt] = t;
+    }
+    const float* Y = use_values ? lds.Vs : lds.Ks;
+#pragma unroll
+    for (int nt = 0; nt < ND; ++nt)
+#pragma unroll
+      for (int jt = 0; jt < NW; ++jt) {
+        if (jt > w) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[nt] = mfma_f32(Y[(16 * jt + 4 * g + i) * S + 16 * nt + tl], sc[jt][i], out[nt]);
+      }
   };
 
   // ---- conjugate gradient -----------------------------------------------------
@@ -282,13 +186,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
   }
 
   // ---- read-out o_t = G_t x_t -------------------------------------------------
-  if constexpr (BF16) {
-    const bf16x8* Gf = static_cast<const bf16x8*>(p.gb) + ((size_t)bh * p.NC + c) * (D * D / 8);
-#pragma unroll
-    for (int nt = 0; nt < ND; ++nt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) mfrag[nt][m] = Gf[(nt * NM + m) * 64 + lane];
-  } else {
+  {
     constexpr int S = L::S;
     __syncthreads();  // every wave is done reading Hb
     const float* Gg = static_cast<const float*>(p.gb) + ((size_t)bh * p.NC + c) * D * D;
@@ -309,19 +207,19 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
   }
 }
 
-template <bool BF16, int D, int C>
+template <int D, int C>
 hipError_t launch_cg_t(const CgParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.BH * p.NC);
-  hipLaunchKernelGGL((cg_kernel<BF16, D, C>), grid, dim3(64 * (C / 16)), 0, s, p);
+  hipLaunchKernelGGL((cg_kernel<D, C>), grid, dim3(64 * (C / 16)), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <int D>
 hipError_t launch_cg_d(int C, const CgParams& p, hipStream_t s) {
   switch (C) {
-    case 16: return launch_cg_t<BF16, D, 16>(p, s);
-    case 32: return launch_cg_t<BF16, D, 32>(p, s);
-    case 64: return launch_cg_t<BF16, D, 64>(p, s);
+    case 16: return launch_cg_t<D, 16>(p, s);
+    case 32: return launch_cg_t<D, 32>(p, s);
+    case 64: return launch_cg_t<D, 64>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -331,10 +229,10 @@ hipError_t launch_cg_d(int C, const CgParams& p, hipStream_t s) {
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s) {
   if (bf16) return launch_cg_bf16(D, C, p, s);
   switch (D) {
-    case 16: return launch_cg_d<false, 16>(C, p, s);
-    case 32: return launch_cg_d<false, 32>(C, p, s);
-    case 64: return launch_cg_d<false, 64>(C, p, s);
-    case 128: return launch_cg_d<false, 128>(C, p, s);
+    case 16: return launch_cg_d<16>(C, p, s);
+    case 32: return launch_cg_d<32>(C, p, s);
+    case 64: return launch_cg_d<64>(C, p, s);
+    case 128: return launch_cg_d<128>(C, p, s);
   }
   return hipErrorInvalidValue;
 }

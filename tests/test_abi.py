@@ -103,6 +103,9 @@ def test_full_lambda_forward_scope_and_validation():
     assert call_fwd_ex(desc(), 1, lam=0) == 1
     assert call_fwd_ex(desc(), 1, o=FAKE + 4) == 3
     assert call_fwd_ex(desc(), 1, wbytes=16) == 4
+    # lambda_full takes 0 or 1 only, like the backward and decode _ex calls
+    assert call_fwd_ex(desc(), 2) == 1
+    assert call_fwd_ex(desc(), -1) == 1
     # lambda_full = 0 keeps the diagonal forward's scope (fp32 and chunk 32 allowed)
     assert call_fwd_ex(desc(in_dtype=mesa.MESA_F32), 0, q=0) == 1
     assert call_fwd_ex(desc(chunk=32), 0, wbytes=16) == 4

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import dev_inputs, rel_l2
+from helpers import check_stops, dev_inputs, rel_l2
 from test_regression_sequence_amd import mesa
 from test_regression_sequence_amd.inputs import CONFIGS, make_decode_inputs, make_full_lambda
 
@@ -43,6 +43,7 @@ def test_full_lambda_matches_oracle(dtype, d, packed, warm):
     ref = mesa_decode_step(x["q"], x["k"], x["v"], x["gamma"], x["beta"], lam, x["h"], x["g"],
                            max_steps=cfg.max_steps, tol=cfg.tol, forced_steps=steps, x0=x0)
     assert rel_l2(r["o"].cpu().numpy(), ref["o"]) <= 1e-4
+    check_stops(steps, ref["res_hist"], cfg.max_steps, cfg.tol, "f32")
     if warm:
         assert rel_l2(xs.cpu().numpy(), ref["x"]) <= 1e-4
     # the stored state is H alone (Lambda is added only for the solve)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import dev_inputs, rel_l2
+from helpers import check_stops, dev_inputs, rel_l2
 from test_regression_sequence_amd import mesa
 from test_regression_sequence_amd.inputs import CONFIGS, make_decode_inputs
 
@@ -46,10 +46,12 @@ def test_pack_unpack_round_trip(d):
 
 
 def oracle_outputs(x, cfg, h, g, steps):
-    """The oracle's step from states h, g at the given per-pair step counts."""
+    """The oracle's step from states h, g at the given per-pair step counts; each
+    stop is checked against the oracle's residuals (the decode CG is fp32)."""
     from oracle import mesa_decode_step
     r = mesa_decode_step(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], h, g,
                          max_steps=cfg.max_steps, tol=cfg.tol, forced_steps=steps)
+    check_stops(steps, r["res_hist"], cfg.max_steps, cfg.tol, "f32")
     return r["o"]
 
 
@@ -96,7 +98,7 @@ def test_packed_step_config5_against_oracle():
     pick = np.random.default_rng(55).choice(cfg.N * cfg.H, 48, replace=False)
     flat = lambda a: a.reshape(cfg.N * cfg.H, *a.shape[2:])
     heads = pick % cfg.H
-    ref = []
+    ref, hist = [], []
     for i, p in enumerate(pick):
         hh = heads[i]
         r = mesa_decode_step(flat(x["q"])[p][None, None], flat(x["k"])[p][None, None],
@@ -105,6 +107,8 @@ def test_packed_step_config5_against_oracle():
                              flat(x["h"])[p][None, None], flat(x["g"])[p][None, None],
                              max_steps=cfg.max_steps, tol=cfg.tol, forced_steps=n[p].reshape(1, 1))
         ref.append(r["o"][0, 0])
+        hist.append(r["res_hist"][0, 0])
     assert rel_l2(o[pick], np.stack(ref)) <= 1e-4
+    check_stops(n[pick], np.stack(hist), cfg.max_steps, cfg.tol, "f32")
     h_after = mesa.sym_unpack(hs, cfg.d).cpu().numpy().reshape(-1, cfg.d, cfg.d)
     assert np.array_equal(h_after, h_after.transpose(0, 2, 1))

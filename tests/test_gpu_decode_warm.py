@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import dev_inputs, rel_l2
+from helpers import check_stops, dev_inputs, rel_l2
 from test_regression_sequence_amd import mesa
 from test_regression_sequence_amd.inputs import CONFIGS, make_decode_inputs
 
@@ -64,13 +64,12 @@ def test_warm_sequence_matches_oracle(dtype, d, packed):
     assert steps.max() > 0
     ref = mesa_forward(seq["q"], seq["k"], seq["v"], seq["gamma"], seq["beta"], x0["lam"],
                        max_steps=cfg.max_steps, tol=cfg.tol, h0=x0["h"], g0=x0["g"], exact=False,
-                       warm_start=True, forced_steps=steps)
+                       warm_start=True, forced_steps=steps, residual_history=True)
     for t in range(T):
         assert rel_l2(os_[t], ref["o_cg"][:, :, t]) <= 1e-4, t
         assert rel_l2(xouts[t], ref["x_cg"][:, :, t]) <= 1e-4, t
-    # a stop before the cap means the oracle's residual (at the GPU's count) is at the tolerance
-    early = steps < cfg.max_steps
-    assert np.all(ref["res_norm"][early] <= cfg.tol * 1.05)
+    # every stop against the oracle's residuals at the GPU's count (fp32 arithmetic)
+    check_stops(steps, ref["res_hist"], cfg.max_steps, cfg.tol, "f32")
 
 
 @pytest.mark.parametrize("packed", [False, True])

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import dev_inputs, oracle_on_slices, rel_l2
+from helpers import check_stops, dev_inputs, oracle_on_slices, rel_l2
 from test_regression_sequence_amd import mesa
 from test_regression_sequence_amd.inputs import make_decode_inputs, make_fwd_inputs, small_fwd, CONFIGS
 
@@ -200,6 +200,7 @@ def test_decode_other_dims_and_dtypes(dtype, d):
     r = mesa_decode_step(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], x["h"], x["g"],
                          max_steps=cfg.max_steps, tol=cfg.tol, forced_steps=n)
     assert np.array_equal(r["steps"], n)
+    check_stops(n, r["res_hist"], cfg.max_steps, cfg.tol, "f32")
     assert rel_l2(res["o"].cpu().numpy(), r["o"]) <= 1e-4
     assert rel_l2(dv["h"].cpu().numpy(), r["h"]) < 1e-6
     assert rel_l2(dv["g"].cpu().numpy(), r["g"]) < 1e-6

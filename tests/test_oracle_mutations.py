@@ -74,6 +74,8 @@ MUTATIONS = {
                          "if solve_at is not None and not solve_at[max(t - 1, 0)]:"),
     "exact_solve_wrong_triangle": ("cho_solve(cho_factor(A[s], lower=True), b[s])",
                                    "cho_solve((np.linalg.cholesky(A[s]), False), b[s])"),
+    "history_index_shifted": ("hist[go, it + 1] = np.sqrt(rho_new[go])", "hist[go, it] = np.sqrt(rho_new[go])"),
+    "history_squared": ("hist[go, it + 1] = np.sqrt(rho_new[go])", "hist[go, it + 1] = rho_new[go]"),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
                                        ("            x_ex[:, t] = xe\n",
                                         "            x_ex[:, t] = xe\n            x_prev = xe\n")],
@@ -127,6 +129,10 @@ def run_pins(m):
         if pins.rel(x[0], ref) > 1e-9:
             failed.append("P4")
             break
+    try:
+        pins.check_residual_history(m.cg_solve, A, qv, Aq, qq)
+    except AssertionError:
+        failed.append("P4-history")
     # P5: one step == scaled GLA
     rng = np.random.default_rng(7)
     T, dk, dv = 10, 5, 4

@@ -243,6 +243,29 @@ def test_p4_cg_iterates_are_krylov_projections(seed, d):
         x, steps = cg_solve(A[None].astype(float), q[None].astype(float), n, 0.0)
         assert steps[0] == n
         assert rel(x[0], ref) < 1e-9, (n, x[0], ref)
+    check_residual_history(cg_solve, A, q, Aq, qq)
+
+
+def _exact_residual_norm(Aq, qq, xq):
+    d = len(qq)
+    r = [qq[i] - sum(Aq[i][j] * xq[j] for j in range(d)) for i in range(d)]
+    return float(sum(z * z for z in r)) ** 0.5
+
+
+def check_residual_history(cg, A, q, Aq, qq):
+    """The residual history of an n-step run: entry n is ||q - A x_n|| of the exact
+    n-th Krylov projection (the recursive residual equals the true one in exact
+    arithmetic); entries past the last executed step are NaN."""
+    d = len(qq)
+    forced = np.array([d - 1])
+    x, steps, hist = cg(A[None].astype(float), q[None].astype(float), d + 2, 0.0,
+                        forced_steps=forced, history=True)
+    assert hist.shape == (1, d + 3)
+    qn = float(sum(z * z for z in qq)) ** 0.5
+    for n in range(d):
+        ref = _exact_residual_norm(Aq, qq, _krylov_iterate(Aq, qq, n))
+        assert abs(hist[0, n] - ref) <= 1e-9 * qn, (n, hist[0, n], ref)
+    assert np.all(np.isnan(hist[0, d:]))
 
 
 # ---------------------------------------------------------------------------
