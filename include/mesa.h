@@ -117,6 +117,37 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Size of the static scratch array behind mesa_fwd_chunked_noalloc: 64 MiB
+ * per GPU the library runs on (for example B*H*T = 65536 token-heads at
+ * dk = 128, chunk 64, or the B=4, H=8, T=2048, dk=64 workload's 16 MiB). */
+#define MESA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* mesa_fwd_chunked for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and error behaviour as mesa_fwd_chunked, without the
+ * workspace: the scratch is a file-scope device array of
+ * MESA_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends.  The
+ * call itself allocates nothing (no hipMalloc, no hipFree); its first call on
+ * a device looks the array's address up once with hipGetSymbolAddress.
+ *
+ *   - A descriptor whose mesa_fwd_workspace_bytes exceeds
+ *     MESA_NOALLOC_SCRATCH_BYTES returns MESA_ERR_UNSUPPORTED and launches
+ *     nothing; every argument check runs before any HIP call.
+ *   - `stream` must belong to the current device (else MESA_ERR_INVALID_ARG);
+ *     the current device's array is used.
+ *   - Every call on a GPU shares that GPU's array, and the array keeps the
+ *     last call's contents.  Calls that overlap in time on one GPU (different
+ *     streams, or host threads racing) race on it: serialise them.
+ *   - Nothing in the array needs clearing between calls: every byte a call
+ *     reads, the same call wrote first. */
+mesa_status mesa_fwd_chunked_noalloc(const mesa_fwd_desc* d,
+                                     const void* q, const void* k, const void* v,
+                                     const float* gamma, const float* beta, const float* lambda,
+                                     const float* h0, const float* g0,
+                                     float* o, float* h_final, float* g_final,
+                                     int32_t* steps, float* x_out,
+                                     hipStream_t stream);
+
 /* mesa_fwd_chunked with the regulariser given either as before or as a full
  * matrix per head (MesaNet page, technical summary, "Mesa layer": Lambda is a
  * symmetric positive definite regulariser of the objective).

@@ -2,6 +2,7 @@
 // Every check runs before the first launch, so a failing call writes nothing.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mesa.h"
 #include "mesa_kernels.h"
@@ -64,11 +65,11 @@ namespace {
 
 enum Phase { kScan = 1, kSolve = 2 };
 
-mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const void* k,
-                     const void* v, const float* gamma, const float* beta, const float* lambda,
-                     const float* h0, const float* g0, float* o, float* h_final, float* g_final,
-                     int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, bool lam_full = false) {
+// every check of a forward call except the workspace's size
+mesa_status fwd_validate(int phases, const mesa_fwd_desc* d, const void* q, const void* k,
+                         const void* v, const float* gamma, const float* beta, const float* lambda,
+                         const float* h0, const float* g0, float* o, float* h_final, float* g_final,
+                         int32_t* steps, float* x_out, const void* workspace, bool lam_full) {
   const mesa_status st = check_desc(d);
   if (st != MESA_OK) return st;
   // a full Lambda is taken by the bf16 kernels at chunk 64, d 64 or 128
@@ -80,6 +81,18 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
   const void* ptrs[] = {q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final, steps, x_out, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+  return MESA_OK;
+}
+
+mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const void* k,
+                     const void* v, const float* gamma, const float* beta, const float* lambda,
+                     const float* h0, const float* g0, float* o, float* h_final, float* g_final,
+                     int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, bool lam_full = false) {
+  const mesa_status st = fwd_validate(phases, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
+                                      steps, x_out, workspace, lam_full);
+  if (st != MESA_OK) return st;
+  const bool any_tokens = d->T > 0;
   const size_t need = mesa_fwd_workspace_bytes(d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MESA_ERR_WORKSPACE;
 
@@ -144,6 +157,67 @@ mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const voi
   if (lambda_full != 0 && lambda_full != 1) return MESA_ERR_INVALID_ARG;
   return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                   steps, x_out, workspace, workspace_bytes, stream, lambda_full != 0);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward ---------------------------------------------------
+// Scratch of mesa_fwd_chunked_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  In host code `mesa_noalloc_scratch` only
+// names the symbol; its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char mesa_noalloc_scratch[MESA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxNoallocDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxNoallocDevices] = {};
+
+// the scratch address on the current device (looked up on its first use there)
+mesa_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MESA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxNoallocDevices) return MESA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MESA_ERR_HIP;
+    if (sdev != dev) return MESA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(mesa_noalloc_scratch)) != hipSuccess || !ptr) return MESA_ERR_HIP;
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = g_noalloc_ptr[dev];
+  return MESA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mesa_status mesa_fwd_chunked_noalloc(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                                     const float* gamma, const float* beta, const float* lambda,
+                                     const float* h0, const float* g0, float* o, float* h_final,
+                                     float* g_final, int32_t* steps, float* x_out, hipStream_t stream) {
+  // every host-side check first: no HIP call for a call that cannot run
+  const mesa_status st = fwd_validate(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final,
+                                      g_final, steps, x_out, nullptr, false);
+  if (st != MESA_OK) return st;
+  const size_t need = mesa_fwd_workspace_bytes(d);
+  if (need > MESA_NOALLOC_SCRATCH_BYTES) return MESA_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (need > 0) {
+    const mesa_status sc = noalloc_scratch(stream, &scratch);
+    if (sc != MESA_OK) return sc;
+  }
+  // nothing in the scratch needs clearing: the scan writes every snapshot and
+  // segment state before they are read, and the CG kernel writes every chunk's
+  // form flag before the strong-decay kernel reads it
+  return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
+                  steps, x_out, scratch, MESA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 mesa_status mesa_fwd_scan(const mesa_fwd_desc* d, const void* k, const void* v, const float* gamma,

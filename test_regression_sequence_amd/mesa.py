@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "MesaError", "lib", "library_path", "FwdDesc", "MESA_F32", "MESA_BF16",
-    "workspace_bytes", "fwd_chunked", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
+    "workspace_bytes", "fwd_chunked", "fwd_chunked_noalloc", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
     "status_string", "sym_state_floats", "sym_pack", "sym_unpack", "decode_step_symh",
 ]
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.mesa_fwd_chunked.restype = ctypes.c_int
         L.mesa_fwd_chunked.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        P, S, P]
+        L.mesa_fwd_chunked_noalloc.restype = ctypes.c_int
+        L.mesa_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 13 + [P]
         L.mesa_fwd_chunked_ex.restype = ctypes.c_int
         L.mesa_fwd_chunked_ex.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, I32, P, P, P, P, P, P,
                                           P, P, S, P]
@@ -165,6 +167,21 @@ def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 
                 out=out, workspace=workspace, stream=stream)
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MESA_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_chunked_noalloc(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
+                        tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
+                        return_steps: bool = True, return_x: bool = False, out=None,
+                        stream=None) -> dict:
+    """``fwd_chunked`` through ``mesa_fwd_chunked_noalloc``: the library uses its
+    static per-GPU scratch (at most ``NOALLOC_SCRATCH_BYTES`` of workspace) and
+    allocates nothing; pass ``out`` to allocate nothing here either."""
+    return _fwd("noalloc", q, k, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, return_state=return_state, return_steps=return_steps, return_x=return_x,
+                out=out, workspace=None, stream=stream)
+
+
 def fwd_chunked_ex(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
                    tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
                    return_steps: bool = True, return_x: bool = False, out=None,
@@ -185,7 +202,8 @@ def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, 
         _need(t, name, (B, H, T, d), q.dtype)
     _need(gamma, "gamma", (B, H, T), torch.float32)
     _need(beta, "beta", (B, H, T), torch.float32)
-    lam_full = ex and lam.dim() == 3
+    noalloc = ex == "noalloc"
+    lam_full = ex is True and lam.dim() == 3
     _need(lam, "lam", (H, d, d) if lam_full else (H, d), torch.float32)
     for name, t in (("h0", h0), ("g0", g0)):
         if t is not None:
@@ -204,6 +222,13 @@ def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, 
     if return_state:
         res["h_final"] = out.get("h_final") if out.get("h_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
         res["g_final"] = out.get("g_final") if out.get("g_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    if noalloc:
+        code_ = L.mesa_fwd_chunked_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                                           _ptr(lam), _ptr(h0), _ptr(g0), _ptr(res["o"]), _ptr(res.get("h_final")),
+                                           _ptr(res.get("g_final")), _ptr(res.get("steps")), _ptr(res.get("x")),
+                                           _stream(stream))
+        _check(code_, "mesa_fwd_chunked_noalloc")
+        return res
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -422,7 +447,8 @@ def _bwd(ex: bool, q, k, v, gamma, beta, lam, x, d_o, *, chunk, max_steps, tol, 
         _need(t, name, (B, H, T, d), q.dtype)
     _need(gamma, "gamma", (B, H, T), torch.float32)
     _need(beta, "beta", (B, H, T), torch.float32)
-    lam_full = ex and lam.dim() == 3
+    noalloc = ex == "noalloc"
+    lam_full = ex is True and lam.dim() == 3
     _need(lam, "lam", (H, d, d) if lam_full else (H, d), torch.float32)
     for name, t in (("x", x), ("d_o", d_o)):
         _need(t, name, (B, H, T, d), torch.float32)

@@ -83,6 +83,29 @@ def test_fwd_rejects_bad_descriptors(kw, expect):
     assert call_fwd(desc(**kw)) == expect
 
 
+def call_fwd_noalloc(d, q=FAKE, lam=FAKE, o=FAKE):
+    P = ctypes.c_void_p
+    return mesa.lib().mesa_fwd_chunked_noalloc(ctypes.byref(d), P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(lam),
+                                               None, None, P(o), None, None, None, None, None)
+
+
+def test_noalloc_forward_validates_before_any_hip_call():
+    """The allocation-free forward rejects, before any HIP call (this runs without
+    a GPU): a workload whose workspace exceeds the static scratch, then the
+    descriptor and pointer rules of mesa_fwd_chunked."""
+    assert mesa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = desc(B=8, H=16, T=4096, dk=128, dv=128)
+    assert ws(big) > mesa.NOALLOC_SCRATCH_BYTES
+    assert call_fwd_noalloc(big) == 2
+    # the largest workload of its shape family that fits: B=4, H=8, T=2048, d=64 (16 MiB)
+    assert ws(desc(B=4, H=8, T=2048, dk=64, dv=64)) <= mesa.NOALLOC_SCRATCH_BYTES
+    assert call_fwd_noalloc(desc(B=0)) == 1
+    assert call_fwd_noalloc(desc(dk=48, dv=48)) == 2
+    assert call_fwd_noalloc(desc(), q=0) == 1
+    assert call_fwd_noalloc(desc(), lam=0) == 1
+    assert call_fwd_noalloc(desc(), o=FAKE + 4) == 3
+
+
 def call_fwd_ex(d, lam_full, q=FAKE, lam=FAKE, o=FAKE, workspace=FAKE, wbytes=1 << 40):
     P = ctypes.c_void_p
     return mesa.lib().mesa_fwd_chunked_ex(ctypes.byref(d), P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(lam),
