@@ -9,17 +9,18 @@
 //   Hhat_t = dH_t + gamma_{t+1} Hhat_{t+1},  Ghat_t likewise (backward in time),
 //   dk_t = beta_t ((Hhat_t + Hhat_t^T) k_t + Ghat_t^T v_t),   dv_t = beta_t Ghat_t k_t,
 //   dbeta_t = k_t^T Hhat_t k_t + v_t^T Ghat_t k_t,   dlambda = -sum_t y_t * x_t.
-// The forget factors: gamma_t dgamma_t = <Hhat_t, H_t> + <Ghat_t, G_t> - beta_t dbeta_t
-// (= gamma_t (<Hhat_t, H_{t-1}> + <Ghat_t, G_{t-1}>)).  Inside a chunk with
-// boundary states Hb, Gb and arriving adjoints Rb (of H; Rs = Rb + Rb^T) and
-// S (of G), and b restarted at the chunk start s, <Hhat_t, H_t> is
+// The forget factors: dgamma_t = <Hhat_t, H_{t-1}> + <Ghat_t, G_{t-1}>.  Inside a
+// chunk with boundary states Hb, Gb and arriving adjoints Rb (of H; Rs = Rb + Rb^T)
+// and S (of G), and b restarted at the chunk start s, gamma_t <Hhat_t, H_{t-1}> is
 //   e^{b_e} <Rb, Hb>                                             (per chunk)
-// + sum_{j<=t} e^{b_e-b_j} beta_j k_j^T Rb k_j                    (prefix)
+// + sum_{j<t} e^{b_e-b_j} beta_j k_j^T Rb k_j                     (prefix)
 // + sum_{t'>=t} e^{b_t'} <dH_t', Hb>                               (suffix)
-// + sum_{j<=t<=t'} e^{b_t'-b_j} beta_j <dH_t', k_j k_j^T>          (pairs)
-// and <Ghat_t, G_t> likewise; every factor is a decay <= 1 and nothing
-// accumulates across chunks (a cumulative sum of dL/db over the whole
-// sequence would cancel to O(1) out of O(T) terms).
+// + sum_{j<t<=t'} e^{b_t'-b_j} beta_j <dH_t', k_j k_j^T>           (pairs)
+// and gamma_t <Ghat_t, G_{t-1}> likewise.  Every term's decay runs from a
+// written token j < t past t, so it carries gamma_t and the division by
+// gamma_t only rescales; every factor is a decay <= 1 and nothing accumulates
+// across chunks (a cumulative sum of dL/db over the whole sequence would
+// cancel to O(1) out of O(T) terms).
 //
 // Kernels (chunks of C = 64 tokens; s..e the chunk, b restarted at s):
 //   bwd_dx_kernel    per chunk: dx = Gamma (d_O Gb) + (W o (d_O V^T)) K with
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tl = lane & 15, g = lane >> 4;
 
   __shared__ float bcum[kC], betas[kC], nus[kC];
-  __shared__ float ta[kC], tsuf[kC], trs[kC], tcol[4][kC], tdb[kC];  // dgamma parts per token
+  __shared__ float ta[kC], tsuf[kC], trs[kC], tcol[4][kC];  // dgamma parts per token
   __shared__ float red[2][4];                                          // <Rs, Hb>, <S, Gb> per wave
   __shared__ __attribute__((aligned(16))) uint16_t r1[R1];
   __shared__ __attribute__((aligned(16))) uint16_t r2[D * LD];          // Hb, Gb, then Rs, S, S^T
@@ -901,14 +902,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       }
       if (tl == 0) p.dbeta[row0 + t] = dbeta;
     }
-    if (tl == 0) tdb[t] = dbeta;
   }
   __syncthreads();
-  // dgamma_t = (per-chunk + prefix + suffix + pair terms - beta_t dbeta_t) / gamma_t
+  // dgamma_t = (per-chunk + prefix + suffix + pair terms, every written token j < t) / gamma_t.
+  // Each such term carries gamma_t (its decay runs from j past t), so the sum is
+  // gamma_t <Hhat_t, H_{t-1}> + gamma_t <Ghat_t, G_{t-1}> formed directly: no
+  // token's own term beta_t dbeta_t is added and taken out again, and the
+  // division only rescales a sum that is already small when gamma_t is.
   if (wave == 0) {
     float A = ta[lane], R = trs[lane], Sf = tsuf[lane];
-    const float cs = tcol[0][lane] + tcol[1][lane] + tcol[2][lane] + tcol[3][lane];
-    float Cl = cs;
+    float Cl = tcol[0][lane] + tcol[1][lane] + tcol[2][lane] + tcol[3][lane];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float a2 = __shfl_up(A, o, 64), r2v = __shfl_up(R, o, 64), c2 = __shfl_up(Cl, o, 64);
@@ -920,11 +923,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       }
       if (lane + o < 64) Sf += s2;
     }
-    // pairs j <= t <= t': sum_{u<=t} rowsum_u - sum_{u<t} colsum_u
-    const float pairs = R - (Cl - cs);
+    // exclusive prefix sums (tokens u < t): the inclusive sums one token back
+    // (every lane shuffles, then lane 0 takes zero)
+    const float a1 = __shfl_up(A, 1, 64), r1v = __shfl_up(R, 1, 64), c1v = __shfl_up(Cl, 1, 64);
+    const float Ae = lane > 0 ? a1 : 0.f;
+    const float Re = lane > 0 ? r1v : 0.f;
+    const float Ce = lane > 0 ? c1v : 0.f;
+    // pairs j < t <= t': sum_{u<t} rowsum_u - sum_{u<t} colsum_u
+    const float pairs = Re - Ce;
     const float c1 = expf(bcum[kC - 1]) *
                      (0.5f * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + red[1][0] + red[1][1] + red[1][2] + red[1][3]);
-    if (lane < Lc) p.dgamma[row0 + lane] = (c1 + A + Sf + pairs - betas[lane] * tdb[lane]) / p.gamma[row0 + lane];
+    if (lane < Lc) p.dgamma[row0 + lane] = (c1 + Ae + Sf + pairs) / p.gamma[row0 + lane];
   }
   (void)h;
 }

@@ -43,10 +43,14 @@ def run_gpu(cfg, x, g, lam):
     return out
 
 
-@pytest.mark.parametrize("d,T,max_steps,tol", [(64, 200, 10, 0.0), (128, 130, 32, 1e-4)])
-def test_full_lambda_gradients_match_oracle(d, T, max_steps, tol):
+@pytest.mark.parametrize("d,T,max_steps,tol,gates", [(64, 200, 10, 0.0, (2.0, 6.0)),
+                                                     (128, 130, 32, 1e-4, (2.0, 6.0)),
+                                                     (128, 150, 12, 0.0, (-3.0, 1.0))])
+def test_full_lambda_gradients_match_oracle(d, T, max_steps, tol, gates):
+    """The last case has strongly decaying gates (every chunk past e^-40: the
+    unscaled full-Lambda kernel for every solve, and small gamma_t for dgamma)."""
     from oracle import mesa_backward
-    cfg = small_fwd(B=2, H=2, T=T, d=d, chunk=64, dtype="bf16", max_steps=max_steps, tol=tol)
+    cfg = small_fwd(B=2, H=2, T=T, d=d, chunk=64, dtype="bf16", max_steps=max_steps, tol=tol, gamma_logit=gates)
     x = make_fwd_inputs(cfg)
     g = make_bwd_inputs(cfg)
     lam = make_full_lambda(cfg.H, d, cfg.seed)
