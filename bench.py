@@ -72,12 +72,12 @@ def time_events(fn, iters):
     return start.elapsed_time(end) / iters
 
 
-def bench_forward(cfg, steps, warmup):
+def bench_forward(cfg, steps, warmup, x=None):
     import torch
     from test_regression_sequence_amd import mesa
     from test_regression_sequence_amd.inputs import make_fwd_inputs
 
-    x = make_fwd_inputs(cfg)
+    x = make_fwd_inputs(cfg) if x is None else x
     dev = "cuda"
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     q = torch.from_numpy(x["q"]).to(dev).to(dt)
@@ -124,7 +124,87 @@ def bench_forward(cfg, steps, warmup):
     cg_ms = [e[1].elapsed_time(e[2]) for e in evs]
     n = st.cpu().numpy()
     return dict(ms=ms, wall_ms=wall, scan_ms=float(np.mean(scan_ms)), cg_ms=float(np.mean(cg_ms)),
-                steps_mean=float(n.mean()), steps_max=int(n.max()), x=x)
+                steps_mean=float(n.mean()), steps_max=int(n.max()), steps=n, x=x)
+
+
+def cg_kernel_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one CG launch (bf16 inputs): per chunk the two
+    bf16 boundary snapshots, q, k, v, gamma, beta read; o and steps written."""
+    chunks = cfg.B * cfg.H * ((cfg.T + cfg.chunk - 1) // cfg.chunk)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    tok = cfg.B * cfg.H * cfg.T
+    return int(chunks * 2 * cfg.d * cfg.d * esz + tok * (3 * cfg.d * esz + 2 * 4 + cfg.d * 4 + 4))
+
+
+def scan_kernel_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one scan launch: k, v and gates read, the two
+    boundary snapshots of every chunk written."""
+    chunks = cfg.B * cfg.H * ((cfg.T + cfg.chunk - 1) // cfg.chunk)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    tok = cfg.B * cfg.H * cfg.T
+    return int(chunks * 2 * cfg.d * cfg.d * esz + tok * (2 * cfg.d * esz + 2 * 4))
+
+
+def forward_report(cfg, fw) -> dict:
+    """Times, counted TFLOP/s and HBM rates of one forward workload."""
+    tokens = cfg.B * cfg.H * cfg.T
+    f = flops_per_token(cfg.d, cfg.chunk, fw["steps_mean"])
+    cg_tf = f["cg_kernel"] * tokens / (fw["cg_ms"] * 1e-3) / 1e12
+    tot_tf = f["total"] * tokens / (fw["ms"] * 1e-3) / 1e12
+    cg_b, sc_b = cg_kernel_bytes(cfg), scan_kernel_bytes(cfg)
+    n = fw["steps"].reshape(cfg.B * cfg.H, -1)
+    T = n.shape[1]
+    pad = (-T) % cfg.chunk
+    nc = np.pad(n, ((0, 0), (0, pad)), constant_values=0).reshape(n.shape[0], -1, cfg.chunk)
+    nt = nc.reshape(n.shape[0], nc.shape[1], cfg.chunk // 16, 16)
+    return {
+        "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} chunk={cfg.chunk} {cfg.dtype}, "
+                    + (f"fixed {cfg.max_steps}" if cfg.tol <= 0 else f"tol {cfg.tol:g} max {cfg.max_steps}")
+                    + " CG steps",
+        "ms_per_call": round(fw["ms"], 4),
+        "tokens_per_s": round(tokens / (fw["ms"] * 1e-3), 1),
+        "kernels_ms": {"scan": round(fw["scan_ms"], 4), "cg": round(fw["cg_ms"], 4)},
+        "cg_counted_TFLOPs": round(cg_tf, 2),
+        "cg_frac_of_mfma_peak": round(cg_tf / PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_of_mfma_peak": round(tot_tf / PEAK_BF16_TFLOPS, 4),
+        "cg_hbm_GBs": round(cg_b / (fw["cg_ms"] * 1e-3) / 1e9, 1),
+        "cg_frac_of_hbm_peak": round(cg_b / (fw["cg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "scan_hbm_GBs": round(sc_b / (fw["scan_ms"] * 1e-3) / 1e9, 1),
+        "scan_frac_of_hbm_peak": round(sc_b / (fw["scan_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "cg_steps_mean": round(fw["steps_mean"], 3),
+        "cg_steps_max": fw["steps_max"],
+        # the work a chunk's wave does follows its tiles' slowest tokens
+        "chunk_max_over_mean": round(float(nc.max(axis=2).mean() / max(fw["steps_mean"], 1e-9)), 4),
+        "tile_max_over_mean": round(float(nt.max(axis=3).mean() / max(fw["steps_mean"], 1e-9)), 4),
+    }
+
+
+def bench_latency(cfg, steps, warmup) -> dict:
+    """One whole mesa_fwd_chunked call on a tiny workload: latency."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs
+    x = make_fwd_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    gamma, beta, lam = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta", "lam"))
+    ws = torch.empty(max(1, mesa.workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, dtype=dt)),
+                     device="cuda", dtype=torch.uint8)
+    res = mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                           workspace=ws)
+
+    def step():
+        mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                         workspace=ws, out=res)
+
+    for _ in range(warmup):
+        step()
+    ms = time_events(step, steps)
+    n = res["steps"].cpu().numpy()
+    return {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} chunk={cfg.chunk} {cfg.dtype}, "
+                        f"tol {cfg.tol:g} max {cfg.max_steps} CG steps",
+            "us_per_call": round(ms * 1e3, 2), "cg_steps_mean": round(float(n.mean()), 3),
+            "cg_steps_max": int(n.max())}
 
 
 def bench_decode(cfg, steps, warmup):
@@ -499,31 +579,67 @@ def measure_copy_bw(mib: int = 512, copies: int = 3, reps: int = 10) -> float:
     return 2 * 4 * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(x, slices: int, tokens: int):
+def _oracle_slice(args):
+    """One (b, h) slice of the oracle's forward (CG schedule only), in a worker."""
     from threadpoolctl import threadpool_limits
     from oracle import mesa_forward
+    q, k, v, gamma, beta, lam, max_steps, tol = args
+    with threadpool_limits(1):
+        mesa_forward(q, k, v, gamma, beta, lam, max_steps=max_steps, tol=tol, exact=False)
+    return q.shape[2]
+
+
+def host_workers() -> int:
+    """Host cores this process may use, at most 16 (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(x, per_worker: int, tokens: int):
+    """The fp64 oracle, untuned, over the host's cores: one worker process per
+    core, each running whole (b, h) slices with one BLAS thread.  Runs before
+    the GPU is initialised, so the workers are plain forks."""
+    import multiprocessing as mp
     cfg = x["cfg"]
+    workers = host_workers()
+    slices = min(cfg.B * cfg.H, workers * per_worker)
     rng = np.random.default_rng(7)
     flat = rng.choice(cfg.B * cfg.H, size=slices, replace=False)
     b, h = flat // cfg.H, flat % cfg.H
     T = min(tokens, cfg.T)
-    sl = lambda a: a[b, h][:, None, :T]
-    lam = x["lam"][h]
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        for i in range(slices):
-            mesa_forward(sl(x["q"])[i:i + 1], sl(x["k"])[i:i + 1], sl(x["v"])[i:i + 1],
-                         sl(x["gamma"])[i:i + 1], sl(x["beta"])[i:i + 1], lam[i:i + 1],
-                         max_steps=cfg.max_steps, tol=cfg.tol, exact=False)
-    dt = time.perf_counter() - t0
+    jobs = [(x["q"][b[i], h[i]][None, None, :T], x["k"][b[i], h[i]][None, None, :T],
+             x["v"][b[i], h[i]][None, None, :T], x["gamma"][b[i], h[i]][None, None, :T],
+             x["beta"][b[i], h[i]][None, None, :T], x["lam"][h[i]][None], cfg.max_steps, cfg.tol)
+            for i in range(slices)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_slice, jobs[:workers])          # warm: imports in every worker
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_slice, jobs, chunksize=1))
+        dt = time.perf_counter() - t0
     return {
-        "value": round(slices * T / dt, 2),
+        "value": round(done / dt, 2),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{slices} (b,h) slices x first {T} tokens of the same workload, fp64 NumPy, "
-                  f"CG schedule only (no exact solve), one BLAS thread; {dt:.1f} s",
-        "host": platform.processor() or platform.machine(),
+        "sample": f"{slices} (b,h) slices x first {T} tokens of the same workload, fp64 NumPy, CG schedule "
+                  f"only (no exact solve), {workers} worker processes with one BLAS thread each; {dt:.1f} s wall, "
+                  f"{dt * workers:.0f} core-s",
+        "host": cpu_model(),
         "host_cpus": os.cpu_count(),
     }
 
@@ -536,8 +652,10 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4],
                     help="forward workload: 2 (d=64), 3 (d=128, default), 4 (T=32768, dynamic CG)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the chosen forward workload only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-slices", type=int, default=5)
+    ap.add_argument("--cpu-slices-per-core", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -549,9 +667,22 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    from test_regression_sequence_amd.inputs import CONFIGS, make_fwd_inputs
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = CONFIGS[args.workload]
+    x_main = None
+    cpu = None
+    if not args.no_cpu_baseline and not args.calibrate_copy:
+        # before any HIP call: the oracle's worker processes are plain forks
+        x_main = make_fwd_inputs(cfg)
+        cpu = cpu_baseline(x_main, args.cpu_slices_per_core, args.cpu_tokens)
+        log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} cores")
+
     import torch
     from test_regression_sequence_amd import mesa
-    from test_regression_sequence_amd.inputs import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -561,11 +692,8 @@ def main():
         return
     mesa.lib()
 
-    def log(msg):
-        print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-    cfg = CONFIGS[args.workload]
-    fw = bench_forward(cfg, args.steps, args.warmup)
+    fw = bench_forward(cfg, args.steps, args.warmup, x_main)
+    x_main = None
     log(f"forward: {fw['ms']:.4f} ms per call")
     tokens = cfg.B * cfg.H * cfg.T
     n_avg = fw["steps_mean"]
@@ -613,6 +741,12 @@ def main():
         "fwd_frac_of_mfma_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(fw["wall_ms"], 4),
     }
+    if args.forward_only:
+        line["forward_detail"] = forward_report(cfg, fw)
+        if cpu is not None:
+            line["cpu_baseline"] = cpu
+        print(json.dumps(line), flush=True)
+        return
     copy_gbs = measure_copy_bw()
     line["measured_peaks"] = {"torch_copy_GBs": round(copy_gbs, 1),
                               "note": "torch device copy of 512 MiB (read + write bytes), three rotating "
@@ -631,9 +765,21 @@ def main():
     if cfg_w.dtype == "bf16" and cfg_w.chunk == 64 and cfg_w.d in (64, 128):
         line["forward_full_lambda"] = bench_forward_full_lambda(cfg_w, args.steps, args.warmup)
         log(f"forward, full Lambda: {line['forward_full_lambda']['ms_per_call']} ms per call")
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(fw["x"], args.cpu_slices, args.cpu_tokens)
-        log("cpu baseline done")
+    # the other forward workloads: latency (1), mid size (2), long context with dynamic CG (4)
+    others = {}
+    others["tiny_fp32"] = bench_latency(CONFIGS[1], args.steps, args.warmup)
+    log(f"tiny fp32: {others['tiny_fp32']['us_per_call']} us per call")
+    for key, c in (("mid_d64", 2), ("long_dynamic", 4)):
+        if c == args.workload:
+            continue
+        fwc = bench_forward(CONFIGS[c], args.steps, args.warmup)
+        fwc.pop("x")
+        others[key] = forward_report(CONFIGS[c], fwc)
+        log(f"workload {c}: {others[key]['ms_per_call']} ms per call")
+    line["other_workloads"] = others
+    line["forward_detail"] = forward_report(cfg, fw)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
