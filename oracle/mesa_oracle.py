@@ -150,7 +150,8 @@ def _flat(a, S, *tail):
 def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                  h0=None, g0=None, forced_steps=None, exact: bool = True,
                  record_every: int | None = None, solve_at=None,
-                 warm_start: bool = False, x_init=None, residual_history: bool = False):
+                 warm_start: bool = False, x_init=None, residual_history: bool = False,
+                 warm_lag: int = 1, warm_chunk: int | None = None):
     """Token-by-token Mesa layer over [B, H, T, d] inputs, fp64.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv]; gamma, beta: [B, H, T];
@@ -161,8 +162,13 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     solve_at: optional [T] bool -- solve and emit outputs only at these token
     positions (the state recurrence still runs over every token); outputs at
     other positions are left at zero.  Used to sample long sequences.
-    warm_start: start token t's CG from token t-1's CG result, token 0's from
-    x_init ([B, H, dk], default 0).  Needs every token solved (no solve_at).
+    warm_start: start token t's CG from token (t - warm_lag)'s CG result.  With
+    warm_lag = 1 and no warm_chunk (the recurrent reading), token 0 starts from
+    x_init ([B, H, dk], default 0).  With warm_chunk = C, a token whose
+    predecessor t - warm_lag lies in an earlier chunk of C tokens (or before
+    the sequence) starts from 0: the chunked reading, in which the chunks of a
+    sequence are solved in parallel and only earlier tokens of the same chunk
+    can hand over their solutions.  Needs every token solved (no solve_at).
     residual_history: also return ``res_hist`` [B, H, T, max_steps + 1], each
     solved token's recursive residual norm after every CG iteration (see
     :func:`cg_solve`; zero rows at tokens not solved).
@@ -186,6 +192,8 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
     fs = None if forced_steps is None else np.asarray(forced_steps).reshape(S, T)
     if warm_start and solve_at is not None:
         raise ValueError("warm start needs every token solved")
+    if warm_lag < 1 or (warm_chunk is not None and (warm_chunk < 1 or x_init is not None)):
+        raise ValueError("warm_lag >= 1; warm_chunk >= 1 and takes no x_init")
     x_prev = np.zeros((S, dk)) if x_init is None else _flat(x_init, S, dk).copy()
 
     o_cg = np.zeros((S, T, dv))
@@ -210,9 +218,15 @@ def mesa_forward(q, k, v, gamma, beta, lam, *, max_steps: int, tol: float,
                                Gs.reshape(B, Hh, dv, dk).copy()))
             continue
         A = Hs + Lam
+        x0 = None
+        if warm_start:
+            if warm_lag == 1 and warm_chunk is None:
+                x0 = x_prev
+            elif t - warm_lag >= 0 and (warm_chunk is None or (t - warm_lag) // warm_chunk == t // warm_chunk):
+                x0 = x_cg[:, t - warm_lag]
         xs, ns, rn, rp, rh = cg_solve(A, qf[:, t], max_steps, tol,
                                       None if fs is None else fs[:, t], residuals=True,
-                                      x0=x_prev if warm_start else None, history=True)
+                                      x0=x0, history=True)
         if residual_history:
             res_hist[:, t] = rh
         x_prev = xs

@@ -76,6 +76,9 @@ MUTATIONS = {
                                    "cho_solve((np.linalg.cholesky(A[s]), False), b[s])"),
     "history_index_shifted": ("hist[go, it + 1] = np.sqrt(rho_new[go])", "hist[go, it] = np.sqrt(rho_new[go])"),
     "history_squared": ("hist[go, it + 1] = np.sqrt(rho_new[go])", "hist[go, it + 1] = rho_new[go]"),
+    "chunked_warm_lag_ignored": ("x0 = x_cg[:, t - warm_lag]", "x0 = x_cg[:, t - 1]"),
+    "chunked_warm_crosses_chunks": ("(warm_chunk is None or (t - warm_lag) // warm_chunk == t // warm_chunk)",
+                                    "(warm_chunk is None or True)"),
     "warm_chain_from_exact_solution": [("        x_prev = xs\n", "\n"),
                                        ("            x_ex[:, t] = xe\n",
                                         "            x_ex[:, t] = xe\n            x_prev = xe\n")],
@@ -161,15 +164,18 @@ def run_pins(m):
         if pins.rel(x[0], ref) > 1e-9:
             failed.append("P4w")
             break
-    # chained warm start over a sequence (exact rationals)
+    # chained warm start over a sequence, recurrent and chunked (exact rationals)
     saved = pins.mesa_forward
     try:
         pins.mesa_forward = m.mesa_forward
-        pins.test_p4w_warm_sequence_chains_previous_solution()
-    except AssertionError:
-        failed.append("P4w-seq")
-    except Exception:
-        failed.append("P4w-seq-crash")
+        for tag, fn in (("P4w-seq", pins.test_p4w_warm_sequence_chains_previous_solution),
+                        ("P4w-chunked", pins.test_p4w_chunked_warm_start_chains_within_chunks)):
+            try:
+                fn()
+            except AssertionError:
+                failed.append(tag)
+            except Exception:
+                failed.append(tag + "-crash")
     finally:
         pins.mesa_forward = saved
     # preprocessing against library convolution and normalisation

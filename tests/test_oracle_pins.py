@@ -429,6 +429,37 @@ def test_p4w_warm_sequence_chains_previous_solution():
     assert rel(res["o_cg"][0, 0], np.array(ref_o)) < 1e-10
 
 
+def test_p4w_chunked_warm_start_chains_within_chunks(T=7, d=3, n=2, lag=2, chunk=4):
+    """The chunked warm start: token t starts from token t-lag's n-step result when
+    both lie in the same chunk of `chunk` tokens, otherwise from 0 -- chained
+    affine Krylov projections with states, forget factors and outputs in exact
+    rationals (tokens 0, 1 and 4, 5 start cold; 2, 3, 6 from 0, 1, 4)."""
+    rng = np.random.default_rng(23)
+    ki = rng.integers(-2, 3, (T, d)); vi = rng.integers(-2, 3, (T, d)); qi = rng.integers(-3, 4, (T, d))
+    gam = [Fraction(int(a), 4) for a in rng.integers(1, 4, T)]
+    bet = [Fraction(int(a), 2) for a in rng.integers(1, 4, T)]
+    lam = [Fraction(int(a), 2) for a in rng.integers(1, 4, d)]
+    Hq = [[Fraction(0)] * d for _ in range(d)]
+    Gq = [[Fraction(0)] * d for _ in range(d)]
+    xs, ref_o = [], []
+    for t in range(T):
+        kk = [Fraction(int(a)) for a in ki[t]]; vv = [Fraction(int(a)) for a in vi[t]]
+        Hq = [[gam[t] * Hq[i][j] + bet[t] * kk[i] * kk[j] for j in range(d)] for i in range(d)]
+        Gq = [[gam[t] * Gq[i][j] + bet[t] * vv[i] * kk[j] for j in range(d)] for i in range(d)]
+        Aq = [[Hq[i][j] + (lam[i] if i == j else 0) for j in range(d)] for i in range(d)]
+        same_chunk = t - lag >= 0 and (t - lag) // chunk == t // chunk
+        x0 = xs[t - lag] if same_chunk else [Fraction(0)] * d
+        xs.append(_krylov_iterate(Aq, [Fraction(int(a)) for a in qi[t]], n, x0))
+        ref_o.append([float(sum(Gq[i][j] * xs[-1][j] for j in range(d))) for i in range(d)])
+    res = mesa_forward(qi[None, None].astype(float), ki[None, None].astype(float),
+                       vi[None, None].astype(float),
+                       np.array([[[float(g) for g in gam]]]), np.array([[[float(b) for b in bet]]]),
+                       np.array([[float(l) for l in lam]]), max_steps=n, tol=0.0, exact=False,
+                       warm_start=True, warm_lag=lag, warm_chunk=chunk)
+    assert rel(res["o_cg"][0, 0], np.array(ref_o)) < 1e-10
+    assert rel(res["x_cg"][0, 0], np.array([[float(z) for z in x] for x in xs])) < 1e-10
+
+
 # ---------------------------------------------------------------------------
 # P5: one CG step is a normalised gated-linear-attention read-out
 # ---------------------------------------------------------------------------
