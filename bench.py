@@ -179,6 +179,63 @@ def forward_report(cfg, fw) -> dict:
     }
 
 
+def bench_warm_forward(cfg, steps, warmup) -> dict:
+    """Cold against warm-started CG in the chunked forward (mesa_fwd_chunked_warm:
+    token t starts from token t-16's solution within its chunk), on the
+    workload's own queries and on slowly varying ones (per-dimension AR(1),
+    lag-1 correlation 0.99).  Whole calls, alternating cold and warm, HIP
+    events, medians; mean CG steps over the tokens a warm start applies to
+    (tiles 1.. of every chunk) and over all, and the mean over 16-token tiles
+    of a tile's slowest token (the wave iterates until it stops)."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs, make_slow_queries
+    base = make_fwd_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    ws = torch.empty(mesa.workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk, dtype=dt), device="cuda",
+                     dtype=torch.uint8)
+    later = (np.arange(cfg.T) % cfg.chunk) >= 16
+    out = {"rule": "token t starts from token t-16's solution when both lie in one chunk, else from 0"}
+    for name, x in (("workload_queries", base), ("slow_queries_ar1_0.99", make_slow_queries(base, 0.99))):
+        q, k, v = (torch.from_numpy(x[n]).cuda().to(dt) for n in ("q", "k", "v"))
+        gamma, beta, lam = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta", "lam"))
+        rec = {}
+        res = {w: mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps,
+                                   tol=cfg.tol, workspace=ws, warm=w) for w in (False, True)}
+        ev = {w: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)] for w in (False, True)}
+
+        def call(w, e=None):
+            if e is not None:
+                e[0].record()
+            mesa.fwd_chunked(q, k, v, gamma, beta, lam, chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol,
+                             workspace=ws, out=res[w], warm=w)
+            if e is not None:
+                e[1].record()
+
+        # cold and warm calls alternate, so that neither profits from the clock
+        # or cache state the other leaves
+        for _ in range(warmup):
+            call(False)
+            call(True)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            call(False, ev[False][i])
+            call(True, ev[True][i])
+        torch.cuda.synchronize()
+        for w in (False, True):
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev[w]]))
+            n = res[w]["steps"].cpu().numpy()
+            rec["warm" if w else "cold"] = {"ms_per_call_median": round(ms, 4),
+                                            "cg_steps_mean": round(float(n.mean()), 3),
+                                            "cg_steps_mean_tiles_1_on": round(float(n[:, :, later].mean()), 3),
+                                            "tile_max_steps_mean": round(float(n.reshape(
+                                                cfg.B * cfg.H, -1, 16).max(axis=2).mean()), 3)}
+        out[name] = rec
+        del q, k, v, gamma, beta, lam
+    return out
+
+
 def bench_latency(cfg, steps, warmup) -> dict:
     """One whole mesa_fwd_chunked call on a tiny workload: latency."""
     import torch
@@ -777,6 +834,8 @@ def main():
         others[key] = forward_report(CONFIGS[c], fwc)
         log(f"workload {c}: {others[key]['ms_per_call']} ms per call")
     line["other_workloads"] = others
+    line["warm_start_forward"] = bench_warm_forward(CONFIGS[4], args.steps, args.warmup)
+    log(f"warm-start forward: {line['warm_start_forward']['workload_queries']}")
     line["forward_detail"] = forward_report(cfg, fw)
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -117,6 +117,30 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* mesa_fwd_chunked with warm-started CG (MesaNet page, technical summary,
+ * "significance": warm-started optimisation as a way to cut the solver's
+ * cost).  The chunks of a sequence are solved in parallel and the tokens of a
+ * chunk in tiles of 16, so a token can start from a solution that an earlier
+ * tile of its own chunk produced: token t starts its CG from x_{t-16}, the
+ * solution of token t-16, when both lie in one chunk, and from 0 otherwise
+ * (the first 16 tokens of every chunk).  The residual starts at
+ * q_t - (H_t + Lambda) x_{t-16}; that product is not counted in steps.  With
+ * a tolerance a good start saves steps; with a fixed step count the result is
+ * the n-step CG iterate from that start.
+ *
+ * Supported for in_dtype MESA_BF16 and every chunk and dk of mesa_fwd_chunked
+ * (at chunk 16 no token has a start in its chunk); fp32 inputs return
+ * MESA_ERR_UNSUPPORTED and launch nothing.  Every argument, the workspace and
+ * the error behaviour are those of mesa_fwd_chunked. */
+mesa_status mesa_fwd_chunked_warm(const mesa_fwd_desc* d,
+                                  const void* q, const void* k, const void* v,
+                                  const float* gamma, const float* beta, const float* lambda,
+                                  const float* h0, const float* g0,
+                                  float* o, float* h_final, float* g_final,
+                                  int32_t* steps, float* x_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Size of the static scratch array behind mesa_fwd_chunked_noalloc: 64 MiB
  * per GPU the library runs on (for example B*H*T = 65536 token-heads at
  * dk = 128, chunk 64, or the B=4, H=8, T=2048, dk=64 workload's 16 MiB). */

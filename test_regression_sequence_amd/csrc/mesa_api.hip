@@ -88,10 +88,12 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
                      const void* v, const float* gamma, const float* beta, const float* lambda,
                      const float* h0, const float* g0, float* o, float* h_final, float* g_final,
                      int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, bool lam_full = false) {
+                     hipStream_t stream, bool lam_full = false, bool warm = false) {
   const mesa_status st = fwd_validate(phases, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                                       steps, x_out, workspace, lam_full);
   if (st != MESA_OK) return st;
+  // the warm start is built into the bf16 kernels with a diagonal Lambda
+  if (warm && (d->in_dtype != MESA_BF16 || lam_full)) return MESA_ERR_UNSUPPORTED;
   const bool any_tokens = d->T > 0;
   const size_t need = mesa_fwd_workspace_bytes(d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MESA_ERR_WORKSPACE;
@@ -131,6 +133,7 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
     cp.BH = BH; cp.H = d->H; cp.T = d->T; cp.NC = NC; cp.max_steps = d->max_steps;
     cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
     cp.lam_full = lam_full ? 1 : 0;
+    cp.warm = warm ? 1 : 0;
     if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
   return MESA_OK;
@@ -147,6 +150,15 @@ mesa_status mesa_fwd_chunked(const mesa_fwd_desc* d, const void* q, const void* 
                              size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                   steps, x_out, workspace, workspace_bytes, stream);
+}
+
+mesa_status mesa_fwd_chunked_warm(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
+                                  const float* gamma, const float* beta, const float* lambda,
+                                  const float* h0, const float* g0, float* o, float* h_final,
+                                  float* g_final, int32_t* steps, float* x_out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
+                  steps, x_out, workspace, workspace_bytes, stream, false, true);
 }
 
 mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,

@@ -47,6 +47,14 @@
 // fragments by an exact MFMA transpose, so the CG loop touches no global
 // memory.  MFMA accumulators stay in VGPRs (built with -amdgpu-mfma-vgpr-form).
 //
+// WARM (warm-started CG; the "significance" section names warm-started
+// optimisation as a way to cut the solver's cost): tile w >= 1 starts each
+// token t from token t-16's solution, which the same lane of the same wave
+// produced in tile w-1, rescaled to the scaled form, xh_0 = e^{b_t - b_{t-16}}
+// xh_{t-16}, with r_0 = q - (A_t / Gamma_t) xh_0 from one more product (not
+// counted as a step).  Tile 0 starts from 0: earlier chunks are solved in
+// parallel.
+//
 // Lambda is diagonal, or (LF) a full symmetric positive definite matrix per
 // head (the page calls the regulariser symmetric positive definite).  The
 // full matrix enters as one more d x d MFMA operand, (Lambda / Gamma_t) p =
@@ -66,9 +74,10 @@ namespace {
 template <int W>
 using tile_c = std::integral_constant<int, W>;
 
-template <int D, int C, bool LF>
+template <int D, int C, bool LF, bool WARM = false>
 __global__ __launch_bounds__(LF ? 128 : 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_kernel(CgParams p) {
+  static_assert(!(LF && WARM), "the warm start takes a diagonal Lambda");
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
   constexpr int NWV = LF ? 2 : 1;  // waves (chunks) per workgroup
 
@@ -305,6 +314,7 @@ void cg_bf16_kernel(CgParams p) {
   };
 
   // ---- conjugate gradient of one tile -------------------------------------------
+  f32x4 xprev[WARM ? ND : 1];  // the previous tile's solutions (WARM)
   auto solve_tile = [&](auto wc) {
     constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
@@ -325,6 +335,23 @@ void cg_bf16_kernel(CgParams p) {
                    : f32x4{0.f, 0.f, 0.f, 0.f};
       x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
       pv[a] = r[a];
+    }
+    if constexpr (WARM && w > 0) {
+      // xh_0 = e^{b_t - b_{t-16}} xh_{t-16}; r_0 = q - (A_t / Gamma_t) xh_0
+      const float sh = valid ? expf(bcum[tloc] - bcum[tloc - 16]) : 0.f;
+      bf16x8 ub[NM];
+#pragma unroll
+      for (int a = 0; a < ND; ++a) x[a] = xprev[a] * sh;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) ub[m] = pack8(x[2 * m], x[2 * m + 1]);
+      pin_operands();
+      matvec(wc, ub);
+#pragma unroll
+      for (int a = 0; a < ND; ++a) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[a][i] -= __builtin_fmaf(lt[a][i], x[a][i], acc[a][i]);
+        pv[a] = r[a];
+      }
     }
     if constexpr (w + 1 < NW) fetch_q(w + 1);
     float rho = 0.f;
@@ -407,6 +434,10 @@ void cg_bf16_kernel(CgParams p) {
     // the last step's x update
 #pragma unroll
     for (int a = 0; a < ND; ++a) x[a] += alpha_p * pv[a];
+    if constexpr (WARM) {
+#pragma unroll
+      for (int a = 0; a < ND; ++a) xprev[a] = x[a];
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m) xs[(w * NM + m) * 64 + lane] = pack8(x[2 * m], x[2 * m + 1]);
     if (valid) {
@@ -465,7 +496,16 @@ template <int D, int C, bool LF = false>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
   // LF: two chunks of one sequence per two-wave workgroup
   const dim3 grid((unsigned)((long long)p.BH * (LF ? (p.NC + 1) / 2 : p.NC)));
-  hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(LF ? 128 : 64), 0, s, p);
+  if constexpr (!LF) {
+    if (p.warm) {
+      hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, true>), grid, dim3(64), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
+    }
+  } else {
+    if (p.warm) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(128), 0, s, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_cg_bf16_unscaled(D, C, p, s);

@@ -18,7 +18,9 @@
 // Register layout (lane l, tl = l%16, g = l/16): CG vectors of token 16w + tl
 // keep dims 16a + 4g + {0..3} as f32x4 v[a].  A full symmetric positive
 // definite Lambda (LF) enters as one more MFMA operand, its bf16 fragments in
-// LDS, applied to the bf16 search direction.
+// LDS, applied to the bf16 search direction.  WARM: tile w >= 1 starts token t
+// from token t-16's solution (the previous tile's, parked in LDS), with
+// r_0 = q - A_t x_0 from one more product, as in the scaled kernel.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
 
@@ -28,9 +30,10 @@ namespace {
 
 constexpr int kChunksPerWave = 8;
 
-template <int D, int C, bool LF>
+template <int D, int C, bool LF, bool WARM = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_unscaled_kernel(CgParams p) {
+  static_assert(!(LF && WARM), "the warm start takes a diagonal Lambda");
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
 
   const int lane = threadIdx.x, tl = lane & 15, g = lane >> 4;
@@ -245,6 +248,22 @@ void cg_bf16_unscaled_kernel(CgParams p) {
         x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         pv[a] = r[a];
       }
+      if (WARM && w > 0) {
+        // x_0 = token t-16's solution (the previous tile's, same lane); r_0 = q - A_t x_0
+        bf16x8 ub[NM], sb[NMJ];
+#pragma unroll
+        for (int a = 0; a < ND; ++a) x[a] = valid ? xs[((w - 1) * ND + a) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) ub[m] = pack8(x[2 * m], x[2 * m + 1]);
+        pin_operands();
+        scores(ub, sb);
+        product(x, ub, sb, true);
+#pragma unroll
+        for (int a = 0; a < ND; ++a) {
+          r[a] -= acc[a];
+          pv[a] = r[a];
+        }
+      }
       float rho = 0.f;
 #pragma unroll
       for (int a = 0; a < ND; ++a) rho += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
@@ -339,7 +358,16 @@ template <int D, int C, bool LF = false>
 hipError_t launch_t(const CgParams& p, hipStream_t s) {
   const long long chunks = (long long)p.BH * p.NC;
   const dim3 grid((unsigned)((chunks + kChunksPerWave - 1) / kChunksPerWave));
-  hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
+  if constexpr (!LF) {
+    if (p.warm) {
+      hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, false, true>), grid, dim3(64), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
+    }
+  } else {
+    if (p.warm) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ struct CgParams {
   int BH, H, T, NC, max_steps;
   float tol2;            // tol*tol, or -1 for the fixed-step mode
   int lam_full;          // lam is a full symmetric matrix per head (bf16 path, chunk 64, D 64 or 128)
+  int warm;              // bf16 path, diagonal Lambda: token t's CG starts from token t-16's
+                         // solution when both lie in one chunk (tiles 1.. of a chunk)
 };
 
 // Largest total decay -sum(log gamma) of a chunk that the scaled bf16 CG kernel

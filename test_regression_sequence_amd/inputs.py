@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
     "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs",
-    "make_full_lambda", "round_to_bf16",
+    "make_full_lambda", "make_slow_queries", "round_to_bf16",
     "bf16_bits", "bits_to_f32",
 ]
 
@@ -180,6 +180,31 @@ def make_fwd_inputs(cfg: FwdConfig) -> dict:
     out = dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam, cfg=cfg)
     if cfg.dtype == "bf16":
         out.update(q_bits=qb, k_bits=kb, v_bits=vb)
+    return out
+
+
+def make_slow_queries(x: dict, rho1: float) -> dict:
+    """A forward workload whose queries drift slowly along each sequence.
+
+    q_t = rho1 q_{t-1} + sqrt(1 - rho1^2) e_t per dimension (e ~ N(0, 1),
+    q_0 = e_0), then L2-normalised per token and rounded like the workload's
+    other q (stream ``default_rng([seed, 6])``).  Keys, values, gates and
+    Lambda are the workload's.  A stand-in for queries that change smoothly
+    from token to token; the pages say nothing about query statistics.
+    """
+    cfg = x["cfg"]
+    rng = np.random.default_rng([cfg.seed, 6])
+    e = rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.d))
+    q = np.empty_like(e)
+    q[:, :, 0] = e[:, :, 0]
+    c = np.sqrt(1.0 - rho1 * rho1)
+    for t in range(1, cfg.T):
+        q[:, :, t] = rho1 * q[:, :, t - 1] + c * e[:, :, t]
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    q32, qb = _finish(q, cfg.dtype)
+    out = dict(x, q=q32)
+    if cfg.dtype == "bf16":
+        out["q_bits"] = qb
     return out
 
 

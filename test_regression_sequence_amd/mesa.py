@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.mesa_fwd_chunked.restype = ctypes.c_int
         L.mesa_fwd_chunked.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        P, S, P]
+        L.mesa_fwd_chunked_warm.restype = ctypes.c_int
+        L.mesa_fwd_chunked_warm.argtypes = list(L.mesa_fwd_chunked.argtypes)
         L.mesa_fwd_chunked_noalloc.restype = ctypes.c_int
         L.mesa_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 13 + [P]
         L.mesa_fwd_chunked_ex.restype = ctypes.c_int
@@ -154,15 +156,17 @@ def workspace_bytes(B, H, T, d, chunk, max_steps=0, tol=0.0, dtype=torch.bfloat1
 def fwd_chunked(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
                 tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
                 return_steps: bool = True, return_x: bool = False, out=None,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                workspace: Optional[torch.Tensor] = None, stream=None, warm: bool = False) -> dict:
     """Chunked Mesa forward; q, k, v [B, H, T, d] (fp32 or bf16) on the GPU.
 
     gamma, beta [B, H, T] fp32; lam [H, d] fp32; h0, g0 optional [B, H, d, d]
     fp32.  Returns a dict with ``o`` [B, H, T, d] fp32 and, on request,
     ``steps`` [B, H, T] int32, ``x`` [B, H, T, d], ``h_final``, ``g_final``.
-    ``out`` may pass preallocated result tensors (same keys).
+    ``out`` may pass preallocated result tensors (same keys).  ``warm`` calls
+    ``mesa_fwd_chunked_warm``: token t's CG starts from token t-16's solution
+    when both lie in one chunk (bf16 inputs).
     """
-    return _fwd(False, q, k, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+    return _fwd("warm" if warm else False, q, k, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
                 g0=g0, return_state=return_state, return_steps=return_steps, return_x=return_x,
                 out=out, workspace=workspace, stream=stream)
 
@@ -236,7 +240,10 @@ def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, 
             _ptr(res.get("steps")), _ptr(res.get("x")), _ptr(workspace), ctypes.c_size_t(wbytes),
             _stream(stream))
     head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam))
-    if ex:
+    if ex == "warm":
+        code_ = L.mesa_fwd_chunked_warm(*head, *rest)
+        _check(code_, "mesa_fwd_chunked_warm")
+    elif ex:
         code_ = L.mesa_fwd_chunked_ex(*head, 1 if lam_full else 0, *rest)
         _check(code_, "mesa_fwd_chunked_ex")
     else:

@@ -89,6 +89,19 @@ def call_fwd_noalloc(d, q=FAKE, lam=FAKE, o=FAKE):
                                                None, None, P(o), None, None, None, None, None)
 
 
+def test_warm_forward_takes_bf16_inputs_only():
+    P = ctypes.c_void_p
+    d = desc(in_dtype=mesa.MESA_F32)
+    code = mesa.lib().mesa_fwd_chunked_warm(ctypes.byref(d), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                            None, None, P(FAKE), None, None, None, None, P(FAKE),
+                                            ctypes.c_size_t(1 << 40), None)
+    assert code == 2
+    d = desc(B=0)
+    assert mesa.lib().mesa_fwd_chunked_warm(ctypes.byref(d), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                            None, None, P(FAKE), None, None, None, None, P(FAKE),
+                                            ctypes.c_size_t(1 << 40), None) == 1
+
+
 def test_noalloc_forward_validates_before_any_hip_call():
     """The allocation-free forward rejects, before any HIP call (this runs without
     a GPU): a workload whose workspace exceeds the static scratch, then the
