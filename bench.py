@@ -236,6 +236,58 @@ def bench_warm_forward(cfg, steps, warmup) -> dict:
     return out
 
 
+def bench_prep_forward(cfg, steps, warmup, window=4) -> dict:
+    """The layer forward on raw queries and keys: the preprocessing kernel then
+    the forward (two calls) against mesa_fwd_chunked_prep (preprocessing fused
+    into the scan and solve loads), with raw histories.  Whole calls, the two
+    forms alternating, HIP events, medians; the outputs are checked equal."""
+    import torch
+    from test_regression_sequence_amd import mesa
+    from test_regression_sequence_amd.inputs import make_fwd_inputs, make_preprocess_inputs
+    x = make_fwd_inputs(cfg)
+    xp = make_preprocess_inputs(cfg, window)
+    qr, kr, hq, hk = (torch.from_numpy(xp[n]).cuda().to(torch.bfloat16) for n in ("q", "k", "hq", "hk"))
+    wq, wk = (torch.from_numpy(xp[n]).cuda() for n in ("wq", "wk"))
+    v = torch.from_numpy(x["v"]).cuda().to(torch.bfloat16)
+    gamma, beta, lam = (torch.from_numpy(x[n]).cuda() for n in ("gamma", "beta", "lam"))
+    del x, xp
+    ws = torch.empty(mesa.workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d, cfg.chunk), device="cuda", dtype=torch.uint8)
+    kw = dict(chunk=cfg.chunk, max_steps=cfg.max_steps, tol=cfg.tol, workspace=ws)
+    pre = mesa.qk_preprocess(qr, kr, wq, wk, q_hist=hq, k_hist=hk)
+    res = {"separate": mesa.fwd_chunked(pre["q"], pre["k"], v, gamma, beta, lam, **kw),
+           "fused": mesa.fwd_chunked_prep(qr, kr, v, gamma, beta, lam, wq, wk, q_hist=hq, k_hist=hk, **kw)}
+
+    def call(form, e=None):
+        if e is not None:
+            e[0].record()
+        if form == "separate":
+            mesa.qk_preprocess(qr, kr, wq, wk, q_hist=hq, k_hist=hk, out=pre)
+            mesa.fwd_chunked(pre["q"], pre["k"], v, gamma, beta, lam, out=res[form], **kw)
+        else:
+            mesa.fwd_chunked_prep(qr, kr, v, gamma, beta, lam, wq, wk, q_hist=hq, k_hist=hk, out=res[form], **kw)
+        if e is not None:
+            e[1].record()
+
+    ev = {f: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for f in res}
+    for _ in range(warmup):
+        for f in res:
+            call(f)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for f in res:
+            call(f, ev[f][i])
+    torch.cuda.synchronize()
+    same = all(torch.equal(res["separate"][k], res["fused"][k]) for k in res["separate"])
+    ms = {f: float(np.median([a.elapsed_time(b) for a, b in ev[f]])) for f in res}
+    tokens = cfg.B * cfg.H * cfg.T
+    return {"workload": f"{cfg.name} shape, raw q/k with window {window} and histories",
+            "separate_ms_median": round(ms["separate"], 4), "fused_ms_median": round(ms["fused"], 4),
+            "saved_ms": round(ms["separate"] - ms["fused"], 4),
+            "fused_tokens_per_s": round(tokens / (ms["fused"] * 1e-3), 1),
+            "outputs_bitwise_equal": bool(same)}
+
+
 def bench_latency(cfg, steps, warmup) -> dict:
     """One whole mesa_fwd_chunked call on a tiny workload: latency."""
     import torch
@@ -711,6 +763,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--forward-only", action="store_true",
                     help="time the chosen forward workload only (profiling runs)")
+    ap.add_argument("--prep-forward", action="store_true",
+                    help="also time the forward on raw q/k: preprocessing kernel + forward against the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices-per-core", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
@@ -798,6 +852,9 @@ def main():
         "fwd_frac_of_mfma_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(fw["wall_ms"], 4),
     }
+    if args.prep_forward:
+        line["forward_with_preprocessing"] = bench_prep_forward(cfg, args.steps, args.warmup)
+        log(f"forward with preprocessing: {line['forward_with_preprocessing']}")
     if args.forward_only:
         line["forward_detail"] = forward_report(cfg, fw)
         if cpu is not None:
@@ -816,6 +873,9 @@ def main():
     line["preprocess"] = bench_preprocess(CONFIGS[args.workload], args.steps, args.warmup)
     line["preprocess"]["vs_torch_copy"] = round(line["preprocess"]["achieved_GBs"] / copy_gbs, 4)
     log(f"preprocess: {line['preprocess']['us_per_call']} us per call")
+    if "forward_with_preprocessing" not in line:
+        line["forward_with_preprocessing"] = bench_prep_forward(cfg, args.steps, args.warmup)
+        log(f"forward with preprocessing: {line['forward_with_preprocessing']}")
     line["backward"] = bench_backward(CONFIGS[args.workload], args.steps, args.warmup)
     log(f"backward: {line['backward']['ms_per_call']} ms per call")
     cfg_w = CONFIGS[args.workload]

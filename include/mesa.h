@@ -141,6 +141,44 @@ mesa_status mesa_fwd_chunked_warm(const mesa_fwd_desc* d,
                                   void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/* mesa_fwd_chunked on raw queries and keys, with the preprocessing of
+ * mesa_qk_preprocess fused into the forward's loads (MesaNet page,
+ * "architecture" section: queries and keys are convolved with a small causal
+ * window and normalised before the Mesa layer).  The result equals
+ * mesa_qk_preprocess (bf16 outputs) followed by mesa_fwd_chunked on its
+ * outputs, bit for bit, without the processed q and k ever reaching memory:
+ * the scan and solve kernels convolve and normalise the raw rows they load.
+ *
+ *   q_raw, k_raw   [B, H, T, dk] bf16      raw projections (the q, k of
+ *                                          mesa_fwd_chunked before processing)
+ *   w_q, w_k       [H, dk, window] fp32    taps; tap i weighs token t-i
+ *   window         1..4
+ *   eps            > 0, finite             out_t = y_t / max(||y_t||, eps)
+ *   q_hist, k_hist [B, H, window-1, dk] bf16 or NULL: raw vectors before
+ *                                          t = 0, oldest first (NULL: zeros)
+ *   q_hist_out, k_hist_out [B, H, window-1, dk] bf16 or NULL: the last
+ *                  window-1 raw vectors of history + sequence (the next
+ *                  call's histories); they may not overlap q_raw, k_raw,
+ *                  q_hist, k_hist or each other (MESA_ERR_INVALID_ARG)
+ *
+ * Every other argument, the workspace (mesa_fwd_workspace_bytes(d)) and the
+ * error behaviour are those of mesa_fwd_chunked.  Supported for in_dtype
+ * MESA_BF16, chunk 64 and dk = dv in {64, 128}; other descriptors, and
+ * window > 4, return MESA_ERR_UNSUPPORTED.  window < 1, eps <= 0 or not
+ * finite, or a NULL w_q / w_k return MESA_ERR_INVALID_ARG.  Nothing is
+ * launched on an error. */
+mesa_status mesa_fwd_chunked_prep(const mesa_fwd_desc* d,
+                                  const void* q_raw, const void* k_raw, const void* v,
+                                  const float* w_q, const float* w_k, int32_t window, float eps,
+                                  const void* q_hist, const void* k_hist,
+                                  const float* gamma, const float* beta, const float* lambda,
+                                  const float* h0, const float* g0,
+                                  float* o, float* h_final, float* g_final,
+                                  int32_t* steps, float* x_out,
+                                  void* q_hist_out, void* k_hist_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Size of the static scratch array behind mesa_fwd_chunked_noalloc: 64 MiB
  * per GPU the library runs on (for example B*H*T = 65536 token-heads at
  * dk = 128, chunk 64, or the B=4, H=8, T=2048, dk=64 workload's 16 MiB). */
@@ -422,7 +460,11 @@ mesa_status mesa_decode_step_ex(int32_t N, int32_t H, int32_t dk, int32_t dv,
  *                window-1 raw vectors of history + sequence, the next call's
  *                history (also for T < window-1, and for a decode step, T = 1)
  *
- * Supported: d in {16, 64, 128}, 1 <= window <= 4, B*H <= 65535, eps > 0.
+ * The scale 1 / max(||y||, eps) is formed as min(1/sqrt(||y||^2), 1/eps)
+ * with the hardware reciprocal square root (1 ulp).
+ *
+ * Supported: d in {16, 64, 128}, 1 <= window <= 4, B*H <= 65535, and
+ * 2^-63 <= eps < inf (else MESA_ERR_INVALID_ARG).
  * Outputs may not overlap the raw inputs or histories (MESA_ERR_INVALID_ARG):
  * every raw vector is read by up to `window` outputs.  Device pointers,
  * 16-byte aligned; asynchronous on `stream`. */

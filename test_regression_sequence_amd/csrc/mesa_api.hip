@@ -32,6 +32,11 @@ mesa_status check_desc(const mesa_fwd_desc* d) {
   return MESA_OK;
 }
 
+// The preprocessing's eps: finite and at least 2^-63 (below it the
+// normalisation would need the norm of a vector whose squared norm is a
+// denormal float).
+bool eps_ok(float eps) { return eps >= 0x1p-63f && !std::isinf(eps); }
+
 }  // namespace
 
 extern "C" {
@@ -84,11 +89,22 @@ mesa_status fwd_validate(int phases, const mesa_fwd_desc* d, const void* q, cons
   return MESA_OK;
 }
 
+// the fused preprocessing of a forward call: taps, window, eps, histories
+struct FwdPrep {
+  const float* wq;
+  const float* wk;
+  const void* q_hist;
+  const void* k_hist;
+  int W;
+  float inv_eps;
+};
+
 mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const void* k,
                      const void* v, const float* gamma, const float* beta, const float* lambda,
                      const float* h0, const float* g0, float* o, float* h_final, float* g_final,
                      int32_t* steps, float* x_out, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, bool lam_full = false, bool warm = false) {
+                     hipStream_t stream, bool lam_full = false, bool warm = false,
+                     const FwdPrep* prep = nullptr) {
   const mesa_status st = fwd_validate(phases, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                                       steps, x_out, workspace, lam_full);
   if (st != MESA_OK) return st;
@@ -124,6 +140,9 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
     sp.BH = BH; sp.T = d->T; sp.NC = NC;
     sp.NS = NS; sp.SEG = mesa::scan_segment_chunks(NC, NS);
     sp.seg_state = seg_state; sp.seg_decay = seg_decay;
+    if (prep) {
+      sp.prep = 1; sp.W = prep->W; sp.H = d->H; sp.wk = prep->wk; sp.k_hist = prep->k_hist; sp.inv_eps = prep->inv_eps;
+    }
     if (mesa::launch_scan(bf16, D, C, sp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
   if ((phases & kSolve) && any_tokens) {
@@ -134,6 +153,10 @@ mesa_status fwd_impl(int phases, const mesa_fwd_desc* d, const void* q, const vo
     cp.tol2 = d->tol > 0.f ? d->tol * d->tol : -1.f;
     cp.lam_full = lam_full ? 1 : 0;
     cp.warm = warm ? 1 : 0;
+    if (prep) {
+      cp.prep = 1; cp.W = prep->W; cp.wq = prep->wq; cp.wk = prep->wk;
+      cp.q_hist = prep->q_hist; cp.k_hist = prep->k_hist; cp.inv_eps = prep->inv_eps;
+    }
     if (mesa::launch_cg(bf16, D, C, cp, stream) != hipSuccess) return MESA_ERR_HIP;
   }
   return MESA_OK;
@@ -159,6 +182,51 @@ mesa_status mesa_fwd_chunked_warm(const mesa_fwd_desc* d, const void* q, const v
                                   size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(kScan | kSolve, d, q, k, v, gamma, beta, lambda, h0, g0, o, h_final, g_final,
                   steps, x_out, workspace, workspace_bytes, stream, false, true);
+}
+
+mesa_status mesa_fwd_chunked_prep(const mesa_fwd_desc* d, const void* q_raw, const void* k_raw, const void* v,
+                                  const float* w_q, const float* w_k, int32_t window, float eps,
+                                  const void* q_hist, const void* k_hist, const float* gamma, const float* beta,
+                                  const float* lambda, const float* h0, const float* g0, float* o,
+                                  float* h_final, float* g_final, int32_t* steps, float* x_out,
+                                  void* q_hist_out, void* k_hist_out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  mesa_status st = fwd_validate(kScan | kSolve, d, q_raw, k_raw, v, gamma, beta, lambda, h0, g0, o, h_final,
+                                g_final, steps, x_out, workspace, false);
+  if (st != MESA_OK) return st;
+  if (window < 1 || !eps_ok(eps) || !w_q || !w_k) return MESA_ERR_INVALID_ARG;
+  if (d->in_dtype != MESA_BF16 || d->chunk != 64 || (d->dk != 64 && d->dk != 128) || window > 4)
+    return MESA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {w_q, w_k, q_hist, k_hist, q_hist_out, k_hist_out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return MESA_ERR_ALIGNMENT;
+  // the next call's histories may not overlap what they are formed from
+  const size_t seq_bytes = (size_t)d->B * d->H * d->T * d->dk * 2;
+  const size_t hist_bytes = (size_t)d->B * d->H * (window - 1) * d->dk * 2;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+  };
+  const void* ins[] = {q_raw, k_raw, q_hist, k_hist};
+  const size_t in_bytes[] = {seq_bytes, seq_bytes, hist_bytes, hist_bytes};
+  const void* outs[] = {q_hist_out, k_hist_out};
+  for (const void* out : outs)
+    for (int b = 0; b < 4; ++b)
+      if (overlap(out, hist_bytes, ins[b], in_bytes[b])) return MESA_ERR_INVALID_ARG;
+  if (overlap(q_hist_out, hist_bytes, k_hist_out, hist_bytes)) return MESA_ERR_INVALID_ARG;
+
+  const FwdPrep prep{w_q, w_k, q_hist, k_hist, window, 1.0f / eps};
+  st = fwd_impl(kScan | kSolve, d, q_raw, k_raw, v, gamma, beta, lambda, h0, g0, o, h_final, g_final, steps,
+                x_out, workspace, workspace_bytes, stream, false, false, &prep);
+  if (st != MESA_OK || window == 1 || (!q_hist_out && !k_hist_out)) return st;
+  mesa::PrepParams pp{};
+  pp.x[0] = q_raw; pp.x[1] = k_raw;
+  pp.hist_in[0] = q_hist; pp.hist_in[1] = k_hist;
+  pp.hist_out[0] = q_hist_out; pp.hist_out[1] = k_hist_out;
+  pp.BH = d->B * d->H; pp.H = d->H; pp.T = d->T; pp.W = window; pp.inv_eps = 1.0f / eps;
+  return mesa::launch_qk_prep(true, d->dk, pp, stream) == hipSuccess ? MESA_OK : MESA_ERR_HIP;
 }
 
 mesa_status mesa_fwd_chunked_ex(const mesa_fwd_desc* d, const void* q, const void* k, const void* v,
@@ -486,7 +554,7 @@ mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32
                                const float* w_q, const float* w_k, const void* q_hist,
                                const void* k_hist, float eps, void* q_out, void* k_out,
                                void* q_hist_out, void* k_hist_out, hipStream_t stream) {
-  if (B < 0 || H < 1 || T < 0 || window < 1 || !(eps > 0.f) || std::isinf(eps)) return MESA_ERR_INVALID_ARG;
+  if (B < 0 || H < 1 || T < 0 || window < 1 || !eps_ok(eps)) return MESA_ERR_INVALID_ARG;
   if (dtype != MESA_F32 && dtype != MESA_BF16) return MESA_ERR_INVALID_ARG;
   if ((d != 16 && d != 64 && d != 128) || window > 4) return MESA_ERR_UNSUPPORTED;
   if ((long long)B * H > 65535) return MESA_ERR_UNSUPPORTED;
@@ -518,7 +586,7 @@ mesa_status mesa_qk_preprocess(int32_t B, int32_t H, int32_t T, int32_t d, int32
   pp.hist_in[0] = q_hist; pp.hist_in[1] = k_hist;
   pp.out[0] = q_out; pp.out[1] = k_out;
   pp.hist_out[0] = q_hist_out; pp.hist_out[1] = k_hist_out;
-  pp.BH = B * H; pp.H = H; pp.T = T; pp.W = window; pp.eps = eps;
+  pp.BH = B * H; pp.H = H; pp.T = T; pp.W = window; pp.inv_eps = 1.0f / eps;
   return mesa::launch_qk_prep(dtype == MESA_BF16, d, pp, stream) == hipSuccess ? MESA_OK : MESA_ERR_HIP;
 }
 

@@ -55,6 +55,13 @@
 // counted as a step).  Tile 0 starts from 0: earlier chunks are solved in
 // parallel.
 //
+// PREP (fused preprocessing, the "architecture" section: queries and keys
+// are convolved with a small causal window and normalised before the layer):
+// q and k arrive raw; the wave forms the chunk's processed keys, then its
+// processed queries, into one LDS buffer (mesa_prep_rows.h, the same
+// arithmetic as the preprocessing kernel) and reads the key row fragments and
+// each tile's queries from there instead of from global memory.
+//
 // Lambda is diagonal, or (LF) a full symmetric positive definite matrix per
 // head (the page calls the regulariser symmetric positive definite).  The
 // full matrix enters as one more d x d MFMA operand, (Lambda / Gamma_t) p =
@@ -66,6 +73,7 @@
 
 #include "mesa_common.h"
 #include "mesa_kernels.h"
+#include "mesa_prep_rows.h"
 
 namespace mesa {
 
@@ -74,10 +82,11 @@ namespace {
 template <int W>
 using tile_c = std::integral_constant<int, W>;
 
-template <int D, int C, bool LF, bool WARM = false>
+template <int D, int C, bool LF, bool WARM = false, bool PREP = false>
 __global__ __launch_bounds__(LF ? 128 : 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_kernel(CgParams p) {
   static_assert(!(LF && WARM), "the warm start takes a diagonal Lambda");
+  static_assert(!PREP || (!LF && !WARM && C == 64), "fused preprocessing: diagonal Lambda, cold start, chunk 64");
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
   constexpr int NWV = LF ? 2 : 1;  // waves (chunks) per workgroup
 
@@ -106,6 +115,10 @@ void cg_bf16_kernel(CgParams p) {
   __shared__ float lam_s[D];
   __shared__ float bcum_[NWV][C];
   __shared__ float betas_[NWV][C];
+  // PREP: the chunk's processed keys, then its processed queries, [row][D]
+  // with the row stride padded by 16 bytes against bank conflicts
+  constexpr int PS = D + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 prow[PREP ? C * PS : 1];
   bf16x8* const xs = xs_[wv];
   float* const bcum = bcum_[wv];
   float* const betas = betas_[wv];
@@ -142,6 +155,19 @@ void cg_bf16_kernel(CgParams p) {
         dst[jt][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
+  };
+  // PREP: the key row fragments from the processed rows in LDS (rows past Lc
+  // hold finite filler, weighted 0 like the repeated rows above)
+  auto load_rows_lds = [&](bf16x8 (&dst)[NW][NM]) {
+#pragma unroll
+    for (int jt = 0; jt < NW; ++jt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const __bf16* src = prow + (16 * jt + tl) * PS + 32 * m + 4 * g;
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(src);
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 16);
+        dst[jt][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
   };
   // Column fragments from row fragments, transposed on the MFMA unit: with B
   // the 0/1 matrix selecting dims 16nt..16nt+15 out of k-block nt/2, the
@@ -209,7 +235,19 @@ void cg_bf16_kernel(CgParams p) {
   auto fetch_q = [&](const int w) {
     const int tq = min(16 * w + tl, Lc - 1);
 #pragma unroll
-    for (int a = 0; a < ND; ++a) qraw[a] = *reinterpret_cast<const u16x4*>(Qg + (row0 + tq) * D + 16 * a + 4 * g);
+    for (int a = 0; a < ND; ++a) {
+      if constexpr (PREP) qraw[a] = *reinterpret_cast<const u16x4*>(prow + (16 * w + tl) * PS + 16 * a + 4 * g);
+      else qraw[a] = *reinterpret_cast<const u16x4*>(Qg + (row0 + tq) * D + 16 * a + 4 * g);
+    }
+  };
+  // PREP: the raw rows of the chunk's keys and queries, loaded in the first
+  // batch and formed into prow one after the other
+  PrepChunk<D, C> kraw, qraw_rows;
+  auto prep_load = [&](PrepChunk<D, C>& pc, const void* X, const void* hist) {
+    pc.load(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(hist), bh, T, p.W, s, Lc, lane);
+  };
+  auto prep_form = [&](const PrepChunk<D, C>& pc, const float* taps) {
+    pc.form(taps, h, p.W, p.inv_eps, prow, PS, lane);
   };
 
   if constexpr (LF) {
@@ -235,9 +273,19 @@ void cg_bf16_kernel(CgParams p) {
 #pragma unroll
     for (int i = 0; i < (D + 63) / 64; ++i)
       lam_v[i] = (!LF && lane + 64 * i < D) ? p.lam[(size_t)h * D + lane + 64 * i] : 0.f;
+    if constexpr (PREP) {
+      prep_load(kraw, p.k, p.k_hist);
+      prep_load(qraw_rows, p.q, p.q_hist);
+    }
     load_state(p.hb);
-    load_rows(Kg, kr);
-    fetch_q(0);
+    if constexpr (PREP) {
+      prep_form(kraw, p.wk);
+      __syncthreads();
+      load_rows_lds(kr);
+    } else {
+      load_rows(Kg, kr);
+      fetch_q(0);
+    }
     lg = lane < Lc ? logf(lg) : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -259,6 +307,13 @@ void cg_bf16_kernel(CgParams p) {
   const bool scaled = __builtin_amdgcn_readfirstlane(bcum[Lc - 1] >= -kMaxScaledDecay ? 1 : 0) != 0;
   if (lane == 0) p.unscaled[chunk] = scaled ? 0 : 1;
   if (!scaled) return;
+  if constexpr (PREP) {
+    // the key fragments are in registers (the barrier above waited for them):
+    // the queries replace the keys in the buffer
+    prep_form(qraw_rows, p.wq);
+    __syncthreads();
+    fetch_q(0);
+  }
   {
     bf16x8 wr[NW][NM];
     weighted_rows(kr, wr);
@@ -497,13 +552,20 @@ hipError_t launch_t(const CgParams& p, hipStream_t s) {
   // LF: two chunks of one sequence per two-wave workgroup
   const dim3 grid((unsigned)((long long)p.BH * (LF ? (p.NC + 1) / 2 : p.NC)));
   if constexpr (!LF) {
-    if (p.warm) {
+    if (p.prep) {
+      if constexpr (C == 64 && D >= 64) {
+        if (p.warm) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false, true>), grid, dim3(64), 0, s, p);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else if (p.warm) {
       hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, true>), grid, dim3(64), 0, s, p);
     } else {
       hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
     }
   } else {
-    if (p.warm) return hipErrorInvalidValue;
+    if (p.warm || p.prep) return hipErrorInvalidValue;
     hipLaunchKernelGGL((cg_bf16_kernel<D, C, LF>), grid, dim3(128), 0, s, p);
   }
   const hipError_t e = hipGetLastError();

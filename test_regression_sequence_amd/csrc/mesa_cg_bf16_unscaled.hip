@@ -20,9 +20,12 @@
 // definite Lambda (LF) enters as one more MFMA operand, its bf16 fragments in
 // LDS, applied to the bf16 search direction.  WARM: tile w >= 1 starts token t
 // from token t-16's solution (the previous tile's, parked in LDS), with
-// r_0 = q - A_t x_0 from one more product, as in the scaled kernel.
+// r_0 = q - A_t x_0 from one more product, as in the scaled kernel.  PREP:
+// q and k arrive raw and are convolved and normalised into LDS as they are
+// loaded, as in the scaled kernel.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
+#include "mesa_prep_rows.h"
 
 namespace mesa {
 
@@ -30,10 +33,11 @@ namespace {
 
 constexpr int kChunksPerWave = 8;
 
-template <int D, int C, bool LF, bool WARM = false>
+template <int D, int C, bool LF, bool WARM = false, bool PREP = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cg_bf16_unscaled_kernel(CgParams p) {
   static_assert(!(LF && WARM), "the warm start takes a diagonal Lambda");
+  static_assert(!PREP || (!LF && !WARM && C == 64), "fused preprocessing: diagonal Lambda, cold start, chunk 64");
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
 
   const int lane = threadIdx.x, tl = lane & 15, g = lane >> 4;
@@ -47,6 +51,9 @@ void cg_bf16_unscaled_kernel(CgParams p) {
   __shared__ bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
   __shared__ float bcum[C];
   __shared__ float betas[C];
+  // PREP: the chunk's processed keys, then its processed queries, [row][D]
+  constexpr int PS = D + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 prow[PREP ? C * PS : 1];
 
   while (todo) {
     const int chunk = first + __builtin_ctzll(todo);
@@ -82,6 +89,29 @@ void cg_bf16_unscaled_kernel(CgParams p) {
           u16x4 lo = u16x4{0, 0, 0, 0}, hi = lo;
           if (j < Lc) {
             const uint16_t* src = X + (row0 + j) * D + 32 * m + 4 * g;
+            lo = *reinterpret_cast<const u16x4*>(src);
+            hi = *reinterpret_cast<const u16x4*>(src + 16);
+          }
+          dst[jt][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+    };
+    // PREP: the chunk's processed rows of raw vectors X into prow, and the key
+    // row fragments from there (zero past Lc)
+    auto prep_rows = [&](const void* X, const void* hist, const float* taps) {
+      PrepChunk<D, C> pc;
+      pc.load(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(hist), bh, T, p.W, s, Lc, lane);
+      pc.form(taps, h, p.W, p.inv_eps, prow, PS, lane);
+    };
+    auto load_rows_lds = [&](bf16x8 (&dst)[NW][NM]) {
+#pragma unroll
+      for (int jt = 0; jt < NW; ++jt) {
+        const int j = 16 * jt + tl;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          u16x4 lo = u16x4{0, 0, 0, 0}, hi = lo;
+          if (j < Lc) {
+            const __bf16* src = prow + j * PS + 32 * m + 4 * g;
             lo = *reinterpret_cast<const u16x4*>(src);
             hi = *reinterpret_cast<const u16x4*>(src + 16);
           }
@@ -130,7 +160,13 @@ void cg_bf16_unscaled_kernel(CgParams p) {
     };
 
     load_state(p.hb);
-    load_rows(Kg, kr);
+    if constexpr (PREP) {
+      prep_rows(p.k, p.k_hist, p.wk);
+      __syncthreads();
+      load_rows_lds(kr);
+    } else {
+      load_rows(Kg, kr);
+    }
     {
       float lg = 0.f, bt = 0.f;
       if (lane < Lc) {
@@ -161,6 +197,11 @@ void cg_bf16_unscaled_kernel(CgParams p) {
       }
     }
     __syncthreads();
+    if constexpr (PREP) {
+      // the key fragments are in registers: the queries replace the keys
+      prep_rows(p.q, p.q_hist, p.wq);
+      __syncthreads();
+    }
     columns_from_rows(kr);
     pin_operands();
 
@@ -244,7 +285,13 @@ void cg_bf16_unscaled_kernel(CgParams p) {
       f32x4 r[ND], x[ND], pv[ND];
 #pragma unroll
       for (int a = 0; a < ND; ++a) {
-        r[a] = valid ? load4<true>(Qg, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (PREP) {
+          const u16x4 u = *reinterpret_cast<const u16x4*>(prow + tloc * PS + 16 * a + 4 * g);
+          r[a] = valid ? f32x4{bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3])}
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          r[a] = valid ? load4<true>(Qg, (row0 + tloc) * D + 16 * a + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         x[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         pv[a] = r[a];
       }
@@ -359,13 +406,20 @@ hipError_t launch_t(const CgParams& p, hipStream_t s) {
   const long long chunks = (long long)p.BH * p.NC;
   const dim3 grid((unsigned)((chunks + kChunksPerWave - 1) / kChunksPerWave));
   if constexpr (!LF) {
-    if (p.warm) {
+    if (p.prep) {
+      if constexpr (C == 64 && D >= 64) {
+        if (p.warm) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, false, false, true>), grid, dim3(64), 0, s, p);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else if (p.warm) {
       hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, false, true>), grid, dim3(64), 0, s, p);
     } else {
       hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
     }
   } else {
-    if (p.warm) return hipErrorInvalidValue;
+    if (p.warm || p.prep) return hipErrorInvalidValue;
     hipLaunchKernelGGL((cg_bf16_unscaled_kernel<D, C, LF>), grid, dim3(64), 0, s, p);
   }
   return hipGetLastError();

@@ -24,6 +24,13 @@ struct ScanParams {
   int SEG, NS;
   float* seg_state;      // [BH, 2, NS-1, D*D]: segment totals, then carry-in states
   float* seg_decay;      // [BH, NS-1]: product of gamma over each segment
+  // fused preprocessing (bf16, chunk 64): k holds raw keys, convolved with the
+  // taps wk [H, D, W] and L2-normalised (eps) as they are staged; k_hist
+  // [BH, W-1, D] raw keys before t = 0, or null (zeros)
+  int prep, W, H;
+  const float* wk;
+  const void* k_hist;
+  float inv_eps;         // 1 / eps
 };
 
 // Segments per sequence for the state scan.  Whole-state workgroups (one per
@@ -71,6 +78,16 @@ struct CgParams {
   int lam_full;          // lam is a full symmetric matrix per head (bf16 path, chunk 64, D 64 or 128)
   int warm;              // bf16 path, diagonal Lambda: token t's CG starts from token t-16's
                          // solution when both lie in one chunk (tiles 1.. of a chunk)
+  // fused preprocessing (bf16, diagonal Lambda, chunk 64, D 64 or 128): q and k
+  // hold raw vectors, convolved with the taps wq / wk [H, D, W] and
+  // L2-normalised (eps) as they are loaded; q_hist / k_hist [BH, W-1, D] raw
+  // vectors before t = 0, or null (zeros)
+  int prep, W;
+  const float* wq;
+  const float* wk;
+  const void* q_hist;
+  const void* k_hist;
+  float inv_eps;         // 1 / eps
 };
 
 // Largest total decay -sum(log gamma) of a chunk that the scaled bf16 CG kernel
@@ -103,7 +120,7 @@ struct PrepParams {
   void* out[2];            // [BH, T, D]
   void* hist_out[2];       // [BH, W-1, D] or null
   int BH, H, T, W;
-  float eps;
+  float inv_eps;           // 1 / eps
 };
 
 // Backward pass (bf16 inputs, chunk 64).

@@ -18,6 +18,7 @@
 // squared norm is summed over the LPR lanes of a row with DPP moves.
 #include "mesa_common.h"
 #include "mesa_kernels.h"
+#include "mesa_prep_rows.h"
 
 namespace mesa {
 
@@ -103,35 +104,18 @@ __global__ __launch_bounds__(kPrepThreads) void qk_prep_kernel(PrepParams p) {
   }
   // this lane's taps: 8 channels x W, contiguous
   float w[8][W];
-  {
-    const float* wp = p.w[which] + ((size_t)h * D + c0) * W;
-#pragma unroll
-    for (int i4 = 0; i4 < 2 * W; ++i4) {
-      const f32x4 t = reinterpret_cast<const f32x4*>(wp)[i4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[(4 * i4 + u) / W][(4 * i4 + u) % W] = t[u];
-    }
-  }
+  prep_taps8<W>(p.w[which], h, D, c0, w);
 
   void* out = p.out[which];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    float y[8];
+    float x8[W][8], y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = 0.f;
+    for (int m = 0; m < W; ++m)
 #pragma unroll
-      for (int i = 0; i < W; ++i) {
-        const int m = s + W - 1 - i;
-        acc = __builtin_fmaf(w[e][i], zero[m] ? 0.f : rows[m].at(e), acc);
-      }
-      y[e] = acc;
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[e], y[e], ss);
-    ss = group_sum<LPR>(ss);
-    const float scale = 1.f / fmaxf(sqrtf(ss), p.eps);
+      for (int e = 0; e < 8; ++e) x8[m][e] = zero[s + m] ? 0.f : rows[s + m].at(e);
+    const float ss = group_sum<LPR>(prep_conv8<W>(w, x8, y));
+    const float scale = prep_scale(ss, p.inv_eps);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] *= scale;
     const int t = t0 + s;
@@ -193,7 +177,8 @@ hipError_t launch_prep_d(int D, const PrepParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_qk_prep(bool bf16, int D, const PrepParams& p, hipStream_t s) {
-  if (p.T > 0) {
+  // without outputs only the next call's histories are formed (the fused forward)
+  if (p.T > 0 && p.out[0] && p.out[1]) {
     const hipError_t e = bf16 ? launch_prep_d<true>(D, p, s) : launch_prep_d<false>(D, p, s);
     if (e != hipSuccess) return e;
   }

@@ -25,6 +25,17 @@
 // carried fp32 state does not pick up a bf16 rounding of beta*tail*x), fp32
 // MFMA for fp32 inputs.
 //
+// PREP (fused preprocessing, bf16, chunk 64): the keys arrive raw and are
+// convolved and L2-normalised as they are staged (mesa_prep_rows.h: a row's
+// D/8 lanes side by side, the same arithmetic as the preprocessing kernel).
+// Each group of D/8 lanes forms RPG consecutive rows of the chunk from the
+// RPG + 3 raw rows that end at them, prefetched like the other operands, and
+// stores them row-major in LDS (16 bytes per lane, whole rows per group: a
+// direct transposed store from this layout would put a group's lanes 8 rows
+// of the transposed array apart, all in one bank).  After a barrier the
+// plain path's pieces are read back from there and staged exactly as the
+// plain path stages loaded keys, so the processed keys never reach HBM.
+//
 // Snapshot layouts (consumed only by the CG kernels):
 //   fp32 path: row-major [D][D] fp32, H[r][c] and G[v][k].
 //   bf16 path: MFMA A-operand fragments.  Fragment f = nt*(D/32) + m holds,
@@ -32,13 +43,14 @@
 //     32m + 4g + {0..3} then 32m + 16 + 4g + {0..3}.  Stored [f][lane][8].
 #include "mesa_common.h"
 #include "mesa_kernels.h"
+#include "mesa_prep_rows.h"
 
 namespace mesa {
 
 namespace {
 
 
-template <bool BF16, int D, int C, bool FULL>
+template <bool BF16, int D, int C, bool FULL, bool PREP = false>
 struct ScanShape {
   static constexpr int ND = D / 16;
   static constexpr int CP = (C < 32) ? 32 : C;       // token dim padded to one bf16 k-block
@@ -63,6 +75,21 @@ struct ScanShape {
   static constexpr int AS = CP + 8;                    // bf16 row stride of transposed LDS arrays
   static constexpr size_t LDS_A = BF16 ? (size_t)MROWS * AS * 2 : (size_t)CP * MROWS * 4;
   static constexpr size_t LDS_B = BF16 ? (size_t)2 * D * AS * 2 : (size_t)CP * D * 4;
+  // PREP: lanes per key row; PG groups of them form the chunk's rows, RPG
+  // consecutive rows each, from NRR raw rows per lane
+  static constexpr int LPR = D / 8;
+  static constexpr int PG = (THREADS / LPR < C) ? THREADS / LPR : C;
+  static constexpr int RPG = C / PG;
+  static constexpr int NRR = PREP ? RPG + kPrepMaxW - 1 : 1;
+  static constexpr int PSS = D + 8;  // bf16 row stride of the processed keys (16-byte rows, 2-way reads)
+  // PREP with a whole state (PF): each X piece (rows 2jp, 2jp+1, channels
+  // 8c8..8c8+7) is convolved by the lane that stages it, from its 5 raw rows
+  // 2jp-3 .. 2jp+1; the row norms come from per-channel-group partial sums in
+  // LDS, SSB floats per row pair (2 rows x D/8 groups + 16 bytes of padding,
+  // so that 8 lanes' 16-byte reads of consecutive pairs hit distinct banks)
+  static constexpr bool PF = PREP && FULL;
+  static constexpr int NKR = PF ? 5 * PPX : NRR;
+  static constexpr int SSB = 2 * (D / 8) + 4;
 };
 
 template <bool BF16>
@@ -74,9 +101,10 @@ struct Piece<false> { f32x4 a; };     // one token row, 4 columns
 
 // TOTALS: the first pass of a segmented walk -- each segment from a zero
 // state, no snapshots, the segment's total state and decay at the end.
-template <bool BF16, int D, int C, bool FULL, bool TOTALS>
+template <bool BF16, int D, int C, bool FULL, bool TOTALS, bool PREP = false>
 __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_kernel(ScanParams p) {
-  using S = ScanShape<BF16, D, C, FULL>;
+  using S = ScanShape<BF16, D, C, FULL, PREP>;
+  static_assert(!PREP || (BF16 && C == 64 && S::PG * S::RPG == C), "fused preprocessing: bf16, chunk 64");
   constexpr int ND = S::ND, CP = S::CP, U = S::U, MROWS = S::MROWS, TPU = S::TPU, UPW = S::UPW;
   constexpr int AS = S::AS;
 
@@ -140,8 +168,26 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   struct Raw {
     Piece<BF16> x[S::PPX];
     Piece<BF16> k[S::PPK];
+    u16x8 kr[S::NKR];   // PREP: raw key rows (whole state: 2jp-3 .. 2jp+1 per piece;
+                        // stripes: j0-3 .. j0+RPG-1 of this lane's group)
     float lg, bt;
   };
+  // PREP: this lane's group of D/8 lanes (groups past PG -- whole waves --
+  // form no rows), its first row and its channels; the head's taps sit in LDS
+  // as [D][kPrepMaxW] (zero past W), read back at staging
+  const int pgrp = tid / S::LPR, pc0 = 8 * (tid % S::LPR), pj0 = pgrp * S::RPG;
+  const bool prow = PREP && (S::PG * S::LPR == S::THREADS || pgrp < S::PG);
+  __shared__ __attribute__((aligned(16))) float ptap_s[PREP ? D * kPrepMaxW : 1];
+  __shared__ __attribute__((aligned(16))) __bf16 prow_s[(PREP && !FULL) ? C * S::PSS : 1];  // processed keys [C][PSS]
+  __shared__ __attribute__((aligned(16))) float ssp_s[S::PF ? 2 * (CP / 2) * S::SSB : 1];  // partials by chunk parity
+  float yk[S::PF ? S::PPX : 1][2][8];  // PF: the next chunk's convolved keys, rows 2jp and 2jp+1 of each piece
+  if constexpr (PREP) {
+    for (int i = tid; i < D * kPrepMaxW; i += S::THREADS) {
+      const int ch = i / kPrepMaxW, tap = i % kPrepMaxW;
+      ptap_s[i] = tap < p.W ? p.wk[((size_t)(bh % p.H) * D + ch) * p.W + tap] : 0.f;
+    }
+    __syncthreads();
+  }
   // Every load is unconditional (indices clamped into the chunk and the piece
   // list) so a fetch never waits on memory: the loads land while the previous
   // chunk is processed.  Rows past the chunk end repeat its last row; their
@@ -153,7 +199,36 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     r.lg = p.gamma[rowbase + s + jl];
     r.bt = p.beta[rowbase + s + jl];
     auto row = [&](int j) { return rowbase + s + min(j, Lc - 1); };
-    if constexpr (BF16) {
+    if constexpr (PREP) {
+      // raw key rows of this lane's group (the previous rows for the window)
+      // and the X pieces as the plain path loads them (for G the values; for
+      // H, whose X is the processed keys formed at staging, raw keys that go
+      // unused -- loaded all the same, so that no branch sits among the loads)
+      const uint16_t* Xg = static_cast<const uint16_t*>(X);
+      const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
+      const uint16_t* Kh = static_cast<const uint16_t*>(p.k_hist);
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = min(tid + q * S::THREADS, S::NPX - 1);
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        r.x[q].a = *reinterpret_cast<const u16x8*>(Xg + row(2 * jp) * D + 8 * c8);
+        r.x[q].b = *reinterpret_cast<const u16x8*>(Xg + row(2 * jp + 1) * D + 8 * c8);
+      }
+      if constexpr (S::PF) {
+#pragma unroll
+        for (int q = 0; q < S::PPX; ++q) {
+          const int pc = min(tid + q * S::THREADS, S::NPX - 1);
+          const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+#pragma unroll
+          for (int m = 0; m < 5; ++m)
+            r.kr[5 * q + m] = prep_load8_w(Kg, Kh, bh, T, D, p.W, min(s + 2 * jp - 3 + m, s + Lc - 1), 8 * c8);
+        }
+      } else if (prow) {
+#pragma unroll
+        for (int m = 0; m < S::NRR; ++m)
+          r.kr[m] = prep_load8_w(Kg, Kh, bh, T, D, p.W, min(s + pj0 - (kPrepMaxW - 1) + m, s + Lc - 1), pc0);
+      }
+    } else if constexpr (BF16) {
       const uint16_t* Xg = static_cast<const uint16_t*>(X);
       const uint16_t* Kg = static_cast<const uint16_t*>(p.k);
 #pragma unroll
@@ -243,8 +318,46 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   };
   if constexpr (FULL)
     if (ce > cb) store_snapshot(cb);
+  // PF: convolve chunk c1's keys from its raw rows (raw), keep them in yk and
+  // publish each row's channel-group partial sums of squares (ssp_s by chunk
+  // parity) for the next step, which scales and stages them after the barrier
+  auto conv_next = [&](const int c1, const Raw& raw) {
+    if constexpr (S::PF) {
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = tid + q * S::THREADS;
+        if (S::NPX % S::THREADS != 0 && pc >= S::NPX) continue;  // whole waves
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        float w[8][kPrepMaxW];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(ptap_s + (8 * c8 + e) * kPrepMaxW);
+#pragma unroll
+          for (int i = 0; i < kPrepMaxW; ++i) w[e][i] = t4[i];
+        }
+        float* ssp = ssp_s + ((c1 & 1) * (CP / 2) + jp) * S::SSB;
+        prep_with_window(p.W, [&](auto wc) {
+          constexpr int WW = decltype(wc)::value;
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr) {
+            const int j = 2 * jp + rr;
+            float x8[kPrepMaxW][8];
+#pragma unroll
+            for (int m = kPrepMaxW - WW; m < kPrepMaxW; ++m)
+              prep_unpack8(prep_zero_row(raw.kr[5 * q + rr + m], p.k_hist, p.W, c1 * C + j - (kPrepMaxW - 1) + m),
+                           x8[m]);
+            ssp[rr * (D / 8) + c8] = prep_conv8_pad<WW>(w, x8, yk[q][rr]);
+          }
+        });
+      }
+    }
+  };
+  if constexpr (S::PF) {
+    if (ce > cb) conv_next(cb, b0);
+    __syncthreads();
+  }
   float seg_log = 0.f;  // sum of log gamma over the segment (wave-uniform)
-  auto step = [&](const int c, const Raw& cur, Raw& pre) {
+  auto step = [&](const int c, const Raw& cur, const Raw& nxt, Raw& pre) {
     fetch(min(c + DEPTH - 1, ce - 1), pre);
 
     // the state before chunk c (stripes: stored here; whole or segment
@@ -271,7 +384,9 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
     // finished chunk c-2's products, which read it, before chunk c-1's barrier
     char* lds_a = lds_a2[c & 1];
     char* lds_b = lds_b2[c & 1];
-    if constexpr (BF16) {
+    // bf16 staging from the X and K pieces: (w .* X)^T split into bf16 hi and
+    // lo parts, and K^T of the owned stripe
+    auto stage_bf16 = [&](const auto* xp, const auto* kp) {
       __bf16* KT = reinterpret_cast<__bf16*>(lds_a);  // [MROWS][AS]: K^T rows of the owned stripe
       __bf16* XH = reinterpret_cast<__bf16*>(lds_b);  // [D][AS]: (w .* X)^T, hi part
       __bf16* XL = XH + D * AS;                       // lo part
@@ -285,7 +400,7 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         const float ww0 = (2 * jp < C) ? w0 : 0.f, ww1 = (2 * jp + 1 < C) ? w1 : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x0 = ww0 * bf16_to_f32(cur.x[q].a[e]), x1 = ww1 * bf16_to_f32(cur.x[q].b[e]);
+          const float x0 = ww0 * bf16_to_f32(xp[q].a[e]), x1 = ww1 * bf16_to_f32(xp[q].b[e]);
           const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
           const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
           const int n = 8 * c8 + e;
@@ -302,9 +417,93 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
         for (int e = 0; e < 8; ++e) {
           const int m = 8 * c8 + e;
           *reinterpret_cast<uint32_t*>(KT + m * AS + 2 * jp) =
-              (uint32_t)cur.k[q].a[e] | ((uint32_t)cur.k[q].b[e] << 16);
+              (uint32_t)kp[q].a[e] | ((uint32_t)kp[q].b[e] << 16);
         }
       }
+    };
+    if constexpr (S::PF) {
+      // chunk c's keys: the row norms from the partial sums (summed in the
+      // order of group_sum over a row's D/8 lanes), scaled and rounded as the
+      // preprocessing kernel does, then staged as loaded keys are; then the
+      // next chunk's convolution, published by this step's barrier
+      Piece<BF16> xk[S::PPX], kk[S::PPX];
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = min(tid + q * S::THREADS, S::NPX - 1);
+        const int jp = pc % (CP / 2);
+        const float* ssp = ssp_s + ((c & 1) * (CP / 2) + jp) * S::SSB;
+        float part[2 * (D / 8)];
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(ssp + 4 * i);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) part[4 * i + u] = t4[u];
+        }
+        const float sc0 = prep_scale(prep_tree_sum<D / 8>(part), p.inv_eps);
+        const float sc1 = prep_scale(prep_tree_sum<D / 8>(part + D / 8), p.inv_eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kk[q].a[e] = __builtin_bit_cast(uint16_t, (__bf16)(yk[q][0][e] * sc0));
+          kk[q].b[e] = __builtin_bit_cast(uint16_t, (__bf16)(yk[q][1][e] * sc1));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xk[q].a[e] = which ? cur.x[q].a[e] : kk[q].a[e];
+          xk[q].b[e] = which ? cur.x[q].b[e] : kk[q].b[e];
+        }
+      }
+      stage_bf16(xk, kk);
+      conv_next(c + 1, nxt);
+    } else if constexpr (PREP) {
+      // the processed keys of the chunk, row-major in prow_s (each lane
+      // group's 16-byte stores fill whole rows), then the same pieces the
+      // plain path loads, read back from there
+      if (prow) {
+        float w[8][kPrepMaxW];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(ptap_s + (pc0 + e) * kPrepMaxW);
+#pragma unroll
+          for (int i = 0; i < kPrepMaxW; ++i) w[e][i] = t4[i];
+        }
+        prep_with_window(p.W, [&](auto wc) {
+          constexpr int WW = decltype(wc)::value;
+#pragma unroll
+          for (int r = 0; r < S::RPG; ++r) {
+            float x8[kPrepMaxW][8], y[8];
+#pragma unroll
+            for (int m = kPrepMaxW - WW; m < kPrepMaxW; ++m)
+              prep_unpack8(prep_zero_row(cur.kr[r + m], p.k_hist, p.W, c * C + pj0 - (kPrepMaxW - 1) + r + m),
+                           x8[m]);
+            const float sc = prep_scale(group_sum<S::LPR>(prep_conv8_pad<WW>(w, x8, y)), p.inv_eps);
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (__bf16)(y[e] * sc);
+            *reinterpret_cast<bf16x8*>(prow_s + (pj0 + r) * S::PSS + pc0) = o;
+          }
+        });
+      }
+      __syncthreads();
+      Piece<BF16> xk[S::PPX], kk[S::PPK];
+#pragma unroll
+      for (int q = 0; q < S::PPX; ++q) {
+        const int pc = min(tid + q * S::THREADS, S::NPX - 1);
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        xk[q].a = *reinterpret_cast<const u16x8*>(prow_s + (2 * jp) * S::PSS + 8 * c8);
+        xk[q].b = *reinterpret_cast<const u16x8*>(prow_s + (2 * jp + 1) * S::PSS + 8 * c8);
+      }
+#pragma unroll
+      for (int q = 0; q < S::PPK; ++q) {
+        const int pc = min(tid + q * S::THREADS, S::NPK - 1);
+        const int jp = pc % (CP / 2), c8 = pc / (CP / 2);
+        const int col = (FULL ? 0 : 16 * mpart) + 8 * c8;
+        kk[q].a = *reinterpret_cast<const u16x8*>(prow_s + (2 * jp) * S::PSS + col);
+        kk[q].b = *reinterpret_cast<const u16x8*>(prow_s + (2 * jp + 1) * S::PSS + col);
+      }
+      if (which == 0) stage_bf16(xk, kk);
+      else stage_bf16(cur.x, kk);
+    } else if constexpr (BF16) {
+      stage_bf16(cur.x, cur.k);
     } else {
       float* Ks = reinterpret_cast<float*>(lds_a);    // [CP][MROWS]
       float* Xs = reinterpret_cast<float*>(lds_b);    // [CP][D] = w_j * X[j][n]
@@ -369,14 +568,14 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   };
   if constexpr (DEPTH == 3) {
     for (int c = cb; c < ce; c += 3) {
-      step(c, b0, b2);
-      if (c + 1 < ce) step(c + 1, b1, b0);
-      if (c + 2 < ce) step(c + 2, b2, b1);
+      step(c, b0, b1, b2);
+      if (c + 1 < ce) step(c + 1, b1, b2, b0);
+      if (c + 2 < ce) step(c + 2, b2, b0, b1);
     }
   } else {
     for (int c = cb; c < ce; c += 2) {
-      step(c, b0, b1);
-      if (c + 1 < ce) step(c + 1, b1, b0);
+      step(c, b0, b1, b1);
+      if (c + 1 < ce) step(c + 1, b1, b0, b0);
     }
   }
 
@@ -437,6 +636,15 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t s) {
   const int groups = (p.BH + 7) / 8;
   const int nsp = TOTALS ? p.NS - 1 : p.NS;
   const dim3 grid(groups * 8 * U * nsp);
+  if constexpr (BF16 && C == 64 && (D == 64 || D == 128)) {
+    if (p.prep) {
+      hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL, TOTALS, true>), grid,
+                         dim3(ScanShape<BF16, D, C, FULL>::THREADS), 0, s, p);
+      return hipGetLastError();
+    }
+  } else {
+    if (p.prep) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((scan_kernel<BF16, D, C, FULL, TOTALS>), grid, dim3(ScanShape<BF16, D, C, FULL>::THREADS), 0, s, p);
   return hipGetLastError();
 }

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "MesaError", "lib", "library_path", "FwdDesc", "MESA_F32", "MESA_BF16",
-    "workspace_bytes", "fwd_chunked", "fwd_chunked_noalloc", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
+    "workspace_bytes", "fwd_chunked", "fwd_chunked_noalloc", "fwd_chunked_prep", "fwd_scan", "fwd_solve", "decode_step", "abi_version",
     "status_string", "sym_state_floats", "sym_pack", "sym_unpack", "decode_step_symh",
 ]
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.mesa_fwd_chunked_warm.argtypes = list(L.mesa_fwd_chunked.argtypes)
         L.mesa_fwd_chunked_noalloc.restype = ctypes.c_int
         L.mesa_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 13 + [P]
+        L.mesa_fwd_chunked_prep.restype = ctypes.c_int
+        L.mesa_fwd_chunked_prep.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, I32, F] + [P] * 15 + [S, P]
         L.mesa_fwd_chunked_ex.restype = ctypes.c_int
         L.mesa_fwd_chunked_ex.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, I32, P, P, P, P, P, P,
                                           P, P, S, P]
@@ -186,6 +188,31 @@ def fwd_chunked_noalloc(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps
                 out=out, workspace=None, stream=stream)
 
 
+def fwd_chunked_prep(q_raw, k_raw, v, gamma, beta, lam, w_q, w_k, *, q_hist=None, k_hist=None,
+                     eps: float = 1e-6, chunk: int = 64, max_steps: int = 30, tol: float = 0.0,
+                     h0=None, g0=None, return_state: bool = False, return_steps: bool = True,
+                     return_x: bool = False, return_history: bool = False, out=None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """``fwd_chunked`` on raw bf16 q, k [B, H, T, d] with ``qk_preprocess`` fused
+    into the forward (``mesa_fwd_chunked_prep``): taps w_q, w_k [H, d, W], raw
+    histories q_hist, k_hist [B, H, W-1, d] (None: zeros).  The result equals
+    ``qk_preprocess`` followed by ``fwd_chunked`` bit for bit; with
+    return_history it also holds the next call's histories ``q_hist``,
+    ``k_hist``.  bf16 inputs, chunk 64, d in {64, 128}, W in 1..4."""
+    B, H, T, d = q_raw.shape
+    W = w_q.shape[-1]
+    _need(w_q, "w_q", (H, d, W), torch.float32)
+    _need(w_k, "w_k", (H, d, W), torch.float32)
+    for name, t in (("q_hist", q_hist), ("k_hist", k_hist)):
+        if t is not None:
+            _need(t, name, (B, H, W - 1, d), q_raw.dtype)
+    prep = {"w_q": w_q, "w_k": w_k, "W": W, "eps": eps, "q_hist": q_hist, "k_hist": k_hist,
+            "return_history": return_history}
+    return _fwd("prep", q_raw, k_raw, v, gamma, beta, lam, chunk=chunk, max_steps=max_steps, tol=tol, h0=h0,
+                g0=g0, return_state=return_state, return_steps=return_steps, return_x=return_x,
+                out=out, workspace=workspace, stream=stream, prep=prep)
+
+
 def fwd_chunked_ex(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int = 30,
                    tol: float = 0.0, h0=None, g0=None, return_state: bool = False,
                    return_steps: bool = True, return_x: bool = False, out=None,
@@ -199,7 +226,7 @@ def fwd_chunked_ex(q, k, v, gamma, beta, lam, *, chunk: int = 64, max_steps: int
 
 
 def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, return_state,
-         return_steps, return_x, out, workspace, stream) -> dict:
+         return_steps, return_x, out, workspace, stream, prep=None) -> dict:
     B, H, T, d = q.shape
     code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -226,6 +253,9 @@ def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, 
     if return_state:
         res["h_final"] = out.get("h_final") if out.get("h_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
         res["g_final"] = out.get("g_final") if out.get("g_final") is not None else torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    if prep is not None and prep["return_history"]:
+        for key in ("q_hist", "k_hist"):
+            res[key] = out.get(key) if out.get(key) is not None else torch.empty((B, H, prep["W"] - 1, d), device=dev, dtype=q.dtype)
     if noalloc:
         code_ = L.mesa_fwd_chunked_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
                                            _ptr(lam), _ptr(h0), _ptr(g0), _ptr(res["o"]), _ptr(res.get("h_final")),
@@ -240,7 +270,13 @@ def _fwd(ex: bool, q, k, v, gamma, beta, lam, *, chunk, max_steps, tol, h0, g0, 
             _ptr(res.get("steps")), _ptr(res.get("x")), _ptr(workspace), ctypes.c_size_t(wbytes),
             _stream(stream))
     head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(lam))
-    if ex == "warm":
+    if ex == "prep":
+        code_ = L.mesa_fwd_chunked_prep(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(prep["w_q"]),
+                                        _ptr(prep["w_k"]), int(prep["W"]), float(prep["eps"]), _ptr(prep["q_hist"]),
+                                        _ptr(prep["k_hist"]), _ptr(gamma), _ptr(beta), _ptr(lam), *rest[:7],
+                                        _ptr(res.get("q_hist")), _ptr(res.get("k_hist")), *rest[7:])
+        _check(code_, "mesa_fwd_chunked_prep")
+    elif ex == "warm":
         code_ = L.mesa_fwd_chunked_warm(*head, *rest)
         _check(code_, "mesa_fwd_chunked_warm")
     elif ex:

@@ -102,6 +102,42 @@ def test_warm_forward_takes_bf16_inputs_only():
                                             ctypes.c_size_t(1 << 40), None) == 1
 
 
+def call_fwd_prep(d, window=4, eps=1e-6, q=FAKE, wq=FAKE, wk=FAKE, qh=None, kh=None, qho=None, kho=None,
+                  o=FAKE, wbytes=1 << 40):
+    P = ctypes.c_void_p
+    return mesa.lib().mesa_fwd_chunked_prep(ctypes.byref(d), P(q), P(FAKE), P(FAKE), P(wq), P(wk), window,
+                                            ctypes.c_float(eps), P(qh), P(kh), P(FAKE), P(FAKE), P(FAKE), None,
+                                            None, P(o), None, None, None, None, P(qho), P(kho), P(FAKE),
+                                            ctypes.c_size_t(wbytes), None)
+
+
+def test_fused_preprocessing_forward_scope_and_validation():
+    """mesa_fwd_chunked_prep takes bf16 inputs, chunk 64, d in {64, 128} and
+    windows 1..4; every rejection happens before any launch."""
+    assert call_fwd_prep(desc(in_dtype=mesa.MESA_F32)) == 2
+    assert call_fwd_prep(desc(chunk=32)) == 2
+    assert call_fwd_prep(desc(dk=32, dv=32)) == 2
+    assert call_fwd_prep(desc(), window=5) == 2
+    assert call_fwd_prep(desc(), window=0) == 1
+    for eps in (0.0, -1.0, 2.0 ** -64, float("inf"), float("nan")):
+        assert call_fwd_prep(desc(), eps=eps) == 1
+    assert call_fwd_prep(desc(), wq=0) == 1
+    assert call_fwd_prep(desc(), wk=0) == 1
+    assert call_fwd_prep(desc(), wq=FAKE + 4) == 3
+    assert call_fwd_prep(desc(), qh=FAKE + 8) == 3
+    # the next call's histories may not overlap the raw inputs or each other
+    assert call_fwd_prep(desc(), qho=FAKE + 1024) == 1
+    far = FAKE + (1 << 32)
+    assert call_fwd_prep(desc(), qho=far, kho=far + 256) == 1
+    assert call_fwd_prep(desc(), qh=far, qho=far) == 1
+    # the forward's own rules still apply
+    assert call_fwd_prep(desc(B=0)) == 1
+    assert call_fwd_prep(desc(dk=48, dv=48)) == 2
+    assert call_fwd_prep(desc(), q=0) == 1
+    assert call_fwd_prep(desc(), o=FAKE + 4) == 3
+    assert call_fwd_prep(desc(), wbytes=16) == 4
+
+
 def test_noalloc_forward_validates_before_any_hip_call():
     """The allocation-free forward rejects, before any HIP call (this runs without
     a GPU): a workload whose workspace exceeds the static scratch, then the
@@ -253,6 +289,8 @@ def test_preprocess_validation():
     assert call(W=0) == 1
     assert call(T=-1) == 1
     assert call(eps=0.0) == 1
+    assert call(eps=2.0 ** -64) == 1   # below 2^-63: the norm of a denormal squared norm
+    assert call(eps=float("inf")) == 1
     assert call(dtype=3) == 1
     assert call(q=0) == 1
     assert call(wq=0) == 1
