@@ -765,6 +765,8 @@ def main():
                     help="time the chosen forward workload only (profiling runs)")
     ap.add_argument("--prep-forward", action="store_true",
                     help="also time the forward on raw q/k: preprocessing kernel + forward against the fused call")
+    ap.add_argument("--backward", action="store_true",
+                    help="with --forward-only: also time the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices-per-core", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
@@ -855,6 +857,9 @@ def main():
     if args.prep_forward:
         line["forward_with_preprocessing"] = bench_prep_forward(cfg, args.steps, args.warmup)
         log(f"forward with preprocessing: {line['forward_with_preprocessing']}")
+    if args.backward and args.forward_only:
+        line["backward"] = bench_backward(cfg, args.steps, args.warmup)
+        log(f"backward: {line['backward']['ms_per_call']} ms per call")
     if args.forward_only:
         line["forward_detail"] = forward_report(cfg, fw)
         if cpu is not None:

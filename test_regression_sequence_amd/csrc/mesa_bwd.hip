@@ -287,15 +287,6 @@ __device__ __forceinline__ Square<D> load_square(const uint16_t* src) {
     r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)(threadIdx.x + it * kThreads) * 8);
   return r;
 }
-// a row-major square into LDS [D][ld]
-template <int D>
-__device__ __forceinline__ void put_square(uint16_t* dst, int ld, const Square<D>& r) {
-#pragma unroll
-  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
-    const int idx = threadIdx.x + it * kThreads;
-    *reinterpret_cast<u16x8*>(dst + (idx / (D / 8)) * ld + 8 * (idx % (D / 8))) = r.v[it];
-  }
-}
 // a boundary snapshot in fragment order into LDS row-major [D][ld]
 template <int D>
 __device__ __forceinline__ void put_frag(uint16_t* dst, int ld, const Square<D>& r) {
@@ -310,67 +301,58 @@ __device__ __forceinline__ void put_frag(uint16_t* dst, int ld, const Square<D>&
     *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{r.v[it][4], r.v[it][5], r.v[it][6], r.v[it][7]};
   }
 }
-// The same pieces in another order, for a square that is also written transposed: per wave
-// and step, 32 consecutive rows by two adjacent 8-column pieces, so a half-wave's 2-byte
-// transposed writes land in 16 distinct dwords of one row run (no bank conflicts).
-template <int D>
-struct TMap {
-  static_assert(D % 32 == 0, "32-row blocks");
-  static constexpr int RB = D / 32;
-  __device__ static int blk(int it) { return (threadIdx.x >> 6) + (kThreads / 64) * it; }
-  __device__ static int row(int it) { return 32 * (blk(it) % RB) + (threadIdx.x & 31); }
-  __device__ static int c8(int it) { return 2 * (blk(it) / RB) + ((threadIdx.x >> 5) & 1); }
-};
-template <int D>
-__device__ __forceinline__ Square<D> load_square_t(const uint16_t* src) {
-  using M = TMap<D>;
-  Square<D> r;
-#pragma unroll
-  for (int it = 0; it < D * D / 8 / kThreads; ++it)
-    r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)M::row(it) * D + 8 * M::c8(it));
-  return r;
+// The adjoint snapshots Rs and S are stored in tile order: the 16x16 tile
+// (mt, nt) of a square is 512 contiguous bytes, lane l of it 8 bytes holding
+// row 16mt + 4(l/16) + l%4, columns 16nt + 4((l%16)/4) + {0..3} -- an MFMA
+// result tile after quad_transpose -- so the adjoint scan stores whole tiles
+// with one contiguous wave store each.  A 16-byte piece idx (as load_square
+// reads it) is lanes 2(idx%32) and 2(idx%32)+1 of tile idx/32: rows r and r+1
+// of one 4-column group.
+__device__ __forceinline__ size_t adj_tile_offset(int D, int mt, int nt, int lane) {
+  return ((size_t)(mt * (D / 16) + nt) * 64 + lane) * 4;
 }
 template <int D>
-__device__ __forceinline__ void put_square_t(uint16_t* dst, int ld, const Square<D>& r) {
-  using M = TMap<D>;
-#pragma unroll
-  for (int it = 0; it < D * D / 8 / kThreads; ++it)
-    *reinterpret_cast<u16x8*>(dst + M::row(it) * ld + 8 * M::c8(it)) = r.v[it];
+__device__ __forceinline__ void adj_piece(int idx, int& row, int& col) {
+  const int u = idx >> 5, l0 = 2 * (idx & 31);
+  const int tl = l0 & 15, g = l0 >> 4;
+  row = 16 * (u / (D / 16)) + 4 * g + (tl & 3);
+  col = 16 * (u % (D / 16)) + 4 * (tl >> 2);
 }
-// the transpose: dst[c][r] = square[r][c]
-template <int D>
-__device__ __forceinline__ void put_transposed_t(uint16_t* dst, int ld, const Square<D>& r) {
-  using M = TMap<D>;
+// a tile-order square into LDS [D][ld], row-major (TRANS: transposed)
+template <int D, bool TRANS>
+__device__ __forceinline__ void put_adj(uint16_t* dst, int ld, const Square<D>& r) {
 #pragma unroll
   for (int it = 0; it < D * D / 8 / kThreads; ++it) {
-    const int row = M::row(it), c0 = 8 * M::c8(it);
+    int row, col;
+    adj_piece<D>(threadIdx.x + it * kThreads, row, col);
+    if constexpr (TRANS) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dst[(c0 + u) * ld + row] = r.v[it][u];
+      for (int u = 0; u < 4; ++u) {
+        dst[(col + u) * ld + row] = r.v[it][u];
+        dst[(col + u) * ld + row + 1] = r.v[it][4 + u];
+      }
+    } else {
+      *reinterpret_cast<u16x4*>(dst + row * ld + col) = u16x4{r.v[it][0], r.v[it][1], r.v[it][2], r.v[it][3]};
+      *reinterpret_cast<u16x4*>(dst + (row + 1) * ld + col) = u16x4{r.v[it][4], r.v[it][5], r.v[it][6], r.v[it][7]};
+    }
   }
 }
+// <A, B> for a tile-order square held in registers and a row-major one in LDS [D][ld];
+// this thread's part
 template <int D>
-__device__ __forceinline__ float dot_square_t(const Square<D>& a, const uint16_t* b, int ld) {
-  using M = TMap<D>;
+__device__ __forceinline__ float dot_adj(const Square<D>& a, const uint16_t* b, int ld) {
   float acc = 0.f;
 #pragma unroll
   for (int it = 0; it < D * D / 8 / kThreads; ++it) {
-    const u16x8 w = *reinterpret_cast<const u16x8*>(b + M::row(it) * ld + 8 * M::c8(it));
+    int row, col;
+    adj_piece<D>(threadIdx.x + it * kThreads, row, col);
+    const u16x4 w0 = *reinterpret_cast<const u16x4*>(b + row * ld + col);
+    const u16x4 w1 = *reinterpret_cast<const u16x4*>(b + (row + 1) * ld + col);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(a.v[it][u]), bf16_to_f32(w[u]), acc);
-  }
-  return acc;
-}
-
-// <A, B> for a row-major square held in registers and one in LDS [D][ld]; this thread's part
-template <int D>
-__device__ __forceinline__ float dot_square(const Square<D>& a, const uint16_t* b, int ld) {
-  float acc = 0.f;
-#pragma unroll
-  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
-    const int idx = threadIdx.x + it * kThreads;
-    const u16x8 w = *reinterpret_cast<const u16x8*>(b + (idx / (D / 8)) * ld + 8 * (idx % (D / 8)));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(bf16_to_f32(a.v[it][u]), bf16_to_f32(w[u]), acc);
+    for (int u = 0; u < 4; ++u) {
+      acc = __builtin_fmaf(bf16_to_f32(a.v[it][u]), bf16_to_f32(w0[u]), acc);
+      acc = __builtin_fmaf(bf16_to_f32(a.v[it][4 + u]), bf16_to_f32(w1[u]), acc);
+    }
   }
   return acc;
 }
@@ -552,15 +534,13 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
       // the adjoints arriving at this chunk's end, one 8-byte store per tile and lane
       uint16_t* snR = p.snap_r + (size_t)chunk * D2;
       uint16_t* snS = p.snap_s + (size_t)chunk * D2;
-      const int qb = tl & 3;  // position in the lane quad
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const int row = r0 + 16 * rt + 4 * g + qb, col = CW * wave + 16 * ct + (tl & ~3);
-          const f32x4 zr = quad_transpose(R[rt][ct]), zs = quad_transpose(S[rt][ct]);
-          *reinterpret_cast<u16x4*>(snR + (size_t)row * D + col) = bf4(zr);
-          *reinterpret_cast<u16x4*>(snS + (size_t)row * D + col) = bf4(zs);
+          const size_t o = adj_tile_offset(D, r0 / 16 + rt, (CW * wave) / 16 + ct, lane);
+          *reinterpret_cast<u16x4*>(snR + o) = bf4(quad_transpose(R[rt][ct]));
+          *reinterpret_cast<u16x4*>(snS + o) = bf4(quad_transpose(S[rt][ct]));
         }
     }
     // the gates, in every wave (lane = token): no barrier between them and the staging
@@ -659,6 +639,189 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// adjoint scan with whole states, for 2 BH >= 256 (one walk per sequence): two
+// workgroups of 8 waves per sequence, one for Rs and one for S, each holding its
+// whole d x d state and staging the chunk's operands once (the stripe walk above
+// stages every chunk's x and y once per 32-row stripe).  Same products, in the
+// same order, as the stripe walk: the snapshots and dh0, dg0 are bitwise those of
+// the stripe walk.
+// ---------------------------------------------------------------------------------------
+constexpr int kFullThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p) {
+  constexpr int NW = kFullThreads / 64, ND = D / 16, UPW = ND * ND / NW;
+  constexpr int L2 = 2 * kC + 8;                      // two token blocks + 16 bytes of padding
+  constexpr int NIT = (kC / 2) * (D / 4) / kFullThreads;  // (token pair, dim quad) items per thread
+  static_assert(UPW * NW == ND * ND && NIT * kFullThreads == (kC / 2) * (D / 4), "whole tiles and items");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
+  // XCD-aware decode: the two workgroups of a sequence share blockIdx % 8, so the
+  // chunk's x they both read comes through one L2
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int which = local & 1;                        // 0: Rs, 1: S
+  const int bh = (local >> 1) * 8 + xcd;
+  if (bh >= p.BH) return;
+  const size_t D2 = (size_t)D * D;
+
+  // Rs: sA = [(-wY)^T | (-wX)^T], sB = [X^T | Y^T]; S: sA = (w d_O)^T, sB = X^T;
+  // double-buffered by chunk parity, so one barrier per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[2][D * L2];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[2][D * L2];
+
+  // start state: the final-state adjoints (zero without them); lane (tl, g) of
+  // tile u = (mt, nt) holds rows 16mt + 4g + i of column 16nt + tl
+  f32x4 R[UPW];
+#pragma unroll
+  for (int ui = 0; ui < UPW; ++ui) {
+    const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
+      float v = 0.f;
+      if (which == 0 && p.d_hfinal) {
+        const float* Dh = p.d_hfinal + (size_t)bh * D2;
+        v = Dh[row * D + col] + Dh[col * D + row];
+      } else if (which == 1 && p.d_gfinal) {
+        v = p.d_gfinal[(size_t)bh * D2 + row * D + col];
+      }
+      R[ui][i] = v;
+    }
+  }
+
+  // one chunk's inputs in registers: x and the second factor (Rs: y / ||dx||,
+  // S: d_o) of this thread's items (tokens 2jp, 2jp+1 x dims 4dq..4dq+3), and
+  // one token's gates per lane
+  struct Raw {
+    f32x4 x[NIT][2], o[NIT][2];
+    float gam, nu;
+  };
+  const float* Og = which ? p.d_o : p.yn;
+  auto fetch = [&](int c, Raw& r) {
+    const int Lc = min(kC, p.T - c * kC);
+    const size_t row0 = (size_t)bh * p.T + c * kC;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int pc = tid + kFullThreads * it, jp = pc % (kC / 2), dq = pc / (kC / 2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const size_t rr = row0 + min(2 * jp + h, Lc - 1);
+        r.x[it][h] = *reinterpret_cast<const f32x4*>(p.x + rr * D + 4 * dq);
+        r.o[it][h] = *reinterpret_cast<const f32x4*>(Og + rr * D + 4 * dq);
+      }
+    }
+    const size_t rl = row0 + min(lane, Lc - 1);
+    r.gam = p.gamma[rl];
+    r.nu = p.nu[rl];
+  };
+  f32x4 lam[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) lam[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the adjoints arriving at chunk c's end, one 8-byte store per tile and lane
+  auto store_snapshot = [&](const int c) {
+    uint16_t* sn = (which ? p.snap_s : p.snap_r) + ((size_t)bh * p.NC + c) * D2;
+#pragma unroll
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
+      *reinterpret_cast<u16x4*>(sn + adj_tile_offset(D, mt, nt, lane)) = bf4(quad_transpose(R[ui]));
+    }
+  };
+  // chunk c from ring buffer cur, with chunk c-2 fetched into pre (two steps ahead)
+  auto step = [&](const int c, const Raw& cur, Raw& pre) {
+    const int Lc = min(kC, p.T - c * kC);
+    uint16_t* sA = sA2[c & 1];
+    uint16_t* sB = sB2[c & 1];
+    fetch(max(c - 2, 0), pre);  // unconditional (clamped): no branch among the loads
+    // the gates (lane = token): w_t = e^{b_t}, b restarted at the chunk start
+    float lg = lane < Lc ? logf(cur.gam) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(lg, o, 64);
+      if (lane >= o) lg += t;
+    }
+    const float wt_l = expf(lg);
+    const float nu_l = lane < Lc ? cur.nu : 0.f;
+    const float blast = __shfl(lg, 63, 64);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int pc = tid + kFullThreads * it, jp = pc % (kC / 2), dq = pc / (kC / 2);
+      const int t0 = 2 * jp, t1 = t0 + 1;
+      const float ws0 = __shfl(wt_l, t0, 64), ws1 = __shfl(wt_l, t1, 64);
+      const float ns0 = __shfl(nu_l, t0, 64), ns1 = __shfl(nu_l, t1, 64);
+      const bool in0 = t0 < Lc, in1 = t1 < Lc;
+      const float w0 = in0 ? ws0 : 0.f, w1 = in1 ? ws1 : 0.f;
+      const float ex0 = in0 ? 1.f : 0.f, ex1 = in1 ? 1.f : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * dq + u;
+        const float xe0 = cur.x[it][0][u] * ex0, xe1 = cur.x[it][1][u] * ex1;
+        *reinterpret_cast<uint32_t*>(sB + i * L2 + t0) = (uint32_t)bf(xe0) | ((uint32_t)bf(xe1) << 16);
+        if (which == 0) {
+          const float ye0 = cur.o[it][0][u] * (in0 ? ns0 : 0.f), ye1 = cur.o[it][1][u] * (in1 ? ns1 : 0.f);
+          *reinterpret_cast<uint32_t*>(sB + i * L2 + kC + t0) = (uint32_t)bf(ye0) | ((uint32_t)bf(ye1) << 16);
+          *reinterpret_cast<uint32_t*>(sA + i * L2 + t0) =
+              (uint32_t)bf(-w0 * ye0) | ((uint32_t)bf(-w1 * ye1) << 16);
+          *reinterpret_cast<uint32_t*>(sA + i * L2 + kC + t0) =
+              (uint32_t)bf(-w0 * xe0) | ((uint32_t)bf(-w1 * xe1) << 16);
+          lam[it][u] = __builtin_fmaf(-ye0, xe0, lam[it][u]);
+          lam[it][u] = __builtin_fmaf(-ye1, xe1, lam[it][u]);
+        } else {
+          *reinterpret_cast<uint32_t*>(sA + i * L2 + t0) =
+              (uint32_t)bf(w0 * cur.o[it][0][u]) | ((uint32_t)bf(w1 * cur.o[it][1][u]) << 16);
+        }
+      }
+    }
+    // every wave finished chunk c+2's products, which read this parity's
+    // buffers, before chunk c+1's barrier
+    __syncthreads();
+    const float decay = expf(blast);
+#pragma unroll
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
+      if (which == 0) R[ui] = mma<2 * kC>(sA + 16 * mt * L2, L2, sB + 16 * nt * L2, L2, R[ui] * decay);
+      else R[ui] = mma<kC>(sA + 16 * mt * L2, L2, sB + 16 * nt * L2, L2, R[ui] * decay);
+    }
+    // the adjoints arriving at chunk c-1's end go out now, so their stores drain
+    // while the next chunk is gated and staged
+    if (c > 0) store_snapshot(c - 1);
+  };
+  Raw b0, b1, b2;
+  if (p.NC > 0) {
+    store_snapshot(p.NC - 1);
+    fetch(p.NC - 1, b0);
+    fetch(max(p.NC - 2, 0), b1);
+  }
+  for (int c = p.NC - 1; c >= 0; c -= 3) {
+    step(c, b0, b2);
+    if (c - 1 >= 0) step(c - 1, b1, b0);
+    if (c - 2 >= 0) step(c - 2, b2, b1);
+  }
+
+  // this sequence's part of dlambda: the 32 threads of a dim quad are one half-wave
+  if (which == 0) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      f32x4 sum;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sum[u] = group_sum<32>(lam[it][u]);
+      const int dq = (tid + kFullThreads * it) / (kC / 2);
+      if ((tid & 31) == 0) *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * dq) = sum;
+    }
+  }
+  // gradients of the initial states
+#pragma unroll
+  for (int ui = 0; ui < UPW; ++ui) {
+    const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
+      if (which == 0 && p.dh0) p.dh0[(size_t)bh * D2 + row * D + col] = 0.5f * R[ui][i];
+      if (which == 1 && p.dg0) p.dg0[(size_t)bh * D2 + row * D + col] = R[ui][i];
+    }
+  }
+}
+
 // Carry pass of a segmented adjoint scan, backwards over the segments: C_{NS-1} is the
 // final-state adjoint and C_{s-1} = Gamma_s C_s + total_s, left in the slot where
 // total_s was (the carry-in state of segment s-1).
@@ -745,7 +908,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
   // ---- dgamma: suffix terms e^{b_t}(<dH_t, Hb> + <dG_t, Gb>) and the per-chunk ones ------
   const Square<D> gbs = load_square<D>(static_cast<const uint16_t*>(p.gb) + sn);  // next phase
   const Square<D> rss = load_square<D>(p.snap_r + sn);                             // Rs: <Rs, Hb>, then staged
-  const Square<D> sqs = load_square_t<D>(p.snap_s + sn);                           // S: <S, Gb>, then staged
+  const Square<D> sqs = load_square<D>(p.snap_s + sn);                             // S: <S, Gb>, then staged
   float cpart[4];
   {
     f32x4 hx[NTL];
@@ -759,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       for (int nt = 0; nt < NTL; ++nt) a = __builtin_fmaf(bf16_to_f32(sY[t * LD + 16 * nt + tl]), hx[nt][i], a);
       cpart[i] = -nus[t] * a;  // <dH_t, Hb> = -y_t^T Hb x_t
     }
-    const float rh = wave_sum(dot_square<D>(rss, r2, LD));
+    const float rh = wave_sum(dot_adj<D>(rss, r2, LD));
     if (lane == 0) red[0][wave] = rh;
   }
   __syncthreads();  // Hb consumed
@@ -778,7 +941,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
       const float tot = group_sum<16>(cpart[i] + a);  // + <dG_t, Gb> = d_o_t^T Gb x_t
       if (tl == 0) tsuf[t] = t < Lc ? expf(bcum[t]) * tot : 0.f;
     }
-    const float sg = wave_sum(dot_square_t<D>(sqs, r2, LD));
+    const float sg = wave_sum(dot_adj<D>(sqs, r2, LD));
     if (lane == 0) red[1][wave] = sg;
   }
   // ---- reverse-causal scores (t' >= t), masked and decayed ----------------------------
@@ -830,7 +993,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
   }
   __syncthreads();  // X, Y, d_O token-major and Gb consumed
   // ---- stored adjoints of the chunk's end, applied to k_t and v_t ---------------------
-  put_square<D>(r2, LD, rss);
+  put_adj<D, false>(r2, LD, rss);
 #pragma unroll
   for (int it = 0; it < CM::N; ++it) {
     const int t = CM::tok(it), i0 = 4 * CM::quad();
@@ -846,12 +1009,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) hk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  put_square_t<D>(r2, LD, sqs);
+  put_adj<D, false>(r2, LD, sqs);
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gk[nt] = mma<D>(sK + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
   __syncthreads();
-  put_transposed_t<D>(r2, LD, sqs);  // S^T, from the S held in registers
+  put_adj<D, true>(r2, LD, sqs);  // S^T, from the S held in registers
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt) gtv[nt] = mma<D>(sV + trow * LD, LD, r2 + 16 * nt * LD, LD, z);
@@ -1019,6 +1182,12 @@ hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
     case 0: hipLaunchKernelGGL((bwd_dx_kernel<D>), chunks, dim3(kThreads), 0, s, p); break;
     case 1: {
       // (sequence, stripe) units padded to whole groups of 8 sequences (one per XCD)
+      if (bwd_scan_whole_state(p.BH, p.NS)) {
+        // two workgroups per sequence, padded to whole groups of 8 sequences (one per XCD)
+        const unsigned wgs = (unsigned)((p.BH + 7) / 8 * 8 * 2);
+        hipLaunchKernelGGL((bwd_scan_full_kernel<D>), dim3(wgs), dim3(kFullThreads), 0, s, p);
+        break;
+      }
       const unsigned units = (unsigned)((p.BH + 7) / 8 * 8 * (D / 32));
       if (p.NS > 1) {
         hipLaunchKernelGGL((bwd_scan_kernel<D, true>), dim3(units * (unsigned)(p.NS - 1)), dim3(kThreads), 0, s, p);

@@ -174,6 +174,10 @@ inline int bwd_scan_segments(long long BH, int NC, int D) {
   return (NC + seg - 1) / seg;
 }
 
+// The adjoint scan walks whole states (two workgroups per sequence, one per CU)
+// once there are enough sequences to fill the chip, else 32-row stripes.
+inline bool bwd_scan_whole_state(long long BH, int NS) { return 2 * BH >= 256 && NS == 1; }
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_scan(bool bf16, int D, int C, const ScanParams& p, hipStream_t s);
 hipError_t launch_cg(bool bf16, int D, int C, const CgParams& p, hipStream_t s);

@@ -126,6 +126,22 @@ def test_empty_sequence_passes_final_state_gradients_through():
     assert np.array_equal(b["dlam"].cpu().numpy(), np.zeros((2, 64), np.float32))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_whole_state_adjoint_scan(d):
+    """128 sequences (B=16, H=8): the adjoint scan walks whole states, two
+    workgroups per sequence; two chunks, the second ragged, with initial states and
+    final-state gradients.  Every gradient against the oracle, dlambda summed over
+    all 16 batch entries."""
+    cfg = small_fwd(B=16, H=8, T=70, d=d, chunk=64, dtype="bf16", max_steps=8, tol=0.0)
+    x = make_fwd_inputs(cfg)
+    g = make_bwd_inputs(cfg)
+    gpu = run_gpu(cfg, x, g)
+    ref = run_oracle(cfg, x, g, gpu)
+    errs = {n: rel_l2(gpu[n], ref[n]) for n in NAMES}
+    print(f"whole-state adjoint scan d={d}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    assert all(e <= 2e-2 for e in errs.values()), errs
+
+
 def test_lm_workload_sampled_slice():
     """B=8, H=16, T=4096, d=128, 30 CG steps: the whole backward on the GPU, one
     (b, h) slice's gradients against the oracle (dlambda sums over the batch and
