@@ -121,50 +121,6 @@ __device__ __forceinline__ void chunk_gates(const float* gamma, const float* bet
   betas[lane] = bt;
 }
 
-// The staging helpers below load everything a thread moves into registers
-// before the first LDS write (compile-time trip counts), so a tile costs one
-// memory round trip.  Rows past Lc load row Lc-1 (every load is unconditional)
-// and are written as zeros.
-
-// token-major [C][D] fp32 tile -> LDS bf16 [C][ld], rows scaled by row_scale
-template <int D>
-__device__ __forceinline__ void stage_rows_f32(uint16_t* dst, int ld, const float* src, int Lc,
-                                               const float* row_scale = nullptr) {
-  constexpr int Q = D / 4, N = kC * Q / kThreads;
-  static_assert(kThreads % Q == 0 && N * kThreads == kC * Q, "whole quads per thread");
-  const int c4 = threadIdx.x % Q, t0 = threadIdx.x / Q;
-  f32x4 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const f32x4*>(src + (size_t)min(t0 + it * (kThreads / Q), Lc - 1) * D + 4 * c4);
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int t = t0 + it * (kThreads / Q);
-    const float sc = t < Lc ? (row_scale ? row_scale[t] : 1.f) : 0.f;
-    u16x4 o;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = bf(v[it][u] * sc);
-    *reinterpret_cast<u16x4*>(dst + t * ld + 4 * c4) = o;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_rows_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
-  constexpr int E = D / 8, N = kC * E / kThreads;
-  static_assert(kThreads % E == 0 && N * kThreads == kC * E, "whole octets per thread");
-  const int c8 = threadIdx.x % E, t0 = threadIdx.x / E;
-  u16x8 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(t0 + it * (kThreads / E), Lc - 1) * D + 8 * c8);
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int t = t0 + it * (kThreads / E);
-    const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    *reinterpret_cast<u16x8*>(dst + t * ld + 8 * c8) = t < Lc ? v[it] : zero;
-  }
-}
-
 // Transposed staging: 8 neighbouring lanes take 8 consecutive tokens of one
 // group of dims, so their LDS writes form 16-byte runs of a row (at most
 // 2-way bank conflicts), while a wave instruction still reads 8 token rows x
@@ -177,56 +133,10 @@ struct ColMap {
   __device__ static int tok(int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / Q + BLKS * it); }
 };
 
-// token-major [C][D] bf16 -> LDS transposed (octets of 8 dims; same token-contiguous lane groups)
-template <int D>
-__device__ __forceinline__ void stage_cols_bf16(uint16_t* dst, int ld, const uint16_t* src, int Lc) {
-  constexpr int E = D / 8, BLKS = 32 / E, N = kC * E / kThreads;
-  const int c8 = (threadIdx.x >> 3) % E;
-  auto tok = [&](int it) { return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / E + BLKS * it); };
-  u16x8 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(tok(it), Lc - 1) * D + 8 * c8);
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int t = tok(it);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = t < Lc ? v[it][u] : uint16_t(0);
-  }
-}
-
-// A boundary snapshot in the scan's bf16 fragment order (fragment
-// f = nt*(D/32) + m, lane l: row 16nt + l%16, columns 32m + 4(l/16) + {0..3},
-// 32m + 16 + 4(l/16) + {0..3}) -> LDS row-major (TRANS: transposed).
-template <int D, bool TRANS>
-__device__ __forceinline__ void stage_snapshot(uint16_t* dst, int ld, const uint16_t* frag) {
-  constexpr int NM = D / 32, N = D * D / 8 / kThreads;
-  u16x8 v[N];
-#pragma unroll
-  for (int it = 0; it < N; ++it)
-    v[it] = *reinterpret_cast<const u16x8*>(frag + (size_t)(threadIdx.x + it * kThreads) * 8);
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const int idx = threadIdx.x + it * kThreads;
-    const int f = idx >> 6, l = idx & 63;
-    const int n = 16 * (f / NM) + (l & 15);
-    const int c0 = 32 * (f % NM) + 4 * (l >> 4);
-    if constexpr (TRANS) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dst[(c0 + u) * ld + n] = v[it][u];
-        dst[(c0 + 16 + u) * ld + n] = v[it][4 + u];
-      }
-    } else {
-      *reinterpret_cast<u16x4*>(dst + n * ld + c0) = u16x4{v[it][0], v[it][1], v[it][2], v[it][3]};
-      *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{v[it][4], v[it][5], v[it][6], v[it][7]};
-    }
-  }
-}
-
-// Split staging for the gradient kernel: the load halves return registers, so a
-// kernel can issue the loads of several tiles (or of a later phase) at once and
-// write LDS afterwards.  Mappings and row handling as in the helpers above.
+// Split staging: the load halves return registers, so a kernel issues the loads
+// of every tile it needs (or of a later phase) at once and writes LDS
+// afterwards -- one memory round trip instead of one per tile.  Rows past Lc
+// load row Lc-1 (every load is unconditional) and are written as zeros.
 template <int D>
 struct TileF32 { f32x4 v[kC * D / 4 / kThreads]; };
 template <int D>
@@ -301,6 +211,54 @@ __device__ __forceinline__ void put_frag(uint16_t* dst, int ld, const Square<D>&
     *reinterpret_cast<u16x4*>(dst + n * ld + c0 + 16) = u16x4{r.v[it][4], r.v[it][5], r.v[it][6], r.v[it][7]};
   }
 }
+// the same, transposed: LDS [D][ld] holding the square's columns as rows
+template <int D>
+__device__ __forceinline__ void put_frag_t(uint16_t* dst, int ld, const Square<D>& r) {
+  constexpr int NM = D / 32;
+#pragma unroll
+  for (int it = 0; it < D * D / 8 / kThreads; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    const int f = idx >> 6, l = idx & 63;
+    const int n = 16 * (f / NM) + (l & 15);
+    const int c0 = 32 * (f % NM) + 4 * (l >> 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dst[(c0 + u) * ld + n] = r.v[it][u];
+      dst[(c0 + 16 + u) * ld + n] = r.v[it][4 + u];
+    }
+  }
+}
+// token-major [C][D] bf16 -> LDS transposed [D][ld] (octets of 8 dims): 8
+// neighbouring lanes take 8 consecutive tokens of one octet, so their LDS
+// writes form 16-byte runs of a row (at most 2-way bank conflicts), while a
+// wave instruction still reads 8 token rows x 128 contiguous bytes
+template <int D>
+__device__ __forceinline__ int cols_tok(int it) {
+  constexpr int E = D / 8, BLKS = 32 / E;
+  return (threadIdx.x & 7) + 8 * ((threadIdx.x >> 3) / E + BLKS * it);
+}
+template <int D>
+__device__ __forceinline__ TileB16<D> load_cols_b16(const uint16_t* src, int Lc) {
+  constexpr int E = D / 8;
+  TileB16<D> r;
+  const int c8 = (threadIdx.x >> 3) % E;
+#pragma unroll
+  for (int it = 0; it < kC * E / kThreads; ++it)
+    r.v[it] = *reinterpret_cast<const u16x8*>(src + (size_t)min(cols_tok<D>(it), Lc - 1) * D + 8 * c8);
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void put_cols_b16(uint16_t* dst, int ld, const TileB16<D>& r, int Lc) {
+  constexpr int E = D / 8;
+  const int c8 = (threadIdx.x >> 3) % E;
+#pragma unroll
+  for (int it = 0; it < kC * E / kThreads; ++it) {
+    const int t = cols_tok<D>(it);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[(8 * c8 + u) * ld + t] = t < Lc ? r.v[it][u] : uint16_t(0);
+  }
+}
+
 // The adjoint snapshots Rs and S are stored in tile order: the 16x16 tile
 // (mt, nt) of a square is 512 contiguous bytes, lane l of it 8 bytes holding
 // row 16mt + 4(l/16) + l%4, columns 16nt + 4((l%16)/4) + {0..3} -- an MFMA
@@ -377,10 +335,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
   uint16_t* sS = sR;                // masked scores [C][LC]  (after Gb^T, V are consumed)
   uint16_t* sKT = sR + kC * LC;     // K^T   [D][LC]
 
+  // every global load of the chunk at once: d_O, V, Gb, and K for the second
+  // product (held in registers until its LDS region is free)
+  const TileF32<D> dov = load_tile_f32<D>(p.d_o + row0 * D, Lc);
+  const TileB16<D> vv = load_tile_b16<D>(static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
+  const Square<D> gbv = load_square<D>(static_cast<const uint16_t*>(p.gb) + (size_t)chunk * D * D);
+  const TileB16<D> kv = load_cols_b16<D>(static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
   if (wave == 0) chunk_gates(p.gamma, p.beta, row0, Lc, bcum, betas);
-  stage_rows_f32<D>(sDO, LD, p.d_o + row0 * D, Lc);
-  stage_rows_bf16<D>(sV, LD, static_cast<const uint16_t*>(p.v) + row0 * D, Lc);
-  stage_snapshot<D, true>(sGT, LD, static_cast<const uint16_t*>(p.gb) + (size_t)chunk * D * D);
+  put_tile_f32<D>(sDO, LD, dov, Lc);
+  put_tile_b16<D>(sV, LD, vv, Lc);
+  put_frag_t<D>(sGT, LD, gbv);
   __syncthreads();
 
   f32x4 u[NTL], pp[4];
@@ -399,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dx_kernel(BwdParams p) {
       const float w = j <= t ? expf(bcum[t] - bcum[j]) * betas[j] : 0.f;
       sS[t * LC + j] = bf(pp[jt][i] * w);
     }
-  stage_cols_bf16<D>(sKT, LC, static_cast<const uint16_t*>(p.k) + row0 * D, Lc);
+  put_cols_b16<D>(sKT, LC, kv, Lc);
   __syncthreads();
 
   f32x4 r[NTL];
