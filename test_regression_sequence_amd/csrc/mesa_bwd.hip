@@ -441,28 +441,39 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
   const bool from_final = !TOTALS && sg == p.NS - 1;
   const float* carry_r = (!TOTALS && !from_final) ? p.seg_state + (((size_t)bh * 2) * (p.NS - 1) + sg) * D2 : nullptr;
   const float* carry_s = carry_r ? carry_r + (size_t)(p.NS - 1) * D2 : nullptr;
+  // (the sources are chosen per workgroup, so each batch of loads is issued at once)
+  const float* src_r = from_final ? (p.d_hfinal ? p.d_hfinal + (size_t)bh * D2 : nullptr) : carry_r;
+  const float* src_s = from_final ? (p.d_gfinal ? p.d_gfinal + (size_t)bh * D2 : nullptr) : carry_s;
   f32x4 R[NRT][NCT], S[NRT][NCT];
+  auto load_square_part = [&](const float* src, bool transposed, f32x4 (&dst)[NRT][NCT]) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
+          dst[rt][ct][ii] = transposed ? src[col * D + row] : src[row * D + col];
+        }
+  };
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct) {
+      R[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  if (src_r) load_square_part(src_r, false, R);
+  if (src_s) load_square_part(src_s, false, S);
+  if (from_final && src_r) {
+    // the final-state adjoint of H enters symmetrised: D_h + D_h^T
+    f32x4 T[NRT][NCT];
+    load_square_part(src_r, true, T);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int row = r0 + 16 * rt + 4 * g + ii, col = CW * wave + 16 * ct + tl;
-        float rv = 0.f, sv = 0.f;
-        if (from_final) {
-          if (p.d_hfinal) {
-            const float* Dh = p.d_hfinal + (size_t)bh * D2;
-            rv = Dh[row * D + col] + Dh[col * D + row];
-          }
-          if (p.d_gfinal) sv = p.d_gfinal[(size_t)bh * D2 + row * D + col];
-        } else if (carry_r) {
-          rv = carry_r[row * D + col];
-          sv = carry_s[row * D + col];
-        }
-        R[rt][ct][ii] = rv;
-        S[rt][ct][ii] = sv;
-      }
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) R[rt][ct] += T[rt][ct];
+  }
 
   // x, y (all dims), d_o (stripe dims) and the gates of a chunk, into registers
   f32x4 xv[NQ], yv[NQ], dv[ND];
@@ -635,21 +646,31 @@ __global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p
 
   // start state: the final-state adjoints (zero without them); lane (tl, g) of
   // tile u = (mt, nt) holds rows 16mt + 4g + i of column 16nt + tl
+  // (the source is chosen per workgroup, so each batch of loads is issued at once)
   f32x4 R[UPW];
+  const float* src = which == 0 ? p.d_hfinal : p.d_gfinal;
+  auto load_tiles = [&](bool transposed, f32x4 (&dst)[UPW]) {
+    const float* F = src + (size_t)bh * D2;
 #pragma unroll
-  for (int ui = 0; ui < UPW; ++ui) {
-    const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
-      float v = 0.f;
-      if (which == 0 && p.d_hfinal) {
-        const float* Dh = p.d_hfinal + (size_t)bh * D2;
-        v = Dh[row * D + col] + Dh[col * D + row];
-      } else if (which == 1 && p.d_gfinal) {
-        v = p.d_gfinal[(size_t)bh * D2 + row * D + col];
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
+        dst[ui][i] = transposed ? F[col * D + row] : F[row * D + col];
       }
-      R[ui][i] = v;
+    }
+  };
+#pragma unroll
+  for (int ui = 0; ui < UPW; ++ui) R[ui] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (src) {
+    load_tiles(false, R);
+    if (which == 0) {
+      // the final-state adjoint of H enters symmetrised: D_h + D_h^T
+      f32x4 T[UPW];
+      load_tiles(true, T);
+#pragma unroll
+      for (int ui = 0; ui < UPW; ++ui) R[ui] += T[ui];
     }
   }
 
