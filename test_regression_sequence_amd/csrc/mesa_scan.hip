@@ -146,23 +146,38 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
   const size_t init_off = (TOTALS || seg == 0)
                               ? (size_t)bh * D * D
                               : (((size_t)bh * 2 + which) * (p.NS - 1) + (seg - 1)) * D * D;
+  // (the source and layout are chosen per workgroup, so the state's loads are
+  // issued as one batch)
 #pragma unroll
   for (int ui = 0; ui < UPW; ++ui)
 #pragma unroll
-    for (int h = 0; h < TPU; ++h) {
-      const int u = wave + S::WAVES * ui;
-      st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if ((S::EVEN || u < S::NU) && init) {
-        const int mt = unit_mt(u, h), nt = unit_nt(u);
-        const float* base = init + init_off;
-        if (which == 0) {
+    for (int h = 0; h < TPU; ++h) st[ui][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (init) {
+    const float* base = init + init_off;
+    if (which == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st[ui][h][i] = base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl];
-        } else {
-          st[ui][h] = *reinterpret_cast<const f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g);
+      for (int ui = 0; ui < UPW; ++ui)
+#pragma unroll
+        for (int h = 0; h < TPU; ++h) {
+          const int u = wave + S::WAVES * ui;
+          const int mt = unit_mt(u, h), nt = unit_nt(u);
+          if (S::EVEN || u < S::NU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[ui][h][i] = base[(size_t)(16 * mt + 4 * g + i) * D + 16 * nt + tl];
+          }
         }
-      }
+    } else {
+#pragma unroll
+      for (int ui = 0; ui < UPW; ++ui)
+#pragma unroll
+        for (int h = 0; h < TPU; ++h) {
+          const int u = wave + S::WAVES * ui;
+          const int mt = unit_mt(u, h), nt = unit_nt(u);
+          if (S::EVEN || u < S::NU)
+            st[ui][h] = *reinterpret_cast<const f32x4*>(base + (size_t)(16 * nt + tl) * D + 16 * mt + 4 * g);
+        }
     }
+  }
 
   // ---- register prefetch of one chunk -------------------------------------------
   struct Raw {
