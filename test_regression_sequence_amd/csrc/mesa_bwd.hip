@@ -616,72 +616,74 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------------------
 // adjoint scan with whole states, for 2 BH >= 256 (one walk per sequence): two
-// workgroups of 8 waves per sequence, one for Rs and one for S, each holding its
-// whole d x d state and staging the chunk's operands once (the stripe walk above
-// stages every chunk's x and y once per 32-row stripe).  Same products, in the
-// same order, as the stripe walk: the snapshots and dh0, dg0 are bitwise those of
-// the stripe walk.
+// workgroups of 8 waves per sequence, each holding one half of the rows of both
+// Rs and S.  The two do equal work and both read the chunk's x and y, so they
+// walk at one pace and the second read of x and y hits in their shared L2 (the
+// stripe walk above stages every chunk's x and y once per 32-row stripe).  Same
+// products, in the same order, as the stripe walk: the snapshots and dh0, dg0
+// are bitwise those of the stripe walk.
 // ---------------------------------------------------------------------------------------
 constexpr int kFullThreads = 512;
 
-template <int D>
-__global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p) {
-  constexpr int NW = kFullThreads / 64, ND = D / 16, UPW = ND * ND / NW;
-  constexpr int L2 = 2 * kC + 8;                      // two token blocks + 16 bytes of padding
+// the walk of one half (HF: rows HF*D/2 .. HF*D/2 + D/2 - 1) of both states
+template <int D, int HF>
+__device__ __forceinline__ void adj_full_walk(const BwdParams& p, int bh, uint16_t (*sB2)[D * (2 * kC + 8)],
+                                              uint16_t (*sAR2)[(D / 2) * (2 * kC + 8)],
+                                              uint16_t (*sAS2)[(D / 2) * (kC + 8)]) {
+  constexpr int NW = kFullThreads / 64, ND = D / 16, NH = ND / 2;  // row tiles per half
+  constexpr int UPW = NH * ND / NW;                   // tiles of each state per wave
+  constexpr int L2 = 2 * kC + 8, LC = kC + 8;         // token blocks + 16 bytes of padding
   constexpr int NIT = (kC / 2) * (D / 4) / kFullThreads;  // (token pair, dim quad) items per thread
-  static_assert(UPW * NW == ND * ND && NIT * kFullThreads == (kC / 2) * (D / 4), "whole tiles and items");
+  constexpr int QH = D / 8;                           // dim quads per half
+  static_assert(UPW * NW == NH * ND && NIT * kFullThreads == (kC / 2) * (D / 4), "whole tiles and items");
+  // items of this half's dims: with D = 128 exactly item HF of every thread,
+  // with D = 64 the one item of the threads whose quad lies in the half
+  constexpr int NMI = NIT > 1 ? 1 : NIT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
-  // XCD-aware decode: the two workgroups of a sequence share blockIdx % 8, so the
-  // chunk's x they both read comes through one L2
-  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int which = local & 1;                        // 0: Rs, 1: S
-  const int bh = (local >> 1) * 8 + xcd;
-  if (bh >= p.BH) return;
   const size_t D2 = (size_t)D * D;
-
-  // Rs: sA = [(-wY)^T | (-wX)^T], sB = [X^T | Y^T]; S: sA = (w d_O)^T, sB = X^T;
-  // double-buffered by chunk parity, so one barrier per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t sA2[2][D * L2];
-  __shared__ __attribute__((aligned(16))) uint16_t sB2[2][D * L2];
+  auto item_dq = [&](int it) { return (tid + kFullThreads * it) / (kC / 2); };
+  auto mine_it = [&](int it) { return NIT > 1 ? it == HF : item_dq(it) / QH == HF; };
+  constexpr int MIT = NIT > 1 ? HF : 0;               // the item slot that can be this half's
 
   // start state: the final-state adjoints (zero without them); lane (tl, g) of
-  // tile u = (mt, nt) holds rows 16mt + 4g + i of column 16nt + tl
-  // (the source is chosen per workgroup, so each batch of loads is issued at once)
-  f32x4 R[UPW];
-  const float* src = which == 0 ? p.d_hfinal : p.d_gfinal;
-  auto load_tiles = [&](bool transposed, f32x4 (&dst)[UPW]) {
-    const float* F = src + (size_t)bh * D2;
+  // tile u = (mt, nt) holds rows 16mt + 4g + i of column 16nt + tl, with
+  // mt = HF * NH + u / ND (each batch of loads is issued at once)
+  f32x4 R[UPW], S[UPW];
+  auto tile_mt = [&](int ui) { return HF * NH + (wave + NW * ui) / ND; };
+  auto tile_nt = [&](int ui) { return (wave + NW * ui) % ND; };
+  auto load_tiles = [&](const float* F, bool transposed, f32x4 (&dst)[UPW]) {
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
+        const int row = 16 * tile_mt(ui) + 4 * g + i, col = 16 * tile_nt(ui) + tl;
         dst[ui][i] = transposed ? F[col * D + row] : F[row * D + col];
       }
     }
   };
 #pragma unroll
-  for (int ui = 0; ui < UPW; ++ui) R[ui] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (src) {
-    load_tiles(false, R);
-    if (which == 0) {
-      // the final-state adjoint of H enters symmetrised: D_h + D_h^T
-      f32x4 T[UPW];
-      load_tiles(true, T);
-#pragma unroll
-      for (int ui = 0; ui < UPW; ++ui) R[ui] += T[ui];
-    }
+  for (int ui = 0; ui < UPW; ++ui) {
+    R[ui] = f32x4{0.f, 0.f, 0.f, 0.f};
+    S[ui] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if (p.d_hfinal) {
+    // the final-state adjoint of H enters symmetrised: D_h + D_h^T
+    const float* F = p.d_hfinal + (size_t)bh * D2;
+    f32x4 T[UPW];
+    load_tiles(F, false, R);
+    load_tiles(F, true, T);
+#pragma unroll
+    for (int ui = 0; ui < UPW; ++ui) R[ui] += T[ui];
+  }
+  if (p.d_gfinal) load_tiles(p.d_gfinal + (size_t)bh * D2, false, S);
 
-  // one chunk's inputs in registers: x and the second factor (Rs: y / ||dx||,
-  // S: d_o) of this thread's items (tokens 2jp, 2jp+1 x dims 4dq..4dq+3), and
+  // one chunk's inputs in registers: x and y / ||dx|| of this thread's items
+  // (tokens 2jp, 2jp+1 x dims 4dq..4dq+3), d_o of its item in this half, and
   // one token's gates per lane
   struct Raw {
-    f32x4 x[NIT][2], o[NIT][2];
+    f32x4 x[NIT][2], y[NIT][2], o[NMI][2];
     float gam, nu;
   };
-  const float* Og = which ? p.d_o : p.yn;
   auto fetch = [&](int c, Raw& r) {
     const int Lc = min(kC, p.T - c * kC);
     const size_t row0 = (size_t)bh * p.T + c * kC;
@@ -692,31 +694,35 @@ __global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p
       for (int h = 0; h < 2; ++h) {
         const size_t rr = row0 + min(2 * jp + h, Lc - 1);
         r.x[it][h] = *reinterpret_cast<const f32x4*>(p.x + rr * D + 4 * dq);
-        r.o[it][h] = *reinterpret_cast<const f32x4*>(Og + rr * D + 4 * dq);
+        r.y[it][h] = *reinterpret_cast<const f32x4*>(p.yn + rr * D + 4 * dq);
+        if (it == MIT && mine_it(it)) r.o[0][h] = *reinterpret_cast<const f32x4*>(p.d_o + rr * D + 4 * dq);
       }
     }
     const size_t rl = row0 + min(lane, Lc - 1);
     r.gam = p.gamma[rl];
     r.nu = p.nu[rl];
   };
-  f32x4 lam[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) lam[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lam = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // the adjoints arriving at chunk c's end, one 8-byte store per tile and lane
   auto store_snapshot = [&](const int c) {
-    uint16_t* sn = (which ? p.snap_s : p.snap_r) + ((size_t)bh * p.NC + c) * D2;
+    uint16_t* sr = p.snap_r + ((size_t)bh * p.NC + c) * D2;
+    uint16_t* ss = p.snap_s + ((size_t)bh * p.NC + c) * D2;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
-      *reinterpret_cast<u16x4*>(sn + adj_tile_offset(D, mt, nt, lane)) = bf4(quad_transpose(R[ui]));
+      const size_t off = adj_tile_offset(D, tile_mt(ui), tile_nt(ui), lane);
+      *reinterpret_cast<u16x4*>(sr + off) = bf4(quad_transpose(R[ui]));
+      *reinterpret_cast<u16x4*>(ss + off) = bf4(quad_transpose(S[ui]));
     }
   };
-  // chunk c from ring buffer cur, with chunk c-2 fetched into pre (two steps ahead)
+  // chunk c from ring buffer cur, with chunk c-2 fetched into pre (two steps ahead).
+  // LDS (this parity): sB = [X^T | Y^T] (all dims); sAR = [(-wY)^T | (-wX)^T] and
+  // sAS = (w d_O)^T (this half's dims)
   auto step = [&](const int c, const Raw& cur, Raw& pre) {
     const int Lc = min(kC, p.T - c * kC);
-    uint16_t* sA = sA2[c & 1];
     uint16_t* sB = sB2[c & 1];
+    uint16_t* sAR = sAR2[c & 1];
+    uint16_t* sAS = sAS2[c & 1];
     fetch(max(c - 2, 0), pre);  // unconditional (clamped): no branch among the loads
     // the gates (lane = token): w_t = e^{b_t}, b restarted at the chunk start
     float lg = lane < Lc ? logf(cur.gam) : 0.f;
@@ -737,23 +743,23 @@ __global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p
       const bool in0 = t0 < Lc, in1 = t1 < Lc;
       const float w0 = in0 ? ws0 : 0.f, w1 = in1 ? ws1 : 0.f;
       const float ex0 = in0 ? 1.f : 0.f, ex1 = in1 ? 1.f : 0.f;
+      const bool mine = it == MIT && mine_it(it);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = 4 * dq + u;
+        const int i = 4 * dq + u, il = i - HF * (D / 2);
         const float xe0 = cur.x[it][0][u] * ex0, xe1 = cur.x[it][1][u] * ex1;
+        const float ye0 = cur.y[it][0][u] * (in0 ? ns0 : 0.f), ye1 = cur.y[it][1][u] * (in1 ? ns1 : 0.f);
         *reinterpret_cast<uint32_t*>(sB + i * L2 + t0) = (uint32_t)bf(xe0) | ((uint32_t)bf(xe1) << 16);
-        if (which == 0) {
-          const float ye0 = cur.o[it][0][u] * (in0 ? ns0 : 0.f), ye1 = cur.o[it][1][u] * (in1 ? ns1 : 0.f);
-          *reinterpret_cast<uint32_t*>(sB + i * L2 + kC + t0) = (uint32_t)bf(ye0) | ((uint32_t)bf(ye1) << 16);
-          *reinterpret_cast<uint32_t*>(sA + i * L2 + t0) =
+        *reinterpret_cast<uint32_t*>(sB + i * L2 + kC + t0) = (uint32_t)bf(ye0) | ((uint32_t)bf(ye1) << 16);
+        if (mine) {
+          *reinterpret_cast<uint32_t*>(sAR + il * L2 + t0) =
               (uint32_t)bf(-w0 * ye0) | ((uint32_t)bf(-w1 * ye1) << 16);
-          *reinterpret_cast<uint32_t*>(sA + i * L2 + kC + t0) =
+          *reinterpret_cast<uint32_t*>(sAR + il * L2 + kC + t0) =
               (uint32_t)bf(-w0 * xe0) | ((uint32_t)bf(-w1 * xe1) << 16);
-          lam[it][u] = __builtin_fmaf(-ye0, xe0, lam[it][u]);
-          lam[it][u] = __builtin_fmaf(-ye1, xe1, lam[it][u]);
-        } else {
-          *reinterpret_cast<uint32_t*>(sA + i * L2 + t0) =
-              (uint32_t)bf(w0 * cur.o[it][0][u]) | ((uint32_t)bf(w1 * cur.o[it][1][u]) << 16);
+          *reinterpret_cast<uint32_t*>(sAS + il * LC + t0) =
+              (uint32_t)bf(w0 * cur.o[0][0][u]) | ((uint32_t)bf(w1 * cur.o[0][1][u]) << 16);
+          lam[u] = __builtin_fmaf(-ye0, xe0, lam[u]);
+          lam[u] = __builtin_fmaf(-ye1, xe1, lam[u]);
         }
       }
     }
@@ -763,9 +769,9 @@ __global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p
     const float decay = expf(blast);
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-      const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
-      if (which == 0) R[ui] = mma<2 * kC>(sA + 16 * mt * L2, L2, sB + 16 * nt * L2, L2, R[ui] * decay);
-      else R[ui] = mma<kC>(sA + 16 * mt * L2, L2, sB + 16 * nt * L2, L2, R[ui] * decay);
+      const int ml = tile_mt(ui) - HF * NH, nt = tile_nt(ui);
+      R[ui] = mma<2 * kC>(sAR + 16 * ml * L2, L2, sB + 16 * nt * L2, L2, R[ui] * decay);
+      S[ui] = mma<kC>(sAS + 16 * ml * LC, LC, sB + 16 * nt * L2, L2, S[ui] * decay);
     }
     // the adjoints arriving at chunk c-1's end go out now, so their stores drain
     // while the next chunk is gated and staged
@@ -783,28 +789,41 @@ __global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p
     if (c - 2 >= 0) step(c - 2, b2, b1);
   }
 
-  // this sequence's part of dlambda: the 32 threads of a dim quad are one half-wave
-  if (which == 0) {
+  // this sequence's part of dlambda over this half's dims: the 32 threads of a
+  // dim quad are one half-wave
+  {
+    f32x4 sum;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      f32x4 sum;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sum[u] = group_sum<32>(lam[it][u]);
-      const int dq = (tid + kFullThreads * it) / (kC / 2);
-      if ((tid & 31) == 0) *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * dq) = sum;
-    }
+    for (int u = 0; u < 4; ++u) sum[u] = group_sum<32>(lam[u]);
+    if ((tid & 31) == 0 && mine_it(MIT))
+      *reinterpret_cast<f32x4*>(p.lam_part + (size_t)bh * D + 4 * item_dq(MIT)) = sum;
   }
   // gradients of the initial states
 #pragma unroll
   for (int ui = 0; ui < UPW; ++ui) {
-    const int u = wave + NW * ui, mt = u / ND, nt = u % ND;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 16 * mt + 4 * g + i, col = 16 * nt + tl;
-      if (which == 0 && p.dh0) p.dh0[(size_t)bh * D2 + row * D + col] = 0.5f * R[ui][i];
-      if (which == 1 && p.dg0) p.dg0[(size_t)bh * D2 + row * D + col] = R[ui][i];
+      const int row = 16 * tile_mt(ui) + 4 * g + i, col = 16 * tile_nt(ui) + tl;
+      if (p.dh0) p.dh0[(size_t)bh * D2 + row * D + col] = 0.5f * R[ui][i];
+      if (p.dg0) p.dg0[(size_t)bh * D2 + row * D + col] = S[ui][i];
     }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kFullThreads) void bwd_scan_full_kernel(BwdParams p) {
+  // XCD-aware decode: the two workgroups of a sequence share blockIdx % 8, so the
+  // chunk's x and y they both read come through one L2
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int half = local & 1;
+  const int bh = (local >> 1) * 8 + xcd;
+  if (bh >= p.BH) return;
+  // double-buffered by chunk parity, so one barrier per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[2][D * (2 * kC + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sAR2[2][(D / 2) * (2 * kC + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sAS2[2][(D / 2) * (kC + 8)];
+  if (half == 0) adj_full_walk<D, 0>(p, bh, sB2, sAR2, sAS2);
+  else adj_full_walk<D, 1>(p, bh, sB2, sAR2, sAS2);
 }
 
 // Carry pass of a segmented adjoint scan, backwards over the segments: C_{NS-1} is the
