@@ -39,6 +39,8 @@
 //                    update is linear in (Rs, S), so a long sequence is
 //                    walked in segments: totals from zero, a carry pass
 //                    (bwd_carry_kernel), then each segment from its carry-in.
+//   bwd_scan_full_kernel  the same walk for many sequences: two workgroups per
+//                    sequence, each holding half the rows of both Rs and S.
 //   bwd_grad_kernel  per chunk: Hhat_t, Ghat_t applied to k_t, v_t as
 //                    e^{b_e-b_t} (stored adjoint) k_t plus the chunk's own
 //                    reverse-causal terms, e.g. Ghat_t k_t gains
