@@ -34,7 +34,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs",
+    "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs", "make_fwd_inputs_device",
     "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs",
     "make_full_lambda", "make_slow_queries", "round_to_bf16",
     "bf16_bits", "bits_to_f32",
@@ -181,6 +181,39 @@ def make_fwd_inputs(cfg: FwdConfig) -> dict:
     if cfg.dtype == "bf16":
         out.update(q_bits=qb, k_bits=kb, v_bits=vb)
     return out
+
+
+def make_fwd_inputs_device(cfg: FwdConfig, device="cuda") -> dict:
+    """The inputs of a forward workload drawn on the device, for sizes whose host
+    copies would not fit (billions of elements): the distributions of
+    :func:`make_fwd_inputs`, drawn in the same order from torch's seeded
+    generator on ``device`` instead of NumPy's.  q, k, v come back in the
+    config's dtype (bf16 or fp32), gamma, beta, lam in fp32; every value is
+    exactly representable in its dtype, so a slice copied to the host (as
+    float64) is the same input for the oracle."""
+    import torch
+
+    if cfg.beta_dist[0] != "uniform":
+        raise ValueError("device generator: uniform beta only")
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def unit_gauss():
+        x = torch.randn(shp, generator=g, device=device)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dt)
+
+    q = unit_gauss()
+    k = unit_gauss()
+    v = torch.randn(shp, generator=g, device=device).to(dt)
+    lo, hi = cfg.gamma_logit
+    gamma = torch.sigmoid(torch.rand(shp[:3], generator=g, device=device) * (hi - lo) + lo)
+    blo, bhi = cfg.beta_dist[1], cfg.beta_dist[2]
+    beta = torch.rand(shp[:3], generator=g, device=device) * (bhi - blo) + blo
+    lam = torch.from_numpy(_lam(np.random.default_rng(cfg.seed), cfg.lam_dist, cfg.H, cfg.d).astype(np.float32))
+    return dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam.to(device), cfg=cfg)
 
 
 def make_slow_queries(x: dict, rho1: float) -> dict:

@@ -1,0 +1,55 @@
+"""Maximum sizes: the chunked forward on arrays of more than 2^31 elements.
+
+q, k, v and o of B=272, H=16, T=4096, d=128 hold 2.28e9 elements each (4.6 GB
+bf16 inputs, 9.1 GB fp32 output; with the boundary snapshots about 41 GB of
+HBM), so every element offset of the last (b, h) slices lies past 2^31 and a
+32-bit index anywhere on the path would show.  The inputs are drawn on the GPU
+(make_fwd_inputs_device); the highest slice, a middle one and the first are
+copied back and run through the fp64 oracle at sampled tokens -- the first
+tokens, both sides of chunk boundaries, the last chunk -- at the forward's bf16
+bar, and their final states against the oracle's at 1e-4.  Needs an MI355X.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import rel_l2
+from test_regression_sequence_amd import mesa
+from test_regression_sequence_amd.inputs import make_fwd_inputs_device, small_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mesa.lib()
+
+
+def test_forward_beyond_2_31_elements():
+    from oracle import mesa_forward
+    cfg = small_fwd(B=272, H=16, T=4096, d=128, chunk=64, dtype="bf16", max_steps=6, tol=0.0, seed=31)
+    assert cfg.B * cfg.H * cfg.T * cfg.d > 2 ** 31
+    x = make_fwd_inputs_device(cfg)
+    r = mesa.fwd_chunked(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], chunk=cfg.chunk,
+                         max_steps=cfg.max_steps, tol=cfg.tol, return_state=True, return_steps=True)
+    torch.cuda.synchronize()
+    assert int(r["steps"].min()) == cfg.max_steps and int(r["steps"].max()) == cfg.max_steps
+    C = cfg.chunk
+    at = np.zeros(cfg.T, bool)
+    at[:4] = True
+    for c in (1, 17, 40, cfg.T // C - 1):
+        at[c * C - 1] = at[c * C] = True
+    at[-C:] = True
+    for b, h in ((cfg.B - 1, cfg.H - 1), (cfg.B // 2, 7), (0, 0)):
+        sl = {n: x[n][b, h][None, None].double().cpu().numpy() for n in ("q", "k", "v", "gamma", "beta")}
+        ref = mesa_forward(sl["q"], sl["k"], sl["v"], sl["gamma"], sl["beta"], x["lam"][h:h + 1].double().cpu().numpy(),
+                           max_steps=cfg.max_steps, tol=cfg.tol, exact=False, solve_at=at)
+        o = r["o"][b, h].cpu().numpy()[at]
+        err = rel_l2(o, ref["o_cg"][0, 0][at])
+        eh = rel_l2(r["h_final"][b, h].cpu().numpy(), ref["H_final"][0, 0])
+        eg = rel_l2(r["g_final"][b, h].cpu().numpy(), ref["G_final"][0, 0])
+        offset = ((b * cfg.H + h) * cfg.T + cfg.T - 1) * cfg.d
+        print(f"slice ({b}, {h}) last element offset {offset:.3e}: o rel L2 {err:.2e}, final states {eh:.1e} {eg:.1e}")
+        assert err <= 2e-2 and eh <= 1e-4 and eg <= 1e-4, (b, h, err, eh, eg)
