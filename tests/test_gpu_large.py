@@ -1,4 +1,4 @@
-"""Maximum sizes: the chunked forward on arrays of more than 2^31 elements.
+"""Maximum sizes: the chunked forward and backward on arrays of more than 2^31 elements.
 
 q, k, v and o of B=272, H=16, T=4096, d=128 hold 2.28e9 elements each (4.6 GB
 bf16 inputs, 9.1 GB fp32 output; with the boundary snapshots about 41 GB of
@@ -53,3 +53,33 @@ def test_forward_beyond_2_31_elements():
         offset = ((b * cfg.H + h) * cfg.T + cfg.T - 1) * cfg.d
         print(f"slice ({b}, {h}) last element offset {offset:.3e}: o rel L2 {err:.2e}, final states {eh:.1e} {eg:.1e}")
         assert err <= 2e-2 and eh <= 1e-4 and eg <= 1e-4, (b, h, err, eh, eg)
+
+
+def test_backward_beyond_2_31_elements():
+    """The backward at B=4352, H=16, T=256, d=128: x, d_o and dq, dk, dv hold
+    2.28e9 elements each (about 150 GB of HBM with the workspaces).  Gradients of
+    three slices against the oracle's backward (dlambda sums over the batch and
+    is covered by the smaller backward tests)."""
+    from oracle import mesa_backward
+    torch.cuda.empty_cache()
+    cfg = small_fwd(B=4352, H=16, T=256, d=128, chunk=64, dtype="bf16", max_steps=4, tol=0.0, seed=37)
+    assert cfg.B * cfg.H * cfg.T * cfg.d > 2 ** 31
+    x = make_fwd_inputs_device(cfg)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed + 1)
+    d_o = torch.randn((cfg.B, cfg.H, cfg.T, cfg.d), generator=gen, device="cuda")
+    f = mesa.fwd_chunked(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], chunk=cfg.chunk,
+                         max_steps=cfg.max_steps, tol=cfg.tol, return_x=True)
+    b = mesa.bwd_chunked(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], f["x"], d_o, chunk=cfg.chunk,
+                         max_steps=cfg.max_steps, tol=cfg.tol, state_grads=True, return_steps=True)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dgamma", "dbeta", "dh0", "dg0")
+    for bb, h in ((cfg.B - 1, cfg.H - 1), (cfg.B // 2, 5), (0, 0)):
+        sl = {n: x[n][bb, h][None, None].double().cpu().numpy() for n in ("q", "k", "v", "gamma", "beta")}
+        ref = mesa_backward(sl["q"], sl["k"], sl["v"], sl["gamma"], sl["beta"], x["lam"][h:h + 1].double().cpu().numpy(),
+                            d_o[bb, h][None, None].double().cpu().numpy(), max_steps=cfg.max_steps, tol=cfg.tol,
+                            forced_steps=f["steps"][bb, h][None, None].cpu().numpy(),
+                            adjoint_forced_steps=b["adj_steps"][bb, h][None, None].cpu().numpy(), chunk=cfg.chunk)
+        errs = {n: rel_l2(b[n][bb, h].cpu().numpy(), ref[n][0, 0]) for n in names}
+        print(f"backward slice ({bb}, {h}): " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        assert all(e <= 2e-2 for e in errs.values()), (bb, h, errs)
