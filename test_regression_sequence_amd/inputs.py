@@ -35,6 +35,7 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "make_fwd_inputs", "make_fwd_inputs_device",
+    "make_decode_inputs_device",
     "make_decode_inputs", "make_decode_stream", "make_preprocess_inputs", "make_bwd_inputs",
     "make_full_lambda", "make_slow_queries", "round_to_bf16",
     "bf16_bits", "bits_to_f32",
@@ -214,6 +215,45 @@ def make_fwd_inputs_device(cfg: FwdConfig, device="cuda") -> dict:
     beta = torch.rand(shp[:3], generator=g, device=device) * (bhi - blo) + blo
     lam = torch.from_numpy(_lam(np.random.default_rng(cfg.seed), cfg.lam_dist, cfg.H, cfg.d).astype(np.float32))
     return dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam.to(device), cfg=cfg)
+
+
+def make_decode_inputs_device(cfg: DecodeConfig, device="cuda", rank: int = 8) -> dict:
+    """A decode step's inputs drawn on the device, for state arrays of billions
+    of elements: q, k, v, gamma, beta, lambda as in :func:`make_decode_inputs`
+    (torch's seeded generator in place of NumPy's), and starting states of the
+    same scale without a prefill pass: h = W W^T / rank + 0.05 I with W
+    [d, rank] Gaussian per pair (symmetric positive semidefinite plus a ridge),
+    g Gaussian times 0.1.  Every value is exact in its dtype."""
+    import torch
+
+    if cfg.beta_dist[0] != "uniform":
+        raise ValueError("device generator: uniform beta only")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed)
+    shp = (cfg.N, cfg.H, cfg.d)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def unit_gauss():
+        x = torch.randn(shp, generator=gen, device=device)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dt)
+
+    q = unit_gauss()
+    k = unit_gauss()
+    v = torch.randn(shp, generator=gen, device=device).to(dt)
+    lo, hi = cfg.gamma_logit
+    gamma = torch.sigmoid(torch.rand(shp[:2], generator=gen, device=device) * (hi - lo) + lo)
+    blo, bhi = cfg.beta_dist[1], cfg.beta_dist[2]
+    beta = torch.rand(shp[:2], generator=gen, device=device) * (bhi - blo) + blo
+    lam = torch.from_numpy(_lam(np.random.default_rng(cfg.seed), cfg.lam_dist, cfg.H, cfg.d).astype(np.float32))
+    pairs = cfg.N * cfg.H
+    w = torch.randn((pairs, cfg.d, rank), generator=gen, device=device)
+    h = torch.bmm(w, w.transpose(1, 2).contiguous()) / rank
+    del w
+    h.diagonal(dim1=1, dim2=2).add_(0.05)
+    g = torch.randn((pairs, cfg.d, cfg.d), generator=gen, device=device) * 0.1
+    return dict(q=q, k=k, v=v, gamma=gamma, beta=beta, lam=lam.to(device),
+                h=h.view(cfg.N, cfg.H, cfg.d, cfg.d), g=g.view(cfg.N, cfg.H, cfg.d, cfg.d), cfg=cfg)
 
 
 def make_slow_queries(x: dict, rho1: float) -> dict:

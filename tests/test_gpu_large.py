@@ -1,4 +1,4 @@
-"""Maximum sizes: the chunked forward and backward on arrays of more than 2^31 elements.
+"""Maximum sizes: the chunked forward, its backward and the decode step on arrays of more than 2^31 elements.
 
 q, k, v and o of B=272, H=16, T=4096, d=128 hold 2.28e9 elements each (4.6 GB
 bf16 inputs, 9.1 GB fp32 output; with the boundary snapshots about 41 GB of
@@ -83,3 +83,37 @@ def test_backward_beyond_2_31_elements():
         errs = {n: rel_l2(b[n][bb, h].cpu().numpy(), ref[n][0, 0]) for n in names}
         print(f"backward slice ({bb}, {h}): " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
         assert all(e <= 2e-2 for e in errs.values()), (bb, h, errs)
+
+
+def test_decode_beyond_2_31_elements():
+    """The decode step with 135,168 (sequence, head) pairs at d=128: h and g hold
+    2.21e9 elements each.  The highest, a middle and the first pair against the
+    oracle's step: output, solution and both updated states."""
+    from oracle import mesa_decode_step
+    from test_regression_sequence_amd.inputs import DecodeConfig, make_decode_inputs_device
+    torch.cuda.empty_cache()
+    cfg = DecodeConfig("decode-large", N=8448, H=16, d=128, prefill=0, dtype="bf16", gamma_logit=(2.0, 6.0),
+                       beta_dist=("uniform", 0.0, 1.0), lam_dist=("uniform", 0.25, 1.0), max_steps=8, tol=0.0,
+                       seed=41)
+    assert cfg.N * cfg.H * cfg.d * cfg.d > 2 ** 31
+    x = make_decode_inputs_device(cfg)
+    picks = ((cfg.N - 1, cfg.H - 1), (cfg.N // 2, 9), (0, 0))
+    before = {(n, h): (x["h"][n, h].double().cpu().numpy(), x["g"][n, h].double().cpu().numpy()) for n, h in picks}
+    r = mesa.decode_step(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["lam"], x["h"], x["g"],
+                         max_steps=cfg.max_steps, tol=cfg.tol, return_x=True)
+    torch.cuda.synchronize()
+    assert int(r["steps"].min()) == cfg.max_steps and int(r["steps"].max()) == cfg.max_steps
+    for n, h in picks:
+        one = {key: x[key][n, h][None, None].double().cpu().numpy() for key in ("q", "k", "v", "gamma", "beta")}
+        h0, g0 = before[(n, h)]
+        ref = mesa_decode_step(one["q"], one["k"], one["v"], one["gamma"], one["beta"],
+                               x["lam"][h:h + 1].double().cpu().numpy(), h0[None, None], g0[None, None],
+                               max_steps=cfg.max_steps, tol=cfg.tol)
+        eo = rel_l2(r["o"][n, h].cpu().numpy(), ref["o"][0, 0])
+        ex = rel_l2(r["x"][n, h].cpu().numpy(), ref["x"][0, 0])
+        eh = rel_l2(x["h"][n, h].cpu().numpy(), ref["h"][0, 0])
+        eg = rel_l2(x["g"][n, h].cpu().numpy(), ref["g"][0, 0])
+        off = ((n * cfg.H + h) * cfg.d + cfg.d - 1) * cfg.d + cfg.d - 1
+        print(f"decode pair ({n}, {h}) last state offset {off:.3e}: o {eo:.2e}, x {ex:.2e}, states {eh:.1e} {eg:.1e}")
+        # the bf16-input bar for the solve, fp32 arithmetic for the state updates
+        assert eo <= 2e-2 and ex <= 2e-2 and eh < 1e-6 and eg < 1e-6, (n, h, eo, ex, eh, eg)
