@@ -418,9 +418,11 @@ void cg_bf16_kernel(CgParams p) {
     // the previous step's alpha and beta: its x step and the new direction are
     // formed block by block at the top of the next iteration, among its MFMAs
     float alpha_p = 0.f, beta_p = 0.f;
-    for (int it = 0; it < p.max_steps; ++it) {
-      const bool active = !stopped && rho > 0.f && rho > p.tol2;
-      if (!__any(active)) break;
+    // the loop runs while some token of the tile is active (one test, at the
+    // bottom, from the state the step left)
+    bool active = rho > 0.f && rho > p.tol2;
+    int it = 0;
+    if (p.max_steps > 0 && __any(active)) do {
       pin_operands();
       // per k-block m (the dims of pv[2m], pv[2m+1]): x += alpha_p p, then
       // p = r + beta_p p in place (three-operand FMA: the two-address form would
@@ -485,7 +487,8 @@ void cg_bf16_kernel(CgParams p) {
       beta_p = bet;
       rho = ok ? rr : rho;
       n += ok ? 1 : 0;
-    }
+      active = !stopped && rho > 0.f && rho > p.tol2;
+    } while (++it < p.max_steps && __any(active));
     // the last step's x update
 #pragma unroll
     for (int a = 0; a < ND; ++a) x[a] += alpha_p * pv[a];
