@@ -62,7 +62,7 @@ def oracle_on_slices(x: dict, idx, steps_gpu=None, exact=False, solve_at=None, *
 
 # Stopping decisions of dynamic CG (MesaNet page, "Mesa layer", dynamic compute:
 # the step count follows a stopping criterion and varies per token).  Step counts
-# near the threshold are not unique in finite precision, so a GPU stop is judged
+# near the threshold are not unique in finite precision, so a GPU stop is checked
 # against the fp64 oracle's recursive residuals after the same number of steps:
 #   * no premature stop: a stop before the cap needs ||r_n|| <= tol (1 + eps);
 #   * at most one step past the fp64 run's own crossing: ||r_{n-2}|| > tol.
