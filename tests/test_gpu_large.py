@@ -27,6 +27,15 @@ def _gpu():
     mesa.lib()
 
 
+@pytest.fixture(autouse=True)
+def _release():
+    """Hand the tens of GB these tests hold back to the device afterwards, so
+    the tests that follow in the same process start from an empty cache."""
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def test_forward_beyond_2_31_elements():
     from oracle import mesa_forward
     cfg = small_fwd(B=272, H=16, T=4096, d=128, chunk=64, dtype="bf16", max_steps=6, tol=0.0, seed=31)
