@@ -122,9 +122,25 @@ def bench_forward(cfg, steps, warmup, x=None):
     ms = evs[0][0].elapsed_time(evs[-1][2]) / steps
     scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
     cg_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     n = st.cpu().numpy()
     return dict(ms=ms, wall_ms=wall, scan_ms=float(np.mean(scan_ms)), cg_ms=float(np.mean(cg_ms)),
+                step_ms=step_ms, cg_ms_each=cg_ms,
                 steps_mean=float(n.mean()), steps_max=int(n.max()), steps=n, x=x)
+
+
+def spread(ms: list) -> dict:
+    """Median and interquartile range of per-step times (ms)."""
+    q1, med, q3 = np.percentile(np.asarray(ms, dtype=np.float64), [25, 50, 75])
+    return {"median": round(float(med), 4), "p25": round(float(q1), 4), "p75": round(float(q3), 4),
+            "iqr": round(float(q3 - q1), 4), "n": len(ms)}
+
+
+def recurrent_flops_per_token(d: int, n_steps: float) -> float:
+    """The token-by-token recurrence's own count: the two state updates, the
+    CG iterations on an explicit H and the read-out; a lower bound on the
+    flops of any form of the layer, reported for context."""
+    return 3 * d * d + 3 * d * d + n_steps * (2 * d * d + 10 * d) + 2 * d * d
 
 
 def cg_kernel_bytes(cfg) -> int:
@@ -171,6 +187,11 @@ def forward_report(cfg, fw) -> dict:
         "cg_frac_of_hbm_peak": round(cg_b / (fw["cg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "scan_hbm_GBs": round(sc_b / (fw["scan_ms"] * 1e-3) / 1e9, 1),
         "scan_frac_of_hbm_peak": round(sc_b / (fw["scan_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "step_ms": spread(fw["step_ms"]),
+        "cg_ms": spread(fw["cg_ms_each"]),
+        "recurrent_form_flops_per_token": recurrent_flops_per_token(cfg.d, fw["steps_mean"]),
+        "recurrent_form_TFLOPs": round(recurrent_flops_per_token(cfg.d, fw["steps_mean"]) * tokens
+                                       / (fw["ms"] * 1e-3) / 1e12, 2),
         "cg_steps_mean": round(fw["steps_mean"], 3),
         "cg_steps_max": fw["steps_max"],
         # the work a chunk's wave does follows its tiles' slowest tokens
@@ -753,6 +774,61 @@ def cpu_baseline(x, per_worker: int, tokens: int):
     }
 
 
+def _oracle_decode(args):
+    """One block of (sequence, head) pairs of the oracle's decode step, in a worker."""
+    from threadpoolctl import threadpool_limits
+    from oracle import mesa_decode_step
+    q, k, v, gamma, beta, lam, h, g, max_steps, tol = args
+    with threadpool_limits(1):
+        mesa_decode_step(q, k, v, gamma, beta, lam, h, g, max_steps=max_steps, tol=tol)
+    return q.shape[0] * q.shape[1]
+
+
+def cpu_other_workloads() -> dict:
+    """The oracle (CG schedule, fp64) on the other workloads, over the host's
+    cores like the main baseline: workloads 1 and 2 in full (every slice), the
+    decode step on 32 sequences x 16 heads drawn with workload 5's
+    distributions.  A reported baseline, not a target."""
+    import multiprocessing as mp
+    from test_regression_sequence_amd.inputs import CONFIGS, make_decode_inputs, make_fwd_inputs
+    workers = host_workers()
+    out = {}
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        for key, c in (("tiny_fp32", 1), ("mid_d64", 2)):
+            cfg = CONFIGS[c]
+            x = make_fwd_inputs(cfg)
+            jobs = [(x["q"][b, h][None, None].astype(np.float64), x["k"][b, h][None, None].astype(np.float64),
+                     x["v"][b, h][None, None].astype(np.float64), x["gamma"][b, h][None, None],
+                     x["beta"][b, h][None, None], x["lam"][h][None], cfg.max_steps, cfg.tol)
+                    for b in range(cfg.B) for h in range(cfg.H)]
+            pool.map(_oracle_slice, jobs[:1])
+            t0 = time.perf_counter()
+            done = sum(pool.map(_oracle_slice, jobs, chunksize=1))
+            dt = time.perf_counter() - t0
+            out[key] = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+                        "sample": f"the whole workload ({len(jobs)} (b,h) slices x {cfg.T} tokens), CG schedule; "
+                                  f"{dt:.2f} s wall"}
+        cfg = CONFIGS[5].replace(N=32)
+        x = make_decode_inputs(cfg)
+        P = 4  # pairs per job, all of one head (the oracle takes one lambda per head of its batch)
+        jobs = []
+        for h in range(cfg.H):
+            for n0 in range(0, cfg.N, P):
+                ns = np.arange(n0, min(n0 + P, cfg.N))
+                jobs.append(tuple(x[key_][ns, h][:, None] for key_ in ("q", "k", "v", "gamma", "beta"))
+                            + (x["lam"][h][None], x["h"][ns, h][:, None], x["g"][ns, h][:, None],
+                               cfg.max_steps, cfg.tol))
+        pool.map(_oracle_decode, jobs[:1])
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_decode, jobs, chunksize=1))
+        dt = time.perf_counter() - t0
+        out["decode"] = {"value": round(done / dt, 2), "unit": "pairs/s", "cores": workers, "kind": "oracle",
+                         "sample": f"{done} (sequence, head) pairs of workload 5's distributions (32 sequences), "
+                                   f"one decode step each, CG schedule; {dt:.2f} s wall"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -788,11 +864,15 @@ def main():
     cfg = CONFIGS[args.workload]
     x_main = None
     cpu = None
+    cpu_other = None
     if not args.no_cpu_baseline and not args.calibrate_copy:
         # before any HIP call: the oracle's worker processes are plain forks
         x_main = make_fwd_inputs(cfg)
         cpu = cpu_baseline(x_main, args.cpu_slices_per_core, args.cpu_tokens)
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} cores")
+        if not args.forward_only:
+            cpu_other = cpu_other_workloads()
+            log(f"cpu baseline, other workloads: {cpu_other}")
 
     import torch
     from test_regression_sequence_amd import mesa
@@ -904,6 +984,8 @@ def main():
     line["forward_detail"] = forward_report(cfg, fw)
     if cpu is not None:
         line["cpu_baseline"] = cpu
+    if cpu_other is not None:
+        line["cpu_baseline_other_workloads"] = cpu_other
     print(json.dumps(line), flush=True)
 
 
