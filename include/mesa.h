@@ -36,6 +36,9 @@
  *     Launch failures reported by the runtime return MESA_ERR_HIP.
  *   - Numeric preconditions are documented, not checked: 0 < gamma <= 1,
  *     beta >= 0, lambda > 0, finite inputs, symmetric h0 / h_state.
+ *   - An output buffer may not overlap another output or an input, except
+ *     where a call updates a state in place (the decode steps) or says
+ *     otherwise.  Only the preprocessing calls check this.
  *   - Tensors are dense and row-major with the last index fastest.  States are
  *     [.., dk, dk] for H and [.., dv, dk] for G (row = value dimension).
  *   - Supported sizes: dk == dv; dk in {16, 32, 64, 128} for MESA_F32 inputs
