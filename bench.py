@@ -844,7 +844,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="with --forward-only: also time the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-slices-per-core", type=int, default=2)
+    ap.add_argument("--cpu-slices-per-core", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
