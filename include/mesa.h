@@ -20,9 +20,12 @@
  *
  * CG: Hestenes-Stiefel from x_0 = 0 with the recursive residual r.  Before
  * each iteration a token stops if max_steps iterations are done, if
- * tol > 0 and ||r||_2 <= tol, or if r.r == 0; it also stops (without
- * updating) if p.(A p) <= 0.  A stopped token never restarts.  steps[t] is
- * the number of executed updates.  tol <= 0 selects the fixed-step mode.
+ * tol > 0 and ||r||_2 <= tol, or if r.r is zero; it also stops (without
+ * updating) if p.(A p) is zero or negative.  "Zero" means below 2^-126, the
+ * smallest normal float: in the fixed-step mode a system solved to rounding
+ * keeps shrinking its recursive residual until r.r underflows, and the
+ * iteration ends there.  A stopped token never restarts.  steps[t] is the
+ * number of executed updates.  tol <= 0 selects the fixed-step mode.
  *
  * Conventions common to every call
  *   - All tensor pointers are device pointers owned by the caller.  The

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
   int n = 0;
   bool stopped = false;
   for (int it = 0; it < p.max_steps; ++it) {
-    const bool active = !stopped && rho > 0.f && rho > p.tol2;
+    const bool active = !stopped && rho >= kCgZero && rho > p.tol2;
     if (!__any(active)) break;
     chunk_product(pv, acc, false);
     float pw = 0.f;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_kernel(CgParams p) {
       pw += dot4(pv[a], acc[a]);
     }
     pw = sum_lane_groups(pw);
-    const bool ok = active && pw > 0.f;
+    const bool ok = active && pw >= kCgZero;
     stopped = !ok;
     const float alpha = ok ? rho / pw : 0.f;
     float rr = 0.f;

@@ -420,7 +420,7 @@ void cg_bf16_kernel(CgParams p) {
     float alpha_p = 0.f, beta_p = 0.f;
     // the loop runs while some token of the tile is active (one test, at the
     // bottom, from the state the step left)
-    bool active = rho > 0.f && rho > p.tol2;
+    bool active = rho >= kCgZero && rho > p.tol2;
     int it = 0;
     if (p.max_steps > 0 && __any(active)) do {
       pin_operands();
@@ -467,7 +467,7 @@ void cg_bf16_kernel(CgParams p) {
         pw1 += pv[a][3] * acc[a][3];
       }
       const float pw = sum_lane_groups(pw0 + pw1);
-      const bool ok = active && pw > 0.f;
+      const bool ok = active && pw >= kCgZero;
       stopped = !ok;
       const float alpha = ok ? rho * __builtin_amdgcn_rcpf(pw) : 0.f;
       float rr0 = 0.f, rr1 = 0.f;
@@ -487,7 +487,7 @@ void cg_bf16_kernel(CgParams p) {
       beta_p = bet;
       rho = ok ? rr : rho;
       n += ok ? 1 : 0;
-      active = !stopped && rho > 0.f && rho > p.tol2;
+      active = !stopped && rho >= kCgZero && rho > p.tol2;
     } while (++it < p.max_steps && __any(active));
     // the last step's x update
 #pragma unroll

@@ -318,7 +318,7 @@ void cg_bf16_unscaled_kernel(CgParams p) {
       int n = 0;
       bool stopped = false;
       for (int it = 0; it < p.max_steps; ++it) {
-        const bool active = !stopped && rho > 0.f && rho > p.tol2;
+        const bool active = !stopped && rho >= kCgZero && rho > p.tol2;
         if (!__any(active)) break;
         pin_operands();
         bf16x8 ub[NM], sb[NMJ];
@@ -331,7 +331,7 @@ void cg_bf16_unscaled_kernel(CgParams p) {
         for (int a = 0; a < ND; ++a)
           pw += pv[a][0] * acc[a][0] + pv[a][1] * acc[a][1] + pv[a][2] * acc[a][2] + pv[a][3] * acc[a][3];
         pw = sum_lane_groups(pw);
-        const bool ok = active && pw > 0.f;
+        const bool ok = active && pw >= kCgZero;
         stopped = !ok;
         const float alpha = ok ? rho * __builtin_amdgcn_rcpf(pw) : 0.f;
         float rr = 0.f;

@@ -14,6 +14,11 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
+// Every CG loop counts r.r and p.(A p) below the smallest normal float as
+// zero: the recursive residual of a system solved to rounding keeps shrinking
+// and can underflow, and a reciprocal of such a value is not finite.
+constexpr float kCgZero = 0x1p-126f;
+
 // D = 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][8(l/16)..+7],
 // B[8(l/16)..+7][l%16] and receives D[4(l/16)..+3][l%16].
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -259,11 +259,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeParams p) 
   float rho = vsum(rv, rv);
   int n = 0;
   for (int it = 0; it < p.max_steps; ++it) {
-    if (!(rho > 0.f && rho > p.tol2)) break;
+    if (!(rho >= kCgZero && rho > p.tol2)) break;
     float wv[EPL];
     apply_a(pv, wv, it & 1);
     const float pw = vsum(pv, wv);
-    if (!(pw > 0.f)) break;
+    if (!(pw >= kCgZero)) break;
     const float alpha = rho / pw;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
