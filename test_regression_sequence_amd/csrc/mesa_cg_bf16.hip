@@ -25,7 +25,11 @@
 // tile leaves its loop as soon as its 16 tokens have stopped), parks every
 // tile's solution in LDS, and finally loads Gb and the values once for the
 // read-out of all tiles.  Every tile has its own straight-line code (the
-// causal extent of a tile is a compile-time constant).
+// causal extent of a tile is a compile-time constant).  A grid with fewer
+// chunks than SIMDs shares each chunk out over 2 or 4 waves instead (tiles
+// {0, 3} and {1, 2}, or one tile each): every wave loads the chunk's operands
+// itself and solves and reads out only its tiles, with the same arithmetic
+// per tile, so the results are bitwise those of one wave per chunk.
 //
 // Register layout (lane l, tl = l%16, g = l/16): every CG vector of token
 // 16w + tl keeps dims 16a + 4g + {0..3} (a < D/16) as f32x4 v[a].  Matrix
@@ -82,11 +86,29 @@ namespace {
 template <int W>
 using tile_c = std::integral_constant<int, W>;
 
-template <int D, int C, bool LF, bool WARM = false, bool PREP = false>
-__global__ __launch_bounds__(LF ? 128 : 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void cg_bf16_kernel(CgParams p) {
+// LDS of one workgroup (declared once per kernel; the bodies below take it by reference)
+template <int D, int C, bool LF, bool PREP>
+struct CgLds {
+  static constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NWV = LF ? 2 : 1;
+  static constexpr int PS = D + 8;  // PREP row stride, padded by 16 bytes against bank conflicts
+  bf16x8 xs_[NWV][NW * NM * 64];    // solutions xh of the tiles as bf16, [tile][m][lane]
+  bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
+  float lam_s[D];
+  float bcum_[NWV][C];
+  float betas_[NWV][C];
+  // PREP: the chunk's processed keys, then its processed queries, [row][D]
+  __attribute__((aligned(16))) __bf16 prow[PREP ? C * PS : 1];
+};
+
+// One wave's work on one chunk.  SP waves share a chunk's token tiles (SP = 1:
+// all of them); PART is this wave's share, known at compile time so that each
+// share is straight-line code of its own.
+template <int D, int C, bool LF, bool WARM, bool PREP, int SP, int PART>
+__device__ __forceinline__ void cg_chunk(const CgParams& p, CgLds<D, C, LF, PREP>& L) {
   static_assert(!(LF && WARM), "the warm start takes a diagonal Lambda");
   static_assert(!PREP || (!LF && !WARM && C == 64), "fused preprocessing: diagonal Lambda, cold start, chunk 64");
+  static_assert(SP == 1 || (!LF && !WARM && !PREP && (SP == 2 || SP == 4) && SP <= C / 16),
+                "shared chunks: the plain kernel, 2 or 4 waves per chunk, at most one per tile");
   constexpr int ND = D / 16, NM = ND / 2, NW = C / 16, NMJ = (NW + 1) / 2;
   constexpr int NWV = LF ? 2 : 1;  // waves (chunks) per workgroup
 
@@ -100,8 +122,9 @@ void cg_bf16_kernel(CgParams p) {
     bh = blockIdx.x / ncp;
     c = 2 * (blockIdx.x % ncp) + wv;
   } else {
-    bh = blockIdx.x / p.NC;
-    c = blockIdx.x % p.NC;
+    const int blk = SP > 1 ? (int)(blockIdx.x / SP) : (int)blockIdx.x;
+    bh = blk / p.NC;
+    c = blk % p.NC;
   }
   const bool has_chunk = c < p.NC;
   if (!has_chunk) c = p.NC - 1;
@@ -110,15 +133,13 @@ void cg_bf16_kernel(CgParams p) {
   const int T = p.T, s = c * C, Lc = min(C, T - s);
   const size_t row0 = (size_t)bh * T + s;
 
-  __shared__ bf16x8 xs_[NWV][NW * NM * 64];  // solutions xh of the tiles as bf16, [tile][m][lane]
-  __shared__ bf16x8 lamf[LF ? ND * NM * 64 : 1];  // full Lambda as A fragments, [nt][m][lane]
-  __shared__ float lam_s[D];
-  __shared__ float bcum_[NWV][C];
-  __shared__ float betas_[NWV][C];
-  // PREP: the chunk's processed keys, then its processed queries, [row][D]
-  // with the row stride padded by 16 bytes against bank conflicts
-  constexpr int PS = D + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 prow[PREP ? C * PS : 1];
+  auto& xs_ = L.xs_;
+  auto& lamf = L.lamf;
+  auto& lam_s = L.lam_s;
+  auto& bcum_ = L.bcum_;
+  auto& betas_ = L.betas_;
+  constexpr int PS = CgLds<D, C, LF, PREP>::PS;
+  auto& prow = L.prow;
   bf16x8* const xs = xs_[wv];
   float* const bcum = bcum_[wv];
   float* const betas = betas_[wv];
@@ -284,7 +305,7 @@ void cg_bf16_kernel(CgParams p) {
       load_rows_lds(kr);
     } else {
       load_rows(Kg, kr);
-      fetch_q(0);
+      fetch_q(PART);  // the wave's first tile (PART, in every split)
     }
     lg = lane < Lc ? logf(lg) : 0.f;
 #pragma unroll
@@ -370,7 +391,7 @@ void cg_bf16_kernel(CgParams p) {
 
   // ---- conjugate gradient of one tile -------------------------------------------
   f32x4 xprev[WARM ? ND : 1];  // the previous tile's solutions (WARM)
-  auto solve_tile = [&](auto wc) {
+  auto solve_tile = [&](auto wc, auto nc) {
     constexpr int w = decltype(wc)::value;
     const int tloc = 16 * w + tl;
     const bool valid = tloc < Lc;
@@ -408,7 +429,7 @@ void cg_bf16_kernel(CgParams p) {
         pv[a] = r[a];
       }
     }
-    if constexpr (w + 1 < NW) fetch_q(w + 1);
+    if constexpr (decltype(nc)::value >= 0) fetch_q(decltype(nc)::value);  // the wave's next tile
     float rho = 0.f;
 #pragma unroll
     for (int a = 0; a < ND; ++a) rho += r[a][0] * r[a][0] + r[a][1] * r[a][1] + r[a][2] * r[a][2] + r[a][3] * r[a][3];
@@ -526,11 +547,28 @@ void cg_bf16_kernel(CgParams p) {
     }
   };
 
+  // The wave's tiles, each with the next one to prefetch (-1: none): all of
+  // them in order (SP == 1); tile PART (SP == NW); or, two waves on four
+  // tiles, {0, 3} and {1, 2}, which balances their causal extents.
   auto for_tiles = [&](auto fn) {
-    fn(tile_c<0>{});
-    if constexpr (NW > 1) fn(tile_c<(NW > 1 ? 1 : 0)>{});
-    if constexpr (NW > 2) fn(tile_c<(NW > 2 ? 2 : 0)>{});
-    if constexpr (NW > 3) fn(tile_c<(NW > 3 ? 3 : 0)>{});
+    using none = tile_c<-1>;
+    if constexpr (SP == 1) {
+      fn(tile_c<0>{}, tile_c<(NW > 1 ? 1 : -1)>{});
+      if constexpr (NW > 1) fn(tile_c<(NW > 1 ? 1 : 0)>{}, tile_c<(NW > 2 ? 2 : -1)>{});
+      if constexpr (NW > 2) fn(tile_c<(NW > 2 ? 2 : 0)>{}, tile_c<(NW > 3 ? 3 : -1)>{});
+      if constexpr (NW > 3) fn(tile_c<(NW > 3 ? 3 : 0)>{}, none{});
+    } else if constexpr (SP == NW) {
+      fn(tile_c<PART>{}, none{});
+    } else {
+      static_assert(SP == 2 && NW == 4, "two waves on four tiles");
+      if constexpr (PART == 0) {
+        fn(tile_c<0>{}, tile_c<3>{});
+        fn(tile_c<3>{}, none{});
+      } else {
+        fn(tile_c<1>{}, tile_c<2>{});
+        fn(tile_c<2>{}, none{});
+      }
+    }
   };
 
   for_tiles(solve_tile);
@@ -547,7 +585,55 @@ void cg_bf16_kernel(CgParams p) {
     columns_from_rows(wr);
   }
   pin_operands();
-  for_tiles(readout_tile);
+  for_tiles([&](auto wc, auto) { readout_tile(wc); });
+}
+
+template <int D, int C, bool LF, bool WARM = false, bool PREP = false, int SP = 1>
+__global__ __launch_bounds__(LF ? 128 : 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void cg_bf16_kernel(CgParams p) {
+  __shared__ CgLds<D, C, LF, PREP> lds;
+  if constexpr (SP == 1) {
+    cg_chunk<D, C, LF, WARM, PREP, 1, 0>(p, lds);
+  } else {
+    // each share is its own code path from the top (no live range crosses
+    // the branch)
+    const int part = (int)(blockIdx.x % SP);
+    if (part == 0) {
+      cg_chunk<D, C, LF, WARM, PREP, SP, 0>(p, lds);
+    } else if (part == 1) {
+      cg_chunk<D, C, LF, WARM, PREP, SP, 1>(p, lds);
+    } else if constexpr (SP == 4) {
+      if (part == 2) cg_chunk<D, C, LF, WARM, PREP, SP, 2>(p, lds);
+      else cg_chunk<D, C, LF, WARM, PREP, SP, 3>(p, lds);
+    }
+  }
+}
+
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Waves per chunk for the plain kernel.  A grid of fewer chunks than SIMDs
+// leaves SIMDs idle while each wave solves its tiles one after another;
+// sharing a chunk's tiles out over 2 or 4 waves (each loads the chunk's
+// operands itself) puts them to work.  A SIMD that already runs a wave gains
+// nothing from a second one: the CG loop keeps its vector unit busy.
+template <int C>
+int split_waves(long long chunks) {
+  constexpr int NW = C / 16;
+  const long long simds = 4LL * device_cus();
+  if (NW >= 4 && 4 * chunks <= simds) return 4;
+  if (NW >= 2 && 2 * chunks <= simds) return 2;
+  return 1;
 }
 
 template <int D, int C, bool LF = false>
@@ -565,7 +651,19 @@ hipError_t launch_t(const CgParams& p, hipStream_t s) {
     } else if (p.warm) {
       hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, true>), grid, dim3(64), 0, s, p);
     } else {
-      hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
+      const long long chunks = (long long)p.BH * p.NC;
+      const int sp = split_waves<C>(chunks);
+      if constexpr (C >= 64) {
+        if (sp == 4)
+          hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false, false, 4>), dim3((unsigned)(4 * chunks)), dim3(64),
+                             0, s, p);
+      }
+      if constexpr (C >= 32) {
+        if (sp == 2)
+          hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false, false, 2>), dim3((unsigned)(2 * chunks)), dim3(64),
+                             0, s, p);
+      }
+      if (sp == 1) hipLaunchKernelGGL((cg_bf16_kernel<D, C, false, false>), grid, dim3(64), 0, s, p);
     }
   } else {
     if (p.warm || p.prep) return hipErrorInvalidValue;
