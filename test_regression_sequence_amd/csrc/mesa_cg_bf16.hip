@@ -73,6 +73,7 @@
 // hold Hb and the keys, and the B operand is the search direction scaled per
 // token.  Two chunks of one sequence share a workgroup (one wave each) and one
 // copy of Lambda, so that four waves still fit a CU's LDS.
+#include <atomic>
 #include <type_traits>
 
 #include "mesa_common.h"
@@ -609,17 +610,18 @@ void cg_bf16_kernel(CgParams p) {
   }
 }
 
-// Compute units of the current device (looked up once per device).
+// Compute units of the current device (looked up once per device; calls from
+// several host threads may look it up at once and store the same value).
 int device_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Waves per chunk for the plain kernel.  A grid of fewer chunks than SIMDs
