@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+NOMINAL_CLOCK_MHZ = 2400.0  # MI355X peak engine clock, the one the MFMA peak is quoted at
 DECODE_STATE_COPIES = 3     # decode calls rotate over this many state copies
 
 
@@ -72,7 +73,7 @@ def time_events(fn, iters):
     return start.elapsed_time(end) / iters
 
 
-def bench_forward(cfg, steps, warmup, x=None):
+def bench_forward(cfg, steps, warmup, x=None, clock=False):
     import torch
     from test_regression_sequence_amd import mesa
     from test_regression_sequence_amd.inputs import make_fwd_inputs
@@ -124,9 +125,72 @@ def bench_forward(cfg, steps, warmup, x=None):
     cg_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     n = st.cpu().numpy()
+    clock = sample_gfx_clock(step, ms) if clock else None
     return dict(ms=ms, wall_ms=wall, scan_ms=float(np.mean(scan_ms)), cg_ms=float(np.mean(cg_ms)),
                 step_ms=step_ms, cg_ms_each=cg_ms,
-                steps_mean=float(n.mean()), steps_max=int(n.max()), steps=n, x=x)
+                steps_mean=float(n.mean()), steps_max=int(n.max()), steps=n, x=x, clock=clock)
+
+
+def sample_gfx_clock(step, ms_per_step: float, seconds: float = 2.5, period: float = 0.1):
+    """The GFX clock (MHz) under the timed work, as the SMI library reports it:
+    after the timed region the step runs back to back for about `seconds`
+    while the host reads the GPU metrics every `period` seconds.  A sample is
+    the mean of the per-XCD current GFX clocks; only samples taken while the
+    GFX engine reports itself at least half busy count (the metrics table is
+    refreshed about once a second, so the first reads still show the idle
+    GPU).  None where the SMI library cannot be read."""
+    import torch
+    try:
+        handle = torch.cuda._get_amdsmi_handler(0)
+        import amdsmi
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception:
+        return None
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
+        act = m.get("average_gfx_activity")
+        if not clks or not isinstance(act, (int, float)) or act < 50:
+            return None
+        return float(sum(clks)) / len(clks)
+
+    n = max(1, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
+    torch.cuda.synchronize()
+    done = torch.cuda.Event()
+    for _ in range(n):
+        step()
+    done.record()
+    samples = []
+    while not done.query():
+        try:
+            c = read()
+        except Exception:
+            break
+        if c is not None:
+            samples.append(c)
+        time.sleep(period)
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    return {"gfx_mhz_median": round(float(np.median(samples)), 1), "gfx_mhz_min": round(min(samples), 1),
+            "gfx_mhz_max": round(max(samples), 1), "samples": len(samples), "steps_run": n}
+
+
+def clock_report(clock, cg_tflops: float):
+    """The sustained GFX clock beside the CG kernel's fraction of the nominal
+    peak, and that fraction rescaled to the clock measured (the nominal peak
+    assumes 2.4 GHz)."""
+    if clock is None:
+        return None
+    r = dict(clock)
+    r["source"] = ("SMI GPU metrics (mean of the per-XCD current GFX clocks, samples at >= 50 % GFX "
+                   "activity) read from the host every 0.1 s while the forward step ran back to back for "
+                   "2.5 s after the timed region")
+    r["nominal_mhz"] = NOMINAL_CLOCK_MHZ
+    peak_at_clock = PEAK_BF16_TFLOPS * clock["gfx_mhz_median"] / NOMINAL_CLOCK_MHZ
+    r["cg_frac_of_peak_at_that_clock"] = round(cg_tflops / peak_at_clock, 4)
+    return r
 
 
 def spread(ms: list) -> dict:
@@ -885,7 +949,7 @@ def main():
         return
     mesa.lib()
 
-    fw = bench_forward(cfg, args.steps, args.warmup, x_main)
+    fw = bench_forward(cfg, args.steps, args.warmup, x_main, clock=True)
     x_main = None
     log(f"forward: {fw['ms']:.4f} ms per call")
     tokens = cfg.B * cfg.H * cfg.T
@@ -929,6 +993,7 @@ def main():
             "flops_per_launch": cg_flops,
             "avg_launch_ms": round(fw["cg_ms"], 4),
         },
+        "clock": clock_report(fw["clock"], cg_tflops),
         "kernels_ms": {"scan": round(fw["scan_ms"], 4), "cg": round(fw["cg_ms"], 4)},
         "fwd_counted_TFLOPs": round(total_tflops, 2),
         "fwd_frac_of_mfma_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),

@@ -1,6 +1,6 @@
 """bench.py's counting helpers against the counts stated for the workloads
 (counted flops per token of the chunked form, the recurrence's own count, the
-decode step's bytes) and its timing summary."""
+decode step's bytes), its timing summary and the clock report."""
 import bench
 
 
@@ -27,3 +27,13 @@ def test_decode_bytes_per_step():
 def test_spread():
     s = bench.spread([1.0, 2.0, 3.0, 4.0, 5.0])
     assert s == {"median": 3.0, "p25": 2.0, "p75": 4.0, "iqr": 2.0, "n": 5}
+
+
+def test_clock_report():
+    # the nominal 2.5 PFLOP/s is quoted at 2.4 GHz: at 2.0 GHz the same kernel
+    # has 2.5 * 2.0 / 2.4 = 2.083 PFLOP/s to reach
+    assert bench.clock_report(None, 775.0) is None
+    c = {"gfx_mhz_median": 2000.0, "gfx_mhz_min": 1950.0, "gfx_mhz_max": 2050.0, "samples": 9, "steps_run": 960}
+    r = bench.clock_report(c, 775.0)
+    assert r["nominal_mhz"] == 2400.0 and r["samples"] == 9
+    assert r["cg_frac_of_peak_at_that_clock"] == round(775.0 / (2500.0 * 2000.0 / 2400.0), 4) == 0.372
