@@ -1124,50 +1124,107 @@ __global__ __launch_bounds__(128) void bwd_lambda_kernel(BwdParams p, int D) {
 // the 256 threads owns a 4 x 4 patch; rows come through LDS in tiles of 64.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_lamfull_part_kernel(BwdParams p) {
-  constexpr int NB = D / 64;  // 64-wide blocks per side
+  // One workgroup forms the whole D x D partial sum of one head over one
+  // split of its (b, t) rows, so every row of y and x is read once.  Rows are
+  // staged 64 at a time in LDS; wave w owns the quadrant (w/2, w%2) and
+  // contracts over the rows on fp32 MFMA (16x16x4): A = the staged y columns
+  // of its row tiles, B = the staged x columns of its column tiles.  The next
+  // 64 rows are loaded into registers while the current ones are multiplied.
+  constexpr int LDP = D + 16;          // row stride (floats): 4 rows of 16 lanes hit distinct banks
+  constexpr int QPR = D / 4;           // float4 quads per row
+  constexpr int RPP = 256 / QPR;       // rows staged per pass of the workgroup
+  constexpr int NP = 64 / RPP;         // passes per 64-row tile
+  constexpr int TQ = D / 32;           // 16-wide tiles per side of a quadrant
   const int sp = blockIdx.x % kLamSplits;
-  const int blk = (blockIdx.x / kLamSplits) % (NB * NB);
-  const int h = blockIdx.x / (kLamSplits * NB * NB);
-  const int ib = blk / NB, jb = blk % NB;
+  const int h = blockIdx.x / kLamSplits;
   const int B = p.BH / p.H;
   const long long R = (long long)B * p.T;  // rows (b, t) of head h
   const long long r_lo = R * sp / kLamSplits, r_hi = R * (sp + 1) / kLamSplits;
-  __shared__ f32x4 Ys[64][16];
-  __shared__ f32x4 Xs[64][16];
-  const int tid = threadIdx.x;
-  const int pi = tid / 16, pj = tid % 16;  // patch rows 4pi.., cols 4pj..
-  f32x4 acc[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
-                  f32x4{0.f, 0.f, 0.f, 0.f}};
-  for (long long r0 = r_lo; r0 < r_hi; r0 += 64) {
-    // stage 64 rows: thread tid loads quads (tid % 16) of rows tid / 16 + 16 u
+  __shared__ __attribute__((aligned(16))) float Ys[64 * LDP];
+  __shared__ __attribute__((aligned(16))) float Xs[64 * LDP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tl = lane & 15, g = lane >> 4;
+  const int q = tid % QPR, rr0 = tid / QPR;
+  const int i0 = (wave >> 1) * (D / 2), j0 = (wave & 1) * (D / 2);
+
+  f32x4 yv[NP], xv[NP];
+  // rows r0 + o of the tile: (b, t) from one division per tile (uniform) and a
+  // 32-bit division of the tile offset, not a 64-bit one per row.  The scale
+  // nu is applied when the rows are stored to LDS, so the loads stay in flight
+  // during the products of the current tile.
+  float nv[NP];
+  auto load_rows = [&](long long r0) {
+    const long long b0 = r0 / p.T;
+    const int t0 = (int)(r0 - b0 * p.T);
+    const int rem = (int)min((long long)64, r_hi - r0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int rr = tid / 16 + 16 * u;
-      const long long r = r0 + rr;
-      f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f}, xv = yv;
-      if (r < r_hi) {
-        const int b = (int)(r / p.T), t = (int)(r % p.T);
-        const size_t row = (size_t)(b * p.H + h) * p.T + t;
-        yv = *reinterpret_cast<const f32x4*>(p.yn + row * D + 64 * ib + 4 * pj) * p.nu[row];
-        xv = *reinterpret_cast<const f32x4*>(p.x + row * D + 64 * jb + 4 * pj);
+    for (int u = 0; u < NP; ++u) {
+      const int o = rr0 + RPP * u;
+      yv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      xv[u] = yv[u];
+      nv[u] = 0.f;
+      if (o < rem) {
+        const unsigned tt = (unsigned)(t0 + o), db = tt / (unsigned)p.T;
+        const int t = (int)(tt - db * (unsigned)p.T);
+        const size_t row = ((size_t)(b0 + db) * p.H + h) * p.T + t;
+        yv[u] = *reinterpret_cast<const f32x4*>(p.yn + row * D + 4 * q);
+        xv[u] = *reinterpret_cast<const f32x4*>(p.x + row * D + 4 * q);
+        nv[u] = p.nu[row];
       }
-      Ys[rr][pj] = yv;
-      Xs[rr][pj] = xv;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int rr = 0; rr < 64; ++rr) {
-      const f32x4 yv = Ys[rr][pi];
-      const f32x4 xv = Xs[rr][pj];
+  };
+  f32x4 acc[TQ][TQ];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a] += yv[a] * xv;
+  for (int a = 0; a < TQ; ++a)
+#pragma unroll
+    for (int c = 0; c < TQ; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (r_lo < r_hi) load_rows(r_lo);
+  for (long long r0 = r_lo; r0 < r_hi; r0 += 64) {
+    __syncthreads();  // the previous tile's reads are done
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      *reinterpret_cast<f32x4*>(Ys + (rr0 + RPP * u) * LDP + 4 * q) = yv[u] * nv[u];
+      *reinterpret_cast<f32x4*>(Xs + (rr0 + RPP * u) * LDP + 4 * q) = xv[u];
     }
     __syncthreads();
+    if (r0 + 64 < r_hi) load_rows(r0 + 64);
+    // operands of step k4 + 1 are read from LDS while step k4's products issue
+    float a[TQ], b[TQ];
+#pragma unroll
+    for (int it = 0; it < TQ; ++it) a[it] = Ys[g * LDP + i0 + 16 * it + tl];
+#pragma unroll
+    for (int jt = 0; jt < TQ; ++jt) b[jt] = Xs[g * LDP + j0 + 16 * jt + tl];
+#pragma unroll
+    for (int k4 = 0; k4 < 16; ++k4) {
+      float an[TQ], bn[TQ];
+      if (k4 < 15) {
+        const int rk = (4 * (k4 + 1) + g) * LDP;
+#pragma unroll
+        for (int it = 0; it < TQ; ++it) an[it] = Ys[rk + i0 + 16 * it + tl];
+#pragma unroll
+        for (int jt = 0; jt < TQ; ++jt) bn[jt] = Xs[rk + j0 + 16 * jt + tl];
+      }
+#pragma unroll
+      for (int it = 0; it < TQ; ++it)
+#pragma unroll
+        for (int jt = 0; jt < TQ; ++jt) acc[it][jt] = mfma_f32(a[it], b[jt], acc[it][jt]);
+      if (k4 < 15) {
+#pragma unroll
+        for (int e = 0; e < TQ; ++e) {
+          a[e] = an[e];
+          b[e] = bn[e];
+        }
+      }
+    }
   }
   float* out = p.lam_full_part + ((size_t)h * kLamSplits + sp) * D * D;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-    *reinterpret_cast<f32x4*>(out + (size_t)(64 * ib + 4 * pi + a) * D + 64 * jb + 4 * pj) = -acc[a];
+  for (int it = 0; it < TQ; ++it)
+#pragma unroll
+    for (int jt = 0; jt < TQ; ++jt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[(size_t)(i0 + 16 * it + 4 * g + e) * D + j0 + 16 * jt + tl] = -acc[it][jt][e];
 }
 
 // dLambda[h] = sum of the splits' partial sums
@@ -1211,8 +1268,7 @@ hipError_t launch_bwd_d(int phase, const BwdParams& p, hipStream_t s) {
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       }
       if (p.lam_full) {
-        constexpr int NB = D / 64;
-        hipLaunchKernelGGL((bwd_lamfull_part_kernel<D>), dim3((unsigned)(p.H * NB * NB * kLamSplits)), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_lamfull_part_kernel<D>), dim3((unsigned)(p.H * kLamSplits)), dim3(256), 0,
                            s, p);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         const size_t n = (size_t)p.H * D * D;
