@@ -44,11 +44,6 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
-// Two bf16 values packed low-first into one dword.
-__device__ __forceinline__ uint32_t pack2(__bf16 lo, __bf16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
 // Sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
 // wave).  Every participating lane receives the bitwise-identical result.
 // Uses the gfx950 cross-row swaps: permlane16_swap(v, v) yields, in every

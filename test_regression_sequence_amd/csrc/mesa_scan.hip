@@ -92,6 +92,14 @@ struct ScanShape {
   static constexpr int SSB = 2 * (D / 8) + 4;
 };
 
+// Two floats rounded to bf16 (nearest even) and packed low-first into one
+// dword by one paired conversion (single conversions need a merge each).
+__device__ __forceinline__ uint32_t cvt_pack2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <bool BF16>
 struct Piece;
 template <>
@@ -416,11 +424,12 @@ __global__ __launch_bounds__((ScanShape<BF16, D, C, FULL>::THREADS)) void scan_k
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x0 = ww0 * bf16_to_f32(xp[q].a[e]), x1 = ww1 * bf16_to_f32(xp[q].b[e]);
-          const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
-          const __bf16 l0 = (__bf16)(x0 - (float)h0), l1 = (__bf16)(x1 - (float)h1);
+          // hi parts, then lo = x - hi rounded: two paired conversions
+          const uint32_t hp = cvt_pack2(x0, x1);
+          const uint32_t lp = cvt_pack2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xffff0000u));
           const int n = 8 * c8 + e;
-          *reinterpret_cast<uint32_t*>(XH + n * AS + 2 * jp) = pack2(h0, h1);
-          *reinterpret_cast<uint32_t*>(XL + n * AS + 2 * jp) = pack2(l0, l1);
+          *reinterpret_cast<uint32_t*>(XH + n * AS + 2 * jp) = hp;
+          *reinterpret_cast<uint32_t*>(XL + n * AS + 2 * jp) = lp;
         }
       }
 #pragma unroll
